@@ -1,0 +1,54 @@
+"""Scalar brute-force re-derivation of LLA latent decode, for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY: used by ``tests/`` to pin ``oracle/lla_oracle.py``.
+
+Written independently of the NumPy oracle and in a different form: plain Python
+floats and lists, RoPE as multiplication of the complex number x_2i + i x_2i+1 by
+exp(i p theta_i) (the complex form of the RoFormer rotation), a max-shifted softmax
+summed with ``math.fsum``, and the codec of "Looped Latent Attention" Section 3
+(Eqs. 2-3) written out element by element. Intended for n <= 8, d <= 8, r <= 8.
+"""
+
+from __future__ import annotations
+
+import cmath
+import math
+
+
+def _row_times_matT(c, w):
+    """c [r] times w^T where w is [d][r] -> [d]."""
+    return [math.fsum(c[k] * w[i][k] for k in range(len(c))) for i in range(len(w))]
+
+
+def brute_decode_one(c_k, c_v, w_up_k_t, mu_k_t, w_up_v_t, mu_v_t, q, base, scale):
+    """One (sequence, head, loop): c_k [n][r_k], c_v [n][r_v], W_up [d][r], mu [d],
+    q [d]. Returns the attention output [d] as a list of floats."""
+    n = len(c_k)
+    d = len(q)
+    if n == 0:
+        return [0.0] * d
+    scores = []
+    for j in range(n):
+        k = [a + b for a, b in zip(_row_times_matT(c_k[j], w_up_k_t), mu_k_t)]
+        s = 0.0
+        for i in range(d // 2):
+            theta = base ** (-(2.0 * i) / d)
+            z = complex(k[2 * i], k[2 * i + 1]) * cmath.exp(1j * (j * theta))
+            s += q[2 * i] * z.real + q[2 * i + 1] * z.imag
+        scores.append(scale * s)
+    m = max(scores)
+    e = [math.exp(s - m) for s in scores]
+    tot = math.fsum(e)
+    out = [0.0] * d
+    for j in range(n):
+        v = [a + b for a, b in zip(_row_times_matT(c_v[j], w_up_v_t), mu_v_t)]
+        w = e[j] / tot
+        for i in range(d):
+            out[i] += w * v[i]
+    return out
+
+
+def brute_encode_one(x, mu, w_down):
+    """Eq. 2 for one vector: x [T*d], mu [T*d], W_down [T*d][r] -> c [r]."""
+    r = len(w_down[0])
+    return [math.fsum((x[i] - mu[i]) * w_down[i][k] for i in range(len(x))) for k in range(r)]

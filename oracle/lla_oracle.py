@@ -1,0 +1,255 @@
+"""fp64 CPU oracle for the Looped Latent Attention (LLA) latent-store decode path.
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, plainly written definition that
+the HIP path is checked against. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it. It shares no code with the HIP
+path and imports nothing from ``latent_decode_attention_lla_amd``.
+
+Source: "Looped Latent Attention: Cross-Loop KV Compression for Looped Transformers"
+(arXiv 2607.15456v2), Section 3 (Eqs. 1-4, "RoPE and reconstruction", "The LLA-2D
+variant", "Initialization and conversion"), Section 7 and Appendix J.
+
+Everything is computed in float64 with nothing factored: the keys and values of every
+cached token are rebuilt explicitly, RoPE is applied to the rebuilt keys, and textbook
+softmax attention follows. Readings taken where the pages are silent:
+
+* RoPE pairs are interleaved, (2i, 2i+1), rotated counter-clockwise by p*theta_i with
+  theta_i = base**(-2i/d) (RoFormer, which the LLA paper cites for RoPE).
+* A cached token's position is its slot index j in [0, n).
+* Queries arrive already rotated (the model rotates q as usual); only keys rebuilt
+  from latents are rotated here.
+* Score scale defaults to 1/sqrt(d_head).
+* Attention over an empty context returns zeros.
+* LLA-2D stacks its input (t, h, d) with the loop index outermost.
+
+Parity: every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms
+printed on the pages, the full-rank special case against textbook attention, RoPE
+invariants, softmax special cases, a scalar brute-force re-derivation, the LLA-2D
+block-diagonal reduction and the Eckart-Young property of the SVD initialisation).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "compression_ratio",
+    "teacher_scalars_per_token_layer",
+    "latent_scalars_per_token_layer",
+    "cache_bytes_per_token",
+    "stack_loops",
+    "encode",
+    "reconstruct",
+    "rope_theta",
+    "apply_rope",
+    "softmax",
+    "attention",
+    "decode",
+    "svd_init",
+    "round_bf16",
+    "encode_stored",
+]
+
+
+# ---------------------------------------------------------------------------
+# Closed forms: Section 3, Eq. 4 and the paragraph before it; Section 7, Table 5.
+# ---------------------------------------------------------------------------
+
+def teacher_scalars_per_token_layer(T: int, H: int, d_head: int) -> int:
+    """Uncompressed loop-indexed cache: K and V for every loop and head (Section 3,
+    "Teacher cache")."""
+    return 2 * T * H * d_head
+
+
+def latent_scalars_per_token_layer(H: int, r_k: int, r_v: int, variant: str = "per_head") -> int:
+    """Latent cache: (r_k + r_v) per head (Section 3, "Cross-loop codec"), or one
+    shared latent of r_k + r_v for LLA-2D (Section 3, "The LLA-2D variant")."""
+    if variant == "per_head":
+        return (r_k + r_v) * H
+    if variant == "2d":
+        return r_k + r_v
+    raise ValueError(variant)
+
+
+def compression_ratio(T: int, d_head: int, r_k: int, r_v: int, H: int = 1,
+                      variant: str = "per_head") -> float:
+    """rho = teacher scalars / latent scalars (Section 3, Eq. 4). For the per-head
+    codec H cancels and rho = 2 T d_head / (r_k + r_v)."""
+    return (teacher_scalars_per_token_layer(T, H, d_head)
+            / latent_scalars_per_token_layer(H, r_k, r_v, variant))
+
+
+def cache_bytes_per_token(D: int, H: int, r_k: int, r_v: int, bytes_per_scalar: int,
+                          variant: str = "per_head") -> int:
+    """Bytes one token occupies across all D layers (Section 7, Table 5 row
+    "KV / token")."""
+    return D * latent_scalars_per_token_layer(H, r_k, r_v, variant) * bytes_per_scalar
+
+
+# ---------------------------------------------------------------------------
+# Codec: Section 3, Eqs. 1-3.
+# ---------------------------------------------------------------------------
+
+def stack_loops(x_loops: np.ndarray) -> np.ndarray:
+    """Eq. 1: stack the T per-loop vectors [..., T, d] into x = [x_1; ...; x_T]
+    of length T*d, loop index outermost."""
+    x_loops = np.asarray(x_loops, dtype=np.float64)
+    return x_loops.reshape(*x_loops.shape[:-2], x_loops.shape[-2] * x_loops.shape[-1])
+
+
+def encode(x: np.ndarray, mu: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """Eq. 2: c = (x - mu) W_down. x: [..., T*d], mu: [T*d], W_down: [T*d, r]."""
+    x = np.asarray(x, dtype=np.float64)
+    return (x - np.asarray(mu, dtype=np.float64)) @ np.asarray(w_down, dtype=np.float64)
+
+
+def reconstruct(c: np.ndarray, w_up_t: np.ndarray, mu_t: np.ndarray) -> np.ndarray:
+    """Eq. 3: x_hat_t = c W_up,t^T + mu_t (row-vector convention). c: [..., r],
+    W_up,t: [d, r], mu_t: [d]."""
+    c = np.asarray(c, dtype=np.float64)
+    return c @ np.asarray(w_up_t, dtype=np.float64).T + np.asarray(mu_t, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# RoPE after reconstruction: Section 3, "RoPE and reconstruction".
+# ---------------------------------------------------------------------------
+
+def rope_theta(d: int, base: float) -> np.ndarray:
+    """theta_i = base^(-2i/d), i = 0 .. d/2-1 (RoFormer frequencies)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * i / d)
+
+
+def apply_rope(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarray:
+    """Rotate each interleaved pair (x_2i, x_2i+1) of x [..., n, d] by angle
+    p * theta_i, p = positions[n]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    phi = np.asarray(positions, dtype=np.float64)[:, None] * rope_theta(d, base)[None, :]
+    cos, sin = np.cos(phi), np.sin(phi)
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x0 * cos - x1 * sin
+    y[..., 1::2] = x0 * sin + x1 * cos
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Attention itself is unchanged by LLA (Section 3, Figure 1 caption).
+# ---------------------------------------------------------------------------
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    """Two-pass softmax over the last axis."""
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Textbook single-query attention: q [d], k [n, d], v [n, d_v] -> [d_v].
+    An empty context (n == 0) returns zeros."""
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[-1], dtype=np.float64)
+    a = softmax(scale * (k @ q))
+    return a @ v
+
+
+# ---------------------------------------------------------------------------
+# Latent-store decode: Section 7 ("caches only the latent and reconstructs on read")
+# with the codec of Eqs. 2-3, RoPE after reconstruction, and LLA-2D.
+# ---------------------------------------------------------------------------
+
+def _mu_slice(mu: np.ndarray, variant: str, t: int, h: int, H: int, d: int) -> np.ndarray:
+    """mu_t for one head. Per-head: mu[h] has length T*d, loop t is its t-th block.
+    LLA-2D: mu[0] has length T*H*d stacked (t, h, d)."""
+    if variant == "per_head":
+        return mu[h, t * d:(t + 1) * d]
+    return mu[0, (t * H + h) * d:(t * H + h + 1) * d]
+
+
+def decode(c_k: np.ndarray, c_v: np.ndarray,
+           w_up_k: np.ndarray, mu_k: np.ndarray,
+           w_up_v: np.ndarray, mu_v: np.ndarray,
+           q: np.ndarray, loop_begin: int = 0,
+           ctx_lens=None, rope_base: float = 10000.0, scale: float | None = None,
+           variant: str = "per_head") -> np.ndarray:
+    """Decode attention for one layer over the latent cache.
+
+    c_k [B, Hc, n, r_k], c_v [B, Hc, n, r_v] : cached latents (Hc = H per head, 1 for 2D)
+    w_up_k [T, H, d, r_k], w_up_v [T, H, d, r_v] : loop-specific up-projections
+    mu_k, mu_v [Hc, T*d] (per head) or [1, T*H*d] (2D) : calibration means
+    q [B, H, L, d] : post-RoPE queries for loops loop_begin .. loop_begin+L-1
+    ctx_lens [B] or None : tokens 0 .. ctx_lens[b]-1 are attended (default all n)
+    returns out [B, H, L, d] float64
+    """
+    c_k = np.asarray(c_k)
+    c_v = np.asarray(c_v)
+    B, Hc, n, _ = c_k.shape
+    L = q.shape[2]
+    H = q.shape[1]
+    d = q.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if ctx_lens is None:
+        ctx_lens = [n] * B
+    out = np.zeros((B, H, L, d), dtype=np.float64)
+    for b in range(B):
+        nb = int(ctx_lens[b])
+        pos = np.arange(nb)
+        for h in range(H):
+            hc = h if variant == "per_head" else 0
+            ck = np.asarray(c_k[b, hc, :nb], dtype=np.float64)
+            cv = np.asarray(c_v[b, hc, :nb], dtype=np.float64)
+            for li in range(L):
+                t = loop_begin + li
+                k_hat = reconstruct(ck, w_up_k[t, h], _mu_slice(mu_k, variant, t, h, H, d))
+                v_hat = reconstruct(cv, w_up_v[t, h], _mu_slice(mu_v, variant, t, h, H, d))
+                k_rot = apply_rope(k_hat, pos, rope_base)
+                out[b, h, li] = attention(np.asarray(q[b, h, li], dtype=np.float64),
+                                          k_rot, v_hat, scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# SVD initialisation: Section 3, "Initialization and conversion"; Appendix A.
+# ---------------------------------------------------------------------------
+
+def svd_init(x: np.ndarray, r: int, T: int, d: int):
+    """Codec from calibration activations x [N, T*d] (stacked loops, pre-RoPE):
+    centre by the per-loop mean, take the top-r right singular vectors of the centred
+    stacked-loop matrix as W_down [T*d, r]; the initial W_up,t are its loop slices
+    [d, r]. Returns (mu [T*d], W_down, W_up [T, d, r])."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=0)
+    _, _, vh = np.linalg.svd(x - mu, full_matrices=False)
+    w_down = vh[:r].T.copy()
+    w_up = np.stack([w_down[t * d:(t + 1) * d, :] for t in range(T)])
+    return mu, w_down, w_up
+
+
+# ---------------------------------------------------------------------------
+# Storage rounding (latents are stored in the cache dtype).
+# ---------------------------------------------------------------------------
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (8 significant bits), ties to
+    even, returned as float64. Normal range only (no overflow or bf16 subnormals are
+    generated by the tests)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def encode_stored(x: np.ndarray, mu: np.ndarray, w_down: np.ndarray, dtype: str) -> np.ndarray:
+    """Eq. 2 followed by rounding to the storage dtype ("f32" or "bf16"), both from
+    the exact fp64 value."""
+    c = encode(x, mu, w_down)
+    if dtype == "bf16":
+        return round_bf16(c)
+    if dtype == "f32":
+        return c.astype(np.float32).astype(np.float64)
+    raise ValueError(dtype)

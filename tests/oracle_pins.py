@@ -1,0 +1,375 @@
+"""Pins for the fp64 oracle: each check ties ``oracle/lla_oracle.py`` to something other
+than itself (values printed on the pages, closed forms, a textbook routine, invariants,
+a scalar brute force). Each returns the largest deviation it saw (0 when exact) so
+that the mutation test can show that a planted mistake moves at least one of them.
+
+All references are to "Looped Latent Attention: Cross-Loop KV Compression for Looped
+Transformers" (arXiv 2607.15456v2) unless another page is named.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import lla_oracle as O
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _orthonormal(n, r, seed):
+    a = _rng(seed).standard_normal((n, r))
+    q, rr = np.linalg.qr(a)
+    return q * np.sign(np.diag(rr))[None, :]
+
+
+# ---------------------------------------------------------------------------
+# Closed forms printed on the pages (Eq. 4, Table 5, Table 8, Table 3, slides).
+# ---------------------------------------------------------------------------
+
+def pin_closed_forms() -> float:
+    g = _load("compression_closed_forms.json")
+    err = 0.0
+    w = g["worked_example"]
+    err = max(err, abs(O.compression_ratio(w["T"], w["d_head"], w["r_k"], w["r_v"]) - w["rho"]))
+    err = max(err, abs(O.teacher_scalars_per_token_layer(w["T"], 1, w["d_head"]) - w["numerator"]))
+    err = max(err, abs(O.latent_scalars_per_token_layer(1, w["r_k"], w["r_v"]) - w["denominator"]))
+    for r_k, r_v, rho in g["table8_ranks"]["rows"]:
+        got = O.compression_ratio(4, 128, r_k, r_v)
+        err = max(err, abs(round(got, 2) - rho))
+    t5 = g["table5_memory"]
+    H, d, T, bps = t5["H"], t5["d_head"], t5["T"], t5["bytes_per_scalar"]
+    for D, key in ((24, "kv_per_token_kib_1p4b"), (48, "kv_per_token_kib_2p6b")):
+        tab = t5[key]
+        teacher = D * O.teacher_scalars_per_token_layer(T, H, d) * bps / 1024
+        err = max(err, abs(teacher - tab["teacher"]))
+        err = max(err, abs(O.cache_bytes_per_token(D, H, 96, 160, bps) / 1024 - tab["lla_4x"]))
+        err = max(err, abs(O.cache_bytes_per_token(D, H, 16, 32, bps) / 1024 - tab["lla_21x"]))
+    gib = t5["kv_1m_context_gib_1p4b"]
+    err = max(err, abs(O.cache_bytes_per_token(24, H, 96, 160, bps) * 2**20 / 2**30 - gib["lla_4x"]))
+    err = max(err, abs(O.cache_bytes_per_token(24, H, 16, 32, bps) * 2**20 / 2**30 - gib["lla_21x"]))
+    err = max(err, abs(round(O.compression_ratio(4, 128, 16, 32), 1) - t5["lla_21x_rho_printed"]))
+    ev = g["eviction_budget"]
+    err = max(err, abs(O.cache_bytes_per_token(24, H, 16, 32, bps) * ev["kept_tokens"] / 2**20
+                       - ev["mib_total"]))
+    # Huginn (Table 3): every printed (rho, r_k, r_v) implies the same d_head via Eq. 4.
+    hu = g["huginn_table3"]
+    implied = [rho * (rk + rv) / (2 * hu["T"]) for rho, rk, rv in hu["rows"]]
+    for rho, rk, rv in hu["rows"]:
+        err = max(err, abs(O.compression_ratio(hu["T"], implied[0], rk, rv) - rho))
+    return err
+
+
+# ---------------------------------------------------------------------------
+# RoPE: the RoFormer rotation, applied after reconstruction (Section 3).
+# ---------------------------------------------------------------------------
+
+def pin_rope() -> float:
+    err = 0.0
+    # theta_i = base^(-2i/d): d=4, base=10000 gives (1, 1/100).
+    err = max(err, float(np.max(np.abs(O.rope_theta(4, 10000.0) - np.array([1.0, 0.01])))))
+    # d=2 has theta_0 = 1 for any base: a counter-clockwise rotation by the position.
+    for p in (0, 1, 3, 17):
+        y = O.apply_rope(np.array([[1.0, 0.0], [0.0, 1.0]])[None], np.array([p]), 500.0)[0]
+        err = max(err, abs(y[0, 0] - math.cos(p)), abs(y[0, 1] - math.sin(p)),
+                  abs(y[1, 0] + math.sin(p)), abs(y[1, 1] - math.cos(p)))
+    # Interleaved pairs: dims (0, 1) form pair 0 at theta_0 = 1 and dims (2, 3) pair 1.
+    y = O.apply_rope(np.array([[[0.0, 0.0, 1.0, 0.0]]]), np.array([5]), 10000.0)[0, 0]
+    err = max(err, abs(y[0]), abs(y[1]), abs(y[2] - math.cos(0.05)), abs(y[3] - math.sin(0.05)))
+    # Position 0 is the identity, norms are preserved, and scores depend on the
+    # position difference only.
+    rng = _rng(3)
+    x = rng.standard_normal((1, 6, 16))
+    err = max(err, float(np.max(np.abs(O.apply_rope(x, np.zeros(6), 10000.0) - x))))
+    pos = np.array([0, 1, 7, 100, 2047, 4095])
+    y = O.apply_rope(x, pos, 10000.0)
+    err = max(err, float(np.max(np.abs(np.linalg.norm(y, axis=-1) - np.linalg.norm(x, axis=-1)))))
+    q, k = rng.standard_normal(16), rng.standard_normal(16)
+    for a, b, shift in ((3, 10, 55), (0, 4000, 77), (120, 7, 1000)):
+        s1 = O.apply_rope(q[None, None], np.array([a]), 10000.0)[0, 0] @ \
+            O.apply_rope(k[None, None], np.array([b]), 10000.0)[0, 0]
+        s2 = O.apply_rope(q[None, None], np.array([a + shift]), 10000.0)[0, 0] @ \
+            O.apply_rope(k[None, None], np.array([b + shift]), 10000.0)[0, 0]
+        err = max(err, abs(s1 - s2))
+    return err
+
+
+# ---------------------------------------------------------------------------
+# Codec round trips and the SVD initialisation (Section 3, Eqs. 2-3).
+# ---------------------------------------------------------------------------
+
+def pin_codec() -> float:
+    err = 0.0
+    T, d = 2, 4
+    rng = _rng(11)
+    x = rng.standard_normal((9, T * d))
+    mu = rng.standard_normal(T * d)
+    # Full rank, orthonormal W_down, W_up,t its loop slices: exact round trip.
+    w = _orthonormal(T * d, T * d, 5)
+    c = O.encode(x, mu, w)
+    for t in range(T):
+        xt = O.reconstruct(c, w[t * d:(t + 1) * d], mu[t * d:(t + 1) * d])
+        err = max(err, float(np.max(np.abs(xt - x[:, t * d:(t + 1) * d]))))
+    # Scalar brute force of Eq. 2.
+    wl = _orthonormal(T * d, 3, 6)
+    cb = [brute.brute_encode_one(list(xi), list(mu), wl.tolist()) for xi in x]
+    err = max(err, float(np.max(np.abs(O.encode(x, mu, wl) - np.array(cb)))))
+    # Low rank with tied weights: reconstruction is the orthogonal projection of x - mu
+    # onto span(W_down): idempotent, residual orthogonal to the span.
+    c = O.encode(x, mu, wl)
+    xh = np.concatenate([O.reconstruct(c, wl[t * d:(t + 1) * d], mu[t * d:(t + 1) * d])
+                         for t in range(T)], axis=1)
+    c2 = O.encode(xh, mu, wl)
+    err = max(err, float(np.max(np.abs(c2 - c))))
+    err = max(err, float(np.max(np.abs((x - xh) @ wl))))
+    return err
+
+
+def pin_svd_init() -> float:
+    err = 0.0
+    T, d, r = 3, 4, 5
+    rng = _rng(21)
+    n = 200
+    base = rng.standard_normal((n, r)) @ rng.standard_normal((r, T * d))
+    mu_true = rng.standard_normal(T * d)
+    # Data of exact rank r after centring is reproduced exactly.
+    x = base - base.mean(axis=0) + mu_true
+    mu, wd, wu = O.svd_init(x, r, T, d)
+    err = max(err, float(np.max(np.abs(mu - x.mean(axis=0)))))
+    c = O.encode(x, mu, wd)
+    for t in range(T):
+        xt = O.reconstruct(c, wu[t], mu[t * d:(t + 1) * d])
+        err = max(err, float(np.max(np.abs(xt - x[:, t * d:(t + 1) * d]))))
+        err = max(err, float(np.max(np.abs(wu[t] - wd[t * d:(t + 1) * d]))))
+    # Eckart-Young: with noise added, the residual energy equals the sum of the
+    # discarded eigenvalues of the centred scatter matrix (computed with eigvalsh).
+    xn = x + 0.3 * rng.standard_normal(x.shape)
+    mu, wd, wu = O.svd_init(xn, r, T, d)
+    c = O.encode(xn, mu, wd)
+    xh = np.concatenate([O.reconstruct(c, wu[t], mu[t * d:(t + 1) * d]) for t in range(T)], 1)
+    xc = xn - xn.mean(axis=0)
+    ev = np.sort(np.linalg.eigvalsh(xc.T @ xc))[::-1]
+    resid = float(np.sum((xn - xh) ** 2))
+    err = max(err, abs(resid - float(np.sum(ev[r:]))) / max(1.0, resid))
+    return err
+
+
+# ---------------------------------------------------------------------------
+# Whole decode: full-rank special case against textbook attention, special cases,
+# the scalar brute force, and the LLA-2D reduction.
+# ---------------------------------------------------------------------------
+
+def _textbook_rope_complex(x: torch.Tensor, pos: torch.Tensor, base: float) -> torch.Tensor:
+    """RoPE as complex multiplication: pairs (x_2i, x_2i+1) -> x_2i + i x_2i+1 times
+    exp(i p theta_i)."""
+    d = x.shape[-1]
+    theta = base ** (-(torch.arange(0, d, 2, dtype=torch.float64)) / d)
+    rot = torch.polar(torch.ones(pos.shape[0], d // 2, dtype=torch.float64),
+                      pos[:, None].double() * theta[None, :])
+    z = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous())
+    return torch.view_as_real(z * rot).reshape(x.shape)
+
+
+def pin_full_rank_textbook() -> float:
+    """r = T*d, orthonormal W_down, W_up,t its loop slices: the latent decode must equal
+    ordinary attention on the original per-loop keys and values (torch SDPA, fp64)."""
+    T, H, d, n, B = 4, 2, 8, 13, 2
+    rng = _rng(31)
+    xk = rng.standard_normal((B, H, n, T, d))
+    xv = rng.standard_normal((B, H, n, T, d))
+    q = rng.standard_normal((B, H, T, d))
+    r = T * d
+    ck = np.empty((B, H, n, r))
+    cv = np.empty((B, H, n, r))
+    wuk = np.empty((T, H, d, r))
+    wuv = np.empty((T, H, d, r))
+    muk = rng.standard_normal((H, T * d))
+    muv = rng.standard_normal((H, T * d))
+    for h in range(H):
+        wk = _orthonormal(r, r, 100 + h)
+        wv = _orthonormal(r, r, 200 + h)
+        ck[:, h] = O.encode(O.stack_loops(xk[:, h]), muk[h], wk)
+        cv[:, h] = O.encode(O.stack_loops(xv[:, h]), muv[h], wv)
+        for t in range(T):
+            wuk[t, h] = wk[t * d:(t + 1) * d]
+            wuv[t, h] = wv[t * d:(t + 1) * d]
+    got = O.decode(ck, cv, wuk, muk, wuv, muv, q, 0, None, 10000.0)
+    pos = torch.arange(n)
+    err = 0.0
+    for t in range(T):
+        k = _textbook_rope_complex(torch.from_numpy(xk[:, :, :, t]), pos, 10000.0)
+        v = torch.from_numpy(xv[:, :, :, t])
+        qt = torch.from_numpy(q[:, :, t])[:, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, k, v)[:, :, 0]
+        err = max(err, float(np.max(np.abs(got[:, :, t] - ref.numpy()))))
+    return err
+
+
+def _tiny(seed, T=2, H=2, d=4, n=5, r_k=3, r_v=4, B=2, variant="per_head"):
+    rng = _rng(seed)
+    Hc = H if variant == "per_head" else 1
+    din = d if variant == "per_head" else H * d
+    return dict(
+        c_k=rng.standard_normal((B, Hc, n, r_k)),
+        c_v=rng.standard_normal((B, Hc, n, r_v)),
+        w_up_k=rng.standard_normal((T, H, d, r_k)) / math.sqrt(r_k),
+        mu_k=rng.standard_normal((Hc, T * din)) * 0.3,
+        w_up_v=rng.standard_normal((T, H, d, r_v)) / math.sqrt(r_v),
+        mu_v=rng.standard_normal((Hc, T * din)) * 0.3,
+        q=rng.standard_normal((B, H, T, d)),
+    )
+
+
+def pin_brute_force() -> float:
+    err = 0.0
+    for variant, seed, base, ctx in (("per_head", 41, 10000.0, [5, 3]), ("per_head", 42, 7.0, [5, 5]),
+                                     ("2d", 43, 100.0, [4, 5])):
+        a = _tiny(seed, variant=variant)
+        T, H, d = a["w_up_k"].shape[0], a["w_up_k"].shape[1], a["w_up_k"].shape[2]
+        got = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"],
+                       a["q"], 0, ctx, base, None, variant)
+        for b in range(a["q"].shape[0]):
+            for h in range(H):
+                hc = h if variant == "per_head" else 0
+                for t in range(T):
+                    if variant == "per_head":
+                        mk = a["mu_k"][h][t * d:(t + 1) * d]
+                        mv = a["mu_v"][h][t * d:(t + 1) * d]
+                    else:
+                        mk = a["mu_k"][0][(t * H + h) * d:(t * H + h + 1) * d]
+                        mv = a["mu_v"][0][(t * H + h) * d:(t * H + h + 1) * d]
+                    ref = brute.brute_decode_one(
+                        a["c_k"][b, hc, :ctx[b]].tolist(), a["c_v"][b, hc, :ctx[b]].tolist(),
+                        a["w_up_k"][t, h].tolist(), list(mk), a["w_up_v"][t, h].tolist(), list(mv),
+                        list(a["q"][b, h, t]), base, 1.0 / math.sqrt(d))
+                    err = max(err, float(np.max(np.abs(got[b, h, t] - np.array(ref)))))
+    return err
+
+
+def pin_special_cases() -> float:
+    err = 0.0
+    a = _tiny(51, n=6)
+    T, H, d = 2, 2, 4
+    # q = 0: uniform weights, so the output is the mean latent pushed through W_up,v
+    # plus mu_v (the V-side identity of Appendix J, "Absorbed attention").
+    q0 = np.zeros_like(a["q"])
+    got = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"], q0)
+    for b in range(2):
+        for h in range(H):
+            for t in range(T):
+                ref = a["c_v"][b, h].mean(axis=0) @ a["w_up_v"][t, h].T + a["mu_v"][h, t * d:(t + 1) * d]
+                err = max(err, float(np.max(np.abs(got[b, h, t] - ref))))
+    # n = 1: the output is that token's rebuilt value, whatever the query.
+    got = O.decode(a["c_k"][:, :, :1], a["c_v"][:, :, :1], a["w_up_k"], a["mu_k"],
+                   a["w_up_v"], a["mu_v"], a["q"] * 50.0)
+    for b in range(2):
+        for h in range(H):
+            for t in range(T):
+                ref = a["c_v"][b, h, 0] @ a["w_up_v"][t, h].T + a["mu_v"][h, t * d:(t + 1) * d]
+                err = max(err, float(np.max(np.abs(got[b, h, t] - ref))))
+    # Empty context: zeros (the reading taken for attention over no tokens).
+    got = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"], a["q"],
+                   0, [0, 6])
+    err = max(err, float(np.max(np.abs(got[0]))))
+    # Loop offset: decoding loops 1.. with loop_begin=1 equals the same slice of a
+    # decode over all loops.
+    full = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"], a["q"])
+    part = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"],
+                    a["q"][:, :, 1:], 1)
+    err = max(err, float(np.max(np.abs(full[:, :, 1:] - part))))
+    return err
+
+
+def pin_lla2d_block_diagonal() -> float:
+    """LLA-2D with a block-diagonal codec (head h owns latent columns h*r_h ..) must equal
+    per-head LLA with rank r_h (Section 3, "The LLA-2D variant": one latent per token
+    and layer reconstructing all heads). Covers both encode and decode."""
+    T, H, d, n, B, rk, rv = 2, 3, 4, 6, 2, 2, 3
+    rng = _rng(61)
+    xk = rng.standard_normal((B, n, H, T, d))
+    xv = rng.standard_normal((B, n, H, T, d))
+    q = rng.standard_normal((B, H, T, d))
+    wdk = rng.standard_normal((H, T * d, rk))
+    wdv = rng.standard_normal((H, T * d, rv))
+    muk = rng.standard_normal((H, T * d))
+    muv = rng.standard_normal((H, T * d))
+    wuk = rng.standard_normal((T, H, d, rk))
+    wuv = rng.standard_normal((T, H, d, rv))
+    # per-head latents
+    ck = np.stack([O.encode(xk[:, :, h].reshape(B, n, T * d), muk[h], wdk[h]) for h in range(H)], 1)
+    cv = np.stack([O.encode(xv[:, :, h].reshape(B, n, T * d), muv[h], wdv[h]) for h in range(H)], 1)
+    ref = O.decode(ck, cv, wuk, muk, wuv, muv, q, 0, None, 10000.0)
+    # 2D: input stacked (t, h, d) with t outermost.
+    x2k = np.transpose(xk, (0, 1, 3, 2, 4)).reshape(B, n, T * H * d)
+    x2v = np.transpose(xv, (0, 1, 3, 2, 4)).reshape(B, n, T * H * d)
+
+    def blockdiag(wd, r):
+        out = np.zeros((T * H * d, H * r))
+        for h in range(H):
+            for t in range(T):
+                out[(t * H + h) * d:(t * H + h + 1) * d, h * r:(h + 1) * r] = wd[h, t * d:(t + 1) * d]
+        return out
+
+    def restack(mu):
+        out = np.zeros(T * H * d)
+        for h in range(H):
+            for t in range(T):
+                out[(t * H + h) * d:(t * H + h + 1) * d] = mu[h, t * d:(t + 1) * d]
+        return out
+
+    def upembed(wu, r):
+        out = np.zeros((T, H, d, H * r))
+        for h in range(H):
+            out[:, h, :, h * r:(h + 1) * r] = wu[:, h]
+        return out
+
+    mu2k, mu2v = restack(muk), restack(muv)
+    c2k = O.encode(x2k, mu2k, blockdiag(wdk, rk))[:, None]
+    c2v = O.encode(x2v, mu2v, blockdiag(wdv, rv))[:, None]
+    err = float(np.max(np.abs(c2k[:, 0].reshape(B, n, H, rk) - np.transpose(ck, (0, 2, 1, 3)))))
+    got = O.decode(c2k, c2v, upembed(wuk, rk), mu2k[None], upembed(wuv, rv), mu2v[None], q, 0,
+                   None, 10000.0, None, "2d")
+    return max(err, float(np.max(np.abs(got - ref))))
+
+
+def pin_round_bf16() -> float:
+    """Round-to-nearest-even to 8 significant bits, checked against torch's float32 ->
+    bfloat16 conversion on values exact in float32, and on explicit ties."""
+    rng = _rng(71)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    err = float(np.max(np.abs(O.round_bf16(x.astype(np.float64)) - ref) / np.abs(ref)))
+    # Explicit ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 (goes to 1, the even
+    # mantissa); 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6 (goes to 1 + 2^-6);
+    # 0.5 + 3*2^-9 lies halfway between 0.5 + 2^-8 and 0.5 + 2^-7 (goes to 0.5 + 2^-7).
+    ties = np.array([1 + 2.0**-8, 1 + 3 * 2.0**-8, -(1 + 2.0**-8), 0.5 + 3 * 2.0**-9])
+    want = np.array([1.0, 1 + 2.0**-6, -1.0, 0.5 + 2.0**-7])
+    err = max(err, float(np.max(np.abs(O.round_bf16(ties) - want))))
+    return err
+
+
+ALL_PINS = {
+    "closed_forms": (pin_closed_forms, 1e-9),
+    "rope": (pin_rope, 1e-12),
+    "codec": (pin_codec, 1e-12),
+    "svd_init": (pin_svd_init, 1e-9),
+    "full_rank_textbook": (pin_full_rank_textbook, 1e-12),
+    "brute_force": (pin_brute_force, 1e-12),
+    "special_cases": (pin_special_cases, 1e-12),
+    "lla2d_block_diagonal": (pin_lla2d_block_diagonal, 1e-12),
+    "round_bf16": (pin_round_bf16, 0.0),
+}

@@ -1,0 +1,122 @@
+"""The oracle against its pins, and a mutation check: a plausible mistake planted in
+the oracle (on the CPU) must move at least one pin past its tolerance."""
+
+import numpy as np
+import pytest
+
+from oracle import lla_oracle as O
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("name", list(P.ALL_PINS))
+def test_pin(name):
+    fn, tol = P.ALL_PINS[name]
+    err = fn()
+    assert err <= tol, f"pin {name}: deviation {err} > {tol}"
+
+
+def _mut_rope_sign(x, positions, base):
+    return _ORIG["apply_rope"](x, -np.asarray(positions), base)
+
+
+def _mut_rope_halfsplit(x, positions, base):
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    phi = np.asarray(positions, dtype=np.float64)[:, None] * O.rope_theta(d, base)[None, :]
+    c, s = np.cos(phi), np.sin(phi)
+    a, b = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def _mut_theta(d, base):
+    i = np.arange(d // 2, dtype=np.float64)
+    return np.power(np.float64(base), -i / d)
+
+
+def _mut_recon_no_mu(c, w_up_t, mu_t):
+    return np.asarray(c, dtype=np.float64) @ np.asarray(w_up_t, dtype=np.float64).T
+
+
+def _mut_recon_transposed_pairs(c, w_up_t, mu_t):
+    out = _ORIG["reconstruct"](c, w_up_t, mu_t)
+    d = out.shape[-1]
+    return out.reshape(*out.shape[:-1], d // 2, 2)[..., ::-1].reshape(out.shape)
+
+
+def _mut_encode_no_center(x, mu, w_down):
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w_down, dtype=np.float64)
+
+
+def _mut_attention_no_scale(q, k, v, scale):
+    return _ORIG["attention"](q, k, v, 1.0)
+
+
+def _mut_attention_softmax_over_wrong_axis(q, k, v, scale):
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[-1])
+    s = scale * (k @ q)
+    a = np.exp(s) / np.exp(s).sum() if s.size < 2 else np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+    return a[::-1] @ v
+
+
+def _mut_mu_slice_2d_head_major(mu, variant, t, h, H, d):
+    if variant == "per_head":
+        return mu[h, t * d:(t + 1) * d]
+    T = mu.shape[1] // (H * d)
+    return mu[0, (h * T + t) * d:(h * T + t + 1) * d]
+
+
+def _mut_mu_slice_wrong_loop(mu, variant, t, h, H, d):
+    T = mu.shape[1] // (d if variant == "per_head" else H * d)
+    return _ORIG["_mu_slice"](mu, variant, (t + 1) % T, h, H, d)
+
+
+def _mut_svd_no_center(x, r, T, d):
+    x = np.asarray(x, dtype=np.float64)
+    _, _, vh = np.linalg.svd(x, full_matrices=False)
+    w = vh[:r].T.copy()
+    return x.mean(axis=0), w, np.stack([w[t * d:(t + 1) * d] for t in range(T)])
+
+
+def _mut_ratio_no_two(T, d_head, r_k, r_v, H=1, variant="per_head"):
+    return T * d_head / (r_k + r_v)
+
+
+def _mut_round_truncate(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.trunc(m * 256.0), e - 8)
+
+
+_ORIG = {name: getattr(O, name) for name in
+         ("apply_rope", "reconstruct", "attention", "_mu_slice", "rope_theta")}
+
+MUTANTS = {
+    "rope_sign": ("apply_rope", _mut_rope_sign),
+    "rope_halfsplit": ("apply_rope", _mut_rope_halfsplit),
+    "rope_theta_exponent": ("rope_theta", _mut_theta),
+    "reconstruct_drops_mu": ("reconstruct", _mut_recon_no_mu),
+    "reconstruct_swaps_pair": ("reconstruct", _mut_recon_transposed_pairs),
+    "encode_no_centering": ("encode", _mut_encode_no_center),
+    "attention_no_scale": ("attention", _mut_attention_no_scale),
+    "attention_reversed_weights": ("attention", _mut_attention_softmax_over_wrong_axis),
+    "mu_2d_head_major": ("_mu_slice", _mut_mu_slice_2d_head_major),
+    "mu_wrong_loop": ("_mu_slice", _mut_mu_slice_wrong_loop),
+    "svd_no_centering": ("svd_init", _mut_svd_no_center),
+    "rho_missing_factor_two": ("compression_ratio", _mut_ratio_no_two),
+    "bf16_truncates": ("round_bf16", _mut_round_truncate),
+}
+
+
+@pytest.mark.parametrize("mutant", list(MUTANTS))
+def test_planted_mistake_is_caught(mutant, monkeypatch):
+    attr, fn = MUTANTS[mutant]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for name, (pin, tol) in P.ALL_PINS.items():
+        try:
+            err = pin()
+        except Exception:  # a crash also counts as caught
+            err = float("inf")
+        if not err <= tol:
+            caught.append(name)
+    assert caught, f"mutant {mutant} passed every pin"
