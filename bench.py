@@ -1,0 +1,246 @@
+"""Throughput of the LLA latent-store decode path on one MI355X.
+
+One step = one decode step of a looped model (T loops x D layers) over the latent cache
+("Looped Latent Attention", Section 7: the latent-store decoder caches only latents and
+rebuilds K/V on read; Appendix A "Decoding and caching"):
+  1. write the new token's latents for every layer (lla_encode, n_new = 1 per sequence),
+  2. decode attention for every (loop, layer) in the model's order, one lla_decode_attn
+     call per (loop, layer) with loop_count = 1.
+Default workload: 21.3x compression at capacity (T=4, D=24, H=16, d_head=128,
+(r_k, r_v) = (16, 32), bfloat16, 768 sequences, context 4096), synthetic seeded data
+resident in HBM before the timed region.
+
+Prints one JSON line. ``value`` is decode tokens/s for the whole step (batch / step time).
+``roofline`` is for the dominant kernel (the decode call), with algorithmic bytes per call
+divided by the average call duration measured with HIP events on the launch stream over
+the timed region. ``cpu_baseline`` times the fp64 oracle on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_capacity_21x_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "latent_decode_attention_lla_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="capacity_21x")
+    p.add_argument("--path", default="auto", choices=["auto", "reconstruct", "rotary_fold"])
+    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-seqs", type=int, default=1)
+    p.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                   help="only run a plain device copy of this size (for counter scaling)")
+    return p.parse_args()
+
+
+def copy_calibration(gib: float):
+    import torch
+    n = int(gib * 2**30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": 3}))
+
+
+def cpu_baseline(w, seqs: int):
+    """The fp64 oracle (as it stands) on `seqs` sequences of the same workload: every head,
+    layer and loop of one decode step, same shapes and distributions (CPU inputs)."""
+    import numpy as np
+    from latent_decode_attention_lla_amd.inputs import decode_inputs
+    from oracle import lla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    sw = w.replace(batch=seqs)
+    t = decode_inputs(sw, seed=12345, device="cpu")
+    t = {k: v.float().numpy().astype(np.float64) for k, v in t.items()}
+    t0 = time.perf_counter()
+    for loop in range(w.T):
+        for layer in range(w.D):
+            O.decode(t["c_k"][layer], t["c_v"][layer], t["w_up_k"][layer], t["mu_k"][layer],
+                     t["w_up_v"][layer], t["mu_v"][layer], t["q"][layer, loop:loop + 1].transpose(1, 2, 0, 3),
+                     loop, None, w.rope_base, None, "per_head" if w.variant == "per_head" else "2d")
+    dt = time.perf_counter() - t0
+    return {"value": seqs / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{seqs} sequence(s) x {w.H} heads x {w.D} layers x {w.T} loops at context "
+                      f"{w.n} (one full decode step for {seqs} of the {w.batch} sequences), fp64 "
+                      f"NumPy, {dt:.1f} s; host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration_gib > 0:
+        copy_calibration(args.copy_calibration_gib)
+        return
+
+    from latent_decode_attention_lla_amd import lla
+    from latent_decode_attention_lla_amd.harness import DeviceLatentStore
+    from latent_decode_attention_lla_amd.inputs import WORKLOADS
+
+    if not os.path.exists(lla.LIB_PATH):
+        from latent_decode_attention_lla_amd import build as _b
+        _b.build()
+    lla.load()
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] allocating {args.workload}: latents "
+          f"{w.D * w.batch * w.Hc * w.n * (w.r_k + w.r_v) * (2 if w.dtype == 'bf16' else 4) / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
+    st = DeviceLatentStore(w, seed=3, device=dev)
+    # Encode-side codec and the new token's finished per-loop K/V for every layer.
+    g = torch.Generator(device=dev).manual_seed(4)
+    K = w.T * w.d_in
+    dt = w.torch_dtype
+    st.t["w_down_k_t"] = (torch.randn(w.D, w.Hc, w.r_k, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
+    st.t["w_down_v_t"] = (torch.randn(w.D, w.Hc, w.r_v, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
+    st.codec = lla.make_codec(st.t["w_down_k_t"], st.t["mu_k"], st.t["w_up_k"], st.t["w_down_v_t"],
+                              st.t["mu_v"], st.t["w_up_v"], st.rope)
+    x_new = [torch.randn(w.D, w.batch, 1, w.Hc, w.T, w.d_in, generator=g, device=dev).to(dt)
+             for _ in range(2)]
+    path = {"auto": lla.LLA_PATH_AUTO, "reconstruct": lla.LLA_PATH_RECONSTRUCT,
+            "rotary_fold": lla.LLA_PATH_ROTARY_FOLD}[args.path]
+    opts = lla.make_opts(args.splits, path)
+    S = lla.lla_decode_num_splits(st.dims, w.n, 1, opts)
+    ws = st.workspace(w.n, 1, opts)
+    out = torch.empty(w.batch, w.H, 1, w.d, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    n_calls = w.D * w.T
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_calls * max(args.steps, 1))]
+
+    def step(record: int | None):
+        for layer in range(w.D):
+            lla.lla_encode(st.dims, st.codec, st.cache, layer, x_new[0][layer], x_new[1][layer],
+                           w.n - 1, 1, sp)
+        k = 0
+        for loop in range(w.T):
+            for layer in range(w.D):
+                q = st.t["q"][layer, loop]
+                if record is not None:
+                    ev[record * n_calls + k][0].record(stream)
+                lla.lla_decode_attn(st.dims, st.codec, st.cache, layer, w.n, None, q, loop, 1, out,
+                                    ws, ws.numel(), opts, sp)
+                if record is not None:
+                    ev[record * n_calls + k][1].record(stream)
+                k += 1
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(s)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    call_ms = [a.elapsed_time(b) for a, b in ev[:n_calls * args.steps]]
+    call_ms.sort()
+    avg_call_ms = sum(call_ms) / len(call_ms)
+    med_call_ms = call_ms[len(call_ms) // 2]
+
+    es = 2 if w.dtype == "bf16" else 4
+    tok = w.batch * w.H * w.n if w.variant == "per_head" else w.batch * w.n
+    lat_bytes = tok * (w.r_k + w.r_v) * es
+    call_bytes = (lat_bytes + 2 * w.batch * w.H * w.d * 4 + w.H * w.d * (w.r_k + w.r_v) * es
+                  + 2 * w.H * w.d * es)
+    call_flops = 2.0 * w.batch * w.H * w.n * w.r_k * w.d
+    achieved_gbs = call_bytes / (avg_call_ms * 1e-3) / 1e9
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("path") == args.path \
+                and tr.get("workload") == args.workload:
+            traffic = tr.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_sample_seqs)
+
+    value = w.batch / (ms_step * 1e-3)
+    res = {
+        "metric": "LLA decode tokens/s (full decode step: D layers x T loops of latent-store "
+                  "attention plus the new token's encode), 1 GPU; decode-call HBM GB/s and "
+                  "fraction of peak",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian latents, codec maps and queries; no model weights)",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "H": w.H, "d_head": w.d, "r_k": w.r_k,
+                   "r_v": w.r_v, "batch": w.batch, "context": w.n, "variant": w.variant,
+                   "path": args.path, "splits": S, "calls_per_step": n_calls,
+                   "encodes_per_step": w.D},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "decode_call": {"avg_ms": round(avg_call_ms, 5), "median_ms": round(med_call_ms, 5),
+                        "algorithmic_bytes": call_bytes, "latent_bytes": lat_bytes,
+                        "loop_step_tokens_per_s": round(w.batch / (avg_call_ms * 1e-3), 1),
+                        "mfma_equiv_tflops": round(call_flops / (avg_call_ms * 1e-3) / 1e12, 2),
+                        "mfma_frac": round(call_flops / (avg_call_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "wall_s_timed": round(wall, 3),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * lla.h - C ABI of the MI355X (gfx950) latent-store decode library for Looped Latent
+ * Attention (LLA).
+ *
+ * Method: "Looped Latent Attention: Cross-Loop KV Compression for Looped Transformers"
+ * (arXiv 2607.15456v2).
+ *   - Section 3, Eq. 1: the T per-loop keys (or values) of one token, layer and head are
+ *     stacked as x = [x_1; ...; x_T] (pre-RoPE).
+ *   - Section 3, Eq. 2: the cache stores c = (x - mu) W_down, with r_k (keys) or r_v
+ *     (values) entries.
+ *   - Section 3, Eq. 3: loop t is rebuilt on read as x_t = c W_up,t^T + mu_t.
+ *   - Section 3, "RoPE and reconstruction": the model's RoPE is applied to the rebuilt
+ *     keys; attention itself is unchanged (Figure 1).
+ *   - Section 3, "The LLA-2D variant": one latent per token and layer rebuilds all heads.
+ *   - Section 7 and Appendix A ("Decoding and caching"): the latent-store decoder caches
+ *     only latents and rebuilds on read.
+ *   - Appendix J ("Absorbed attention"): the value side may be applied to the
+ *     softmax-weighted latent, sum_i a_i W c_i = W sum_i a_i c_i; with sum_i a_i = 1 the
+ *     mean term passes through unchanged.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers named as device pointers must point to HIP device memory (or memory
+ *     the device can address) and be 16-byte aligned. The caller owns every buffer; the
+ *     library allocates nothing and keeps no state beyond cached device properties.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and is
+ *     asynchronous: no host synchronisation happens inside the library.
+ *   - Arguments are validated on the host before anything is enqueued. A rejected call
+ *     returns a negative lla_status and enqueues nothing. A launch failure is reported
+ *     as LLA_ERR_HIP.
+ *   - Floating-point outputs are float32. Accumulation is float32 throughout.
+ *
+ * Tensor layouts (row-major, no padding). Hc = H and d_in = d_head for the per-head
+ * codec; Hc = 1 and d_in = H * d_head for LLA-2D. Element type of every codec and
+ * cache tensor is `dims.dtype` (float32 or bfloat16).
+ *   cache.c_k          [D][batch][Hc][n_max][r_k]   latents of keys
+ *   cache.c_v          [D][batch][Hc][n_max][r_v]   latents of values
+ *   codec.w_down_k_t   [D][Hc][r_k][T*d_in]          W_down of Eq. 2, stored transposed
+ *   codec.mu_k         [D][Hc][T*d_in]               mu of Eq. 2 (mu_t is loop t's slice;
+ *                                                    LLA-2D stacks (t, h, d), t outermost)
+ *   codec.w_up_k       [D][T][H][d_head][r_k]        W_up,t of Eq. 3 for every loop/head
+ *   (same for _v with r_v)
+ *   codec.rope_table   built by lla_rope_table_build for (d_head, n_max, rope_base)
+ */
+#ifndef LLA_H_
+#define LLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LLA_OK = 0,
+  LLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer, out of range */
+  LLA_ERR_UNSUPPORTED = -2, /* valid but not built: a (d_head, r_k, r_v) or dtype combo */
+  LLA_ERR_WORKSPACE = -3,   /* workspace smaller than lla_decode_workspace_bytes */
+  LLA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
+} lla_status;
+
+typedef enum { LLA_F32 = 0, LLA_BF16 = 1 } lla_dtype;
+typedef enum { LLA_PER_HEAD = 0, LLA_2D = 1 } lla_variant;
+
+/* Decode kernel family.
+ *   LLA_PATH_RECONSTRUCT : rebuild each key tile with MFMA (K^T = W_up,k,t C_k^T + mu_k,t),
+ *                          rotate it in registers, dot with q, online softmax.
+ *   LLA_PATH_ROTARY_FOLD : the same scores via an exact rewrite: for every rotary pair i
+ *                          q.R(j theta_i)k = cos(j theta_i) P_i + sin(j theta_i) Q_i with
+ *                          P_i, Q_i linear in the latent, so the score is
+ *                          c_j . (CS_j M) + CS_j m, where CS_j holds cos/sin of position j
+ *                          (shared by all heads) and M (d_head x r_k) folds q into W_up.
+ *                          bfloat16 only; CS and M enter the MFMA as float16.
+ *   LLA_PATH_AUTO        : ROTARY_FOLD for bfloat16 per-head, RECONSTRUCT otherwise. */
+typedef enum { LLA_PATH_AUTO = 0, LLA_PATH_RECONSTRUCT = 1, LLA_PATH_ROTARY_FOLD = 2 } lla_path;
+
+typedef struct {
+  int32_t T;        /* loops (recurrence steps) */
+  int32_t D;        /* layers */
+  int32_t H;        /* attention heads */
+  int32_t d_head;   /* head width; 64 or 128 */
+  int32_t r_k;      /* key latent size; multiple of 16 */
+  int32_t r_v;      /* value latent size; multiple of 8 */
+  int32_t batch;    /* sequences */
+  int32_t n_max;    /* cache capacity in tokens per sequence */
+  int32_t variant;  /* lla_variant */
+  int32_t dtype;    /* lla_dtype of latents and codec weights */
+  float rope_base;  /* RoPE base, e.g. 10000 */
+  float scale;      /* score scale; 0 selects 1/sqrt(d_head) */
+} lla_dims;
+
+typedef struct {
+  const void* w_down_k_t; /* encode only */
+  const void* mu_k;
+  const void* w_up_k;
+  const void* w_down_v_t; /* encode only */
+  const void* mu_v;
+  const void* w_up_v;
+  const void* rope_table; /* decode only */
+} lla_codec;
+
+typedef struct {
+  void* c_k;
+  void* c_v;
+} lla_cache;
+
+typedef struct {
+  int32_t num_splits; /* context splits per (sequence, head, loop); 0 = choose */
+  int32_t path;       /* lla_path */
+} lla_decode_opts;
+
+/* Human-readable name of a status code. Never NULL. */
+const char* lla_status_string(int32_t status);
+
+/* Compression ratio rho of Eq. 4 for these dims: 2 T H d_head / ((r_k + r_v) Hc).
+ * Returns a negative value when dims is NULL or has non-positive sizes. */
+double lla_compression_ratio(const lla_dims* dims);
+
+/* Bytes one token occupies in the latent cache over all D layers:
+ * D * Hc * (r_k + r_v) * sizeof(dtype) (Section 7, Table 5 "KV / token").
+ * Returns a negative value on invalid dims. */
+double lla_cache_bytes_per_token(const lla_dims* dims);
+
+/* Size in bytes of the RoPE table for dims (d_head, n_max). */
+size_t lla_rope_table_bytes(const lla_dims* dims);
+
+/* Fill `table` (device, lla_rope_table_bytes(dims) bytes) with cos/sin of p*theta_i,
+ * theta_i = rope_base^(-2i/d_head), for every position p < n_max, evaluated in float64
+ * and rounded once (float32 and float16 copies). Pairs are interleaved (2i, 2i+1), as
+ * in RoFormer, which the LLA paper cites for RoPE. Build once per (d_head, n_max,
+ * rope_base) and pass it in lla_codec.rope_table. */
+int32_t lla_rope_table_build(const lla_dims* dims, void* table, void* stream);
+
+/* Encode (Section 3, Eq. 2): for every sequence b, new token j < n_new and latent head
+ * hc, c = (x - mu) W_down for keys and values of `layer`, stored with round-to-nearest-
+ * even into cache row pos_start + j.
+ *   x_k, x_v : device, [batch][n_new][Hc][T][d_in] of dtype, pre-RoPE, loop t of the
+ *              stacked vector at [t][*] (Eq. 1). Must be the finished T-loop values.
+ *   requires 0 <= layer < D, n_new >= 0, 0 <= pos_start, pos_start + n_new <= n_max.
+ * n_new == 0 enqueues nothing and returns LLA_OK. */
+int32_t lla_encode(const lla_dims* dims, const lla_codec* codec, const lla_cache* cache,
+                   int32_t layer, const void* x_k, const void* x_v, int32_t pos_start,
+                   int32_t n_new, void* stream);
+
+/* Workspace bytes lla_decode_attn needs for this call shape (0 is never returned for
+ * valid dims; returns 0 on invalid arguments). */
+size_t lla_decode_workspace_bytes(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,
+                                  const lla_decode_opts* opts);
+
+/* Latent-store decode attention for one layer and loops loop_begin .. loop_begin +
+ * loop_count - 1 (Section 7; Eqs. 3 and RoPE after reconstruction; Appendix J value
+ * identity). For every sequence b, head h and loop t:
+ *   K_t[j] = RoPE_j(c_k[j] W_up,k,t^T + mu_k,t),  V_t[j] = c_v[j] W_up,v,t^T + mu_v,t,
+ *   out[b][h][t] = softmax_j(scale * q . K_t[j]) V_t   over j < len_b,
+ * with RoPE at position j = the cache slot. The value side is computed as
+ * (sum_j a_j c_v[j]) W_up,v,t^T + mu_v,t.
+ *   q        : device float32 [batch][H][loop_count][d_head], queries already rotated.
+ *   out      : device float32 [batch][H][loop_count][d_head]; len_b == 0 gives zeros.
+ *   ctx_lens : device int32 [batch] or NULL. NULL: len_b = n_ctx for all b. Otherwise
+ *              len_b = ctx_lens[b], clamped by the kernels to [0, n_ctx].
+ *   requires 0 <= n_ctx <= n_max, 0 <= layer < D, 0 <= loop_begin,
+ *            1 <= loop_count, loop_begin + loop_count <= T.
+ *   workspace: device, >= lla_decode_workspace_bytes(dims, n_ctx, loop_count, opts).
+ *   opts     : NULL for defaults. */
+int32_t lla_decode_attn(const lla_dims* dims, const lla_codec* codec, const lla_cache* cache,
+                        int32_t layer, int32_t n_ctx, const int32_t* ctx_lens, const float* q,
+                        int32_t loop_begin, int32_t loop_count, float* out, void* workspace,
+                        size_t workspace_bytes, const lla_decode_opts* opts, void* stream);
+
+/* Number of context splits lla_decode_attn would use (after `opts`), for reporting. */
+int32_t lla_decode_num_splits(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,
+                              const lla_decode_opts* opts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLA_H_ */

@@ -1,0 +1,267 @@
+// C ABI of the LLA latent-store decode library: host-side validation, launch planning
+// and dispatch to the gfx950 kernels. See include/lla.h for the contract of every entry
+// point. Nothing here allocates device memory or synchronises the stream.
+#include "lla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "lla_kernels.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(const lla_dims& d) { return d.dtype == LLA_F32 ? 4 : 2; }
+int latent_heads(const lla_dims& d) { return d.variant == LLA_PER_HEAD ? d.H : 1; }
+int d_in(const lla_dims& d) { return d.variant == LLA_PER_HEAD ? d.d_head : d.H * d.d_head; }
+
+// Shape checks shared by every entry point.
+int32_t check_dims(const lla_dims* d) {
+  if (d == nullptr) return LLA_ERR_INVALID_ARG;
+  if (d->T < 1 || d->D < 1 || d->H < 1 || d->batch < 1 || d->n_max < 1) return LLA_ERR_INVALID_ARG;
+  if (d->d_head < 2 || d->d_head % 2 != 0) return LLA_ERR_INVALID_ARG;
+  if (d->r_k < 1 || d->r_v < 1) return LLA_ERR_INVALID_ARG;
+  if (d->variant != LLA_PER_HEAD && d->variant != LLA_2D) return LLA_ERR_INVALID_ARG;
+  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16) return LLA_ERR_INVALID_ARG;
+  if (!(d->rope_base > 0.f) || !std::isfinite(d->rope_base)) return LLA_ERR_INVALID_ARG;
+  if (!(d->scale >= 0.f) || !std::isfinite(d->scale)) return LLA_ERR_INVALID_ARG;
+  // Built shapes: d_head 64 or 128, r_k a multiple of 16, r_v a multiple of 8.
+  if (d->d_head != 64 && d->d_head != 128) return LLA_ERR_UNSUPPORTED;
+  if (d->r_k % 16 != 0 || d->r_v % 8 != 0) return LLA_ERR_UNSUPPORTED;
+  // Index arithmetic inside the kernels is 32-bit per (sequence, head) plane offset
+  // products and 64-bit for whole-tensor offsets; keep the per-plane sizes in range.
+  if (static_cast<long long>(d->n_max) * (d->r_k > d->r_v ? d->r_k : d->r_v) >= (1LL << 31))
+    return LLA_ERR_UNSUPPORTED;
+  return LLA_OK;
+}
+
+struct Plan {
+  int S;
+  int split_len;
+};
+
+Plan plan_splits(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_opts* opts) {
+  Plan p{1, 16};
+  if (n_ctx <= 0) return p;
+  const long long units = static_cast<long long>(d.batch) * d.H * loop_count;
+  long long S;
+  if (opts != nullptr && opts->num_splits > 0) {
+    S = opts->num_splits;
+  } else {
+    const long long target = 2048;  // waves in flight wanted across 256 CUs
+    S = (target + units - 1) / units;
+    const long long max_by_len = (n_ctx + 255) / 256;  // keep splits >= 256 tokens
+    if (S > max_by_len) S = max_by_len;
+  }
+  if (S < 1) S = 1;
+  long long len = (n_ctx + S - 1) / S;
+  len = (len + 15) / 16 * 16;
+  p.split_len = static_cast<int>(len);
+  p.S = static_cast<int>((n_ctx + len - 1) / len);
+  return p;
+}
+
+int resolve_path(const lla_dims& d, const lla_decode_opts* opts) {
+  const int want = opts ? opts->path : LLA_PATH_AUTO;
+  if (want == LLA_PATH_AUTO) {
+    if (d.dtype == LLA_BF16 &&
+        lla::decode_rotary_fold_supported(d.dtype, d.d_head, d.r_k, d.r_v) &&
+        d.variant == LLA_PER_HEAD)
+      return LLA_PATH_ROTARY_FOLD;
+    return LLA_PATH_RECONSTRUCT;
+  }
+  return want;
+}
+
+int32_t hip_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LLA_OK : LLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lla_status_string(int32_t status) {
+  switch (status) {
+    case LLA_OK: return "ok";
+    case LLA_ERR_INVALID_ARG: return "invalid argument";
+    case LLA_ERR_UNSUPPORTED: return "unsupported shape, dtype or path";
+    case LLA_ERR_WORKSPACE: return "workspace too small";
+    case LLA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+double lla_compression_ratio(const lla_dims* d) {
+  if (d == nullptr || d->T < 1 || d->H < 1 || d->d_head < 1 || d->r_k < 1 || d->r_v < 1) return -1.0;
+  const double teacher = 2.0 * d->T * d->H * d->d_head;
+  const double latent = static_cast<double>(d->r_k + d->r_v) * (d->variant == LLA_2D ? 1 : d->H);
+  return teacher / latent;
+}
+
+double lla_cache_bytes_per_token(const lla_dims* d) {
+  if (d == nullptr || d->D < 1 || d->H < 1 || d->r_k < 1 || d->r_v < 1) return -1.0;
+  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16) return -1.0;
+  const double hc = d->variant == LLA_2D ? 1.0 : d->H;
+  return static_cast<double>(d->D) * hc * (d->r_k + d->r_v) * static_cast<double>(elem_bytes(*d));
+}
+
+size_t lla_rope_table_bytes(const lla_dims* d) {
+  if (d == nullptr || d->n_max < 1 || d->d_head < 2) return 0;
+  return static_cast<size_t>(d->n_max) * d->d_head * (4 + 2);
+}
+
+int32_t lla_rope_table_build(const lla_dims* d, void* table, void* stream) {
+  const int32_t st = check_dims(d);
+  if (st != LLA_OK) return st;
+  if (table == nullptr || !aligned16(table)) return LLA_ERR_INVALID_ARG;
+  float* t32 = static_cast<float*>(table);
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(static_cast<char*>(table) +
+                                               static_cast<size_t>(d->n_max) * d->d_head * 4);
+  lla::launch_rope_table(d->d_head, d->n_max, static_cast<double>(d->rope_base), t32, t16,
+                         static_cast<hipStream_t>(stream));
+  return hip_status();
+}
+
+int32_t lla_encode(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                   int32_t layer, const void* x_k, const void* x_v, int32_t pos_start,
+                   int32_t n_new, void* stream) {
+  int32_t st = check_dims(d);
+  if (st != LLA_OK) return st;
+  if (codec == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
+  if (n_new < 0 || pos_start < 0 || static_cast<long long>(pos_start) + n_new > d->n_max)
+    return LLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_k, x_v, codec->w_down_k_t, codec->w_down_v_t, codec->mu_k, codec->mu_v,
+                        cache->c_k, cache->c_v};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+  const int Hc = latent_heads(*d);
+  const int K = d->T * d_in(*d);
+  if (!lla::encode_supported(d->dtype, d->r_k, K) || !lla::encode_supported(d->dtype, d->r_v, K))
+    return LLA_ERR_UNSUPPORTED;
+  if (n_new == 0) return LLA_OK;
+  const size_t es = elem_bytes(*d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rs[2] = {d->r_k, d->r_v};
+  const void* xs[2] = {x_k, x_v};
+  const void* wds[2] = {codec->w_down_k_t, codec->w_down_v_t};
+  const void* mus[2] = {codec->mu_k, codec->mu_v};
+  void* cs[2] = {cache->c_k, cache->c_v};
+  for (int ax = 0; ax < 2; ++ax) {
+    const int r = rs[ax];
+    lla::EncodeArgs a;
+    a.x = xs[ax];
+    a.w_down_t = static_cast<const char*>(wds[ax]) + static_cast<size_t>(layer) * Hc * r * K * es;
+    a.mu = static_cast<const char*>(mus[ax]) + static_cast<size_t>(layer) * Hc * K * es;
+    a.c = static_cast<char*>(cs[ax]) +
+          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * r * es;
+    a.B = d->batch;
+    a.Hc = Hc;
+    a.Kdim = K;
+    a.n_new = n_new;
+    a.pos_start = pos_start;
+    a.n_max = d->n_max;
+    if (!lla::launch_encode(d->dtype, r, a, s)) return LLA_ERR_UNSUPPORTED;
+  }
+  return hip_status();
+}
+
+int32_t lla_decode_num_splits(const lla_dims* d, int32_t n_ctx, int32_t loop_count,
+                              const lla_decode_opts* opts) {
+  if (check_dims(d) != LLA_OK || n_ctx < 0 || loop_count < 1) return 0;
+  return plan_splits(*d, n_ctx, loop_count, opts).S;
+}
+
+size_t lla_decode_workspace_bytes(const lla_dims* d, int32_t n_ctx, int32_t loop_count,
+                                  const lla_decode_opts* opts) {
+  if (check_dims(d) != LLA_OK || n_ctx < 0 || n_ctx > d->n_max || loop_count < 1) return 0;
+  const Plan p = plan_splits(*d, n_ctx, loop_count, opts);
+  const size_t bytes = static_cast<size_t>(d->batch) * d->H * loop_count * p.S * (2 + d->r_v) * 4;
+  return (bytes + 255) / 256 * 256;
+}
+
+int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                        int32_t layer, int32_t n_ctx, const int32_t* ctx_lens, const float* q,
+                        int32_t loop_begin, int32_t loop_count, float* out, void* workspace,
+                        size_t workspace_bytes, const lla_decode_opts* opts, void* stream) {
+  int32_t st = check_dims(d);
+  if (st != LLA_OK) return st;
+  if (codec == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
+  if (n_ctx < 0 || n_ctx > d->n_max) return LLA_ERR_INVALID_ARG;
+  if (loop_begin < 0 || loop_count < 1 || static_cast<long long>(loop_begin) + loop_count > d->T)
+    return LLA_ERR_INVALID_ARG;
+  if (opts != nullptr && (opts->num_splits < 0 || opts->path < LLA_PATH_AUTO ||
+                          opts->path > LLA_PATH_ROTARY_FOLD))
+    return LLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {codec->mu_k, codec->w_up_k, codec->mu_v, codec->w_up_v, codec->rope_table,
+                        cache->c_k, cache->c_v, q, out, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+  if (ctx_lens != nullptr && (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) != 0) return LLA_ERR_INVALID_ARG;
+
+  const int path = resolve_path(*d, opts);
+  if (path == LLA_PATH_ROTARY_FOLD) {
+    if (d->dtype != LLA_BF16 || d->variant != LLA_PER_HEAD ||
+        !lla::decode_rotary_fold_supported(d->dtype, d->d_head, d->r_k, d->r_v))
+      return LLA_ERR_UNSUPPORTED;
+  } else if (!lla::decode_reconstruct_supported(d->dtype, d->d_head, d->r_k, d->r_v)) {
+    return LLA_ERR_UNSUPPORTED;
+  }
+  if (workspace_bytes < lla_decode_workspace_bytes(d, n_ctx, loop_count, opts)) return LLA_ERR_WORKSPACE;
+
+  const Plan p = plan_splits(*d, n_ctx, loop_count, opts);
+  const size_t es = elem_bytes(*d);
+  const int Hc = latent_heads(*d);
+  const int K = d->T * d_in(*d);
+  lla::DecodeArgs a;
+  a.c_k = static_cast<const char*>(cache->c_k) +
+          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * d->r_k * es;
+  a.c_v = static_cast<const char*>(cache->c_v) +
+          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * d->r_v * es;
+  a.w_up_k = static_cast<const char*>(codec->w_up_k) +
+             static_cast<size_t>(layer) * d->T * d->H * d->d_head * d->r_k * es;
+  a.w_up_v = static_cast<const char*>(codec->w_up_v) +
+             static_cast<size_t>(layer) * d->T * d->H * d->d_head * d->r_v * es;
+  a.mu_k = static_cast<const char*>(codec->mu_k) + static_cast<size_t>(layer) * Hc * K * es;
+  a.mu_v = static_cast<const char*>(codec->mu_v) + static_cast<size_t>(layer) * Hc * K * es;
+  a.rope32 = static_cast<const float*>(codec->rope_table);
+  a.rope16 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(codec->rope_table) +
+                                               static_cast<size_t>(d->n_max) * d->d_head * 4);
+  a.q = q;
+  a.ctx_lens = ctx_lens;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.B = d->batch;
+  a.H = d->H;
+  a.Hc = Hc;
+  a.T = d->T;
+  a.L = loop_count;
+  a.loop_begin = loop_begin;
+  a.n_max = d->n_max;
+  a.n_ctx = n_ctx;
+  a.S = p.S;
+  a.split_len = p.split_len;
+  a.variant = d->variant;
+  const double scale = d->scale > 0.f ? d->scale : 1.0 / std::sqrt(static_cast<double>(d->d_head));
+  a.scale_log2e = static_cast<float>(scale * kLog2e);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool ok = path == LLA_PATH_ROTARY_FOLD
+                ? lla::launch_decode_rotary_fold(d->dtype, d->d_head, d->r_k, d->r_v, a, s)
+                : lla::launch_decode_reconstruct(d->dtype, d->d_head, d->r_k, d->r_v, a, s);
+  if (!ok) return LLA_ERR_UNSUPPORTED;
+  st = hip_status();
+  if (st != LLA_OK) return st;
+  if (!lla::launch_combine(d->dtype, d->d_head, d->r_v, a, s)) return LLA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+"""Device-side setup shared by the GPU tests, smoke() and bench.py: allocate a workload's
+tensors in HBM (through torch), build the RoPE table, size the workspace, and call the
+C ABI. Marshalling only; all arithmetic of the path runs in liblla.so.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import lla
+from .inputs import Workload, decode_inputs
+
+
+def dims_for(w: Workload, n_max: int | None = None, batch: int | None = None) -> lla.lla_dims:
+    return lla.make_dims(w.T, w.D, w.H, w.d, w.r_k, w.r_v, batch or w.batch, n_max or w.n,
+                         lla.LLA_PER_HEAD if w.variant == "per_head" else lla.LLA_2D,
+                         lla.LLA_F32 if w.dtype == "f32" else lla.LLA_BF16, w.rope_base, 0.0)
+
+
+class DeviceLatentStore:
+    """A latent cache plus decode-side codec for one workload, resident on ``device``."""
+
+    def __init__(self, w: Workload, seed: int, device="cuda", n_alloc: int | None = None,
+                 tensors: dict | None = None, with_q: bool = True):
+        self.w = w
+        self.device = torch.device(device)
+        self.n_max = n_alloc or w.n
+        t = tensors if tensors is not None else decode_inputs(w, seed, device, self.n_max, with_q)
+        self.t = {k: v.to(self.device).contiguous() for k, v in t.items()}
+        self.dims = dims_for(w, self.n_max)
+        tb = lla.lla_rope_table_bytes(self.dims)
+        self.rope = torch.empty(tb, dtype=torch.uint8, device=self.device)
+        lla.lla_rope_table_build(self.dims, self.rope)
+        self.codec = lla.make_codec(self.t.get("w_down_k_t"), self.t["mu_k"], self.t["w_up_k"],
+                                    self.t.get("w_down_v_t"), self.t["mu_v"], self.t["w_up_v"],
+                                    self.rope)
+        self.cache = lla.make_cache(self.t["c_k"], self.t["c_v"])
+        self._ws = None
+
+    def workspace(self, n_ctx: int, loop_count: int, opts=None) -> torch.Tensor:
+        nb = lla.lla_decode_workspace_bytes(self.dims, n_ctx, loop_count, opts)
+        if self._ws is None or self._ws.numel() < nb:
+            self._ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode(self, layer: int, loop_begin: int, loop_count: int, q: torch.Tensor | None = None,
+               n_ctx: int | None = None, ctx_lens: torch.Tensor | None = None, opts=None,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        w = self.w
+        n_ctx = w.n if n_ctx is None else n_ctx
+        if q is None:
+            # stored per (layer, loop) as [B][H][d]; the call wants [B][H][L][d]
+            if loop_count == 1:
+                q = self.t["q"][layer, loop_begin]
+            else:
+                q = self.t["q"][layer, loop_begin:loop_begin + loop_count].permute(1, 2, 0, 3).contiguous()
+        if out is None:
+            out = torch.empty(w.batch, w.H, loop_count, w.d, dtype=torch.float32, device=self.device)
+        ws = self.workspace(n_ctx, loop_count, opts)
+        lla.lla_decode_attn(self.dims, self.codec, self.cache, layer, n_ctx, ctx_lens, q,
+                            loop_begin, loop_count, out, ws, ws.numel(), opts, stream)
+        return out
+
+    def encode(self, layer: int, x_k: torch.Tensor, x_v: torch.Tensor, pos_start: int,
+               n_new: int, stream=None) -> None:
+        lla.lla_encode(self.dims, self.codec, self.cache, layer, x_k, x_v, pos_start, n_new, stream)

@@ -1,0 +1,206 @@
+"""Thin ctypes binding of ``liblla.so`` (the C ABI in include/lla.h).
+
+Argument marshalling only: every step of the decode and encode path runs in the
+library's gfx950 kernels. Functions carry the C names; device buffers may be passed as
+torch tensors (their ``data_ptr()`` is used) or as integer addresses. ``stream=None``
+uses torch's current HIP stream. A non-OK status raises :class:`LLAError`.
+
+The library is loaded on first use; if it has not been built (``python -m
+latent_decode_attention_lla_amd.build``) the call fails loudly. There is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblla.so")
+
+LLA_OK = 0
+LLA_ERR_INVALID_ARG = -1
+LLA_ERR_UNSUPPORTED = -2
+LLA_ERR_WORKSPACE = -3
+LLA_ERR_HIP = -4
+
+LLA_F32 = 0
+LLA_BF16 = 1
+LLA_PER_HEAD = 0
+LLA_2D = 1
+LLA_PATH_AUTO = 0
+LLA_PATH_RECONSTRUCT = 1
+LLA_PATH_ROTARY_FOLD = 2
+
+EXPORTED = (
+    "lla_status_string", "lla_compression_ratio", "lla_cache_bytes_per_token",
+    "lla_rope_table_bytes", "lla_rope_table_build", "lla_encode",
+    "lla_decode_workspace_bytes", "lla_decode_attn", "lla_decode_num_splits",
+)
+
+
+class LLAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({lla_status_string(status)})")
+
+
+class lla_dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("d_head", ctypes.c_int32), ("r_k", ctypes.c_int32), ("r_v", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("n_max", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("rope_base", ctypes.c_float), ("scale", ctypes.c_float)]
+
+
+class lla_codec(ctypes.Structure):
+    _fields_ = [("w_down_k_t", ctypes.c_void_p), ("mu_k", ctypes.c_void_p),
+                ("w_up_k", ctypes.c_void_p), ("w_down_v_t", ctypes.c_void_p),
+                ("mu_v", ctypes.c_void_p), ("w_up_v", ctypes.c_void_p),
+                ("rope_table", ctypes.c_void_p)]
+
+
+class lla_cache(ctypes.Structure):
+    _fields_ = [("c_k", ctypes.c_void_p), ("c_v", ctypes.c_void_p)]
+
+
+class lla_decode_opts(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("path", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load liblla.so (once). Raises if it is missing: the HIP path is the only path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"LLA HIP library not built: {LIB_PATH} is missing "
+                           "(run python -m latent_decode_attention_lla_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.lla_status_string.argtypes = [i32]
+    lib.lla_status_string.restype = ctypes.c_char_p
+    lib.lla_compression_ratio.argtypes = [P(lla_dims)]
+    lib.lla_compression_ratio.restype = ctypes.c_double
+    lib.lla_cache_bytes_per_token.argtypes = [P(lla_dims)]
+    lib.lla_cache_bytes_per_token.restype = ctypes.c_double
+    lib.lla_rope_table_bytes.argtypes = [P(lla_dims)]
+    lib.lla_rope_table_bytes.restype = sz
+    lib.lla_rope_table_build.argtypes = [P(lla_dims), vp, vp]
+    lib.lla_rope_table_build.restype = i32
+    lib.lla_encode.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, vp, vp, i32, i32, vp]
+    lib.lla_encode.restype = i32
+    lib.lla_decode_workspace_bytes.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
+    lib.lla_decode_workspace_bytes.restype = sz
+    lib.lla_decode_num_splits.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
+    lib.lla_decode_num_splits.restype = i32
+    lib.lla_decode_attn.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, i32, vp, vp,
+                                    i32, i32, vp, vp, sz, P(lla_decode_opts), vp]
+    lib.lla_decode_attn.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status):
+    if status != LLA_OK:
+        raise LLAError(fn, status)
+
+
+def make_dims(T, D, H, d_head, r_k, r_v, batch, n_max, variant=LLA_PER_HEAD, dtype=LLA_BF16,
+              rope_base=10000.0, scale=0.0) -> lla_dims:
+    return lla_dims(T, D, H, d_head, r_k, r_v, batch, n_max, variant, dtype, rope_base, scale)
+
+
+def make_codec(w_down_k_t=None, mu_k=None, w_up_k=None, w_down_v_t=None, mu_v=None, w_up_v=None,
+               rope_table=None) -> lla_codec:
+    return lla_codec(_ptr(w_down_k_t), _ptr(mu_k), _ptr(w_up_k), _ptr(w_down_v_t), _ptr(mu_v),
+                     _ptr(w_up_v), _ptr(rope_table))
+
+
+def make_cache(c_k, c_v) -> lla_cache:
+    return lla_cache(_ptr(c_k), _ptr(c_v))
+
+
+def make_opts(num_splits=0, path=LLA_PATH_AUTO) -> lla_decode_opts:
+    return lla_decode_opts(num_splits, path)
+
+
+def lla_status_string(status: int) -> str:
+    return load().lla_status_string(status).decode()
+
+
+def lla_compression_ratio(dims: lla_dims) -> float:
+    return load().lla_compression_ratio(ctypes.byref(dims))
+
+
+def lla_cache_bytes_per_token(dims: lla_dims) -> float:
+    return load().lla_cache_bytes_per_token(ctypes.byref(dims))
+
+
+def lla_rope_table_bytes(dims: lla_dims) -> int:
+    return load().lla_rope_table_bytes(ctypes.byref(dims))
+
+
+def lla_rope_table_build(dims: lla_dims, table, stream=None) -> None:
+    _check("lla_rope_table_build",
+           load().lla_rope_table_build(ctypes.byref(dims), _ptr(table), _stream(stream)))
+
+
+def lla_encode(dims: lla_dims, codec: lla_codec, cache: lla_cache, layer: int, x_k, x_v,
+               pos_start: int, n_new: int, stream=None) -> None:
+    _check("lla_encode", load().lla_encode(ctypes.byref(dims), ctypes.byref(codec),
+                                           ctypes.byref(cache), layer, _ptr(x_k), _ptr(x_v),
+                                           pos_start, n_new, _stream(stream)))
+
+
+def lla_decode_workspace_bytes(dims: lla_dims, n_ctx: int, loop_count: int, opts=None) -> int:
+    return load().lla_decode_workspace_bytes(ctypes.byref(dims), n_ctx, loop_count,
+                                             ctypes.byref(opts) if opts is not None else None)
+
+
+def lla_decode_num_splits(dims: lla_dims, n_ctx: int, loop_count: int, opts=None) -> int:
+    return load().lla_decode_num_splits(ctypes.byref(dims), n_ctx, loop_count,
+                                        ctypes.byref(opts) if opts is not None else None)
+
+
+def lla_decode_attn(dims: lla_dims, codec: lla_codec, cache: lla_cache, layer: int, n_ctx: int,
+                    ctx_lens, q, loop_begin: int, loop_count: int, out, workspace,
+                    workspace_bytes: int, opts=None, stream=None) -> None:
+    _check("lla_decode_attn", load().lla_decode_attn(
+        ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), layer, n_ctx,
+        _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out), _ptr(workspace),
+        workspace_bytes, ctypes.byref(opts) if opts is not None else None, _stream(stream)))
+
+
+def lla_decode_attn_status(dims, codec, cache, layer, n_ctx, ctx_lens, q, loop_begin, loop_count,
+                           out, workspace, workspace_bytes, opts=None, stream=0) -> int:
+    """Same call, returning the raw status instead of raising (for argument tests)."""
+    return load().lla_decode_attn(
+        ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), layer, n_ctx,
+        _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out), _ptr(workspace),
+        workspace_bytes, ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def lla_encode_status(dims, codec, cache, layer, x_k, x_v, pos_start, n_new, stream=0) -> int:
+    return load().lla_encode(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), layer,
+                             _ptr(x_k), _ptr(x_v), pos_start, n_new, stream)

@@ -1,0 +1,158 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every
+entry point include/lla.h declares, computes the closed forms of Eq. 4 and Table 5, and
+rejects bad arguments before anything is enqueued."""
+
+import os
+import re
+
+import pytest
+import torch
+
+from latent_decode_attention_lla_amd import lla
+from oracle import lla_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "lla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lla_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lla.load()
+    declared = _declared_symbols()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(lib, name), f"liblla.so does not export {name}"
+    assert set(declared) == set(lla.EXPORTED)
+
+
+def test_status_strings():
+    for st in (lla.LLA_OK, lla.LLA_ERR_INVALID_ARG, lla.LLA_ERR_UNSUPPORTED, lla.LLA_ERR_WORKSPACE,
+               lla.LLA_ERR_HIP, 12345):
+        assert isinstance(lla.lla_status_string(st), str)
+
+
+@pytest.mark.parametrize("T,D,H,d,rk,rv,variant,dtype", [
+    (4, 24, 16, 128, 96, 160, lla.LLA_PER_HEAD, lla.LLA_BF16),
+    (4, 24, 16, 128, 16, 32, lla.LLA_PER_HEAD, lla.LLA_BF16),
+    (4, 48, 16, 128, 96, 160, lla.LLA_PER_HEAD, lla.LLA_BF16),
+    (4, 24, 16, 128, 96, 160, lla.LLA_2D, lla.LLA_BF16),
+    (4, 1, 2, 64, 16, 24, lla.LLA_PER_HEAD, lla.LLA_F32),
+])
+def test_closed_forms_match_oracle(T, D, H, d, rk, rv, variant, dtype):
+    dims = lla.make_dims(T, D, H, d, rk, rv, 1, 16, variant, dtype)
+    v = "per_head" if variant == lla.LLA_PER_HEAD else "2d"
+    assert lla.lla_compression_ratio(dims) == pytest.approx(O.compression_ratio(T, d, rk, rv, H, v), rel=1e-12)
+    bps = 4 if dtype == lla.LLA_F32 else 2
+    assert lla.lla_cache_bytes_per_token(dims) == O.cache_bytes_per_token(D, H, rk, rv, bps, v)
+
+
+def test_rope_table_bytes():
+    dims = lla.make_dims(4, 1, 16, 128, 16, 32, 1, 4096)
+    assert lla.lla_rope_table_bytes(dims) == 4096 * 128 * 6
+
+
+def test_workspace_and_splits_planning():
+    dims = lla.make_dims(4, 24, 16, 128, 16, 32, 768, 4096)
+    assert lla.lla_decode_num_splits(dims, 4096, 1) == 1  # 12288 units fill the chip
+    assert lla.lla_decode_workspace_bytes(dims, 4096, 1) >= 768 * 16 * (2 + 32) * 4
+    small = lla.make_dims(4, 1, 16, 128, 96, 160, 8, 8192)
+    s = lla.lla_decode_num_splits(small, 8192, 1)
+    assert s > 1  # 128 units need a context split
+    opts = lla.make_opts(num_splits=7)
+    assert lla.lla_decode_num_splits(small, 8192, 1, opts) == 7
+    assert lla.lla_decode_workspace_bytes(small, 8193, 1) == 0  # n_ctx > n_max
+    assert lla.lla_decode_num_splits(small, 0, 1) == 1
+
+
+# Argument validation with fake (never dereferenced) addresses. Every case below must be
+# rejected on the host; they are skipped where a GPU is visible so that a validation bug
+# can never turn into a launch with bogus pointers.
+needs_no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                  reason="fake-pointer validation runs only without a GPU")
+
+FAKE = 0x10000
+
+
+def _decode_args(**over):
+    dims = lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256)
+    codec = lla.make_codec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    cache = lla.make_cache(FAKE, FAKE)
+    a = dict(dims=dims, codec=codec, cache=cache, layer=0, n_ctx=256, ctx_lens=None, q=FAKE,
+             loop_begin=0, loop_count=1, out=FAKE, workspace=FAKE, workspace_bytes=1 << 30,
+             opts=None)
+    a.update(over)
+    return a
+
+
+def _call(a):
+    return lla.lla_decode_attn_status(a["dims"], a["codec"], a["cache"], a["layer"], a["n_ctx"],
+                                      a["ctx_lens"], a["q"], a["loop_begin"], a["loop_count"],
+                                      a["out"], a["workspace"], a["workspace_bytes"], a["opts"], 0)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("over,expect", [
+    (dict(layer=2), lla.LLA_ERR_INVALID_ARG),
+    (dict(layer=-1), lla.LLA_ERR_INVALID_ARG),
+    (dict(n_ctx=257), lla.LLA_ERR_INVALID_ARG),
+    (dict(n_ctx=-1), lla.LLA_ERR_INVALID_ARG),
+    (dict(loop_begin=3, loop_count=2), lla.LLA_ERR_INVALID_ARG),
+    (dict(loop_count=0), lla.LLA_ERR_INVALID_ARG),
+    (dict(q=None), lla.LLA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 4), lla.LLA_ERR_INVALID_ARG),
+    (dict(out=None), lla.LLA_ERR_INVALID_ARG),
+    (dict(workspace=None), lla.LLA_ERR_INVALID_ARG),
+    (dict(ctx_lens=FAKE + 2), lla.LLA_ERR_INVALID_ARG),
+    (dict(workspace_bytes=16), lla.LLA_ERR_WORKSPACE),
+    (dict(opts=lla.make_opts(-1, 0)), lla.LLA_ERR_INVALID_ARG),
+    (dict(opts=lla.make_opts(0, 9)), lla.LLA_ERR_INVALID_ARG),
+    (dict(codec=lla.make_codec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)), lla.LLA_ERR_INVALID_ARG),
+    (dict(cache=lla.make_cache(FAKE, None)), lla.LLA_ERR_INVALID_ARG),
+    (dict(dims=lla.make_dims(4, 2, 16, 96, 16, 32, 4, 256)), lla.LLA_ERR_UNSUPPORTED),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 24, 32, 4, 256)), lla.LLA_ERR_UNSUPPORTED),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 16, 36, 4, 256)), lla.LLA_ERR_UNSUPPORTED),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 48, 48, 4, 256)), lla.LLA_ERR_UNSUPPORTED),
+    (dict(dims=lla.make_dims(0, 2, 16, 128, 16, 32, 4, 256)), lla.LLA_ERR_INVALID_ARG),
+    (dict(dims=lla.make_dims(4, 2, 16, 127, 16, 32, 4, 256)), lla.LLA_ERR_INVALID_ARG),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256, variant=5)), lla.LLA_ERR_INVALID_ARG),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256, dtype=7)), lla.LLA_ERR_INVALID_ARG),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256, rope_base=-1.0)), lla.LLA_ERR_INVALID_ARG),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256, scale=float("nan"))), lla.LLA_ERR_INVALID_ARG),
+    (dict(opts=lla.make_opts(0, lla.LLA_PATH_ROTARY_FOLD),
+          dims=lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256, dtype=lla.LLA_F32)), lla.LLA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_arguments(over, expect):
+    assert _call(_decode_args(**over)) == expect
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("over,expect", [
+    (dict(layer=2), lla.LLA_ERR_INVALID_ARG),
+    (dict(pos_start=250, n_new=7), lla.LLA_ERR_INVALID_ARG),
+    (dict(n_new=-1), lla.LLA_ERR_INVALID_ARG),
+    (dict(pos_start=-1), lla.LLA_ERR_INVALID_ARG),
+    (dict(x_k=None), lla.LLA_ERR_INVALID_ARG),
+    (dict(x_v=FAKE + 8), lla.LLA_ERR_INVALID_ARG),
+    (dict(codec=lla.make_codec(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)), lla.LLA_ERR_INVALID_ARG),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 48, 32, 4, 256)), lla.LLA_ERR_UNSUPPORTED),
+])
+def test_encode_rejects_bad_arguments(over, expect):
+    a = dict(dims=lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256),
+             codec=lla.make_codec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE),
+             cache=lla.make_cache(FAKE, FAKE), layer=0, x_k=FAKE, x_v=FAKE, pos_start=0, n_new=8)
+    a.update(over)
+    st = lla.lla_encode_status(a["dims"], a["codec"], a["cache"], a["layer"], a["x_k"], a["x_v"],
+                               a["pos_start"], a["n_new"], 0)
+    assert st == expect
+
+
+@needs_no_gpu
+def test_encode_zero_tokens_enqueues_nothing():
+    st = lla.lla_encode_status(lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256),
+                               lla.make_codec(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE),
+                               lla.make_cache(FAKE, FAKE), 0, FAKE, FAKE, 0, 0, 0)
+    assert st == lla.LLA_OK

@@ -1,0 +1,187 @@
+"""GPU parity of lla_decode_attn against the fp64 oracle, through the C ABI.
+
+Workloads are the seeded synthetic recipes of latent_decode_attention_lla_amd.inputs
+(Ouro-1.4B shapes from "Looped Latent Attention", Appendix A; ranks from Tables 5
+and 8). Small cases are checked element by element over every output; the full-size
+launch configurations are checked on a seeded sample of sequences (all heads, the
+loops named), which the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from latent_decode_attention_lla_amd import lla
+from latent_decode_attention_lla_amd.harness import DeviceLatentStore
+from latent_decode_attention_lla_amd.inputs import WORKLOADS
+from tests.gpu_util import (BF16_TOL, F32_TOL, announce, ensure_built, f64, max_abs,
+                            oracle_decode, rel_note)
+
+pytestmark = pytest.mark.gpu
+
+RECON = lla.LLA_PATH_RECONSTRUCT
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+
+
+# ---------------------------------------------------------------------------
+# tiny float32 workload: T=4, H=2, d=64, (16, 24), batch 1, context 128
+# ---------------------------------------------------------------------------
+
+def test_tiny_f32_all_loops_one_call():
+    w = WORKLOADS["tiny_f32"]
+    announce(f"tiny_f32 all loops, seed 1")
+    st = DeviceLatentStore(w, seed=1)
+    out = st.decode(0, 0, 4, opts=lla.make_opts(0, RECON))
+    torch.cuda.synchronize()
+    ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n)
+    err = max_abs(f64(out), ref)
+    announce(f"tiny_f32 4 loops: {rel_note(err, F32_TOL)}")
+    assert err <= F32_TOL
+
+
+@pytest.mark.parametrize("loop", [0, 1, 2, 3])
+def test_tiny_f32_per_loop_calls(loop):
+    w = WORKLOADS["tiny_f32"]
+    st = DeviceLatentStore(w, seed=1)
+    out = st.decode(0, loop, 1, opts=lla.make_opts(0, RECON))
+    ref = oracle_decode(st, 0, loop, 1, range(w.batch), w.n)
+    assert max_abs(f64(out), ref) <= F32_TOL
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 8])
+def test_tiny_f32_split_invariance(splits):
+    """Any split count gives the oracle's answer (the log-sum-exp merge is exact up to
+    rounding); splits of a 128-token context are at most 8 tiles of 16."""
+    w = WORKLOADS["tiny_f32"].replace(batch=2)
+    st = DeviceLatentStore(w, seed=2)
+    opts = lla.make_opts(splits, RECON)
+    eff = lla.lla_decode_num_splits(st.dims, w.n, 4, opts)
+    assert 1 <= eff <= splits
+    announce(f"tiny_f32 requested {splits} splits, planned {eff}")
+    out = st.decode(0, 0, 4, opts=opts)
+    ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n)
+    assert max_abs(f64(out), ref) <= F32_TOL
+
+
+def test_tiny_f32_ragged_contexts_and_poisoned_tail():
+    """Per-sequence lengths (a full one, a ragged one, one token, none) over a cache whose
+    rows past each length hold NaN: the kernels must never read them."""
+    w = WORKLOADS["tiny_f32"].replace(batch=4, n=128)
+    st = DeviceLatentStore(w, seed=3, n_alloc=160)
+    lens = [128, 77, 1, 0]
+    for b, n_b in enumerate(lens):
+        st.t["c_k"][0, b, :, n_b:] = float("nan")
+        st.t["c_v"][0, b, :, n_b:] = float("nan")
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for splits in (0, 3):
+        out = st.decode(0, 0, 4, n_ctx=128, ctx_lens=ctx, opts=lla.make_opts(splits, RECON))
+        got = f64(out)
+        assert np.isfinite(got).all()
+        assert np.all(got[3] == 0.0)  # empty context -> zeros
+        # oracle on clean copies of the attended rows only
+        ref = oracle_decode(st, 0, 0, 4, range(3), 128, ctx_lens=lens)
+        assert max_abs(got[:3], ref) <= F32_TOL
+
+
+def test_tiny_f32_zero_query_and_single_token():
+    w = WORKLOADS["tiny_f32"]
+    st = DeviceLatentStore(w, seed=4)
+    q0 = torch.zeros(w.batch, w.H, 4, w.d, device="cuda")
+    out = st.decode(0, 0, 4, q=q0, opts=lla.make_opts(0, RECON))
+    ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n, q=q0)
+    assert max_abs(f64(out), ref) <= F32_TOL
+    out1 = st.decode(0, 0, 4, n_ctx=1, opts=lla.make_opts(0, RECON))
+    ref1 = oracle_decode(st, 0, 0, 4, range(w.batch), 1)
+    assert max_abs(f64(out1), ref1) <= F32_TOL
+
+
+def test_empty_context_gives_zeros():
+    w = WORKLOADS["tiny_f32"]
+    st = DeviceLatentStore(w, seed=5)
+    out = st.decode(0, 0, 4, n_ctx=0, opts=lla.make_opts(0, RECON))
+    assert torch.all(out == 0)
+
+
+def test_rope_base_one_million():
+    """RoPE base is an argument (Ouro-family models use 1e6 per the Ragged-KV page)."""
+    w = WORKLOADS["tiny_f32"].replace(rope_base=1.0e6)
+    st = DeviceLatentStore(w, seed=6)
+    out = st.decode(0, 0, 4, opts=lla.make_opts(0, RECON))
+    ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n)
+    assert max_abs(f64(out), ref) <= F32_TOL
+
+
+def test_determinism_bitwise():
+    w = WORKLOADS["ouro_layer_4x"].replace(batch=2, n=300)
+    st = DeviceLatentStore(w, seed=7)
+    a = st.decode(0, 0, 4).clone()
+    b = st.decode(0, 0, 4).clone()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 per-head workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,batch,n,splits", [
+    ("ouro_layer_4x", 2, 300, 0),
+    ("ouro_layer_4x", 2, 300, 5),
+    ("capacity_21x", 3, 517, 0),
+    ("capacity_21x", 3, 517, 4),
+])
+def test_bf16_small_every_output(name, batch, n, splits):
+    w = WORKLOADS[name].replace(batch=batch, n=n, D=2)
+    announce(f"{name} B={batch} n={n} splits={splits}")
+    st = DeviceLatentStore(w, seed=11)
+    for layer in (0, 1):
+        out = st.decode(layer, 0, 4, opts=lla.make_opts(splits, RECON))
+        ref = oracle_decode(st, layer, 0, 4, range(batch), n)
+        err = max_abs(f64(out), ref)
+        announce(f"  layer {layer}: {rel_note(err, BF16_TOL)}")
+        assert err <= BF16_TOL
+
+
+def test_capacity_21x_full_launch_sampled():
+    """The 21.3x capacity point at its real launch shape: 768 sequences x 16 heads,
+    context 4096, one (layer, loop) per call. One layer is resident (the call shape does
+    not depend on D); a seeded sample of sequences is checked against the oracle."""
+    w = WORKLOADS["capacity_21x"].replace(D=1)
+    announce("capacity_21x full launch, B=768 n=4096")
+    st = DeviceLatentStore(w, seed=3)
+    rng = np.random.default_rng(3)
+    seqs = sorted(rng.choice(w.batch, size=4, replace=False).tolist()) + [w.batch - 1]
+    for loop in (0, 3):
+        out = st.decode(0, loop, 1)
+        torch.cuda.synchronize()
+        ref = oracle_decode(st, 0, loop, 1, seqs, w.n)
+        got = f64(out[seqs])
+        err = max_abs(got, ref)
+        announce(f"  loop {loop}: {rel_note(err, BF16_TOL)}")
+        assert err <= BF16_TOL
+        assert torch.isfinite(out).all()
+
+
+def test_lla2d_full_launch_sampled():
+    """LLA-2D (one latent per token shared by 16 heads), batch 16, context 16384."""
+    w = WORKLOADS["lla2d_long"].replace(D=1)
+    announce("lla2d_long full launch, B=16 n=16384")
+    st = DeviceLatentStore(w, seed=5)
+    out = st.decode(0, 2, 1)
+    torch.cuda.synchronize()
+    seqs = [0, 9]
+    ref = oracle_decode(st, 0, 2, 1, seqs, w.n)
+    err = max_abs(f64(out[seqs]), ref)
+    announce(f"  lla2d loop 2: {rel_note(err, BF16_TOL)}")
+    assert err <= BF16_TOL
+
+
+def test_lla2d_small_every_output():
+    w = WORKLOADS["lla2d_long"].replace(D=1, batch=2, n=200)
+    st = DeviceLatentStore(w, seed=6)
+    out = st.decode(0, 0, 4, opts=lla.make_opts(3, RECON))
+    ref = oracle_decode(st, 0, 0, 4, range(2), 200)
+    assert max_abs(f64(out), ref) <= BF16_TOL

@@ -1,0 +1,205 @@
+"""GPU parity of lla_encode (Eq. 2 of "Looped Latent Attention", Section 3) against the
+fp64 oracle, and encode-then-decode round trips through the C ABI.
+
+Bound for stored latents. The GPU forms y = x W_down - mu W_down in float32 and rounds
+once; the oracle forms c = (x - mu) W_down exactly and rounds once. With u = 2^-24 and K
+the contraction length, the float32 error obeys |y - c| <= delta = (K + 2) u
+(sum_k |x_k W_k| + sum_k |mu_k W_k|) (the usual bound for a dot product accumulated in
+K steps), so the two rounded values differ by at most one spacing of the storage type
+plus delta. For bfloat16 that is bf16_ulp(c) + delta; near-zero latents, where the
+cancellation in x W - mu W dominates, are covered by delta. float32 latents use
+u-scaled delta plus 1e-6.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from latent_decode_attention_lla_amd import lla
+from latent_decode_attention_lla_amd.harness import DeviceLatentStore
+from latent_decode_attention_lla_amd.inputs import WORKLOADS, encode_codec_orthonormal, encode_x
+from oracle import lla_oracle as O
+from tests.gpu_util import (BF16_TOL, F32_TOL, announce, bf16_ulp, ensure_built, f64, max_abs,
+                            oracle_decode, rel_note)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+
+
+def _store_for_encode(w, codec, seed, n_max=None, sentinel=0.0):
+    """Device tensors for encode: empty cache (filled with ``sentinel``), the codec (W_down
+    transposed), queries for decode."""
+    n_max = n_max or w.n
+    dt = w.torch_dtype
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    t = {
+        "c_k": torch.full((w.D, w.batch, w.Hc, n_max, w.r_k), sentinel, dtype=dt),
+        "c_v": torch.full((w.D, w.batch, w.Hc, n_max, w.r_v), sentinel, dtype=dt),
+        "w_down_k_t": codec["w_down_k"].transpose(-1, -2).contiguous().to(dt),
+        "w_down_v_t": codec["w_down_v"].transpose(-1, -2).contiguous().to(dt),
+        "mu_k": codec["mu_k"].to(dt), "mu_v": codec["mu_v"].to(dt),
+        "w_up_k": codec["w_up_k"].to(dt), "w_up_v": codec["w_up_v"].to(dt),
+        "q": torch.randn(w.D, w.T, w.batch, w.H, w.d, generator=g),
+    }
+    return DeviceLatentStore(w, seed, n_alloc=n_max, tensors=t)
+
+
+def _oracle_latents(st, layer, x, axis, dtype):
+    """Oracle Eq. 2 for every token of x [B][n][Hc][T][d_in] -> ([B][Hc][n][r] rounded to
+    the storage type, float32 error bound delta of the GPU's accumulation)."""
+    t = st.t
+    wd = f64(t[f"w_down_{axis}_t"][layer]).transpose(0, 2, 1)  # [Hc][K][r]
+    mu = f64(t[f"mu_{axis}"][layer])
+    xx = f64(x)
+    B, n, Hc = xx.shape[:3]
+    xs = xx.reshape(B, n, Hc, -1)
+    K = xs.shape[-1]
+    out = np.empty((B, Hc, n, wd.shape[-1]))
+    delta = np.empty_like(out)
+    for hc in range(Hc):
+        out[:, hc] = O.encode_stored(xs[:, :, hc], mu[hc], wd[hc], dtype)
+        s_abs = np.abs(xs[:, :, hc]) @ np.abs(wd[hc]) + np.abs(mu[hc]) @ np.abs(wd[hc])
+        delta[:, hc] = (K + 2) * 2.0 ** -24 * s_abs
+    return out, delta
+
+
+def _check_latents(got, ref_delta, dtype):
+    ref, delta = ref_delta
+    if dtype == "bf16":
+        allowed = bf16_ulp(ref) + delta
+        bad = np.abs(got - ref) > allowed * (1 + 1e-12)
+        assert not bad.any(), f"{int(bad.sum())} latents off by more than one bf16 spacing + delta"
+        return float(np.max(np.abs(got - ref) / bf16_ulp(ref)))
+    bad = np.abs(got - ref) > delta + 1e-6
+    assert not bad.any(), f"{int(bad.sum())} float32 latents outside the accumulation bound"
+    return max_abs(got, ref)
+
+
+def test_encode_f32_tiny_and_untouched_rows():
+    w = WORKLOADS["tiny_f32"]
+    codec = encode_codec_orthonormal(w, seed=1)
+    st = _store_for_encode(w, codec, seed=1, sentinel=7.0)
+    xk, xv = encode_x(w, 100, seed=2, device="cuda")
+    st.encode(0, xk, xv, pos_start=10, n_new=100)
+    torch.cuda.synchronize()
+    for axis, x in (("k", xk), ("v", xv)):
+        got = f64(st.t[f"c_{axis}"][0])
+        ref = _oracle_latents(st, 0, x, axis, "f32")
+        _check_latents(got[:, :, 10:110], ref, "f32")
+        assert np.all(got[:, :, :10] == 7.0) and np.all(got[:, :, 110:] == 7.0)
+
+
+def test_full_rank_f32_encode_decode_equals_textbook_attention():
+    """r = T d with orthonormal W_down and W_up,t its loop slices: the latent decode of the
+    GPU-encoded cache equals attention on the original keys and values (rotated with
+    the oracle's RoPE), the exactness special case."""
+    w = WORKLOADS["tiny_f32"].replace(r_k=256, r_v=256, batch=2)
+    codec = encode_codec_orthonormal(w, seed=3)
+    st = _store_for_encode(w, codec, seed=3)
+    xk, xv = encode_x(w, w.n, seed=4, device="cuda")
+    st.encode(0, xk, xv, 0, w.n)
+    out = st.decode(0, 0, 4, opts=lla.make_opts(0, lla.LLA_PATH_RECONSTRUCT))
+    got = f64(out)
+    ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n)
+    assert max_abs(got, ref) <= F32_TOL
+    # textbook attention on the original per-loop K/V
+    K, V, q = f64(xk), f64(xv), f64(st.t["q"][0])  # [B][n][H][T][d], q [T][B][H][d]
+    for b in range(w.batch):
+        for h in range(w.H):
+            for t in range(w.T):
+                k = O.apply_rope(K[b, :, h, t][None], np.arange(w.n), w.rope_base)[0]
+                o = O.attention(q[t, b, h], k, V[b, :, h, t], 1.0 / np.sqrt(w.d))
+                assert max_abs(got[b, h, t], o) <= 1e-4
+
+
+@pytest.mark.parametrize("name,batch,n_new,correlated", [
+    ("ouro_layer_4x", 2, 300, False),
+    ("encode_heavy", 1, 77, True),
+    ("lla2d_long", 2, 45, False),
+])
+def test_encode_bf16_small_every_latent(name, batch, n_new, correlated):
+    w = WORKLOADS[name].replace(D=1, batch=batch, n=n_new + 20)
+    announce(f"encode {name} B={batch} n_new={n_new}")
+    codec = encode_codec_orthonormal(w, seed=5) if w.variant == "per_head" else None
+    if codec is None:  # LLA-2D: Gaussian codec (orthonormal 8192 x r also fine but slow)
+        g = torch.Generator().manual_seed(5)
+        K = w.T * w.d_in
+        codec = {"w_down_k": torch.randn(1, 1, K, w.r_k, generator=g, dtype=torch.float64) / K ** 0.5,
+                 "w_down_v": torch.randn(1, 1, K, w.r_v, generator=g, dtype=torch.float64) / K ** 0.5,
+                 "mu_k": torch.randn(1, 1, K, generator=g, dtype=torch.float64) * 0.3,
+                 "mu_v": torch.randn(1, 1, K, generator=g, dtype=torch.float64) * 0.3,
+                 "w_up_k": torch.randn(1, w.T, w.H, w.d, w.r_k, generator=g, dtype=torch.float64) / w.r_k ** 0.5,
+                 "w_up_v": torch.randn(1, w.T, w.H, w.d, w.r_v, generator=g, dtype=torch.float64) / w.r_v ** 0.5}
+    st = _store_for_encode(w, codec, seed=5)
+    xk, xv = encode_x(w, n_new, seed=6, device="cuda", correlated=correlated)
+    st.encode(0, xk, xv, pos_start=20, n_new=n_new)
+    torch.cuda.synchronize()
+    for axis, x in (("k", xk), ("v", xv)):
+        got = f64(st.t[f"c_{axis}"][0])[:, :, 20:20 + n_new]
+        ulps = _check_latents(got, _oracle_latents(st, 0, x, axis, "bf16"), "bf16")
+        announce(f"  {axis}: max {ulps:.2f} bf16 spacings")
+    out = st.decode(0, 0, 4, n_ctx=20 + n_new)
+    ref = oracle_decode(st, 0, 0, 4, range(batch), 20 + n_new)
+    assert max_abs(f64(out), ref) <= BF16_TOL
+
+
+def test_ouro_layer_4x_full_encode_then_decode():
+    """Ouro-1.4B layer at 4x: encode 32 x 4096 tokens (Gaussian per-loop K/V, orthonormal
+    codec), then one decode step over all 4 loops; sampled checks."""
+    w = WORKLOADS["ouro_layer_4x"]
+    announce("ouro_layer_4x full: encode 32x4096, decode 4 loops")
+    codec = encode_codec_orthonormal(w, seed=8)
+    st = _store_for_encode(w, codec, seed=8)
+    xk, xv = encode_x(w, w.n, seed=9, device="cuda")
+    st.encode(0, xk, xv, 0, w.n)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    seqs = [0, int(rng.integers(1, w.batch))]
+    for axis, x in (("k", xk), ("v", xv)):
+        got = f64(st.t[f"c_{axis}"][0][seqs])
+        _check_latents(got, _oracle_latents(st, 0, x[seqs], axis, "bf16"), "bf16")
+    out = st.decode(0, 0, 4)
+    ref = oracle_decode(st, 0, 0, 4, seqs, w.n)
+    err = max_abs(f64(out[seqs]), ref)
+    announce(f"  decode: {rel_note(err, BF16_TOL)}")
+    assert err <= BF16_TOL
+
+
+def test_encode_heavy_full_svd_codec():
+    """Encode-heavy prefill: 8 x 8192 loop-correlated tokens (x_t = x_1 + 0.3 t eps),
+    codec from the SVD initialisation (Section 3) of a 4096-token calibration subsample,
+    then a decode step at context 8192; sampled checks."""
+    w = WORKLOADS["encode_heavy"]
+    announce("encode_heavy full: SVD codec, encode 8x8192, decode at 8192")
+    xk, xv = encode_x(w, w.n, seed=10, device="cuda", correlated=True)
+    rng = np.random.default_rng(10)
+    calib = rng.choice(w.batch * w.n, size=4096, replace=False)
+    codec = {}
+    for axis, x in (("k", xk), ("v", xv)):
+        r = w.r_k if axis == "k" else w.r_v
+        xs = f64(x.reshape(w.batch * w.n, w.H, w.T * w.d)[torch.as_tensor(calib, device="cuda")])
+        wd = np.empty((1, w.H, w.T * w.d, r))
+        wu = np.empty((1, w.T, w.H, w.d, r))
+        mu = np.empty((1, w.H, w.T * w.d))
+        for h in range(w.H):
+            m, W, Wu = O.svd_init(xs[:, h], r, w.T, w.d)
+            wd[0, h], mu[0, h], wu[0, :, h] = W, m, Wu
+        codec[f"w_down_{axis}"] = torch.from_numpy(wd)
+        codec[f"w_up_{axis}"] = torch.from_numpy(wu)
+        codec[f"mu_{axis}"] = torch.from_numpy(mu)
+    st = _store_for_encode(w, codec, seed=10)
+    st.encode(0, xk, xv, 0, w.n)
+    torch.cuda.synchronize()
+    seqs = [3]
+    for axis, x in (("k", xk), ("v", xv)):
+        got = f64(st.t[f"c_{axis}"][0][seqs])
+        _check_latents(got, _oracle_latents(st, 0, x[seqs], axis, "bf16"), "bf16")
+    out = st.decode(0, 1, 1)
+    ref = oracle_decode(st, 0, 1, 1, seqs, w.n)
+    err = max_abs(f64(out[seqs]), ref)
+    announce(f"  decode: {rel_note(err, BF16_TOL)}")
+    assert err <= BF16_TOL
