@@ -1,10 +1,369 @@
-// Latent-store decode, rotary-fold path (gfx950). Placeholder until the kernel lands.
+// Latent-store decode, rotary-fold path (gfx950, wave64, bfloat16 cache and codec).
+//
+// Computes exactly the scores of the reconstruct path ("Looped Latent Attention",
+// Section 3: k_t = c W_up,t^T + mu_t, then RoPE; attention unchanged) through an exact
+// rewrite that moves the rotation onto the matrix cores. For one rotary pair i of a key
+// k rotated by angle j*theta_i, and a query q:
+//   q . R(j theta_i) k = cos(j theta_i) (q_2i k_2i + q_2i+1 k_2i+1)
+//                      + sin(j theta_i) (q_2i+1 k_2i - q_2i k_2i+1).
+// Both brackets are linear in the latent c_j, so with
+//   M[i][r]       = q_2i W[2i][r] + q_2i+1 W[2i+1][r]          (i <  d/2, cosine rows)
+//   M[d/2+i][r]   = q_2i+1 W[2i][r] - q_2i W[2i+1][r]          (sine rows)
+//   M[.][r_k]     = the same with mu_t in place of W[.][r]      (the mean's term)
+// and CS_j = (cos(j theta_0..), sin(j theta_0..)), the score of token j is
+//   s_j = sum_{r < r_k} c_j[r] G_j[r] + G_j[r_k],   G_j = CS_j M   (d x (r_k + 1)).
+// CS is the same for every sequence, head and loop; M depends on (b, h, t) only.
+// G^T = M^T CS^T runs on v_mfma_f32_16x16x32_f16 with M^T (scaled by scale*log2 e, in
+// float16) held in registers for the whole context and CS^T tiles (float16, laid out in
+// fragment order by lla_rope_table_build) staged once per workgroup in LDS and shared by
+// its waves. The lane that holds G_j[4g .. 4g+3] also holds c_j[4g .. 4g+3] (the same
+// layout as a 16x16x16 B fragment of the cache row), so the per-token dot is four FMAs
+// and two cross-lane adds. The value side accumulates softmax-weighted value latents
+// (Appendix J, "Absorbed attention") and applies W_up,v,t and mu_v,t once at the end.
+//
+// Workgroup: HPW waves = HPW heads of one (sequence, loop, context split); they walk the
+// same token range, TPC tiles of 16 tokens per chunk, with the next chunk's cache rows
+// and table tile loaded while the current one is computed. Each lane keeps an online
+// softmax for its token column; the running max is raised only when a score exceeds it
+// by more than 2^8 (scores live in the exp2 domain), which is exact because the same max
+// is used by the running sum and the accumulator.
+#include "lla_device.h"
 #include "lla_kernels.h"
 
 namespace lla {
 
-bool decode_rotary_fold_supported(int, int, int, int) { return false; }
+namespace {
 
-bool launch_decode_rotary_fold(int, int, int, int, const DecodeArgs&, hipStream_t) { return false; }
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleSlack = 8.0f;
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+// native 16-byte vector (HIP's uint4 is a struct whose copies go through memcpy)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8_t& a, const f16x8_t& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Cache rows of one chunk (TPC tiles of 16 tokens) for one lane.
+template <int RK, int RV, int TPC>
+struct Rows {
+  uint2 k[TPC][RK / 16];  // c_k[tok][16 m + 4 g .. +3], bf16
+  u32x4 v[TPC][RV / 32];  // c_v[tok][g RV/4 .. +RV/4), bf16, 16 bytes at a time
+};
+
+template <int RK, int RV, int TPC>
+__device__ __forceinline__ void load_rows(Rows<RK, RV, TPC>& R, const uint16_t* ck, const uint16_t* cv,
+                                          int tok0, int s1, int lo, int hi) {
+#pragma unroll
+  for (int tt = 0; tt < TPC; ++tt) {
+    const int row = min(tok0 + 16 * tt + lo, s1 - 1);
+    const uint16_t* kp = ck + static_cast<size_t>(row) * RK + 4 * hi;
+#pragma unroll
+    for (int m = 0; m < RK / 16; ++m) R.k[tt][m] = *reinterpret_cast<const uint2*>(kp + 16 * m);
+    const uint16_t* vp = cv + static_cast<size_t>(row) * RV + hi * (RV / 4);
+#pragma unroll
+    for (int m = 0; m < RV / 32; ++m) R.v[tt][m] = *reinterpret_cast<const u32x4*>(vp + 8 * m);
+  }
+}
+
+template <int D, int RK, int RV, int HPW, int TPC>
+__global__ __launch_bounds__(64 * HPW) void decode_rotary_fold_kernel(DecodeArgs a) {
+  constexpr int NKS = D / 32;        // k-steps of 32 over the cos|sin index
+  constexpr int NMT = RK / 16 + 1;   // row tiles of M^T: r_k latent rows + the mean row
+  constexpr int NCK = RK / 16;       // 8-byte key-latent pieces per lane per tile
+  constexpr int VS = RV / 4;         // value-latent entries per lane
+  constexpr int NTHR = 64 * HPW;
+  constexpr int TAB_CHUNK = TPC * NKS * 64;  // 16-byte units of table per chunk
+  static_assert(RK % 16 == 0 && RV % 32 == 0 && D % 32 == 0, "shape");
+  static_assert(TAB_CHUNK % NTHR == 0, "table chunk must split evenly over threads");
+  constexpr int TPT = TAB_CHUNK / NTHR;
+  constexpr int WT_STRIDE = D + 8;   // float16 row stride of the transposed W staging
+  constexpr int STAGE_UNITS = HPW * 16 * WT_STRIDE * 2 / 16;
+  constexpr int LDS_UNITS = (2 * TAB_CHUNK > STAGE_UNITS) ? 2 * TAB_CHUNK : STAGE_UNITS;
+
+  __shared__ u32x4 lds[LDS_UNITS];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int lo = lane & 15, hi = lane >> 4;
+  const int split = blockIdx.x;
+  const int groups = a.H / HPW;
+  const int li = blockIdx.y / groups;
+  const int h = (blockIdx.y - li * groups) * HPW + wave;
+  const int b = blockIdx.z;
+  const int t = a.loop_begin + li;
+
+  int len = a.n_ctx;
+  if (a.ctx_lens != nullptr) len = max(0, min(a.ctx_lens[b], a.n_ctx));
+  const int s0 = split * a.split_len;
+  const int s1 = min(len, s0 + a.split_len);
+  const int ntok = max(0, s1 - s0);
+  const int nchunk = (ntok + 16 * TPC - 1) / (16 * TPC);
+
+  // ---- M^T fragments (A operand), float16, scaled into the exp2 domain ----------------
+  // For each 16-row tile of M^T the wave stages W_up,k,t[:, 16 mt .. 16 mt + 15] (or mu for
+  // the mean row) transposed in LDS, then every lane reads the 16 consecutive entries of
+  // its row that its 8 pairs need.
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w_up_k) + static_cast<size_t>(t * a.H + h) * D * RK;
+  const uint16_t* mu = reinterpret_cast<const uint16_t*>(a.mu_k) + static_cast<size_t>(h * a.T + t) * D;
+  const float* q = a.q + (static_cast<size_t>(b * a.H + h) * a.L + li) * D;
+  const float sc = a.scale_log2e;
+  uint16_t* wt = reinterpret_cast<uint16_t*>(lds) + wave * 16 * WT_STRIDE;
+  f16x8_t mf[NMT][NKS];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    // stage: lane handles head-dim rows c = lane + 64 k
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int c = lane + 64 * k;
+      if (mt < NCK) {
+        const uint4* src = reinterpret_cast<const uint4*>(W + static_cast<size_t>(c) * RK + 16 * mt);
+        const uint4 x0 = src[0], x1 = src[1];
+        const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          wt[(2 * j) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] & 0xffffu);
+          wt[(2 * j + 1) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] >> 16);
+        }
+      } else {
+        wt[c] = mu[c];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) wt[j * WT_STRIDE + c] = 0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks2 = 0; ks2 < NKS / 2; ++ks2) {
+      const int p0 = 32 * ks2 + 8 * hi;  // first of this lane's 8 pairs
+      const uint4* wrow = reinterpret_cast<const uint4*>(wt + lo * WT_STRIDE + 2 * p0);
+      const uint4 y0 = wrow[0], y1 = wrow[1];
+      const uint32_t wp[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};  // (W[2p], W[2p+1])
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x0 = __uint_as_float(wp[e] << 16);
+        const float x1 = __uint_as_float(wp[e] & 0xffff0000u);
+        const float2 qp = *reinterpret_cast<const float2*>(q + 2 * (p0 + e));
+        mf[mt][ks2][e] = static_cast<_Float16>((qp.x * x0 + qp.y * x1) * sc);
+        mf[mt][ks2 + NKS / 2][e] = static_cast<_Float16>((qp.y * x0 - qp.x * x1) * sc);
+      }
+    }
+    __syncthreads();
+  }
+
+  const size_t plane = static_cast<size_t>(b * a.H + h) * a.n_max;
+  const uint16_t* ck = reinterpret_cast<const uint16_t*>(a.c_k) + plane * RK;
+  const uint16_t* cv = reinterpret_cast<const uint16_t*>(a.c_v) + plane * RV;
+  const u32x4* tab_g = reinterpret_cast<const u32x4*>(a.rope16);
+  const int tile_max = (s1 > 0 ? (s1 - 1) >> 4 : 0);
+
+  float m_run = kNegInf, l_run = 0.f;
+  float acc[VS];
+#pragma unroll
+  for (int e = 0; e < VS; ++e) acc[e] = 0.f;
+
+  // One chunk: TPC tiles of 16 tokens, from the rows in R and the table in LDS buffer tcur.
+  auto compute_chunk = [&](int c, const Rows<RK, RV, TPC>& R, const u32x4* tcur) {
+#pragma unroll
+    for (int tt = 0; tt < TPC; ++tt) {
+      const int tok = s0 + (c * TPC + tt) * 16 + lo;
+      const bool valid = tok < s1;
+      f32x4 g[NMT];
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) g[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const f16x8_t bf = __builtin_bit_cast(f16x8_t, tcur[(tt * NKS + ks) * 64 + lane]);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) g[mt] = mfma_f16(mf[mt][ks], bf, g[mt]);
+      }
+      float part = (hi == 0) ? g[NMT - 1][0] : 0.f;
+#pragma unroll
+      for (int m = 0; m < NCK; ++m) {
+        const uint2 w = R.k[tt][m];
+        part += __uint_as_float(w.x << 16) * g[m][0] + __uint_as_float(w.x & 0xffff0000u) * g[m][1] +
+                __uint_as_float(w.y << 16) * g[m][2] + __uint_as_float(w.y & 0xffff0000u) * g[m][3];
+      }
+      part += shfl_xor(part, 16);
+      part += shfl_xor(part, 32);
+      const float s = valid ? part : kNegInf;
+
+      // online softmax for this lane's token column, lazily rescaled
+      const bool raise = s > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? s : m_run;
+        const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < VS; ++e) acc[e] *= alpha;
+        m_run = m_new;
+      }
+      const float p = fast_exp2(s - (m_run == kNegInf ? 0.f : m_run));
+      l_run += p;
+#pragma unroll
+      for (int m = 0; m < RV / 32; ++m) {
+        const u32x4 w = R.v[tt][m];
+        acc[8 * m + 0] += p * __uint_as_float(w.x << 16);
+        acc[8 * m + 1] += p * __uint_as_float(w.x & 0xffff0000u);
+        acc[8 * m + 2] += p * __uint_as_float(w.y << 16);
+        acc[8 * m + 3] += p * __uint_as_float(w.y & 0xffff0000u);
+        acc[8 * m + 4] += p * __uint_as_float(w.z << 16);
+        acc[8 * m + 5] += p * __uint_as_float(w.z & 0xffff0000u);
+        acc[8 * m + 6] += p * __uint_as_float(w.w << 16);
+        acc[8 * m + 7] += p * __uint_as_float(w.w & 0xffff0000u);
+      }
+    }
+  };
+
+  // Two row buffers used in turn: chunk c computes from one while chunk c + 1 loads into
+  // the other; the table of chunk c + 1 goes through registers into the other LDS half.
+  Rows<RK, RV, TPC> ra, rb;
+  u32x4 tb[TPT];
+  u32x4* tab0 = lds;
+  u32x4* tab1 = lds + TAB_CHUNK;
+#define LLA_LOAD_TAB(tile0)                                                                   \
+  _Pragma("unroll") for (int k = 0; k < TPT; ++k) {                                           \
+    const int u = k * NTHR + static_cast<int>(threadIdx.x);                                   \
+    const int tile = min((tile0) + u / (NKS * 64), tile_max);                                 \
+    tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];                   \
+  }
+#define LLA_STORE_TAB(dst) \
+  _Pragma("unroll") for (int k = 0; k < TPT; ++k) (dst)[k * NTHR + threadIdx.x] = tb[k];
+
+  if (nchunk > 0) {
+    LLA_LOAD_TAB(s0 >> 4)
+    load_rows<RK, RV, TPC>(ra, ck, cv, s0, s1, lo, hi);
+    LLA_STORE_TAB(tab0)
+  }
+  __syncthreads();
+  for (int c = 0; c < nchunk; c += 2) {
+    // even chunk: compute from (ra, tab0), prefetch into (rb, tab1)
+    const bool more1 = c + 1 < nchunk;
+    if (more1) {
+      LLA_LOAD_TAB((s0 >> 4) + (c + 1) * TPC)
+      load_rows<RK, RV, TPC>(rb, ck, cv, s0 + (c + 1) * TPC * 16, s1, lo, hi);
+    }
+    compute_chunk(c, ra, tab0);
+    if (more1) {
+      LLA_STORE_TAB(tab1)
+    }
+    __syncthreads();
+    if (!more1) break;
+    // odd chunk: compute from (rb, tab1), prefetch into (ra, tab0)
+    const bool more2 = c + 2 < nchunk;
+    if (more2) {
+      LLA_LOAD_TAB((s0 >> 4) + (c + 2) * TPC)
+      load_rows<RK, RV, TPC>(ra, ck, cv, s0 + (c + 2) * TPC * 16, s1, lo, hi);
+    }
+    compute_chunk(c + 1, rb, tab1);
+    if (more2) {
+      LLA_STORE_TAB(tab0)
+    }
+    __syncthreads();
+  }
+#undef LLA_LOAD_TAB
+#undef LLA_STORE_TAB
+
+  // ---- merge the 16 token columns of each lane group ---------------------------------
+  float mx = m_run;
+#pragma unroll
+  for (int msk = 1; msk < 16; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
+  const float scl = (mx == kNegInf) ? 0.f : fast_exp2(m_run - mx);
+  float lsum = l_run * scl;
+#pragma unroll
+  for (int msk = 1; msk < 16; msk <<= 1) lsum += shfl_xor(lsum, msk);
+#pragma unroll
+  for (int e = 0; e < VS; ++e) {
+    float v = acc[e] * scl;
+#pragma unroll
+    for (int msk = 1; msk < 16; msk <<= 1) v += shfl_xor(v, msk);
+    acc[e] = v;
+  }
+
+  const size_t unit = static_cast<size_t>(b * a.H + h) * a.L + li;
+  if (a.S > 1) {
+    float* out = a.part + (unit * a.S + split) * (2 + RV);
+    if (lo == 0) {
+#pragma unroll
+      for (int e = 0; e < VS; ++e) out[2 + hi * VS + e] = acc[e];
+      if (hi == 0) {
+        out[0] = mx;
+        out[1] = lsum;
+      }
+    }
+    return;
+  }
+
+  // ---- single split: finish here, out = (acc / sum) W_up,v,t^T + mu_v,t ---------------
+  float* abar = reinterpret_cast<float*>(lds) + wave * RV;
+  static_assert(sizeof(lds) >= sizeof(float) * RV * HPW, "LDS reuse for the normalised latent");
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  if (lo == 0) {
+#pragma unroll
+    for (int e = 0; e < VS; ++e) abar[hi * VS + e] = acc[e] * inv;
+  }
+  __syncthreads();
+  const uint16_t* Wv = reinterpret_cast<const uint16_t*>(a.w_up_v) + static_cast<size_t>(t * a.H + h) * D * RV;
+  const uint16_t* muv = reinterpret_cast<const uint16_t*>(a.mu_v) + static_cast<size_t>(h * a.T + t) * D;
+  float* out = a.out + unit * D;
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) {
+    const int i = lane + 64 * k;
+    float o = 0.f;
+    if (lsum > 0.f) {
+#pragma unroll
+      for (int r0 = 0; r0 < RV; r0 += 8) {
+        const uint4 w = *reinterpret_cast<const uint4*>(Wv + static_cast<size_t>(i) * RV + r0);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          o += abar[r0 + 2 * k2] * __uint_as_float(ws[k2] << 16);
+          o += abar[r0 + 2 * k2 + 1] * __uint_as_float(ws[k2] & 0xffff0000u);
+        }
+      }
+      o += bf16_to_f32(muv[i]);
+    }
+    out[i] = o;
+  }
+}
+
+template <int D, int RK, int RV, int HPW, int TPC>
+void launch(const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.S, (a.H / HPW) * a.L, a.B);
+  hipLaunchKernelGGL((decode_rotary_fold_kernel<D, RK, RV, HPW, TPC>), grid, dim3(64 * HPW), 0, s, a);
+}
+
+}  // namespace
+
+// (d, r_k, r_v, tiles per chunk); heads per workgroup is 4 (H must be a multiple of 4).
+#define LLA_FOLD_SHAPES(X) \
+  X(128, 16, 32, 4)        \
+  X(128, 32, 64, 2)        \
+  X(128, 96, 160, 1)       \
+  X(128, 128, 128, 1)      \
+  X(64, 16, 32, 4)         \
+  X(64, 32, 32, 2)
+
+bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v) {
+  if (dtype != 1) return false;
+#define X(D_, RK_, RV_, TPC_) \
+  if (d == D_ && r_k == RK_ && r_v == RV_) return true;
+  LLA_FOLD_SHAPES(X)
+#undef X
+  return false;
+}
+
+bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
+                               hipStream_t s) {
+  if (dtype != 1 || a.H % 4 != 0) return false;
+#define X(D_, RK_, RV_, TPC_)                       \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {        \
+    launch<D_, RK_, RV_, 4, TPC_>(a, s);            \
+    return true;                                    \
+  }
+  LLA_FOLD_SHAPES(X)
+#undef X
+  return false;
+}
 
 }  // namespace lla

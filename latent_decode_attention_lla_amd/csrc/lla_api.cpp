@@ -66,12 +66,15 @@ Plan plan_splits(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_
   return p;
 }
 
+bool fold_ok(const lla_dims& d) {
+  return d.dtype == LLA_BF16 && d.variant == LLA_PER_HEAD && d.H % 4 == 0 &&
+         lla::decode_rotary_fold_supported(d.dtype, d.d_head, d.r_k, d.r_v);
+}
+
 int resolve_path(const lla_dims& d, const lla_decode_opts* opts) {
   const int want = opts ? opts->path : LLA_PATH_AUTO;
   if (want == LLA_PATH_AUTO) {
-    if (d.dtype == LLA_BF16 &&
-        lla::decode_rotary_fold_supported(d.dtype, d.d_head, d.r_k, d.r_v) &&
-        d.variant == LLA_PER_HEAD)
+    if (fold_ok(d))
       return LLA_PATH_ROTARY_FOLD;
     return LLA_PATH_RECONSTRUCT;
   }
@@ -114,7 +117,8 @@ double lla_cache_bytes_per_token(const lla_dims* d) {
 
 size_t lla_rope_table_bytes(const lla_dims* d) {
   if (d == nullptr || d->n_max < 1 || d->d_head < 2) return 0;
-  return static_cast<size_t>(d->n_max) * d->d_head * (4 + 2);
+  const size_t n_pad = (static_cast<size_t>(d->n_max) + 15) / 16 * 16;
+  return static_cast<size_t>(d->n_max) * d->d_head * 4 + n_pad * d->d_head * 2;
 }
 
 int32_t lla_rope_table_build(const lla_dims* d, void* table, void* stream) {
@@ -209,9 +213,7 @@ int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cac
 
   const int path = resolve_path(*d, opts);
   if (path == LLA_PATH_ROTARY_FOLD) {
-    if (d->dtype != LLA_BF16 || d->variant != LLA_PER_HEAD ||
-        !lla::decode_rotary_fold_supported(d->dtype, d->d_head, d->r_k, d->r_v))
-      return LLA_ERR_UNSUPPORTED;
+    if (!fold_ok(*d)) return LLA_ERR_UNSUPPORTED;
   } else if (!lla::decode_reconstruct_supported(d->dtype, d->d_head, d->r_k, d->r_v)) {
     return LLA_ERR_UNSUPPORTED;
   }
@@ -260,6 +262,9 @@ int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cac
   if (!ok) return LLA_ERR_UNSUPPORTED;
   st = hip_status();
   if (st != LLA_OK) return st;
+  // The rotary-fold kernel finishes a single split itself (value up-projection in its
+  // epilogue); everything else goes through the split merge.
+  if (path == LLA_PATH_ROTARY_FOLD && p.S == 1) return LLA_OK;
   if (!lla::launch_combine(d->dtype, d->d_head, d->r_v, a, s)) return LLA_ERR_UNSUPPORTED;
   return hip_status();
 }

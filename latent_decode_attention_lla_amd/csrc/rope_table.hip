@@ -7,7 +7,11 @@
 //
 // The angle, cosine and sine are evaluated in float64 and rounded once:
 //   t32[p][i] = (cos, sin) as float32, pairs interleaved      (reconstruct path)
-//   t16[p][i] = cos as float16, t16[p][d/2 + i] = sin as float16 (rotary-fold path)
+//   t16: CS_p[k] = cos(p theta_k) for k < d/2, sin(p theta_(k-d/2)) for k >= d/2, as
+//        float16, stored in the order a 16x16x32 MFMA B fragment is read: position
+//        p = 16 tile + j, index k = 32 ks + 8 g + e lives at
+//        ((tile * (d/32) + ks) * 64 + j + 16 g) * 8 + e, so one wave reads a fragment
+//        as 1 KiB of consecutive bytes. Positions are padded to a multiple of 16.
 #include <math.h>
 
 #include "lla_kernels.h"
@@ -31,25 +35,34 @@ __device__ uint16_t f64_to_f16_bits(double x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+__device__ __forceinline__ size_t frag_offset(int p, int k, int d) {
+  const int tile = p >> 4, j = p & 15;
+  const int ks = k >> 5, g = (k & 31) >> 3, e = k & 7;
+  return ((static_cast<size_t>(tile) * (d / 32) + ks) * 64 + j + 16 * g) * 8 + e;
+}
+
 __global__ void rope_table_kernel(int d, int n_max, double base, float* t32, uint16_t* t16) {
   const int half = d / 2;
+  const int n_pad = (n_max + 15) / 16 * 16;
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<long long>(n_max) * half) return;
+  if (idx >= static_cast<long long>(n_pad) * half) return;
   const int p = static_cast<int>(idx / half);
   const int i = static_cast<int>(idx - static_cast<long long>(p) * half);
   const double theta = pow(base, -2.0 * i / d);
   const double phi = static_cast<double>(p) * theta;
   const double c = cos(phi), s = sin(phi);
-  t32[(static_cast<size_t>(p) * half + i) * 2] = static_cast<float>(c);
-  t32[(static_cast<size_t>(p) * half + i) * 2 + 1] = static_cast<float>(s);
-  t16[static_cast<size_t>(p) * d + i] = f64_to_f16_bits(c);
-  t16[static_cast<size_t>(p) * d + half + i] = f64_to_f16_bits(s);
+  if (p < n_max) {
+    t32[(static_cast<size_t>(p) * half + i) * 2] = static_cast<float>(c);
+    t32[(static_cast<size_t>(p) * half + i) * 2 + 1] = static_cast<float>(s);
+  }
+  t16[frag_offset(p, i, d)] = f64_to_f16_bits(c);
+  t16[frag_offset(p, half + i, d)] = f64_to_f16_bits(s);
 }
 
 }  // namespace
 
 void launch_rope_table(int d, int n_max, double base, float* t32, uint16_t* t16, hipStream_t s) {
-  const long long total = static_cast<long long>(n_max) * (d / 2);
+  const long long total = static_cast<long long>((n_max + 15) / 16 * 16) * (d / 2);
   const int threads = 256;
   const int blocks = static_cast<int>((total + threads - 1) / threads);
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(threads), 0, s, d, n_max, base, t32, t16);

@@ -20,6 +20,8 @@ from tests.gpu_util import (BF16_TOL, F32_TOL, announce, ensure_built, f64, max_
 pytestmark = pytest.mark.gpu
 
 RECON = lla.LLA_PATH_RECONSTRUCT
+FOLD = lla.LLA_PATH_ROTARY_FOLD
+BF16_PATHS = [pytest.param(RECON, id="reconstruct"), pytest.param(FOLD, id="rotary_fold")]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -127,35 +129,40 @@ def test_determinism_bitwise():
 # bfloat16 per-head workloads
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("path", BF16_PATHS)
 @pytest.mark.parametrize("name,batch,n,splits", [
     ("ouro_layer_4x", 2, 300, 0),
     ("ouro_layer_4x", 2, 300, 5),
     ("capacity_21x", 3, 517, 0),
+    ("capacity_21x", 3, 517, 1),
     ("capacity_21x", 3, 517, 4),
+    ("capacity_21x", 2, 16, 1),
+    ("capacity_21x", 2, 1, 1),
 ])
-def test_bf16_small_every_output(name, batch, n, splits):
+def test_bf16_small_every_output(name, batch, n, splits, path):
     w = WORKLOADS[name].replace(batch=batch, n=n, D=2)
-    announce(f"{name} B={batch} n={n} splits={splits}")
+    announce(f"{name} B={batch} n={n} splits={splits} path={path}")
     st = DeviceLatentStore(w, seed=11)
     for layer in (0, 1):
-        out = st.decode(layer, 0, 4, opts=lla.make_opts(splits, RECON))
+        out = st.decode(layer, 0, 4, opts=lla.make_opts(splits, path))
         ref = oracle_decode(st, layer, 0, 4, range(batch), n)
         err = max_abs(f64(out), ref)
         announce(f"  layer {layer}: {rel_note(err, BF16_TOL)}")
         assert err <= BF16_TOL
 
 
-def test_capacity_21x_full_launch_sampled():
+@pytest.mark.parametrize("path", BF16_PATHS)
+def test_capacity_21x_full_launch_sampled(path):
     """The 21.3x capacity point at its real launch shape: 768 sequences x 16 heads,
     context 4096, one (layer, loop) per call. One layer is resident (the call shape does
     not depend on D); a seeded sample of sequences is checked against the oracle."""
     w = WORKLOADS["capacity_21x"].replace(D=1)
-    announce("capacity_21x full launch, B=768 n=4096")
+    announce(f"capacity_21x full launch, B=768 n=4096 path={path}")
     st = DeviceLatentStore(w, seed=3)
     rng = np.random.default_rng(3)
     seqs = sorted(rng.choice(w.batch, size=4, replace=False).tolist()) + [w.batch - 1]
     for loop in (0, 3):
-        out = st.decode(0, loop, 1)
+        out = st.decode(0, loop, 1, opts=lla.make_opts(0, path))
         torch.cuda.synchronize()
         ref = oracle_decode(st, 0, loop, 1, seqs, w.n)
         got = f64(out[seqs])
@@ -185,3 +192,47 @@ def test_lla2d_small_every_output():
     out = st.decode(0, 0, 4, opts=lla.make_opts(3, RECON))
     ref = oracle_decode(st, 0, 0, 4, range(2), 200)
     assert max_abs(f64(out), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("path", BF16_PATHS)
+def test_bf16_ragged_contexts_poisoned_tail(path):
+    """Ragged per-sequence lengths with NaN in every cache row past a sequence's length."""
+    w = WORKLOADS["capacity_21x"].replace(D=1, batch=5, n=300)
+    st = DeviceLatentStore(w, seed=12, n_alloc=320)
+    lens = [300, 257, 17, 1, 0]
+    for b, n_b in enumerate(lens):
+        st.t["c_k"][0, b, :, n_b:] = float("nan")
+        st.t["c_v"][0, b, :, n_b:] = float("nan")
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for splits in (1, 0, 3):
+        out = st.decode(0, 0, 4, n_ctx=300, ctx_lens=ctx, opts=lla.make_opts(splits, path))
+        got = f64(out)
+        assert np.isfinite(got).all()
+        assert np.all(got[4] == 0.0)
+        ref = oracle_decode(st, 0, 0, 4, range(4), 300, ctx_lens=lens)
+        assert max_abs(got[:4], ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("path", BF16_PATHS)
+def test_bf16_ouro_layer_full_sampled(path):
+    """Ouro-1.4B layer at 4x, batch 32, context 4096, all 4 loops in one call."""
+    w = WORKLOADS["ouro_layer_4x"]
+    st = DeviceLatentStore(w, seed=13)
+    out = st.decode(0, 0, 4, opts=lla.make_opts(0, path))
+    seqs = [0, 31]
+    ref = oracle_decode(st, 0, 0, 4, seqs, w.n)
+    err = max_abs(f64(out[seqs]), ref)
+    announce(f"ouro_layer_4x full path={path}: {rel_note(err, BF16_TOL)}")
+    assert err <= BF16_TOL
+
+
+def test_fold_and_reconstruct_agree_at_scale():
+    """Both paths compute the same scores; their outputs over a whole 768 x 16 launch
+    agree to the float16 rounding of the folded operands."""
+    w = WORKLOADS["capacity_21x"].replace(D=1, batch=96)
+    st = DeviceLatentStore(w, seed=14)
+    a = f64(st.decode(0, 1, 1, opts=lla.make_opts(0, RECON)))
+    b = f64(st.decode(0, 1, 1, opts=lla.make_opts(0, FOLD)))
+    err = max_abs(a, b)
+    announce(f"fold vs reconstruct over 96 x 16 outputs: max-abs {err:.3e}")
+    assert err <= BF16_TOL
