@@ -13,7 +13,9 @@
 // from the float32 accumulator, so no intermediate is rounded to bfloat16. The result is
 // rounded once (nearest, ties to even) into the storage type.
 //
-// One wave: 32 tokens (two 16-column tiles) of one (sequence, latent head), all r.
+// One wave: 32 tokens (two 16-column tiles) of one latent head, all r. Tokens are taken
+// over (sequence, new token) jointly, so appending one token to each of many sequences
+// (the decode-time encode) fills the tiles as well as a long prompt does.
 #include "lla_device.h"
 #include "lla_kernels.h"
 
@@ -47,10 +49,10 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a) {
 
   const int lane = threadIdx.x;
   const int lo = lane & 15, hi = lane >> 4;
-  const int j0 = blockIdx.x * (16 * NT);
+  const int j0 = blockIdx.x * (16 * NT);  // flattened (sequence, new token) index
   const int hc = blockIdx.y;
-  const int b = blockIdx.z;
   const int K = a.Kdim;
+  const int total = a.B * a.n_new;
 
   const T* w = static_cast<const T*>(a.w_down_t) + static_cast<size_t>(hc) * R * K;
   const T* mu = static_cast<const T*>(a.mu) + static_cast<size_t>(hc) * K;
@@ -59,9 +61,9 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int tok = j0 + 16 * nt + lo;
-    valid[nt] = tok < a.n_new;
-    const int row = valid[nt] ? tok : a.n_new - 1;
-    xrow[nt] = static_cast<const T*>(a.x) + (static_cast<size_t>(b * a.n_new + row) * a.Hc + hc) * K;
+    valid[nt] = tok < total;
+    const int row = valid[nt] ? tok : total - 1;
+    xrow[nt] = static_cast<const T*>(a.x) + (static_cast<size_t>(row) * a.Hc + hc) * K;
   }
 
   f32x4 acc[NT][NR];
@@ -102,8 +104,10 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a) {
   for (int nt = 0; nt < NT; ++nt) {
     if (!valid[nt]) continue;
     const int tok = j0 + 16 * nt + lo;
+    const int b = tok / a.n_new;
+    const int j = tok - b * a.n_new;
     T* crow = static_cast<T*>(a.c) +
-              (static_cast<size_t>(b * a.Hc + hc) * a.n_max + a.pos_start + tok) * R;
+              (static_cast<size_t>(b * a.Hc + hc) * a.n_max + a.pos_start + j) * R;
 #pragma unroll
     for (int rt = 0; rt < NR; ++rt) {
       f32x4 v = acc[nt][rt];
@@ -115,7 +119,8 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeArgs a) {
 
 template <typename T, int R>
 void launch(const EncodeArgs& a, hipStream_t s) {
-  dim3 grid((a.n_new + 31) / 32, a.Hc, a.B);
+  const long long total = static_cast<long long>(a.B) * a.n_new;
+  dim3 grid(static_cast<unsigned>((total + 31) / 32), a.Hc, 1);
   hipLaunchKernelGGL((encode_kernel<T, R>), grid, dim3(64), 0, s, a);
 }
 

@@ -151,6 +151,8 @@ int32_t lla_encode(const lla_dims* d, const lla_codec* codec, const lla_cache* c
   if (!lla::encode_supported(d->dtype, d->r_k, K) || !lla::encode_supported(d->dtype, d->r_v, K))
     return LLA_ERR_UNSUPPORTED;
   if (n_new == 0) return LLA_OK;
+  // tokens are tiled over (sequence, new token) with a 32-bit flattened index
+  if (static_cast<long long>(d->batch) * n_new >= (1LL << 31) - 64) return LLA_ERR_UNSUPPORTED;
   const size_t es = elem_bytes(*d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int rs[2] = {d->r_k, d->r_v};
