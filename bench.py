@@ -35,12 +35,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_capacity_21x_traffic.json"
 
 
 def kernel_source_hash() -> str:
+    """Hash of the HIP/C++ sources with comments and whitespace removed: it changes when
+    the compiled code can change, not when a comment does."""
+    import re
     csrc = os.path.join(ROOT, "latent_decode_attention_lla_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+            with open(os.path.join(csrc, f)) as fh:
+                src = fh.read()
+            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", " ", src)
+            src = re.sub(r"\s+", " ", src)
+            h.update(f.encode() + src.encode())
     return h.hexdigest()[:16]
 
 

@@ -37,9 +37,36 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;
 
+// Launch-shape knobs (tuned on MI355X; overridable at build time).
+#ifndef LLA_FOLD_HPW
+#define LLA_FOLD_HPW 4          // heads (waves) per workgroup
+#endif
+#ifndef LLA_FOLD_TPC16
+#define LLA_FOLD_TPC16 2        // 16-token tiles per chunk for r_k = 16
+#endif
+#ifndef LLA_FOLD_NT
+#define LLA_FOLD_NT 1           // 1: stream cache rows with non-temporal loads
+#endif
+#ifndef LLA_FOLD_PERMLANE
+#define LLA_FOLD_PERMLANE 1     // 1: cross-lane sums with permlane swaps, 0: LDS shuffles
+#endif
+#ifndef LLA_FOLD_WAVES_PER_EU
+#define LLA_FOLD_WAVES_PER_EU 0  // 0: let the compiler choose
+#endif
+
+template <typename V>
+__device__ __forceinline__ V stream_load(const V* p) {
+#if LLA_FOLD_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 // native 16-byte vector (HIP's uint4 is a struct whose copies go through memcpy)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma_f16(const f16x8_t& a, const f16x8_t& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -60,15 +87,22 @@ __device__ __forceinline__ void load_rows(Rows<RK, RV, TPC>& R, const uint16_t* 
     const int row = min(tok0 + 16 * tt + lo, s1 - 1);
     const uint16_t* kp = ck + static_cast<size_t>(row) * RK + 4 * hi;
 #pragma unroll
-    for (int m = 0; m < RK / 16; ++m) R.k[tt][m] = *reinterpret_cast<const uint2*>(kp + 16 * m);
+    for (int m = 0; m < RK / 16; ++m) {
+      const u32x2 kk = stream_load(reinterpret_cast<const u32x2*>(kp + 16 * m));
+      R.k[tt][m] = make_uint2(kk.x, kk.y);
+    }
     const uint16_t* vp = cv + static_cast<size_t>(row) * RV + hi * (RV / 4);
 #pragma unroll
-    for (int m = 0; m < RV / 32; ++m) R.v[tt][m] = *reinterpret_cast<const u32x4*>(vp + 8 * m);
+    for (int m = 0; m < RV / 32; ++m) R.v[tt][m] = stream_load(reinterpret_cast<const u32x4*>(vp + 8 * m));
   }
 }
 
 template <int D, int RK, int RV, int HPW, int TPC>
-__global__ __launch_bounds__(64 * HPW) void decode_rotary_fold_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * HPW)
+#if LLA_FOLD_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(LLA_FOLD_WAVES_PER_EU)))
+#endif
+void decode_rotary_fold_kernel(DecodeArgs a) {
   constexpr int NKS = D / 32;        // k-steps of 32 over the cos|sin index
   constexpr int NMT = RK / 16 + 1;   // row tiles of M^T: r_k latent rows + the mean row
   constexpr int NCK = RK / 16;       // 8-byte key-latent pieces per lane per tile
@@ -76,8 +110,8 @@ __global__ __launch_bounds__(64 * HPW) void decode_rotary_fold_kernel(DecodeArgs
   constexpr int NTHR = 64 * HPW;
   constexpr int TAB_CHUNK = TPC * NKS * 64;  // 16-byte units of table per chunk
   static_assert(RK % 16 == 0 && RV % 32 == 0 && D % 32 == 0, "shape");
-  static_assert(TAB_CHUNK % NTHR == 0, "table chunk must split evenly over threads");
-  constexpr int TPT = TAB_CHUNK / NTHR;
+  constexpr int TPT = (TAB_CHUNK + NTHR - 1) / NTHR;  // table units per thread per chunk
+  constexpr bool kTabEven = TAB_CHUNK % NTHR == 0;
   constexpr int WT_STRIDE = D + 8;   // float16 row stride of the transposed W staging
   constexpr int STAGE_UNITS = HPW * 16 * WT_STRIDE * 2 / 16;
   constexpr int LDS_UNITS = (2 * TAB_CHUNK > STAGE_UNITS) ? 2 * TAB_CHUNK : STAGE_UNITS;
@@ -184,8 +218,12 @@ __global__ __launch_bounds__(64 * HPW) void decode_rotary_fold_kernel(DecodeArgs
         part += __uint_as_float(w.x << 16) * g[m][0] + __uint_as_float(w.x & 0xffff0000u) * g[m][1] +
                 __uint_as_float(w.y << 16) * g[m][2] + __uint_as_float(w.y & 0xffff0000u) * g[m][3];
       }
+#if LLA_FOLD_PERMLANE
+      part = sum_xor32(sum_xor16(part));
+#else
       part += shfl_xor(part, 16);
       part += shfl_xor(part, 32);
+#endif
       const float s = valid ? part : kNegInf;
 
       // online softmax for this lane's token column, lazily rescaled
@@ -223,12 +261,15 @@ __global__ __launch_bounds__(64 * HPW) void decode_rotary_fold_kernel(DecodeArgs
   u32x4* tab1 = lds + TAB_CHUNK;
 #define LLA_LOAD_TAB(tile0)                                                                   \
   _Pragma("unroll") for (int k = 0; k < TPT; ++k) {                                           \
-    const int u = k * NTHR + static_cast<int>(threadIdx.x);                                   \
+    const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);               \
     const int tile = min((tile0) + u / (NKS * 64), tile_max);                                 \
     tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];                   \
   }
-#define LLA_STORE_TAB(dst) \
-  _Pragma("unroll") for (int k = 0; k < TPT; ++k) (dst)[k * NTHR + threadIdx.x] = tb[k];
+#define LLA_STORE_TAB(dst)                                                                    \
+  _Pragma("unroll") for (int k = 0; k < TPT; ++k) {                                           \
+    const int u = k * NTHR + static_cast<int>(threadIdx.x);                                   \
+    if (kTabEven || u < TAB_CHUNK) (dst)[u] = tb[k];                                          \
+  }
 
   if (nchunk > 0) {
     LLA_LOAD_TAB(s0 >> 4)
@@ -335,9 +376,10 @@ void launch(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// (d, r_k, r_v, tiles per chunk); heads per workgroup is 4 (H must be a multiple of 4).
-#define LLA_FOLD_SHAPES(X) \
-  X(128, 16, 32, 4)        \
+// (d, r_k, r_v, tiles per chunk); heads per workgroup is LLA_FOLD_HPW (H must be a
+// multiple of it).
+#define LLA_FOLD_SHAPES(X)        \
+  X(128, 16, 32, LLA_FOLD_TPC16)  \
   X(128, 32, 64, 2)        \
   X(128, 96, 160, 1)       \
   X(128, 128, 128, 1)      \
@@ -355,10 +397,10 @@ bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v) {
 
 bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                hipStream_t s) {
-  if (dtype != 1 || a.H % 4 != 0) return false;
+  if (dtype != 1 || a.H % LLA_FOLD_HPW != 0) return false;
 #define X(D_, RK_, RV_, TPC_)                       \
   if (d == D_ && r_k == RK_ && r_v == RV_) {        \
-    launch<D_, RK_, RV_, 4, TPC_>(a, s);            \
+    launch<D_, RK_, RV_, LLA_FOLD_HPW, TPC_>(a, s); \
     return true;                                    \
   }
   LLA_FOLD_SHAPES(X)

@@ -67,7 +67,7 @@ Plan plan_splits(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_
 }
 
 bool fold_ok(const lla_dims& d) {
-  return d.dtype == LLA_BF16 && d.variant == LLA_PER_HEAD && d.H % 4 == 0 &&
+  return d.dtype == LLA_BF16 && d.variant == LLA_PER_HEAD && d.H % lla::kFoldHeadsPerGroup == 0 &&
          lla::decode_rotary_fold_supported(d.dtype, d.d_head, d.r_k, d.r_v);
 }
 

@@ -167,6 +167,20 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// v + (v of lane l ^ 16) and v + (v of lane l ^ 32), with the gfx950 permlane swaps: a
+// swap of a register with itself leaves the two row groups that are exchanged in the
+// two results, so their sum is the butterfly sum without a trip through LDS.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace lla

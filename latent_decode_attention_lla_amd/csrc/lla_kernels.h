@@ -33,7 +33,13 @@ struct EncodeArgs {
   int B, Hc, Kdim, n_new, pos_start, n_max;
 };
 
-// Returns false when no kernel is built for (dtype, d, r_k, r_v) on that path.
+// Heads per workgroup of the rotary-fold kernel; H must be a multiple of it.
+#ifndef LLA_FOLD_HPW
+#define LLA_FOLD_HPW 4
+#endif
+constexpr int kFoldHeadsPerGroup = LLA_FOLD_HPW;
+
+// Launchers return false when no kernel is built for (dtype, d, r_k, r_v) on that path.
 bool launch_decode_reconstruct(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                hipStream_t s);
 bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,

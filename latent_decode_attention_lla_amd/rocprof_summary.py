@@ -1,0 +1,98 @@
+"""Summarise rocprofv3 result databases (rocpd SQLite) into the short text tables kept
+under profiles/.
+
+  python -m latent_decode_attention_lla_amd.rocprof_summary kernels RUN_results.db
+  python -m latent_decode_attention_lla_amd.rocprof_summary traffic \
+      --fetch F.db --write W.db --copy-fetch CF.db --copy-write CW.db \
+      --copy-bytes N --kernel decode_rotary_fold --out traffic.json
+
+``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the named kernel by
+what the same counters read for a plain device copy of N bytes read and N bytes written
+(the copy kernel whose counters are largest in the copy runs), and reports HBM bytes per
+launch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import sqlite3
+import sys
+
+
+def kernel_table(db: str):
+    con = sqlite3.connect(db)
+    rows = con.execute(
+        "select name, count(*), avg(duration), sum(duration), min(duration), max(duration) "
+        "from kernels group by name order by sum(duration) desc").fetchall()
+    total = sum(r[3] for r in rows) or 1
+    return [{"kernel": r[0], "calls": r[1], "avg_us": r[2] / 1e3, "total_ms": r[3] / 1e6,
+             "min_us": r[4] / 1e3, "max_us": r[5] / 1e3, "pct": 100.0 * r[3] / total} for r in rows]
+
+
+def counter_per_kernel(db: str, counter: str):
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                       (counter,)).fetchall()
+    agg = {}
+    for name, v in rows:
+        agg.setdefault(name, []).append(float(v))
+    return {k: (len(v), sum(v) / len(v)) for k, v in agg.items()}
+
+
+def _pick(agg: dict, sub: str):
+    hits = [(k, v) for k, v in agg.items() if sub in k]
+    if not hits:
+        raise SystemExit(f"no kernel matching {sub!r}")
+    return max(hits, key=lambda kv: kv[1][1])
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sp = p.add_subparsers(dest="cmd", required=True)
+    k = sp.add_parser("kernels")
+    k.add_argument("db")
+    k.add_argument("--top", type=int, default=12)
+    t = sp.add_parser("traffic")
+    for name in ("fetch", "write", "copy-fetch", "copy-write"):
+        t.add_argument(f"--{name}", required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--out")
+    t.add_argument("--extra", default="{}", help="JSON merged into the output")
+    a = p.parse_args(argv)
+    if a.cmd == "kernels":
+        rows = kernel_table(a.db)
+        print("| calls | avg us | min us | max us | total ms | % | kernel |")
+        print("|---:|---:|---:|---:|---:|---:|---|")
+        for r in rows[:a.top]:
+            print(f"| {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} | "
+                  f"{r['total_ms']:.3f} | {r['pct']:.2f} | `{r['kernel'][:120]}` |")
+        return
+    fk, (fn, fv) = _pick(counter_per_kernel(a.fetch, "FETCH_SIZE"), a.kernel)
+    wk, (wn, wv) = _pick(counter_per_kernel(a.write, "WRITE_SIZE"), a.kernel)
+    ck, (_, cf) = max(counter_per_kernel(a.copy_fetch, "FETCH_SIZE").items(), key=lambda kv: kv[1][1])
+    cw_k, (_, cw) = max(counter_per_kernel(a.copy_write, "WRITE_SIZE").items(), key=lambda kv: kv[1][1])
+    f_scale = a.copy_bytes / (cf * 1024.0)
+    w_scale = a.copy_bytes / (cw * 1024.0)
+    res = {
+        "kernel": fk,
+        "dispatches_fetch": fn, "dispatches_write": wn,
+        "fetch_kib_per_dispatch": fv, "write_kib_per_dispatch": wv,
+        "copy_kernel": ck, "copy_write_kernel": cw_k, "copy_bytes": a.copy_bytes,
+        "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_read_bytes_per_launch": fv * 1024.0 * f_scale,
+        "hbm_write_bytes_per_launch": wv * 1024.0 * w_scale,
+    }
+    res["hbm_bytes_per_launch"] = res["hbm_read_bytes_per_launch"] + res["hbm_write_bytes_per_launch"]
+    res.update(json.loads(a.extra))
+    txt = json.dumps(res, indent=1)
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(txt + "\n")
+    print(txt)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
