@@ -105,6 +105,40 @@ def cpu_baseline(w, seqs: int):
                       f"NumPy, {dt:.1f} s; host os.cpu_count()={os.cpu_count()}"}
 
 
+def algorithmic(w, kind: str, L: int = 1, n_new: int = 0):
+    """Algorithmic HBM bytes and matrix-core flops of one call.
+    decode: every cached latent read once, q and out, one loop's W_up and mu slices;
+            flops are those of rebuilding the keys, 2 r_k d per (token, head) (LLA-2D adds
+            the shared-latent value accumulation, 2 r_v per (token, head)).
+    encode: x_k and x_v read once, latents written once, W_down and mu read once;
+            flops 2 T d_in (r_k + r_v) per (token, latent head)."""
+    es = 2 if w.dtype == "bf16" else 4
+    if kind == "decode":
+        tok = w.batch * w.Hc * w.n
+        nbytes = (tok * (w.r_k + w.r_v) * es + 2 * w.batch * w.H * L * w.d * 4
+                  + L * w.H * w.d * (w.r_k + w.r_v) * es + 2 * L * w.H * w.d * es)
+        if w.variant == "per_head":
+            flops = 2.0 * w.batch * w.H * w.n * L * w.r_k * w.d
+        else:
+            flops = 2.0 * w.batch * w.n * w.H * L * (w.r_k * w.d + w.r_v)
+        return nbytes, flops
+    K = w.T * w.d_in
+    toks = w.batch * n_new * w.Hc
+    nbytes = (2 * toks * K * es + toks * (w.r_k + w.r_v) * es + w.Hc * (w.r_k + w.r_v) * K * es
+              + 2 * w.Hc * K * es)
+    return nbytes, 2.0 * toks * K * (w.r_k + w.r_v)
+
+
+def roofline(nbytes, flops, ms, traffic=None):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    if flops / max(nbytes, 1) > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        return {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -128,11 +162,18 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # Step shape: "append" workloads decode over an existing cache after appending one new
+    # token per sequence; "prefill" workloads encode a whole prompt of n tokens per
+    # sequence for one layer, then take one decode step over all loops of that layer.
+    prefill = args.workload in ("ouro_layer_4x", "encode_heavy")
+    n_new = w.n if prefill else 1
+    pos = 0 if prefill else w.n - 1
+    layers = 1 if prefill else w.D
     print(f"[bench] allocating {args.workload}: latents "
           f"{w.D * w.batch * w.Hc * w.n * (w.r_k + w.r_v) * (2 if w.dtype == 'bf16' else 4) / 2**30:.1f} GiB",
           file=sys.stderr, flush=True)
     st = DeviceLatentStore(w, seed=3, device=dev)
-    # Encode-side codec and the new token's finished per-loop K/V for every layer.
+    # Encode-side codec and the finished per-loop K/V to encode for every layer used.
     g = torch.Generator(device=dev).manual_seed(4)
     K = w.T * w.d_in
     dt = w.torch_dtype
@@ -140,7 +181,7 @@ def main():
     st.t["w_down_v_t"] = (torch.randn(w.D, w.Hc, w.r_v, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
     st.codec = lla.make_codec(st.t["w_down_k_t"], st.t["mu_k"], st.t["w_up_k"], st.t["w_down_v_t"],
                               st.t["mu_v"], st.t["w_up_v"], st.rope)
-    x_new = [torch.randn(w.D, w.batch, 1, w.Hc, w.T, w.d_in, generator=g, device=dev).to(dt)
+    x_new = [torch.randn(layers, w.batch, n_new, w.Hc, w.T, w.d_in, generator=g, device=dev).to(dt)
              for _ in range(2)]
     path = {"auto": lla.LLA_PATH_AUTO, "reconstruct": lla.LLA_PATH_RECONSTRUCT,
             "rotary_fold": lla.LLA_PATH_ROTARY_FOLD}[args.path]
@@ -150,24 +191,32 @@ def main():
     out = torch.empty(w.batch, w.H, 1, w.d, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    n_calls = w.D * w.T
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_calls * max(args.steps, 1))]
+    n_dec = layers * w.T
+    n_enc = layers
+    steps = max(args.steps, 1)
+    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_dec * steps)]
+    ev_enc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_enc * steps)]
 
-    def step(record: int | None):
-        for layer in range(w.D):
+    def step(record):
+        for layer in range(layers):
+            if record is not None:
+                ev_enc[record * n_enc + layer][0].record(stream)
             lla.lla_encode(st.dims, st.codec, st.cache, layer, x_new[0][layer], x_new[1][layer],
-                           w.n - 1, 1, sp)
+                           pos, n_new, sp)
+            if record is not None:
+                ev_enc[record * n_enc + layer][1].record(stream)
         k = 0
         for loop in range(w.T):
-            for layer in range(w.D):
+            for layer in range(layers):
                 q = st.t["q"][layer, loop]
                 if record is not None:
-                    ev[record * n_calls + k][0].record(stream)
+                    ev_dec[record * n_dec + k][0].record(stream)
                 lla.lla_decode_attn(st.dims, st.codec, st.cache, layer, w.n, None, q, loop, 1, out,
                                     ws, ws.numel(), opts, sp)
                 if record is not None:
-                    ev[record * n_calls + k][1].record(stream)
+                    ev_dec[record * n_dec + k][1].record(stream)
                 k += 1
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
@@ -177,7 +226,6 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(args.steps):
@@ -185,20 +233,17 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    call_ms = [a.elapsed_time(b) for a, b in ev[:n_calls * args.steps]]
-    call_ms.sort()
-    avg_call_ms = sum(call_ms) / len(call_ms)
-    med_call_ms = call_ms[len(call_ms) // 2]
+    ms_step = t_start.elapsed_time(t_end) / args.steps
 
-    es = 2 if w.dtype == "bf16" else 4
-    tok = w.batch * w.H * w.n if w.variant == "per_head" else w.batch * w.n
-    lat_bytes = tok * (w.r_k + w.r_v) * es
-    call_bytes = (lat_bytes + 2 * w.batch * w.H * w.d * 4 + w.H * w.d * (w.r_k + w.r_v) * es
-                  + 2 * w.H * w.d * es)
-    call_flops = 2.0 * w.batch * w.H * w.n * w.r_k * w.d
-    achieved_gbs = call_bytes / (avg_call_ms * 1e-3) / 1e9
+    def avg(evs):
+        xs = sorted(a.elapsed_time(b) for a, b in evs[:len(evs)])
+        return sum(xs) / len(xs), xs[len(xs) // 2]
+
+    dec_ms, dec_med = avg(ev_dec[:n_dec * args.steps])
+    enc_ms, enc_med = avg(ev_enc[:n_enc * args.steps])
+    dec_bytes, dec_flops = algorithmic(w, "decode")
+    enc_bytes, enc_flops = algorithmic(w, "encode", n_new=n_new)
+
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
@@ -208,6 +253,9 @@ def main():
             traffic = tr.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
+    dec_roof = roofline(dec_bytes, dec_flops, dec_ms, traffic)
+    enc_roof = roofline(enc_bytes, enc_flops, enc_ms)
+    dominant = "decode" if dec_ms * n_dec >= enc_ms * n_enc else "encode"
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -215,9 +263,13 @@ def main():
         cpu = cpu_baseline(w, args.cpu_sample_seqs)
 
     value = w.batch / (ms_step * 1e-3)
+    step_desc = (f"encode a {n_new}-token prompt per sequence for one layer, then {w.T} decode calls"
+                 if prefill else
+                 f"encode the new token for {w.D} layers, then {w.D} x {w.T} decode calls")
     res = {
-        "metric": "LLA decode tokens/s (full decode step: D layers x T loops of latent-store "
-                  "attention plus the new token's encode), 1 GPU; decode-call HBM GB/s and "
+        "metric": "LLA decode tokens/s (one decode step of the looped model over the latent "
+                  "cache: the new token's encode plus D layers x T loops of latent-store "
+                  "attention), 1 GPU; HBM GB/s or MFMA TFLOP/s of the dominant kernel and "
                   "fraction of peak",
         "value": round(value, 2),
         "unit": "tokens/s",
@@ -232,17 +284,20 @@ def main():
         "data": "synthetic (seeded Gaussian latents, codec maps and queries; no model weights)",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "H": w.H, "d_head": w.d, "r_k": w.r_k,
                    "r_v": w.r_v, "batch": w.batch, "context": w.n, "variant": w.variant,
-                   "path": args.path, "splits": S, "calls_per_step": n_calls,
-                   "encodes_per_step": w.D},
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                   "path": args.path, "splits": S, "step": step_desc,
+                   "decode_calls_per_step": n_dec, "encode_calls_per_step": n_enc},
+        "roofline": dec_roof if dominant == "decode" else enc_roof,
+        "roofline_kernel": "lla_decode_attn" if dominant == "decode" else "lla_encode",
         "cpu_baseline": cpu,
-        "decode_call": {"avg_ms": round(avg_call_ms, 5), "median_ms": round(med_call_ms, 5),
-                        "algorithmic_bytes": call_bytes, "latent_bytes": lat_bytes,
-                        "loop_step_tokens_per_s": round(w.batch / (avg_call_ms * 1e-3), 1),
-                        "mfma_equiv_tflops": round(call_flops / (avg_call_ms * 1e-3) / 1e12, 2),
-                        "mfma_frac": round(call_flops / (avg_call_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "decode_call": {"avg_ms": round(dec_ms, 5), "median_ms": round(dec_med, 5),
+                        "algorithmic_bytes": dec_bytes, "algorithmic_flops": dec_flops,
+                        "loop_step_tokens_per_s": round(w.batch / (dec_ms * 1e-3), 1),
+                        "roofline": dec_roof},
+        "encode_call": {"avg_ms": round(enc_ms, 5), "median_ms": round(enc_med, 5),
+                        "tokens": w.batch * n_new, "algorithmic_bytes": enc_bytes,
+                        "algorithmic_flops": enc_flops,
+                        "tokens_per_s": round(w.batch * n_new / (enc_ms * 1e-3), 1),
+                        "roofline": enc_roof},
         "wall_s_timed": round(wall, 3),
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -1,0 +1,431 @@
+// Latent-store decode, rotary-fold path for wide latents (r_k >= 64), per-head and
+// LLA-2D (gfx950, wave64, bfloat16 cache and codec).
+//
+// Same exact rewrite as decode_rotary_fold.hip ("Looped Latent Attention", Section 3
+// Eq. 3 and "RoPE and reconstruction"; the value identity of Appendix J "Absorbed
+// attention"): the score of token j is c_j . G_j + G_j[r_k] with G_j = CS_j M, M built from
+// q, W_up,k,t and mu_k,t; the value side accumulates softmax-weighted value latents and
+// applies W_up,v,t and mu_v,t once.
+//
+// Wide latents do not fit one wave's registers (M alone is (r_k + 1) x d float16), so each
+// head is served by a pair of waves that split the latent dimension:
+//   half 0: M rows 0 .. 16*NR0-1,             value entries 0 .. r_v/2-1
+//   half 1: M rows 16*NR0 .. r_k-1 + mean row, value entries r_v/2 .. r_v-1
+// Per tile of 16 tokens both halves compute their partial scores, swap them through LDS,
+// and then run the same online softmax on the full scores (so both hold identical maxima
+// and sums) while accumulating their own half of the value latent. Cache rows and cos/sin
+// tiles reach LDS through direct-to-LDS loads issued LLA_WIDE_STAGES - 1 tiles ahead, so
+// the prefetch depth costs no registers.
+//
+// LLA-2D (Section 3, "The LLA-2D variant"): every head reads the same latent plane of its
+// sequence, and mu_t of head h is the (t, h) slice of the stacked mean. Workgroups that
+// share a (sequence, split) are placed on the same XCD (blocks are dealt to the 8 XCDs
+// round robin), so the shared cache rows are read from HBM once into that XCD's L2.
+#include "lla_device.h"
+#include "lla_kernels.h"
+
+namespace lla {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kXcds = 8;
+
+#ifndef LLA_WIDE_STAGES
+#define LLA_WIDE_STAGES 3  // depth of the direct-to-LDS ring (tiles in flight + 1)
+#endif
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8_t& a, const f16x8_t& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int D, int RK, int RV, int HPW, bool SHARED>
+__global__ __launch_bounds__(128 * HPW) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_fold_wide_kernel(DecodeArgs a) {
+  constexpr int NKS = D / 32;
+  constexpr int NCK = RK / 16;            // latent row tiles of M^T
+  constexpr int NR0 = (NCK + 2) / 2;      // row tiles of half 0 (half 1 also has the mean row)
+  constexpr int NT0 = NR0;                // MFMA row tiles of half 0
+  constexpr int NT1 = NCK - NR0 + 1;      // MFMA row tiles of half 1 (last is the mean row)
+  constexpr int NTMAX = NT0 > NT1 ? NT0 : NT1;
+  constexpr int RVH = RV / 2;             // value entries per half
+  constexpr int VSH = RVH / 4;            // value entries per lane
+  constexpr int WT_STRIDE = D + 8;
+  constexpr int STAGE_UNITS = 2 * HPW * 16 * WT_STRIDE * 2 / 16;
+  constexpr int XCH_FLOATS = 2 * HPW * 16;  // partial scores of one tile
+  constexpr int RING_UNITS =
+      LLA_WIDE_STAGES * ((SHARED ? 1 : HPW) * (((16 * (RK / 8 + 1) + 63) / 64) + ((16 * (RV / 8 + 1) + 63) / 64)) + D / 32) * 64;
+  constexpr int LDS_UNITS_RING = RING_UNITS + (XCH_FLOATS + 3) / 4;
+  constexpr int LDS_UNITS = LDS_UNITS_RING > STAGE_UNITS ? LDS_UNITS_RING : STAGE_UNITS;
+  static_assert(RK % 16 == 0 && RV % 16 == 0 && VSH % 4 == 0 && D % 32 == 0, "shape");
+
+  __shared__ u32x4 lds[LDS_UNITS];
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int lo = lane & 15, hi = lane >> 4;
+  const int half = wave & 1;
+  const int hw = wave >> 1;  // head within the workgroup
+
+  // Block placement. Per-head: grid (S, (H / HPW) * L, B). LLA-2D: a flat grid where the
+  // H / HPW head groups of one (sequence, loop, split) sit on the same XCD.
+  const int groups = a.H / HPW;
+  int split, li, hg, b;
+  if constexpr (!SHARED) {
+    split = blockIdx.x;
+    li = blockIdx.y / groups;
+    hg = blockIdx.y - li * groups;
+    b = blockIdx.z;
+  } else {
+    const int L = static_cast<int>(blockIdx.x);
+    const int xcd = L % kXcds;
+    const int slot = L / kXcds;
+    const int unit = xcd + kXcds * (slot / groups);  // (b, li, split) index
+    hg = slot % groups;
+    split = unit % a.S;
+    li = (unit / a.S) % a.L;
+    b = unit / (a.S * a.L);
+    if (b >= a.B) return;  // padding blocks of the last XCD round (whole workgroup exits)
+  }
+  const int h = hg * HPW + hw;
+  const int t = a.loop_begin + li;
+
+  int len = a.n_ctx;
+  if (a.ctx_lens != nullptr) len = max(0, min(a.ctx_lens[b], a.n_ctx));
+  const int s0 = split * a.split_len;
+  const int s1 = min(len, s0 + a.split_len);
+  const int ntok = max(0, s1 - s0);
+
+  // ---- this half's M^T fragments, through a per-wave LDS transpose of W_up,k,t ----
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w_up_k) + static_cast<size_t>(t * a.H + h) * D * RK;
+  const size_t mu_off = SHARED ? static_cast<size_t>(t * a.H + h) * D : static_cast<size_t>(h * a.T + t) * D;
+  const uint16_t* mu = reinterpret_cast<const uint16_t*>(a.mu_k) + mu_off;
+  const float* q = a.q + (static_cast<size_t>(b * a.H + h) * a.L + li) * D;
+  const float sc = a.scale_log2e;
+  uint16_t* wt = reinterpret_cast<uint16_t*>(lds) + wave * 16 * WT_STRIDE;
+  f16x8_t mf[NTMAX][NKS];
+#pragma unroll
+  for (int i = 0; i < NTMAX; ++i) {
+    const int tile = half == 0 ? i : NR0 + i;  // latent row tile, NCK means the mean row
+    const bool active = half == 0 ? (i < NT0) : (i < NT1);
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int c = lane + 64 * k;
+      if (active && tile < NCK) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(c) * RK + 16 * tile);
+        const u32x4 x0 = src[0], x1 = src[1];
+        const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          wt[(2 * j) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] & 0xffffu);
+          wt[(2 * j + 1) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] >> 16);
+        }
+      } else {
+        wt[c] = (active && tile == NCK) ? mu[c] : static_cast<uint16_t>(0);
+#pragma unroll
+        for (int j = 1; j < 16; ++j) wt[j * WT_STRIDE + c] = 0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks2 = 0; ks2 < NKS / 2; ++ks2) {
+      const int p0 = 32 * ks2 + 8 * hi;
+      const u32x4* wrow = reinterpret_cast<const u32x4*>(wt + lo * WT_STRIDE + 2 * p0);
+      const u32x4 y0 = wrow[0], y1 = wrow[1];
+      const uint32_t wp[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x0 = __uint_as_float(wp[e] << 16);
+        const float x1 = __uint_as_float(wp[e] & 0xffff0000u);
+        const float2 qp = *reinterpret_cast<const float2*>(q + 2 * (p0 + e));
+        mf[i][ks2][e] = static_cast<_Float16>((qp.x * x0 + qp.y * x1) * sc);
+        mf[i][ks2 + NKS / 2][e] = static_cast<_Float16>((qp.y * x0 - qp.x * x1) * sc);
+      }
+    }
+    __syncthreads();
+  }
+
+  const size_t plane = SHARED ? static_cast<size_t>(b) * a.n_max
+                              : static_cast<size_t>(b * a.H + h) * a.n_max;
+  const char* ck = reinterpret_cast<const char*>(a.c_k) + plane * RK * 2;
+  const char* cv = reinterpret_cast<const char*>(a.c_v) + plane * RV * 2;
+  const char* tab_g = reinterpret_cast<const char*>(a.rope16);
+  const int tile_max = (s1 > 0 ? (s1 - 1) >> 4 : 0);
+  const int k_tile0 = half == 0 ? 0 : NR0;  // first latent row tile of this half
+  constexpr int NCKH0 = NR0, NCKH1 = NCK - NR0;
+  constexpr int NCKH = NCKH0 > NCKH1 ? NCKH0 : NCKH1;
+  const int ntile = (ntok + 15) >> 4;
+
+  // ---- the ring: per stage one tile of 16 tokens --------------------------------------
+  // For every latent plane of the stage a key region (16 rows of KSP 16-byte slots: the
+  // row's KSL slots plus one padding slot, so that the 16 rows start in different LDS
+  // banks) and a value region (VSP slots per row), then the NKS 1 KiB blocks of the
+  // cos/sin tile. Every region is filled by 1 KiB direct-to-LDS loads
+  // (global_load_lds_dwordx4: lane l writes bytes 16 l .. 16 l + 15 of the block).
+  constexpr int KSL = RK / 8, KSP = KSL + 1;
+  constexpr int VSL = RV / 8, VSP = VSL + 1;
+  constexpr int NIK = (16 * KSP + 63) / 64;
+  constexpr int NIV = (16 * VSP + 63) / 64;
+  constexpr int NPL = SHARED ? 1 : HPW;
+  constexpr int PLB = NIK + NIV;                    // 1 KiB blocks per plane
+  constexpr int STAGE_BLOCKS = NPL * PLB + NKS;
+  constexpr int NW = 2 * HPW;
+  constexpr int NIW = (STAGE_BLOCKS + NW - 1) / NW;  // blocks each wave loads per stage
+  constexpr int NB = LLA_WIDE_STAGES;
+  static_assert(NB >= 2 && (NB - 2) * NIW <= 63, "vmcnt range");
+  static_assert(NB * STAGE_BLOCKS * 64 + (XCH_FLOATS + 3) / 4 <= LDS_UNITS_RING, "ring size");
+  u32x4* ring = lds;
+  float* xch = reinterpret_cast<float*>(lds + NB * STAGE_BLOCKS * 64);  // [wave][16]
+
+  // Per block slot of this wave: which block of the stage, and this lane's source row and
+  // byte column inside its tile (row < 0 marks a table block).
+  // (block index, kind and plane are the same for the whole wave; the row and byte column
+  // are packed as row | col << 8)
+  int blk[NIW], kind[NIW], bpl[NIW];
+  uint32_t rc[NIW];
+#pragma unroll
+  for (int k = 0; k < NIW; ++k) {
+    int bi = wave + NW * k;
+    if (bi >= STAGE_BLOCKS) bi = wave;  // even out the per-wave count with a repeat
+    blk[k] = bi;
+    if (bi >= NPL * PLB) {
+      kind[k] = 2;  // table block ks = bi - NPL * PLB
+      bpl[k] = bi - NPL * PLB;
+      rc[k] = static_cast<uint32_t>(lane * 16) << 8;
+    } else {
+      const int pl = bi / PLB, r = bi - pl * PLB;
+      bpl[k] = pl;
+      const bool isk = r < NIK;
+      kind[k] = isk ? 0 : 1;
+      const int sp = isk ? KSP : VSP, sl = isk ? KSL : VSL;
+      const int slot = (isk ? r : r - NIK) * 64 + lane;
+      rc[k] = static_cast<uint32_t>(min(slot / sp, 15)) |
+              (static_cast<uint32_t>(min(slot % sp, sl - 1) * 16) << 8);
+    }
+  }
+  // plane offsets (elements) of the heads of this workgroup, relative to `plane`
+  auto plane_off = [&](int pl) -> size_t {
+    return SHARED ? 0 : static_cast<size_t>(pl - hw) * a.n_max;
+  };
+
+  auto issue = [&](int tl) {
+    const int stage = tl % NB;
+    const int tok0 = s0 + 16 * tl;
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+      const char* src;
+      const int srow = static_cast<int>(rc[k] & 0xffu);
+      const int scol = static_cast<int>(rc[k] >> 8);
+      if (kind[k] == 2) {
+        const int tile = min((s0 >> 4) + tl, tile_max);
+        src = tab_g + (static_cast<size_t>(tile) * NKS + bpl[k]) * 1024 + scol;
+      } else {
+        const int tok = min(tok0 + srow, s1 - 1);
+        if (kind[k] == 0) {
+          src = ck + (plane_off(bpl[k]) + tok) * static_cast<size_t>(RK * 2) + scol;
+        } else {
+          src = cv + (plane_off(bpl[k]) + tok) * static_cast<size_t>(RV * 2) + scol;
+        }
+      }
+      u32x4* dst = ring + (stage * STAGE_BLOCKS + blk[k]) * 64;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  float acc[VSH];
+#pragma unroll
+  for (int e = 0; e < VSH; ++e) acc[e] = 0.f;
+
+  const int mypl = SHARED ? 0 : hw;
+  if (ntile > 0) {
+#pragma unroll
+    for (int tl = 0; tl < NB - 1; ++tl) issue(tl);
+  }
+  for (int c = 0; c < ntile; ++c) {
+    // this wave's blocks of tile c have landed once at most the later (NB - 2) tiles' are
+    // outstanding; the barrier then makes every wave's blocks visible, and also tells that
+    // every wave is done with tile c - 1, whose stage the next issue overwrites
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * NIW) : "memory");
+    __syncthreads();
+    issue(c + NB - 1);
+    const u32x4* st = ring + (c % NB) * STAGE_BLOCKS * 64;
+    const char* kreg = reinterpret_cast<const char*>(st + (mypl * PLB) * 64);
+    const char* vreg = reinterpret_cast<const char*>(st + (mypl * PLB + NIK) * 64);
+    const u32x4* treg = st + (NPL * PLB) * 64;
+
+    // (1) this half's partial score for the 16 tokens, published to LDS
+    f32x4 g[NTMAX];
+#pragma unroll
+    for (int i = 0; i < NTMAX; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const f16x8_t bf = __builtin_bit_cast(f16x8_t, treg[ks * 64 + lane]);
+#pragma unroll
+      for (int i = 0; i < NTMAX; ++i) {
+        if (i < (half == 0 ? NT0 : NT1)) g[i] = mfma_f16(mf[i][ks], bf, g[i]);
+      }
+    }
+    float pp = 0.f;
+    if (half == 1 && hi == 0) pp = g[NT1 - 1][0];  // the mean row
+#pragma unroll
+    for (int m = 0; m < NCKH; ++m) {
+      if (m < (half == 0 ? NCKH0 : NCKH1)) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(kreg + lo * (KSP * 16) + 32 * (k_tile0 + m) + 8 * hi);
+        pp += __uint_as_float(w.x << 16) * g[m][0] + __uint_as_float(w.x & 0xffff0000u) * g[m][1] +
+              __uint_as_float(w.y << 16) * g[m][2] + __uint_as_float(w.y & 0xffff0000u) * g[m][3];
+      }
+    }
+    const float part = sum_xor32(sum_xor16(pp));
+    if (hi == 0) xch[wave * 16 + lo] = part;
+    __syncthreads();
+
+    // (2) full score, online softmax, this half's value update
+    const int tok = s0 + 16 * c + lo;
+    const bool valid = tok < s1;
+    const float other = xch[(wave ^ 1) * 16 + lo];
+    const float full = half == 0 ? part + other : other + part;  // same order in both halves
+    const float s = valid ? full : kNegInf;
+    const bool raise = s > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? s : m_run;
+      const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < VSH; ++e) acc[e] *= alpha;
+      m_run = m_new;
+    }
+    const float p = fast_exp2(s - (m_run == kNegInf ? 0.f : m_run));
+    l_run += p;
+    const char* vp = vreg + lo * (VSP * 16) + 2 * (half * RVH + hi * VSH);
+#pragma unroll
+    for (int m = 0; m < VSH / 4; ++m) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(vp + 8 * m);
+      acc[4 * m + 0] += p * __uint_as_float(w.x << 16);
+      acc[4 * m + 1] += p * __uint_as_float(w.x & 0xffff0000u);
+      acc[4 * m + 2] += p * __uint_as_float(w.y << 16);
+      acc[4 * m + 3] += p * __uint_as_float(w.y & 0xffff0000u);
+    }
+  }
+  // no direct-to-LDS load may land after this point (the LDS is reused below and at exit)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // ---- merge the 16 token columns (identical maxima and sums in both halves) ----
+  float mx = m_run;
+#pragma unroll
+  for (int msk = 1; msk < 16; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
+  const float scl = (mx == kNegInf) ? 0.f : fast_exp2(m_run - mx);
+  float lsum = l_run * scl;
+#pragma unroll
+  for (int msk = 1; msk < 16; msk <<= 1) lsum += shfl_xor(lsum, msk);
+#pragma unroll
+  for (int e = 0; e < VSH; ++e) {
+    float v = acc[e] * scl;
+#pragma unroll
+    for (int msk = 1; msk < 16; msk <<= 1) v += shfl_xor(v, msk);
+    acc[e] = v;
+  }
+
+  const size_t unit = static_cast<size_t>(b * a.H + h) * a.L + li;
+  if (a.S > 1) {
+    float* out = a.part + (unit * a.S + split) * (2 + RV);
+    if (lo == 0) {
+#pragma unroll
+      for (int e = 0; e < VSH; ++e) out[2 + half * RVH + hi * VSH + e] = acc[e];
+      if (hi == 0 && half == 0) {
+        out[0] = mx;
+        out[1] = lsum;
+      }
+    }
+    return;
+  }
+
+  // ---- single split: out = (acc / sum) W_up,v,t^T + mu_v,t; the pair shares the work ----
+  float* abar = reinterpret_cast<float*>(lds) + hw * RV;
+  static_assert(sizeof(lds) >= sizeof(float) * RV * HPW, "LDS reuse for the normalised latent");
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  if (lo == 0) {
+#pragma unroll
+    for (int e = 0; e < VSH; ++e) abar[half * RVH + hi * VSH + e] = acc[e] * inv;
+  }
+  __syncthreads();
+  const uint16_t* Wv = reinterpret_cast<const uint16_t*>(a.w_up_v) + static_cast<size_t>(t * a.H + h) * D * RV;
+  const size_t muv_off = SHARED ? static_cast<size_t>(t * a.H + h) * D : static_cast<size_t>(h * a.T + t) * D;
+  const uint16_t* muv = reinterpret_cast<const uint16_t*>(a.mu_v) + muv_off;
+  float* out = a.out + unit * D;
+  for (int i = half * (D / 2) + lane; i < (half + 1) * (D / 2); i += 64) {
+    float o = 0.f;
+    if (lsum > 0.f) {
+#pragma unroll 4
+      for (int r0 = 0; r0 < RV; r0 += 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(Wv + static_cast<size_t>(i) * RV + r0);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          o += abar[r0 + 2 * k2] * __uint_as_float(ws[k2] << 16);
+          o += abar[r0 + 2 * k2 + 1] * __uint_as_float(ws[k2] & 0xffff0000u);
+        }
+      }
+      o += bf16_to_f32(muv[i]);
+    }
+    out[i] = o;
+  }
+}
+
+template <int D, int RK, int RV, int HPW, bool SHARED>
+void launch(const DecodeArgs& a, hipStream_t s) {
+  if constexpr (!SHARED) {
+    dim3 grid(a.S, (a.H / HPW) * a.L, a.B);
+    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, SHARED>), grid, dim3(128 * HPW), 0, s, a);
+  } else {
+    // (b, loop, split) units dealt to XCDs so that one unit's head groups share an XCD
+    const long long units = static_cast<long long>(a.B) * a.L * a.S;
+    const long long rounds = (units + kXcds - 1) / kXcds;
+    const long long blocks = rounds * kXcds * (a.H / HPW);
+    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, SHARED>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(128 * HPW), 0, s, a);
+  }
+}
+
+}  // namespace
+
+#ifndef LLA_WIDE_HPW
+#define LLA_WIDE_HPW 2
+#endif
+
+// (d, r_k, r_v) built for the wide path.
+#define LLA_WIDE_SHAPES(X) X(128, 96, 160) X(128, 128, 128) X(64, 256, 256) X(128, 64, 64)
+
+bool decode_fold_wide_supported(int dtype, int d, int r_k, int r_v) {
+  if (dtype != 1) return false;
+#define X(D_, RK_, RV_) \
+  if (d == D_ && r_k == RK_ && r_v == RV_) return true;
+  LLA_WIDE_SHAPES(X)
+#undef X
+  return false;
+}
+
+bool launch_decode_fold_wide(int dtype, int d, int r_k, int r_v, bool shared, const DecodeArgs& a,
+                             hipStream_t s) {
+  if (dtype != 1 || a.H % LLA_WIDE_HPW != 0) return false;
+#define X(D_, RK_, RV_)                                                           \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                                      \
+    if (shared) launch<D_, RK_, RV_, LLA_WIDE_HPW, true>(a, s);     \
+    else launch<D_, RK_, RV_, LLA_WIDE_HPW, false>(a, s);           \
+    return true;                                                                  \
+  }
+  LLA_WIDE_SHAPES(X)
+#undef X
+  return false;
+}
+
+int fold_wide_heads_per_group() { return LLA_WIDE_HPW; }
+
+}  // namespace lla

@@ -378,12 +378,11 @@ void launch(const DecodeArgs& a, hipStream_t s) {
 
 // (d, r_k, r_v, tiles per chunk); heads per workgroup is LLA_FOLD_HPW (H must be a
 // multiple of it).
+// Wider latents go to decode_fold_wide.hip (a pair of waves per head).
 #define LLA_FOLD_SHAPES(X)        \
   X(128, 16, 32, LLA_FOLD_TPC16)  \
-  X(128, 32, 64, 2)        \
-  X(128, 96, 160, 1)       \
-  X(128, 128, 128, 1)      \
-  X(64, 16, 32, 4)         \
+  X(128, 32, 64, 2)               \
+  X(64, 16, 32, 4)                \
   X(64, 32, 32, 2)
 
 bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v) {

@@ -66,10 +66,22 @@ Plan plan_splits(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_
   return p;
 }
 
-bool fold_ok(const lla_dims& d) {
-  return d.dtype == LLA_BF16 && d.variant == LLA_PER_HEAD && d.H % lla::kFoldHeadsPerGroup == 0 &&
-         lla::decode_rotary_fold_supported(d.dtype, d.d_head, d.r_k, d.r_v);
+// Rotary-fold kernels: narrow latents (one wave per head) for the per-head codec, and the
+// wide kernel (a pair of waves per head) for wide latents and for LLA-2D.
+enum FoldKind { kFoldNone = 0, kFoldNarrow = 1, kFoldWide = 2 };
+
+int fold_kind(const lla_dims& d) {
+  if (d.dtype != LLA_BF16) return kFoldNone;
+  if (d.variant == LLA_PER_HEAD && d.H % lla::kFoldHeadsPerGroup == 0 &&
+      lla::decode_rotary_fold_supported(d.dtype, d.d_head, d.r_k, d.r_v))
+    return kFoldNarrow;
+  if (d.H % lla::fold_wide_heads_per_group() == 0 &&
+      lla::decode_fold_wide_supported(d.dtype, d.d_head, d.r_k, d.r_v))
+    return kFoldWide;
+  return kFoldNone;
 }
+
+bool fold_ok(const lla_dims& d) { return fold_kind(d) != kFoldNone; }
 
 int resolve_path(const lla_dims& d, const lla_decode_opts* opts) {
   const int want = opts ? opts->path : LLA_PATH_AUTO;
@@ -258,9 +270,15 @@ int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cac
   a.scale_log2e = static_cast<float>(scale * kLog2e);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  bool ok = path == LLA_PATH_ROTARY_FOLD
-                ? lla::launch_decode_rotary_fold(d->dtype, d->d_head, d->r_k, d->r_v, a, s)
-                : lla::launch_decode_reconstruct(d->dtype, d->d_head, d->r_k, d->r_v, a, s);
+  bool ok;
+  if (path == LLA_PATH_ROTARY_FOLD) {
+    ok = fold_kind(*d) == kFoldNarrow
+             ? lla::launch_decode_rotary_fold(d->dtype, d->d_head, d->r_k, d->r_v, a, s)
+             : lla::launch_decode_fold_wide(d->dtype, d->d_head, d->r_k, d->r_v,
+                                            d->variant == LLA_2D, a, s);
+  } else {
+    ok = lla::launch_decode_reconstruct(d->dtype, d->d_head, d->r_k, d->r_v, a, s);
+  }
   if (!ok) return LLA_ERR_UNSUPPORTED;
   st = hip_status();
   if (st != LLA_OK) return st;

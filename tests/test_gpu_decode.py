@@ -138,6 +138,8 @@ def test_determinism_bitwise():
     ("capacity_21x", 3, 517, 4),
     ("capacity_21x", 2, 16, 1),
     ("capacity_21x", 2, 1, 1),
+    ("ouro_layer_4x", 3, 77, 1),
+    ("ouro_layer_4x", 1, 16, 1),
 ])
 def test_bf16_small_every_output(name, batch, n, splits, path):
     w = WORKLOADS[name].replace(batch=batch, n=n, D=2)
@@ -172,26 +174,47 @@ def test_capacity_21x_full_launch_sampled(path):
         assert torch.isfinite(out).all()
 
 
-def test_lla2d_full_launch_sampled():
+@pytest.mark.parametrize("path", BF16_PATHS)
+def test_lla2d_full_launch_sampled(path):
     """LLA-2D (one latent per token shared by 16 heads), batch 16, context 16384."""
     w = WORKLOADS["lla2d_long"].replace(D=1)
-    announce("lla2d_long full launch, B=16 n=16384")
+    announce(f"lla2d_long full launch, B=16 n=16384 path={path}")
     st = DeviceLatentStore(w, seed=5)
-    out = st.decode(0, 2, 1)
+    out = st.decode(0, 2, 1, opts=lla.make_opts(0, path))
     torch.cuda.synchronize()
-    seqs = [0, 9]
+    seqs = [0, 9, 15]
     ref = oracle_decode(st, 0, 2, 1, seqs, w.n)
     err = max_abs(f64(out[seqs]), ref)
     announce(f"  lla2d loop 2: {rel_note(err, BF16_TOL)}")
     assert err <= BF16_TOL
 
 
-def test_lla2d_small_every_output():
-    w = WORKLOADS["lla2d_long"].replace(D=1, batch=2, n=200)
+@pytest.mark.parametrize("path", BF16_PATHS)
+@pytest.mark.parametrize("batch,n,splits", [(2, 200, 0), (2, 200, 1), (2, 200, 3), (3, 17, 1), (9, 64, 2)])
+def test_lla2d_small_every_output(path, batch, n, splits):
+    w = WORKLOADS["lla2d_long"].replace(D=1, batch=batch, n=n)
     st = DeviceLatentStore(w, seed=6)
-    out = st.decode(0, 0, 4, opts=lla.make_opts(3, RECON))
-    ref = oracle_decode(st, 0, 0, 4, range(2), 200)
-    assert max_abs(f64(out), ref) <= BF16_TOL
+    out = st.decode(0, 0, 4, opts=lla.make_opts(splits, path))
+    ref = oracle_decode(st, 0, 0, 4, range(batch), n)
+    err = max_abs(f64(out), ref)
+    announce(f"lla2d B={batch} n={n} splits={splits} path={path}: {rel_note(err, BF16_TOL)}")
+    assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("path", BF16_PATHS)
+def test_lla2d_ragged_poisoned(path):
+    w = WORKLOADS["lla2d_long"].replace(D=1, batch=4, n=150)
+    st = DeviceLatentStore(w, seed=7, n_alloc=160)
+    lens = [150, 33, 1, 0]
+    for b, n_b in enumerate(lens):
+        st.t["c_k"][0, b, :, n_b:] = float("nan")
+        st.t["c_v"][0, b, :, n_b:] = float("nan")
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for splits in (1, 2):
+        got = f64(st.decode(0, 1, 2, n_ctx=150, ctx_lens=ctx, opts=lla.make_opts(splits, path)))
+        assert np.isfinite(got).all() and np.all(got[3] == 0.0)
+        ref = oracle_decode(st, 0, 1, 2, range(3), 150, ctx_lens=lens)
+        assert max_abs(got[:3], ref) <= BF16_TOL
 
 
 @pytest.mark.parametrize("path", BF16_PATHS)
