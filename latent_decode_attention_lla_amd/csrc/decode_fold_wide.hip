@@ -44,20 +44,32 @@ __device__ __forceinline__ f32x4 mfma_f16(const f16x8_t& a, const f16x8_t& b, f3
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int RK, int RV, int HPW, bool SHARED>
-__global__ __launch_bounds__(128 * HPW) __attribute__((amdgpu_waves_per_eu(2)))
+// Workgroup barrier for the ring loop. __syncthreads() also fences memory, and the
+// compiler implements that fence by waiting for every outstanding direct-to-LDS load
+// (vmcnt(0)), which would drain the ring at each barrier. The ring's loads are waited for
+// explicitly (vmcnt(n) before the barrier that publishes a stage); this barrier only
+// needs this wave's own LDS reads and writes to be complete, and the "memory" clobber
+// keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D, int RK, int RV, int HPW, int NH, bool SHARED>
+__global__ __launch_bounds__(64 * NH * HPW) __attribute__((amdgpu_waves_per_eu(NH == 2 ? 2 : 1)))
 void decode_fold_wide_kernel(DecodeArgs a) {
   constexpr int NKS = D / 32;
   constexpr int NCK = RK / 16;            // latent row tiles of M^T
-  constexpr int NR0 = (NCK + 2) / 2;      // row tiles of half 0 (half 1 also has the mean row)
-  constexpr int NT0 = NR0;                // MFMA row tiles of half 0
-  constexpr int NT1 = NCK - NR0 + 1;      // MFMA row tiles of half 1 (last is the mean row)
+  // NH == 2: half 0 owns latent row tiles [0, NR0), half 1 owns [NR0, NCK) and the mean row.
+  // NH == 1: the single wave owns every row tile and the mean row.
+  constexpr int NR0 = NH == 2 ? (NCK + 2) / 2 : NCK;
+  constexpr int NT0 = NH == 2 ? NR0 : NCK + 1;  // MFMA row tiles of half 0
+  constexpr int NT1 = NCK - NR0 + 1;            // MFMA row tiles of half 1 (last is the mean)
   constexpr int NTMAX = NT0 > NT1 ? NT0 : NT1;
-  constexpr int RVH = RV / 2;             // value entries per half
+  constexpr int RVH = RV / NH;            // value entries per half
   constexpr int VSH = RVH / 4;            // value entries per lane
   constexpr int WT_STRIDE = D + 8;
-  constexpr int STAGE_UNITS = 2 * HPW * 16 * WT_STRIDE * 2 / 16;
-  constexpr int XCH_FLOATS = 2 * HPW * 16;  // partial scores of one tile
+  constexpr int STAGE_UNITS = NH * HPW * 16 * WT_STRIDE * 2 / 16;
+  constexpr int XCH_FLOATS = NH * HPW * 16;  // partial scores of one tile
   constexpr int RING_UNITS =
       LLA_WIDE_STAGES * ((SHARED ? 1 : HPW) * (((16 * (RK / 8 + 1) + 63) / 64) + ((16 * (RV / 8 + 1) + 63) / 64)) + D / 32) * 64;
   constexpr int LDS_UNITS_RING = RING_UNITS + (XCH_FLOATS + 3) / 4;
@@ -69,8 +81,8 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int lo = lane & 15, hi = lane >> 4;
-  const int half = wave & 1;
-  const int hw = wave >> 1;  // head within the workgroup
+  const int half = NH == 2 ? (wave & 1) : 0;
+  const int hw = NH == 2 ? (wave >> 1) : wave;  // head within the workgroup
 
   // Block placement. Per-head: grid (S, (H / HPW) * L, B). LLA-2D: a flat grid where the
   // H / HPW head groups of one (sequence, loop, split) sit on the same XCD.
@@ -111,7 +123,7 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   f16x8_t mf[NTMAX][NKS];
 #pragma unroll
   for (int i = 0; i < NTMAX; ++i) {
-    const int tile = half == 0 ? i : NR0 + i;  // latent row tile, NCK means the mean row
+    const int tile = half == 0 ? i : NR0 + i;  // latent row tile; NCK is the mean row
     const bool active = half == 0 ? (i < NT0) : (i < NT1);
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) {
@@ -157,7 +169,7 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   const char* tab_g = reinterpret_cast<const char*>(a.rope16);
   const int tile_max = (s1 > 0 ? (s1 - 1) >> 4 : 0);
   const int k_tile0 = half == 0 ? 0 : NR0;  // first latent row tile of this half
-  constexpr int NCKH0 = NR0, NCKH1 = NCK - NR0;
+  constexpr int NCKH0 = NR0, NCKH1 = NH == 2 ? NCK - NR0 : 0;
   constexpr int NCKH = NCKH0 > NCKH1 ? NCKH0 : NCKH1;
   const int ntile = (ntok + 15) >> 4;
 
@@ -174,7 +186,7 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   constexpr int NPL = SHARED ? 1 : HPW;
   constexpr int PLB = NIK + NIV;                    // 1 KiB blocks per plane
   constexpr int STAGE_BLOCKS = NPL * PLB + NKS;
-  constexpr int NW = 2 * HPW;
+  constexpr int NW = NH * HPW;
   constexpr int NIW = (STAGE_BLOCKS + NW - 1) / NW;  // blocks each wave loads per stage
   constexpr int NB = LLA_WIDE_STAGES;
   static_assert(NB >= 2 && (NB - 2) * NIW <= 63, "vmcnt range");
@@ -253,7 +265,7 @@ void decode_fold_wide_kernel(DecodeArgs a) {
     // outstanding; the barrier then makes every wave's blocks visible, and also tells that
     // every wave is done with tile c - 1, whose stage the next issue overwrites
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * NIW) : "memory");
-    __syncthreads();
+    ring_barrier();
     issue(c + NB - 1);
     const u32x4* st = ring + (c % NB) * STAGE_BLOCKS * 64;
     const char* kreg = reinterpret_cast<const char*>(st + (mypl * PLB) * 64);
@@ -273,7 +285,10 @@ void decode_fold_wide_kernel(DecodeArgs a) {
       }
     }
     float pp = 0.f;
-    if (half == 1 && hi == 0) pp = g[NT1 - 1][0];  // the mean row
+    if (hi == 0) {
+      if (NH == 1) pp = g[NT0 - 1][0];                 // the mean row
+      else if (half == 1) pp = g[NT1 - 1][0];
+    }
 #pragma unroll
     for (int m = 0; m < NCKH; ++m) {
       if (m < (half == 0 ? NCKH0 : NCKH1)) {
@@ -283,14 +298,17 @@ void decode_fold_wide_kernel(DecodeArgs a) {
       }
     }
     const float part = sum_xor32(sum_xor16(pp));
-    if (hi == 0) xch[wave * 16 + lo] = part;
-    __syncthreads();
+    float full = part;
+    if constexpr (NH == 2) {
+      if (hi == 0) xch[wave * 16 + lo] = part;
+      ring_barrier();
+      const float other = xch[(wave ^ 1) * 16 + lo];
+      full = half == 0 ? part + other : other + part;  // same order in both halves
+    }
 
     // (2) full score, online softmax, this half's value update
     const int tok = s0 + 16 * c + lo;
     const bool valid = tok < s1;
-    const float other = xch[(wave ^ 1) * 16 + lo];
-    const float full = half == 0 ? part + other : other + part;  // same order in both halves
     const float s = valid ? full : kNegInf;
     const bool raise = s > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -350,6 +368,7 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   // ---- single split: out = (acc / sum) W_up,v,t^T + mu_v,t; the pair shares the work ----
   float* abar = reinterpret_cast<float*>(lds) + hw * RV;
   static_assert(sizeof(lds) >= sizeof(float) * RV * HPW, "LDS reuse for the normalised latent");
+  static_assert(NH == 1 || NH == 2, "one or two waves per head");
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   if (lo == 0) {
 #pragma unroll
@@ -360,7 +379,7 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   const size_t muv_off = SHARED ? static_cast<size_t>(t * a.H + h) * D : static_cast<size_t>(h * a.T + t) * D;
   const uint16_t* muv = reinterpret_cast<const uint16_t*>(a.mu_v) + muv_off;
   float* out = a.out + unit * D;
-  for (int i = half * (D / 2) + lane; i < (half + 1) * (D / 2); i += 64) {
+  for (int i = half * (D / NH) + lane; i < (half + 1) * (D / NH); i += 64) {
     float o = 0.f;
     if (lsum > 0.f) {
 #pragma unroll 4
@@ -379,53 +398,69 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int RK, int RV, int HPW, bool SHARED>
+template <int D, int RK, int RV, int HPW, int NH, bool SHARED>
 void launch(const DecodeArgs& a, hipStream_t s) {
   if constexpr (!SHARED) {
     dim3 grid(a.S, (a.H / HPW) * a.L, a.B);
-    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, SHARED>), grid, dim3(128 * HPW), 0, s, a);
+    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, NH, SHARED>), grid, dim3(64 * NH * HPW), 0, s, a);
   } else {
     // (b, loop, split) units dealt to XCDs so that one unit's head groups share an XCD
     const long long units = static_cast<long long>(a.B) * a.L * a.S;
     const long long rounds = (units + kXcds - 1) / kXcds;
     const long long blocks = rounds * kXcds * (a.H / HPW);
-    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, SHARED>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(128 * HPW), 0, s, a);
+    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, NH, SHARED>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * NH * HPW), 0, s, a);
   }
 }
 
 }  // namespace
 
-#ifndef LLA_WIDE_HPW
-#define LLA_WIDE_HPW 2
+// Per shape: (d, r_k, r_v, heads per workgroup per head, heads per workgroup LLA-2D).
+// Ring depth is LLA_WIDE_STAGES; the LDS of a workgroup must stay within 160 KiB.
+#ifndef LLA_WIDE_HPW_PH
+#define LLA_WIDE_HPW_PH 2
 #endif
-
-// (d, r_k, r_v) built for the wide path.
-#define LLA_WIDE_SHAPES(X) X(128, 96, 160) X(128, 128, 128) X(64, 256, 256) X(128, 64, 64)
+#ifndef LLA_WIDE_HPW_2D
+#define LLA_WIDE_HPW_2D 2
+#endif
+#ifndef LLA_WIDE_NH
+#define LLA_WIDE_NH 2  // waves per head: 2 splits the latent dimension, 1 keeps it whole
+#endif
+#define LLA_WIDE_SHAPES(X)                                    \
+  X(128, 96, 160, LLA_WIDE_HPW_PH, LLA_WIDE_HPW_2D)           \
+  X(128, 128, 128, LLA_WIDE_HPW_PH, LLA_WIDE_HPW_2D)          \
+  X(128, 64, 64, LLA_WIDE_HPW_PH, LLA_WIDE_HPW_2D)            \
+  X(64, 256, 256, 2, 2)
 
 bool decode_fold_wide_supported(int dtype, int d, int r_k, int r_v) {
   if (dtype != 1) return false;
-#define X(D_, RK_, RV_) \
+#define X(D_, RK_, RV_, HP_, H2_) \
   if (d == D_ && r_k == RK_ && r_v == RV_) return true;
   LLA_WIDE_SHAPES(X)
 #undef X
   return false;
 }
 
+int fold_wide_heads_per_group(int d, int r_k, int r_v, bool shared) {
+#define X(D_, RK_, RV_, HP_, H2_) \
+  if (d == D_ && r_k == RK_ && r_v == RV_) return shared ? H2_ : HP_;
+  LLA_WIDE_SHAPES(X)
+#undef X
+  return 1 << 30;
+}
+
 bool launch_decode_fold_wide(int dtype, int d, int r_k, int r_v, bool shared, const DecodeArgs& a,
                              hipStream_t s) {
-  if (dtype != 1 || a.H % LLA_WIDE_HPW != 0) return false;
-#define X(D_, RK_, RV_)                                                           \
-  if (d == D_ && r_k == RK_ && r_v == RV_) {                                      \
-    if (shared) launch<D_, RK_, RV_, LLA_WIDE_HPW, true>(a, s);     \
-    else launch<D_, RK_, RV_, LLA_WIDE_HPW, false>(a, s);           \
-    return true;                                                                  \
+  if (dtype != 1 || a.H % fold_wide_heads_per_group(d, r_k, r_v, shared) != 0) return false;
+#define X(D_, RK_, RV_, HP_, H2_)                          \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {               \
+    if (shared) launch<D_, RK_, RV_, H2_, LLA_WIDE_NH, true>(a, s);  \
+    else launch<D_, RK_, RV_, HP_, LLA_WIDE_NH, false>(a, s);        \
+    return true;                                           \
   }
   LLA_WIDE_SHAPES(X)
 #undef X
   return false;
 }
-
-int fold_wide_heads_per_group() { return LLA_WIDE_HPW; }
 
 }  // namespace lla

@@ -75,8 +75,8 @@ int fold_kind(const lla_dims& d) {
   if (d.variant == LLA_PER_HEAD && d.H % lla::kFoldHeadsPerGroup == 0 &&
       lla::decode_rotary_fold_supported(d.dtype, d.d_head, d.r_k, d.r_v))
     return kFoldNarrow;
-  if (d.H % lla::fold_wide_heads_per_group() == 0 &&
-      lla::decode_fold_wide_supported(d.dtype, d.d_head, d.r_k, d.r_v))
+  if (lla::decode_fold_wide_supported(d.dtype, d.d_head, d.r_k, d.r_v) &&
+      d.H % lla::fold_wide_heads_per_group(d.d_head, d.r_k, d.r_v, d.variant == LLA_2D) == 0)
     return kFoldWide;
   return kFoldNone;
 }

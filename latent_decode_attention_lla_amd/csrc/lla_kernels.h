@@ -45,11 +45,11 @@ bool launch_decode_reconstruct(int dtype, int d, int r_k, int r_v, const DecodeA
 bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                hipStream_t s);
 // Wide latents (r_k >= 64): a pair of waves per head; `shared` selects LLA-2D (all heads
-// read one latent plane). H must be a multiple of fold_wide_heads_per_group().
+// read one latent plane). H must be a multiple of fold_wide_heads_per_group(...).
 bool launch_decode_fold_wide(int dtype, int d, int r_k, int r_v, bool shared, const DecodeArgs& a,
                              hipStream_t s);
 bool decode_fold_wide_supported(int dtype, int d, int r_k, int r_v);
-int fold_wide_heads_per_group();
+int fold_wide_heads_per_group(int d, int r_k, int r_v, bool shared);
 bool launch_combine(int dtype, int d, int r_v, const DecodeArgs& a, hipStream_t s);
 bool decode_reconstruct_supported(int dtype, int d, int r_k, int r_v);
 bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v);
