@@ -203,3 +203,46 @@ def test_encode_heavy_full_svd_codec():
     err = max_abs(f64(out[seqs]), ref)
     announce(f"  decode: {rel_note(err, BF16_TOL)}")
     assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("name,batch,n_new,sampled,over", [
+    ("tiny_f32", 3, 10923, False, {}),     # float32 ring kernel, r_v = 24 (partial row tile)
+    ("ouro_layer_4x", 3, 2731, False, {}),  # bfloat16 register-resident stream, r = 96 / 160
+    ("ouro_layer_4x", 2, 8197, False,       # stream with K = 256, r = 256 (8 waves) and 24
+     {"d": 64, "H": 4, "r_k": 256, "r_v": 24}),
+    ("lla2d_long", 5, 13109, True, {}),     # LLA-2D: ring kernel, contraction 8192
+])
+def test_encode_long_prompt_ragged(name, batch, n_new, sampled, over):
+    """Long prompts take the streaming encodes; token counts that are not a multiple of
+    the workgroup's token run leave a ragged last workgroup. Every latent (or, for LLA-2D,
+    a sample that includes the last tokens) against Eq. 2; the rows before and after stay
+    untouched."""
+    w = WORKLOADS[name].replace(D=1, batch=batch, n=n_new + 7, **over)
+    announce(f"long-prompt encode {name} B={batch} n_new={n_new}")
+    K = w.T * w.d_in
+    g = torch.Generator().manual_seed(11)
+    codec = {"w_down_k": torch.randn(1, w.Hc, K, w.r_k, generator=g, dtype=torch.float64) / K ** 0.5,
+             "w_down_v": torch.randn(1, w.Hc, K, w.r_v, generator=g, dtype=torch.float64) / K ** 0.5,
+             "mu_k": torch.randn(1, w.Hc, K, generator=g, dtype=torch.float64) * 0.3,
+             "mu_v": torch.randn(1, w.Hc, K, generator=g, dtype=torch.float64) * 0.3,
+             "w_up_k": torch.randn(1, w.T, w.H, w.d, w.r_k, generator=g, dtype=torch.float64) / w.r_k ** 0.5,
+             "w_up_v": torch.randn(1, w.T, w.H, w.d, w.r_v, generator=g, dtype=torch.float64) / w.r_v ** 0.5}
+    st = _store_for_encode(w, codec, seed=11, sentinel=5.0)
+    xk, xv = encode_x(w, n_new, seed=12, device="cuda")
+    st.encode(0, xk, xv, pos_start=3, n_new=n_new)
+    torch.cuda.synchronize()
+    for axis, x in (("k", xk), ("v", xv)):
+        c = st.t[f"c_{axis}"][0]
+        if sampled:
+            rng = np.random.default_rng(13)
+            flat = np.concatenate([rng.choice(batch * n_new - 64, size=448, replace=False),
+                                   np.arange(batch * n_new - 64, batch * n_new)])
+            bs, js = flat // n_new, flat % n_new
+            xs = x[torch.as_tensor(bs, device="cuda"), torch.as_tensor(js, device="cuda")][None]
+            got = f64(c[torch.as_tensor(bs, device="cuda"), :, torch.as_tensor(js + 3, device="cuda")])
+            ref, delta = _oracle_latents(st, 0, xs, axis, w.dtype)
+            _check_latents(got[None].transpose(0, 2, 1, 3), (ref, delta), w.dtype)
+        else:
+            got = f64(c)
+            _check_latents(got[:, :, 3:3 + n_new], _oracle_latents(st, 0, x, axis, w.dtype), w.dtype)
+            assert np.all(got[:, :, :3] == 5.0) and np.all(got[:, :, 3 + n_new:] == 5.0)
