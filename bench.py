@@ -31,24 +31,53 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_capacity_21x_traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP/C++ sources with comments and whitespace removed: it changes when
-    the compiled code can change, not when a comment does."""
+# Sources whose compiled code (or launch plan) a kernel's measured traffic depends on.
+_COMMON_SOURCES = ("lla_device.h", "lla_kernels.h", "lla_api.cpp")
+KERNEL_SOURCES = {
+    "decode": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip",
+                                 "decode_reconstruct.hip", "combine.hip", "rope_table.hip"),
+    "encode": _COMMON_SOURCES + ("encode.hip",),
+}
+
+
+def kernel_source_hash(kind: str) -> str:
+    """Hash of the HIP/C++ sources behind one call kind ("decode" or "encode") with comments
+    and whitespace removed: it changes when that call's compiled code or launch plan can
+    change, not when a comment or the other call's sources do."""
     import re
     csrc = os.path.join(ROOT, "latent_decode_attention_lla_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f)) as fh:
-                src = fh.read()
-            src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-            src = re.sub(r"//[^\n]*", " ", src)
-            src = re.sub(r"\s+", " ", src)
-            h.update(f.encode() + src.encode())
+    files = [os.path.join(csrc, f) for f in sorted(KERNEL_SOURCES[kind])]
+    files.append(os.path.join(ROOT, "latent_decode_attention_lla_amd", "build.py"))  # flags
+    for path in files:
+        f = os.path.basename(path)
+        with open(path) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        src = re.sub(r"\s+", " ", src)
+        h.update(f.encode() + src.encode())
     return h.hexdigest()[:16]
+
+
+def traffic_file(kind: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.json")
+
+
+def measured_traffic(kind: str, workload: str, path: str):
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or
+    None when there is none or the call's sources have changed since it was taken."""
+    try:
+        with open(traffic_file(kind, workload)) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tr.get("kernel_source_hash") == kernel_source_hash(kind) and tr.get("path") == path \
+            and tr.get("workload") == workload:
+        return tr.get("hbm_bytes_per_launch")
+    return None
 
 
 def parse():
@@ -103,6 +132,12 @@ def cpu_baseline(w, seqs: int):
             "sample": f"{seqs} sequence(s) x {w.H} heads x {w.D} layers x {w.T} loops at context "
                       f"{w.n} (one full decode step for {seqs} of the {w.batch} sequences), fp64 "
                       f"NumPy, {dt:.1f} s; host os.cpu_count()={os.cpu_count()}"}
+
+
+def step_shape(w):
+    """(prefill, tokens encoded per sequence, layers) of one step of workload ``w``."""
+    prefill = w.name in ("ouro_layer_4x", "encode_heavy")
+    return prefill, (w.n if prefill else 1), (1 if prefill else w.D)
 
 
 def algorithmic(w, kind: str, L: int = 1, n_new: int = 0):
@@ -165,10 +200,8 @@ def main():
     # Step shape: "append" workloads decode over an existing cache after appending one new
     # token per sequence; "prefill" workloads encode a whole prompt of n tokens per
     # sequence for one layer, then take one decode step over all loops of that layer.
-    prefill = args.workload in ("ouro_layer_4x", "encode_heavy")
-    n_new = w.n if prefill else 1
+    prefill, n_new, layers = step_shape(w)
     pos = 0 if prefill else w.n - 1
-    layers = 1 if prefill else w.D
     print(f"[bench] allocating {args.workload}: latents "
           f"{w.D * w.batch * w.Hc * w.n * (w.r_k + w.r_v) * (2 if w.dtype == 'bf16' else 4) / 2**30:.1f} GiB",
           file=sys.stderr, flush=True)
@@ -244,17 +277,10 @@ def main():
     dec_bytes, dec_flops = algorithmic(w, "decode")
     enc_bytes, enc_flops = algorithmic(w, "encode", n_new=n_new)
 
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("path") == args.path \
-                and tr.get("workload") == args.workload:
-            traffic = tr.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
-        pass
-    dec_roof = roofline(dec_bytes, dec_flops, dec_ms, traffic)
-    enc_roof = roofline(enc_bytes, enc_flops, enc_ms)
+    dec_roof = roofline(dec_bytes, dec_flops, dec_ms,
+                        measured_traffic("decode", args.workload, args.path))
+    enc_roof = roofline(enc_bytes, enc_flops, enc_ms,
+                        measured_traffic("encode", args.workload, args.path))
     dominant = "decode" if dec_ms * n_dec >= enc_ms * n_enc else "encode"
 
     cpu = None
@@ -299,7 +325,7 @@ def main():
                         "tokens_per_s": round(w.batch * n_new / (enc_ms * 1e-3), 1),
                         "roofline": enc_roof},
         "wall_s_timed": round(wall, 3),
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(res))
 

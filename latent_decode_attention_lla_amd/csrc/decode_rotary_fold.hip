@@ -27,6 +27,8 @@
 // softmax for its token column; the running max is raised only when a score exceeds it
 // by more than 2^8 (scores live in the exp2 domain), which is exact because the same max
 // is used by the running sum and the accumulator.
+#include <type_traits>
+
 #include "lla_device.h"
 #include "lla_kernels.h"
 
@@ -35,6 +37,10 @@ namespace lla {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+// Running maxima start at a finite stand-in for -inf: the first valid score always raises
+// it (so exp2(s - m) never sees inf - inf), and columns or splits without a valid token
+// keep a zero sum, so no per-token test for an empty column is needed.
+constexpr float kMaxInit = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;
 
 // Launch-shape knobs (tuned on MI355X; overridable at build time).
@@ -42,7 +48,7 @@ constexpr float kRescaleSlack = 8.0f;
 #define LLA_FOLD_HPW 4          // heads (waves) per workgroup
 #endif
 #ifndef LLA_FOLD_TPC16
-#define LLA_FOLD_TPC16 2        // 16-token tiles per chunk for r_k = 16
+#define LLA_FOLD_TPC16 4        // 16-token tiles per chunk for r_k = 16
 #endif
 #ifndef LLA_FOLD_NT
 #define LLA_FOLD_NT 1           // 1: stream cache rows with non-temporal loads
@@ -79,12 +85,14 @@ struct Rows {
   u32x4 v[TPC][RV / 32];  // c_v[tok][g RV/4 .. +RV/4), bf16, 16 bytes at a time
 };
 
-template <int RK, int RV, int TPC>
+// CLAMP: rows past the context end re-read its last row (their weights are zero, and the
+// rows themselves may hold anything); full chunks skip the clamp.
+template <bool CLAMP, int RK, int RV, int TPC>
 __device__ __forceinline__ void load_rows(Rows<RK, RV, TPC>& R, const uint16_t* ck, const uint16_t* cv,
                                           int tok0, int s1, int lo, int hi) {
 #pragma unroll
   for (int tt = 0; tt < TPC; ++tt) {
-    const int row = min(tok0 + 16 * tt + lo, s1 - 1);
+    const int row = CLAMP ? min(tok0 + 16 * tt + lo, s1 - 1) : tok0 + 16 * tt + lo;
     const uint16_t* kp = ck + static_cast<size_t>(row) * RK + 4 * hi;
 #pragma unroll
     for (int m = 0; m < RK / 16; ++m) {
@@ -134,6 +142,7 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
   const int s1 = min(len, s0 + a.split_len);
   const int ntok = max(0, s1 - s0);
   const int nchunk = (ntok + 16 * TPC - 1) / (16 * TPC);
+  const int nfull = ntok / (16 * TPC);  // chunks whose tokens are all in the context
 
   // ---- M^T fragments (A operand), float16, scaled into the exp2 domain ----------------
   // For each 16-row tile of M^T the wave stages W_up,k,t[:, 16 mt .. 16 mt + 15] (or mu for
@@ -191,17 +200,18 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
   const u32x4* tab_g = reinterpret_cast<const u32x4*>(a.rope16);
   const int tile_max = (s1 > 0 ? (s1 - 1) >> 4 : 0);
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kMaxInit, l_run = 0.f;
   float acc[VS];
 #pragma unroll
   for (int e = 0; e < VS; ++e) acc[e] = 0.f;
 
   // One chunk: TPC tiles of 16 tokens, from the rows in R and the table in LDS buffer tcur.
-  auto compute_chunk = [&](int c, const Rows<RK, RV, TPC>& R, const u32x4* tcur) {
+  // FULL: every token of the chunk is in the context (no masking).
+  auto compute_chunk = [&](int c, const Rows<RK, RV, TPC>& R, const u32x4* tcur, auto full) {
+    constexpr bool FULL = decltype(full)::value;
 #pragma unroll
     for (int tt = 0; tt < TPC; ++tt) {
       const int tok = s0 + (c * TPC + tt) * 16 + lo;
-      const bool valid = tok < s1;
       f32x4 g[NMT];
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) g[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -211,7 +221,9 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt) g[mt] = mfma_f16(mf[mt][ks], bf, g[mt]);
       }
-      float part = (hi == 0) ? g[NMT - 1][0] : 0.f;
+      // element 0 of the mean tile is the mean row for hi = 0 and an all-zero padding row
+      // of M^T (so exactly 0) for the other lane groups
+      float part = g[NMT - 1][0];
 #pragma unroll
       for (int m = 0; m < NCK; ++m) {
         const uint2 w = R.k[tt][m];
@@ -224,7 +236,7 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
       part += shfl_xor(part, 16);
       part += shfl_xor(part, 32);
 #endif
-      const float s = valid ? part : kNegInf;
+      const float s = (FULL || tok < s1) ? part : kNegInf;
 
       // online softmax for this lane's token column, lazily rescaled
       const bool raise = s > m_run + kRescaleSlack;
@@ -236,7 +248,7 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
         for (int e = 0; e < VS; ++e) acc[e] *= alpha;
         m_run = m_new;
       }
-      const float p = fast_exp2(s - (m_run == kNegInf ? 0.f : m_run));
+      const float p = fast_exp2(s - m_run);
       l_run += p;
 #pragma unroll
       for (int m = 0; m < RV / 32; ++m) {
@@ -259,57 +271,65 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
   u32x4 tb[TPT];
   u32x4* tab0 = lds;
   u32x4* tab1 = lds + TAB_CHUNK;
-#define LLA_LOAD_TAB(tile0)                                                                   \
-  _Pragma("unroll") for (int k = 0; k < TPT; ++k) {                                           \
-    const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);               \
-    const int tile = min((tile0) + u / (NKS * 64), tile_max);                                 \
-    tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];                   \
-  }
-#define LLA_STORE_TAB(dst)                                                                    \
-  _Pragma("unroll") for (int k = 0; k < TPT; ++k) {                                           \
-    const int u = k * NTHR + static_cast<int>(threadIdx.x);                                   \
-    if (kTabEven || u < TAB_CHUNK) (dst)[u] = tb[k];                                          \
-  }
+  auto load_chunk = [&](Rows<RK, RV, TPC>& R, int c) {
+    const int tile0 = (s0 >> 4) + c * TPC;
+    const int tok0 = s0 + c * TPC * 16;
+    if (c < nfull) {
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
+        tb[k] = tab_g[static_cast<size_t>(tile0) * NKS * 64 + u];
+      }
+      load_rows<false, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
+    } else {
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
+        const int tile = min(tile0 + u / (NKS * 64), tile_max);
+        tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];
+      }
+      load_rows<true, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
+    }
+  };
+  auto store_tab = [&](u32x4* dst) {
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int u = k * NTHR + static_cast<int>(threadIdx.x);
+      if (kTabEven || u < TAB_CHUNK) dst[u] = tb[k];
+    }
+  };
+  auto compute = [&](int c, const Rows<RK, RV, TPC>& R, const u32x4* tcur) {
+    if (c < nfull) compute_chunk(c, R, tcur, std::true_type{});
+    else compute_chunk(c, R, tcur, std::false_type{});
+  };
 
   if (nchunk > 0) {
-    LLA_LOAD_TAB(s0 >> 4)
-    load_rows<RK, RV, TPC>(ra, ck, cv, s0, s1, lo, hi);
-    LLA_STORE_TAB(tab0)
+    load_chunk(ra, 0);
+    store_tab(tab0);
   }
   __syncthreads();
   for (int c = 0; c < nchunk; c += 2) {
     // even chunk: compute from (ra, tab0), prefetch into (rb, tab1)
     const bool more1 = c + 1 < nchunk;
-    if (more1) {
-      LLA_LOAD_TAB((s0 >> 4) + (c + 1) * TPC)
-      load_rows<RK, RV, TPC>(rb, ck, cv, s0 + (c + 1) * TPC * 16, s1, lo, hi);
-    }
-    compute_chunk(c, ra, tab0);
-    if (more1) {
-      LLA_STORE_TAB(tab1)
-    }
+    if (more1) load_chunk(rb, c + 1);
+    compute(c, ra, tab0);
+    if (more1) store_tab(tab1);
     __syncthreads();
     if (!more1) break;
     // odd chunk: compute from (rb, tab1), prefetch into (ra, tab0)
     const bool more2 = c + 2 < nchunk;
-    if (more2) {
-      LLA_LOAD_TAB((s0 >> 4) + (c + 2) * TPC)
-      load_rows<RK, RV, TPC>(ra, ck, cv, s0 + (c + 2) * TPC * 16, s1, lo, hi);
-    }
-    compute_chunk(c + 1, rb, tab1);
-    if (more2) {
-      LLA_STORE_TAB(tab0)
-    }
+    if (more2) load_chunk(ra, c + 2);
+    compute(c + 1, rb, tab1);
+    if (more2) store_tab(tab0);
     __syncthreads();
   }
-#undef LLA_LOAD_TAB
-#undef LLA_STORE_TAB
+
 
   // ---- merge the 16 token columns of each lane group ---------------------------------
   float mx = m_run;
 #pragma unroll
   for (int msk = 1; msk < 16; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
-  const float scl = (mx == kNegInf) ? 0.f : fast_exp2(m_run - mx);
+  const float scl = fast_exp2(m_run - mx);
   float lsum = l_run * scl;
 #pragma unroll
   for (int msk = 1; msk < 16; msk <<= 1) lsum += shfl_xor(lsum, msk);

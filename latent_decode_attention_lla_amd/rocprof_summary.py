@@ -9,7 +9,9 @@ under profiles/.
 ``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the named kernel by
 what the same counters read for a plain device copy of N bytes read and N bytes written
 (the copy kernel whose counters are largest in the copy runs), and reports HBM bytes per
-launch.
+launch. ``--kernel`` takes comma-separated name fragments; with ``--sum`` the per-dispatch
+averages of every kernel matching one of them are added (the kernels one API call
+launches once each, e.g. the key and value encodes, or a split decode and its combine).
 """
 
 from __future__ import annotations
@@ -40,11 +42,16 @@ def counter_per_kernel(db: str, counter: str):
     return {k: (len(v), sum(v) / len(v)) for k, v in agg.items()}
 
 
-def _pick(agg: dict, sub: str):
-    hits = [(k, v) for k, v in agg.items() if sub in k]
+def _pick(agg: dict, sub: str, add: bool = False):
+    subs = [x for x in sub.split(",") if x]
+    hits = [(k, v) for k, v in agg.items() if any(x in k for x in subs)]
     if not hits:
         raise SystemExit(f"no kernel matching {sub!r}")
-    return max(hits, key=lambda kv: kv[1][1])
+    if not add:
+        return max(hits, key=lambda kv: kv[1][1])
+    hits.sort()
+    return (" + ".join(k for k, _ in hits),
+            (min(v[0] for _, v in hits), sum(v[1] for _, v in hits)))
 
 
 def main(argv=None):
@@ -58,8 +65,12 @@ def main(argv=None):
         t.add_argument(f"--{name}", required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--kernel", required=True)
+    t.add_argument("--sum", action="store_true")
     t.add_argument("--out")
     t.add_argument("--extra", default="{}", help="JSON merged into the output")
+    t.add_argument("--call", choices=["decode", "encode"],
+                   help="with --workload: record the call's source hash and algorithmic bytes")
+    t.add_argument("--workload")
     a = p.parse_args(argv)
     if a.cmd == "kernels":
         rows = kernel_table(a.db)
@@ -69,8 +80,8 @@ def main(argv=None):
             print(f"| {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} | "
                   f"{r['total_ms']:.3f} | {r['pct']:.2f} | `{r['kernel'][:120]}` |")
         return
-    fk, (fn, fv) = _pick(counter_per_kernel(a.fetch, "FETCH_SIZE"), a.kernel)
-    wk, (wn, wv) = _pick(counter_per_kernel(a.write, "WRITE_SIZE"), a.kernel)
+    fk, (fn, fv) = _pick(counter_per_kernel(a.fetch, "FETCH_SIZE"), a.kernel, a.sum)
+    wk, (wn, wv) = _pick(counter_per_kernel(a.write, "WRITE_SIZE"), a.kernel, a.sum)
     ck, (_, cf) = max(counter_per_kernel(a.copy_fetch, "FETCH_SIZE").items(), key=lambda kv: kv[1][1])
     cw_k, (_, cw) = max(counter_per_kernel(a.copy_write, "WRITE_SIZE").items(), key=lambda kv: kv[1][1])
     f_scale = a.copy_bytes / (cf * 1024.0)
@@ -86,6 +97,18 @@ def main(argv=None):
         "hbm_write_bytes_per_launch": wv * 1024.0 * w_scale,
     }
     res["hbm_bytes_per_launch"] = res["hbm_read_bytes_per_launch"] + res["hbm_write_bytes_per_launch"]
+    if a.call and a.workload:
+        import os
+        sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+        import bench
+        from latent_decode_attention_lla_amd.inputs import WORKLOADS
+        w = WORKLOADS[a.workload]
+        _, n_new, _ = bench.step_shape(w)
+        alg, _ = bench.algorithmic(w, a.call, n_new=n_new)
+        res.update({"call": a.call, "workload": a.workload, "path": "auto",
+                    "kernel_source_hash": bench.kernel_source_hash(a.call),
+                    "algorithmic_bytes_per_launch": alg,
+                    "traffic_over_algorithmic": res["hbm_bytes_per_launch"] / alg})
     res.update(json.loads(a.extra))
     txt = json.dumps(res, indent=1)
     if a.out:
