@@ -21,6 +21,8 @@
 // sequence, and mu_t of head h is the (t, h) slice of the stacked mean. Workgroups that
 // share a (sequence, split) are placed on the same XCD (blocks are dealt to the 8 XCDs
 // round robin), so the shared cache rows are read from HBM once into that XCD's L2.
+#include <type_traits>
+
 #include "lla_device.h"
 #include "lla_kernels.h"
 
@@ -29,6 +31,9 @@ namespace lla {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+// Running maxima start at a finite stand-in for -inf: the first valid score always raises
+// it, and columns or splits without a valid token keep a zero sum.
+constexpr float kMaxInit = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kXcds = 8;
 
@@ -168,10 +173,9 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   const char* cv = reinterpret_cast<const char*>(a.c_v) + plane * RV * 2;
   const char* tab_g = reinterpret_cast<const char*>(a.rope16);
   const int tile_max = (s1 > 0 ? (s1 - 1) >> 4 : 0);
-  const int k_tile0 = half == 0 ? 0 : NR0;  // first latent row tile of this half
   constexpr int NCKH0 = NR0, NCKH1 = NH == 2 ? NCK - NR0 : 0;
-  constexpr int NCKH = NCKH0 > NCKH1 ? NCKH0 : NCKH1;
   const int ntile = (ntok + 15) >> 4;
+  const int nfull = ntok >> 4;  // tiles whose 16 tokens all lie in the context
 
   // ---- the ring: per stage one tile of 16 tokens --------------------------------------
   // For every latent plane of the stage a key region (16 rows of KSP 16-byte slots: the
@@ -194,63 +198,68 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   u32x4* ring = lds;
   float* xch = reinterpret_cast<float*>(lds + NB * STAGE_BLOCKS * 64);  // [wave][16]
 
-  // Per block slot of this wave: which block of the stage, and this lane's source row and
-  // byte column inside its tile (row < 0 marks a table block).
-  // (block index, kind and plane are the same for the whole wave; the row and byte column
-  // are packed as row | col << 8)
-  int blk[NIW], kind[NIW], bpl[NIW];
-  uint32_t rc[NIW];
+  // Per block slot of this wave: the block index in the stage, this lane's source address
+  // for the next tile to be issued, and the byte step from one tile to the next. Tiles
+  // wholly inside the context advance the address by the step; the last, partial tile (and
+  // the ring's run-out past the end) recomputes it with the token clamped to the last one
+  // in the context (the clamped rows get zero weight) and the table tile to the last used.
+  int blk[NIW], srow[NIW];
+  const char* nxt[NIW];
+  const char* sbase[NIW];  // slot's source at tile 0 minus its row offset (rows clamp)
+  int rbytes[NIW];         // bytes per source row (0 marks a table block)
+  size_t step[NIW];        // bytes from one tile's source to the next
 #pragma unroll
   for (int k = 0; k < NIW; ++k) {
     int bi = wave + NW * k;
     if (bi >= STAGE_BLOCKS) bi = wave;  // even out the per-wave count with a repeat
     blk[k] = bi;
     if (bi >= NPL * PLB) {
-      kind[k] = 2;  // table block ks = bi - NPL * PLB
-      bpl[k] = bi - NPL * PLB;
-      rc[k] = static_cast<uint32_t>(lane * 16) << 8;
+      const int ks = bi - NPL * PLB;
+      rbytes[k] = 0;
+      srow[k] = 0;
+      step[k] = static_cast<size_t>(NKS) * 1024;
+      sbase[k] = tab_g + static_cast<size_t>(ks) * 1024 + lane * 16;
+      nxt[k] = sbase[k] + static_cast<size_t>(s0 >> 4) * NKS * 1024;
     } else {
       const int pl = bi / PLB, r = bi - pl * PLB;
-      bpl[k] = pl;
       const bool isk = r < NIK;
-      kind[k] = isk ? 0 : 1;
       const int sp = isk ? KSP : VSP, sl = isk ? KSL : VSL;
       const int slot = (isk ? r : r - NIK) * 64 + lane;
-      rc[k] = static_cast<uint32_t>(min(slot / sp, 15)) |
-              (static_cast<uint32_t>(min(slot % sp, sl - 1) * 16) << 8);
+      const int row = min(slot / sp, 15);
+      const int col = min(slot % sp, sl - 1) * 16;
+      const size_t poff = SHARED ? 0 : static_cast<size_t>(pl - hw) * a.n_max;
+      rbytes[k] = isk ? RK * 2 : RV * 2;
+      srow[k] = row;
+      step[k] = static_cast<size_t>(16) * rbytes[k];
+      sbase[k] = (isk ? ck + poff * (RK * 2) : cv + poff * (RV * 2)) + col;
+      nxt[k] = sbase[k] + static_cast<size_t>(s0 + row) * rbytes[k];
     }
   }
-  // plane offsets (elements) of the heads of this workgroup, relative to `plane`
-  auto plane_off = [&](int pl) -> size_t {
-    return SHARED ? 0 : static_cast<size_t>(pl - hw) * a.n_max;
-  };
 
+  auto dma = [&](const char* src, u32x4* dst) {
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                     (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+  };
   auto issue = [&](int tl) {
-    const int stage = tl % NB;
-    const int tok0 = s0 + 16 * tl;
+    u32x4* stage = ring + (tl % NB) * STAGE_BLOCKS * 64;
+    if (tl < nfull) {
 #pragma unroll
-    for (int k = 0; k < NIW; ++k) {
-      const char* src;
-      const int srow = static_cast<int>(rc[k] & 0xffu);
-      const int scol = static_cast<int>(rc[k] >> 8);
-      if (kind[k] == 2) {
-        const int tile = min((s0 >> 4) + tl, tile_max);
-        src = tab_g + (static_cast<size_t>(tile) * NKS + bpl[k]) * 1024 + scol;
-      } else {
-        const int tok = min(tok0 + srow, s1 - 1);
-        if (kind[k] == 0) {
-          src = ck + (plane_off(bpl[k]) + tok) * static_cast<size_t>(RK * 2) + scol;
-        } else {
-          src = cv + (plane_off(bpl[k]) + tok) * static_cast<size_t>(RV * 2) + scol;
-        }
+      for (int k = 0; k < NIW; ++k) {
+        dma(nxt[k], stage + blk[k] * 64);
+        nxt[k] += step[k];
       }
-      u32x4* dst = ring + (stage * STAGE_BLOCKS + blk[k]) * 64;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NIW; ++k) {
+        const char* src =
+            rbytes[k] == 0 ? sbase[k] + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * NKS * 1024
+                           : sbase[k] + static_cast<size_t>(min(s0 + 16 * tl + srow[k], s1 - 1)) * rbytes[k];
+        dma(src, stage + blk[k] * 64);
+      }
     }
   };
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kMaxInit, l_run = 0.f;
   float acc[VSH];
 #pragma unroll
   for (int e = 0; e < VSH; ++e) acc[e] = 0.f;
@@ -260,76 +269,84 @@ void decode_fold_wide_kernel(DecodeArgs a) {
 #pragma unroll
     for (int tl = 0; tl < NB - 1; ++tl) issue(tl);
   }
-  for (int c = 0; c < ntile; ++c) {
-    // this wave's blocks of tile c have landed once at most the later (NB - 2) tiles' are
-    // outstanding; the barrier then makes every wave's blocks visible, and also tells that
-    // every wave is done with tile c - 1, whose stage the next issue overwrites
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * NIW) : "memory");
-    ring_barrier();
-    issue(c + NB - 1);
-    const u32x4* st = ring + (c % NB) * STAGE_BLOCKS * 64;
-    const char* kreg = reinterpret_cast<const char*>(st + (mypl * PLB) * 64);
-    const char* vreg = reinterpret_cast<const char*>(st + (mypl * PLB + NIK) * 64);
-    const u32x4* treg = st + (NPL * PLB) * 64;
 
-    // (1) this half's partial score for the 16 tokens, published to LDS
-    f32x4 g[NTMAX];
+  // The tile loop, compiled once per half so that which row tiles, latent rows and value
+  // entries a wave owns are compile-time constants (no branches inside the loop).
+  auto run = [&](auto half_c) {
+    constexpr int HALF = decltype(half_c)::value;
+    constexpr int NT = HALF == 0 ? NT0 : NT1;          // MFMA row tiles of this half
+    constexpr int NCKh = HALF == 0 ? NCKH0 : NCKH1;    // latent row tiles of this half
+    constexpr int KT0 = HALF == 0 ? 0 : NR0;           // its first latent row tile
+    constexpr bool MEAN = NH == 1 || HALF == 1;        // its last MFMA tile holds the mean row
+    for (int c = 0; c < ntile; ++c) {
+      // this wave's blocks of tile c have landed once at most the later (NB - 2) tiles'
+      // are outstanding; the barrier then makes every wave's blocks visible, and also tells
+      // that every wave is done with tile c - 1, whose stage the next issue overwrites
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * NIW) : "memory");
+      ring_barrier();
+      issue(c + NB - 1);
+      const u32x4* st = ring + (c % NB) * STAGE_BLOCKS * 64;
+      const char* kreg = reinterpret_cast<const char*>(st + (mypl * PLB) * 64);
+      const char* vreg = reinterpret_cast<const char*>(st + (mypl * PLB + NIK) * 64);
+      const u32x4* treg = st + (NPL * PLB) * 64;
+
+      // (1) this half's partial score for the 16 tokens, published to LDS
+      f32x4 g[NT];
 #pragma unroll
-    for (int i = 0; i < NTMAX; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NT; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const f16x8_t bf = __builtin_bit_cast(f16x8_t, treg[ks * 64 + lane]);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const f16x8_t bf = __builtin_bit_cast(f16x8_t, treg[ks * 64 + lane]);
 #pragma unroll
-      for (int i = 0; i < NTMAX; ++i) {
-        if (i < (half == 0 ? NT0 : NT1)) g[i] = mfma_f16(mf[i][ks], bf, g[i]);
+        for (int i = 0; i < NT; ++i) g[i] = mfma_f16(mf[i][ks], bf, g[i]);
       }
-    }
-    float pp = 0.f;
-    if (hi == 0) {
-      if (NH == 1) pp = g[NT0 - 1][0];                 // the mean row
-      else if (half == 1) pp = g[NT1 - 1][0];
-    }
+      // element 0 of the mean tile: the mean row for hi = 0, an all-zero padding row of
+      // M^T (so exactly 0) for the other lane groups
+      float pp = MEAN ? g[NT - 1][0] : 0.f;
 #pragma unroll
-    for (int m = 0; m < NCKH; ++m) {
-      if (m < (half == 0 ? NCKH0 : NCKH1)) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(kreg + lo * (KSP * 16) + 32 * (k_tile0 + m) + 8 * hi);
+      for (int m = 0; m < NCKh; ++m) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(kreg + lo * (KSP * 16) + 32 * (KT0 + m) + 8 * hi);
         pp += __uint_as_float(w.x << 16) * g[m][0] + __uint_as_float(w.x & 0xffff0000u) * g[m][1] +
               __uint_as_float(w.y << 16) * g[m][2] + __uint_as_float(w.y & 0xffff0000u) * g[m][3];
       }
-    }
-    const float part = sum_xor32(sum_xor16(pp));
-    float full = part;
-    if constexpr (NH == 2) {
-      if (hi == 0) xch[wave * 16 + lo] = part;
-      ring_barrier();
-      const float other = xch[(wave ^ 1) * 16 + lo];
-      full = half == 0 ? part + other : other + part;  // same order in both halves
-    }
+      const float part = sum_xor32(sum_xor16(pp));
+      float full = part;
+      if constexpr (NH == 2) {
+        if (hi == 0) xch[wave * 16 + lo] = part;
+        ring_barrier();
+        const float other = xch[(wave ^ 1) * 16 + lo];
+        full = HALF == 0 ? part + other : other + part;  // same order in both halves
+      }
 
-    // (2) full score, online softmax, this half's value update
-    const int tok = s0 + 16 * c + lo;
-    const bool valid = tok < s1;
-    const float s = valid ? full : kNegInf;
-    const bool raise = s > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float m_new = raise ? s : m_run;
-      const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;
-      l_run *= alpha;
+      // (2) full score, online softmax, this half's value update
+      const float s = (c < nfull || s0 + 16 * c + lo < s1) ? full : kNegInf;
+      const bool raise = s > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? s : m_run;
+        const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;
+        l_run *= alpha;
 #pragma unroll
-      for (int e = 0; e < VSH; ++e) acc[e] *= alpha;
-      m_run = m_new;
-    }
-    const float p = fast_exp2(s - (m_run == kNegInf ? 0.f : m_run));
-    l_run += p;
-    const char* vp = vreg + lo * (VSP * 16) + 2 * (half * RVH + hi * VSH);
+        for (int e = 0; e < VSH; ++e) acc[e] *= alpha;
+        m_run = m_new;
+      }
+      const float p = fast_exp2(s - m_run);
+      l_run += p;
+      const char* vp = vreg + lo * (VSP * 16) + 2 * (HALF * RVH + hi * VSH);
 #pragma unroll
-    for (int m = 0; m < VSH / 4; ++m) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(vp + 8 * m);
-      acc[4 * m + 0] += p * __uint_as_float(w.x << 16);
-      acc[4 * m + 1] += p * __uint_as_float(w.x & 0xffff0000u);
-      acc[4 * m + 2] += p * __uint_as_float(w.y << 16);
-      acc[4 * m + 3] += p * __uint_as_float(w.y & 0xffff0000u);
+      for (int m = 0; m < VSH / 4; ++m) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(vp + 8 * m);
+        acc[4 * m + 0] += p * __uint_as_float(w.x << 16);
+        acc[4 * m + 1] += p * __uint_as_float(w.x & 0xffff0000u);
+        acc[4 * m + 2] += p * __uint_as_float(w.y << 16);
+        acc[4 * m + 3] += p * __uint_as_float(w.y & 0xffff0000u);
+      }
     }
+  };
+  if constexpr (NH == 2) {
+    if (half == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 0>{});
   }
   // no direct-to-LDS load may land after this point (the LDS is reused below and at exit)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -339,7 +356,7 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   float mx = m_run;
 #pragma unroll
   for (int msk = 1; msk < 16; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
-  const float scl = (mx == kNegInf) ? 0.f : fast_exp2(m_run - mx);
+  const float scl = fast_exp2(m_run - mx);
   float lsum = l_run * scl;
 #pragma unroll
   for (int msk = 1; msk < 16; msk <<= 1) lsum += shfl_xor(lsum, msk);
