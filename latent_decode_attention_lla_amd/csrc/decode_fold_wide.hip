@@ -458,6 +458,8 @@ bool decode_fold_wide_supported(int dtype, int d, int r_k, int r_v) {
   return false;
 }
 
+int fold_wide_waves_per_head() { return LLA_WIDE_NH; }
+
 int fold_wide_heads_per_group(int d, int r_k, int r_v, bool shared) {
 #define X(D_, RK_, RV_, HP_, H2_) \
   if (d == D_ && r_k == RK_ && r_v == RV_) return shared ? H2_ : HP_;

@@ -45,10 +45,14 @@ struct Plan {
   int split_len;
 };
 
+int waves_per_unit(const lla_dims& d, const lla_decode_opts* opts);
+
+// Context splits: enough (sequence, head, loop, split) waves to fill the GPU, counting the
+// waves the chosen kernel spends per head.
 Plan plan_splits(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_opts* opts) {
   Plan p{1, 16};
   if (n_ctx <= 0) return p;
-  const long long units = static_cast<long long>(d.batch) * d.H * loop_count;
+  const long long units = static_cast<long long>(d.batch) * d.H * loop_count * waves_per_unit(d, opts);
   long long S;
   if (opts != nullptr && opts->num_splits > 0) {
     S = opts->num_splits;
@@ -91,6 +95,12 @@ int resolve_path(const lla_dims& d, const lla_decode_opts* opts) {
     return LLA_PATH_RECONSTRUCT;
   }
   return want;
+}
+
+int waves_per_unit(const lla_dims& d, const lla_decode_opts* opts) {
+  if (resolve_path(d, opts) == LLA_PATH_ROTARY_FOLD && fold_kind(d) == kFoldWide)
+    return lla::fold_wide_waves_per_head();
+  return 1;
 }
 
 int32_t hip_status() {

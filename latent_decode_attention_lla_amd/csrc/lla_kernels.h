@@ -50,6 +50,7 @@ bool launch_decode_fold_wide(int dtype, int d, int r_k, int r_v, bool shared, co
                              hipStream_t s);
 bool decode_fold_wide_supported(int dtype, int d, int r_k, int r_v);
 int fold_wide_heads_per_group(int d, int r_k, int r_v, bool shared);
+int fold_wide_waves_per_head();
 bool launch_combine(int dtype, int d, int r_v, const DecodeArgs& a, hipStream_t s);
 bool decode_reconstruct_supported(int dtype, int d, int r_k, int r_v);
 bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v);

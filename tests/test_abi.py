@@ -68,6 +68,17 @@ def test_workspace_and_splits_planning():
     assert lla.lla_decode_num_splits(small, 0, 1) == 1
 
 
+def test_splits_count_the_kernels_waves_per_head():
+    """About 2048 waves in flight: the wide fold kernel spends a pair of waves per head,
+    the reconstruct kernel one."""
+    recon = lla.make_opts(0, lla.LLA_PATH_RECONSTRUCT)
+    for B, n, variant, wide in ((32, 4096, lla.LLA_PER_HEAD, 2), (8, 8192, lla.LLA_PER_HEAD, 8),
+                                (16, 16384, lla.LLA_2D, 4)):
+        dims = lla.make_dims(4, 1, 16, 128, 96, 160, B, n, variant)
+        assert lla.lla_decode_num_splits(dims, n, 1) == wide
+        assert lla.lla_decode_num_splits(dims, n, 1, recon) == 2 * wide
+
+
 # Argument validation with fake (never dereferenced) addresses. Every case below must be
 # rejected on the host; they are skipped where a GPU is visible so that a validation bug
 # can never turn into a launch with bogus pointers.
