@@ -52,3 +52,27 @@ def brute_encode_one(x, mu, w_down):
     """Eq. 2 for one vector: x [T*d], mu [T*d], W_down [T*d][r] -> c [r]."""
     r = len(w_down[0])
     return [math.fsum((x[i] - mu[i]) * w_down[i][k] for i in range(len(x))) for k in range(r)]
+
+
+def brute_decode_absorbed_one(c_k, c_v, k_rope, w_up_k_t, mu_k_t, w_up_v_t, mu_v_t, q, d_rope,
+                              scale):
+    """One (head, loop) of the decoupled decode with scalar loops: for every token the
+    score is the rotary dot over dimensions i < d_rope (stored rotated key) plus the
+    content dot over i >= d_rope of the reconstructed key (Eq. 3, no rotation)."""
+    d = len(q)
+    scores = []
+    for j in range(len(c_k)):
+        k_hat = _row_times_matT(c_k[j], w_up_k_t)
+        s = [q[i] * k_rope[j][i] for i in range(d_rope)]
+        s += [q[i] * (k_hat[i] + mu_k_t[i]) for i in range(d_rope, d)]
+        scores.append(scale * math.fsum(s))
+    if not scores:
+        return [0.0] * d
+    m = max(scores)
+    w = [math.exp(x - m) for x in scores]
+    tot = math.fsum(w)
+    out = []
+    for i in range(d):
+        out.append(math.fsum(w[j] * (_row_times_matT(c_v[j], w_up_v_t)[i] + mu_v_t[i])
+                             for j in range(len(c_v))) / tot)
+    return out

@@ -21,11 +21,16 @@ softmax attention follows. Readings taken where the pages are silent:
 * Score scale defaults to 1/sqrt(d_head).
 * Attention over an empty context returns zeros.
 * LLA-2D stacks its input (t, h, d) with the loop index outermost.
+* Decoupled (absorbed) decode, Appendix J: dimensions 0 .. d_rope-1 of a head are the
+  rotary branch (one stored, already rotated key per token, shared by every loop), the
+  rest the content path (the loop's reconstructed key without RoPE); scale 1/sqrt(d).
 
 Parity: every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms
 printed on the pages, the full-rank special case against textbook attention, RoPE
 invariants, softmax special cases, a scalar brute-force re-derivation, the LLA-2D
-block-diagonal reduction and the Eckart-Young property of the SVD initialisation).
+block-diagonal reduction and the Eckart-Young property of the SVD initialisation;
+the decoupled decode against textbook attention on the original keys and values, a
+scalar brute force, and its reduction to the full-RoPE decode).
 """
 
 from __future__ import annotations
@@ -47,6 +52,9 @@ __all__ = [
     "softmax",
     "attention",
     "decode",
+    "absorbed_scale",
+    "absorbed_keys",
+    "decode_absorbed",
     "svd_init",
     "round_bf16",
     "encode_stored",
@@ -211,6 +219,70 @@ def decode(c_k: np.ndarray, c_v: np.ndarray,
                 k_rot = apply_rope(k_hat, pos, rope_base)
                 out[b, h, li] = attention(np.asarray(q[b, h, li], dtype=np.float64),
                                           k_rot, v_hat, scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Absorbed decode with a decoupled rotary branch: Appendix J, "Absorbed attention"
+# (an MLA-style content path without RoPE plus a small explicit rotary branch that every
+# loop of a token shares). The pages give no formulas for the split; the reading taken
+# here: the first d_rope dimensions of every head are the rotary branch, whose key is
+# stored per (sequence, head, token) already rotated to the token's position; the other
+# d - d_rope dimensions are the content path, whose key is the loop-t reconstruction
+# (Eq. 3) without RoPE. The score scale stays 1/sqrt(d).
+# ---------------------------------------------------------------------------
+
+def absorbed_scale(d: int, d_rope: int) -> float:
+    """Default score scale of the decoupled decode: 1/sqrt(d) of the whole head."""
+    return 1.0 / math.sqrt(d)
+
+
+def absorbed_keys(k_rope: np.ndarray, k_hat: np.ndarray, d_rope: int) -> np.ndarray:
+    """Key rows of the decoupled decode: rotary branch in dimensions 0 .. d_rope-1,
+    content (the reconstructed key, no RoPE) in d_rope .. d-1. k_rope [n, d_rope],
+    k_hat [n, d] -> [n, d]."""
+    return np.concatenate([np.asarray(k_rope, dtype=np.float64).reshape(k_hat.shape[0], d_rope),
+                           k_hat[:, d_rope:]], axis=1)
+
+
+def decode_absorbed(c_k: np.ndarray, c_v: np.ndarray, k_rope: np.ndarray,
+                    w_up_k: np.ndarray, mu_k: np.ndarray,
+                    w_up_v: np.ndarray, mu_v: np.ndarray,
+                    q: np.ndarray, d_rope: int, loop_begin: int = 0,
+                    ctx_lens=None, scale: float | None = None,
+                    variant: str = "per_head") -> np.ndarray:
+    """Decode attention for one layer with the decoupled key, written out explicitly:
+    keys [k_rope ; K_t content], values V_t, both reconstructed per token (Eq. 3).
+
+    k_rope [B, H, n, d_rope] : rotary keys, rotated to their positions, one per token
+                               for all loops
+    q [B, H, L, d]           : queries; entries 0 .. d_rope-1 are the rotated rotary part
+    other arguments as in `decode`; returns out [B, H, L, d] float64
+    """
+    c_k = np.asarray(c_k)
+    c_v = np.asarray(c_v)
+    B, Hc, n, _ = c_k.shape
+    L = q.shape[2]
+    H = q.shape[1]
+    d = q.shape[3]
+    if scale is None:
+        scale = absorbed_scale(d, d_rope)
+    if ctx_lens is None:
+        ctx_lens = [n] * B
+    out = np.zeros((B, H, L, d), dtype=np.float64)
+    for b in range(B):
+        nb = int(ctx_lens[b])
+        for h in range(H):
+            hc = h if variant == "per_head" else 0
+            ck = np.asarray(c_k[b, hc, :nb], dtype=np.float64)
+            cv = np.asarray(c_v[b, hc, :nb], dtype=np.float64)
+            kr = np.asarray(k_rope[b, h, :nb], dtype=np.float64)
+            for li in range(L):
+                t = loop_begin + li
+                k_hat = reconstruct(ck, w_up_k[t, h], _mu_slice(mu_k, variant, t, h, H, d))
+                v_hat = reconstruct(cv, w_up_v[t, h], _mu_slice(mu_v, variant, t, h, H, d))
+                out[b, h, li] = attention(np.asarray(q[b, h, li], dtype=np.float64),
+                                          absorbed_keys(kr, k_hat, d_rope), v_hat, scale)
     return out
 
 

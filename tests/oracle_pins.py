@@ -362,6 +362,94 @@ def pin_round_bf16() -> float:
     return err
 
 
+def pin_absorbed_textbook() -> float:
+    """Decoupled decode with a full-rank codec (r = T*d, orthonormal W_down, W_up,t its
+    loop slices, so Eq. 3 gives back the original per-loop keys and values): it must equal
+    ordinary attention (torch SDPA, fp64) whose keys are the stored rotary keys in
+    dimensions < d_rope and the original keys elsewhere, with scale 1/sqrt(d). Covers
+    d_rope = 0 (content only), a mixed split and d_rope = d (rotary only)."""
+    T, H, d, n, B = 2, 2, 8, 11, 2
+    rng = _rng(61)
+    xk = rng.standard_normal((B, H, n, T, d))
+    xv = rng.standard_normal((B, H, n, T, d))
+    q = rng.standard_normal((B, H, T, d))
+    r = T * d
+    ck = np.empty((B, H, n, r))
+    cv = np.empty((B, H, n, r))
+    wuk = np.empty((T, H, d, r))
+    wuv = np.empty((T, H, d, r))
+    muk = rng.standard_normal((H, T * d))
+    muv = rng.standard_normal((H, T * d))
+    for h in range(H):
+        wk = _orthonormal(r, r, 300 + h)
+        wv = _orthonormal(r, r, 400 + h)
+        ck[:, h] = O.encode(O.stack_loops(xk[:, h]), muk[h], wk)
+        cv[:, h] = O.encode(O.stack_loops(xv[:, h]), muv[h], wv)
+        for t in range(T):
+            wuk[t, h] = wk[t * d:(t + 1) * d]
+            wuv[t, h] = wv[t * d:(t + 1) * d]
+    err = 0.0
+    for d_rope in (0, 4, d):
+        kr = rng.standard_normal((B, H, n, d_rope))
+        got = O.decode_absorbed(ck, cv, kr, wuk, muk, wuv, muv, q, d_rope)
+        for t in range(T):
+            k = torch.from_numpy(np.concatenate([kr, xk[:, :, :, t, d_rope:]], axis=-1))
+            v = torch.from_numpy(xv[:, :, :, t])
+            qt = torch.from_numpy(q[:, :, t])[:, :, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, k, v, scale=1.0 / math.sqrt(d))[:, :, 0]
+            err = max(err, float(np.max(np.abs(got[:, :, t] - ref.numpy()))))
+    return err
+
+
+def pin_absorbed_brute_force() -> float:
+    """Decoupled decode against the scalar re-derivation, low-rank codec, ragged
+    contexts, per head and LLA-2D."""
+    err = 0.0
+    for variant, seed, ctx, d_rope in (("per_head", 71, [5, 2], 2), ("2d", 72, [4, 5], 2),
+                                       ("per_head", 73, [5, 5], 4)):
+        a = _tiny(seed, variant=variant)
+        T, H, d = a["w_up_k"].shape[0], a["w_up_k"].shape[1], a["w_up_k"].shape[2]
+        B, n = a["q"].shape[0], a["c_k"].shape[2]
+        kr = _rng(seed + 100).standard_normal((B, H, n, d_rope))
+        got = O.decode_absorbed(a["c_k"], a["c_v"], kr, a["w_up_k"], a["mu_k"], a["w_up_v"],
+                                a["mu_v"], a["q"], d_rope, 0, ctx, None, variant)
+        for b in range(B):
+            for h in range(H):
+                hc = h if variant == "per_head" else 0
+                for t in range(T):
+                    if variant == "per_head":
+                        mk = a["mu_k"][h][t * d:(t + 1) * d]
+                        mv = a["mu_v"][h][t * d:(t + 1) * d]
+                    else:
+                        mk = a["mu_k"][0][(t * H + h) * d:(t * H + h + 1) * d]
+                        mv = a["mu_v"][0][(t * H + h) * d:(t * H + h + 1) * d]
+                    ref = brute.brute_decode_absorbed_one(
+                        a["c_k"][b, hc, :ctx[b]].tolist(), a["c_v"][b, hc, :ctx[b]].tolist(),
+                        kr[b, h, :ctx[b]].tolist(), a["w_up_k"][t, h].tolist(), list(mk),
+                        a["w_up_v"][t, h].tolist(), list(mv), list(a["q"][b, h, t]), d_rope,
+                        1.0 / math.sqrt(d))
+                    err = max(err, float(np.max(np.abs(got[b, h, t] - np.array(ref)))))
+    return err
+
+
+def pin_absorbed_equals_full_rope() -> float:
+    """With a single loop, d_rope = d and the rotary keys set to the rotated
+    reconstructions (computed here by complex multiplication), the decoupled decode is
+    the full-RoPE latent decode."""
+    a = _tiny(81, T=1, n=6)
+    B, H, n = a["q"].shape[0], a["q"].shape[1], a["c_k"].shape[2]
+    d = a["w_up_k"].shape[2]
+    kr = np.empty((B, H, n, d))
+    for b in range(B):
+        for h in range(H):
+            k_hat = a["c_k"][b, h] @ a["w_up_k"][0, h].T + a["mu_k"][h][:d]
+            kr[b, h] = _textbook_rope_complex(torch.from_numpy(k_hat), torch.arange(n), 10000.0).numpy()
+    got = O.decode_absorbed(a["c_k"], a["c_v"], kr, a["w_up_k"], a["mu_k"], a["w_up_v"],
+                            a["mu_v"], a["q"], d)
+    ref = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"], a["q"])
+    return float(np.max(np.abs(got - ref)))
+
+
 ALL_PINS = {
     "closed_forms": (pin_closed_forms, 1e-9),
     "rope": (pin_rope, 1e-12),
@@ -372,4 +460,7 @@ ALL_PINS = {
     "special_cases": (pin_special_cases, 1e-12),
     "lla2d_block_diagonal": (pin_lla2d_block_diagonal, 1e-12),
     "round_bf16": (pin_round_bf16, 0.0),
+    "absorbed_textbook": (pin_absorbed_textbook, 1e-12),
+    "absorbed_brute_force": (pin_absorbed_brute_force, 1e-12),
+    "absorbed_equals_full_rope": (pin_absorbed_equals_full_rope, 1e-12),
 }

@@ -87,8 +87,27 @@ def _mut_round_truncate(x):
     return np.ldexp(np.trunc(m * 256.0), e - 8)
 
 
+def _mut_absorbed_rotary_last(k_rope, k_hat, d_rope):
+    n, d = k_hat.shape
+    return np.concatenate([k_hat[:, :d - d_rope],
+                           np.asarray(k_rope, dtype=np.float64).reshape(n, d_rope)], axis=1)
+
+
+def _mut_absorbed_drops_rotary(k_rope, k_hat, d_rope):
+    return np.concatenate([np.zeros((k_hat.shape[0], d_rope)), k_hat[:, d_rope:]], axis=1)
+
+
+def _mut_absorbed_content_rotated(k_rope, k_hat, d_rope):
+    return _ORIG["absorbed_keys"](k_rope, O.apply_rope(k_hat, np.arange(k_hat.shape[0]), 10000.0),
+                                  d_rope)
+
+
+def _mut_absorbed_scale_content_only(d, d_rope):
+    return 1.0 / np.sqrt(max(d - d_rope, 1))
+
+
 _ORIG = {name: getattr(O, name) for name in
-         ("apply_rope", "reconstruct", "attention", "_mu_slice", "rope_theta")}
+         ("apply_rope", "reconstruct", "attention", "_mu_slice", "rope_theta", "absorbed_keys")}
 
 MUTANTS = {
     "rope_sign": ("apply_rope", _mut_rope_sign),
@@ -104,6 +123,10 @@ MUTANTS = {
     "svd_no_centering": ("svd_init", _mut_svd_no_center),
     "rho_missing_factor_two": ("compression_ratio", _mut_ratio_no_two),
     "bf16_truncates": ("round_bf16", _mut_round_truncate),
+    "absorbed_rotary_last": ("absorbed_keys", _mut_absorbed_rotary_last),
+    "absorbed_drops_rotary": ("absorbed_keys", _mut_absorbed_drops_rotary),
+    "absorbed_content_rotated": ("absorbed_keys", _mut_absorbed_content_rotated),
+    "absorbed_scale_content_only": ("absorbed_scale", _mut_absorbed_scale_content_only),
 }
 
 
