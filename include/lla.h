@@ -171,6 +171,36 @@ int32_t lla_decode_attn(const lla_dims* dims, const lla_codec* codec, const lla_
 int32_t lla_decode_num_splits(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,
                               const lla_decode_opts* opts);
 
+/* Decoupled-RoPE absorbed decode (Appendix J, "Absorbed attention": an MLA-style content
+ * path without RoPE plus a small explicit rotary branch that all loops of a token share).
+ * Dimensions 0 .. d_rope-1 of every head are the rotary branch, d_rope .. d_head-1 the
+ * content path. For every sequence b, head h and loop t:
+ *   key_t[j] = [ k_rope[j] ; (c_k[j] W_up,k,t^T + mu_k,t)[d_rope ..] ]   (no RoPE here)
+ *   out[b][h][t] = softmax_j(scale * q . key_t[j]) V_t   over j < len_b,
+ * computed without rebuilding keys: q~ = W_up,k,t[d_rope ..]^T q[d_rope ..] scores the
+ * latent directly, and the value side is (sum_j a_j c_v[j]) W_up,v,t^T + mu_v,t.
+ *   k_rope : device [D][batch][H][n_max][d_rope] in the cache dtype: the rotary keys,
+ *            already rotated to their positions (RoPE of the slot index), one per token
+ *            for every loop. Written by the caller.
+ *   d_rope : 16 <= d_rope < d_head, a multiple of 16; built shapes are listed by
+ *            lla_decode_absorbed_supported.
+ *   q      : device float32 [batch][H][loop_count][d_head]; entries 0 .. d_rope-1 are the
+ *            rotated rotary query, the rest the content query.
+ *   scale  : dims->scale, 0 = 1/sqrt(d_head).
+ *   other arguments and errors as lla_decode_attn (the path field of opts is ignored);
+ *   workspace >= lla_decode_absorbed_workspace_bytes(dims, d_rope, n_ctx, loop_count, opts)
+ *   (it holds the folded queries and the split partials). */
+size_t lla_decode_absorbed_workspace_bytes(const lla_dims* dims, int32_t d_rope, int32_t n_ctx,
+                                           int32_t loop_count, const lla_decode_opts* opts);
+int32_t lla_decode_attn_absorbed(const lla_dims* dims, const lla_codec* codec,
+                                 const lla_cache* cache, const void* k_rope, int32_t d_rope,
+                                 int32_t layer, int32_t n_ctx, const int32_t* ctx_lens,
+                                 const float* q, int32_t loop_begin, int32_t loop_count,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 const lla_decode_opts* opts, void* stream);
+/* 1 when a kernel is built for (dims' dtype, d_head, r_k, r_v, d_rope), else 0. */
+int32_t lla_decode_absorbed_supported(const lla_dims* dims, int32_t d_rope);
+
 #ifdef __cplusplus
 }
 #endif

@@ -103,6 +103,13 @@ int waves_per_unit(const lla_dims& d, const lla_decode_opts* opts) {
   return 1;
 }
 
+// Absorbed decode: one wave per (sequence, head, loop, split).
+Plan plan_absorbed(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_opts* opts) {
+  lla_decode_opts o{0, LLA_PATH_RECONSTRUCT};  // one wave per unit, like the reconstruct kernel
+  if (opts != nullptr) o.num_splits = opts->num_splits;
+  return plan_splits(d, n_ctx, loop_count, &o);
+}
+
 int32_t hip_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? LLA_OK : LLA_ERR_HIP;
@@ -295,6 +302,97 @@ int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cac
   // The rotary-fold kernel finishes a single split itself (value up-projection in its
   // epilogue); everything else goes through the split merge.
   if (path == LLA_PATH_ROTARY_FOLD && p.S == 1) return LLA_OK;
+  if (!lla::launch_combine(d->dtype, d->d_head, d->r_v, a, s)) return LLA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
+size_t lla_decode_absorbed_workspace_bytes(const lla_dims* d, int32_t d_rope, int32_t n_ctx,
+                                           int32_t loop_count, const lla_decode_opts* opts) {
+  if (check_dims(d) != LLA_OK || n_ctx < 0 || n_ctx > d->n_max || loop_count < 1) return 0;
+  if (d_rope < 16 || d_rope >= d->d_head || d_rope % 16 != 0) return 0;
+  const Plan p = plan_absorbed(*d, n_ctx, loop_count, opts);
+  const size_t units = static_cast<size_t>(d->batch) * d->H * loop_count;
+  const size_t qa = (units * lla::absorbed_query_floats(d->r_k, d_rope) * 4 + 255) / 256 * 256;
+  const size_t part = units * p.S * (2 + d->r_v) * 4;
+  return qa + (part + 255) / 256 * 256;
+}
+
+int32_t lla_decode_absorbed_supported(const lla_dims* d, int32_t d_rope) {
+  if (check_dims(d) != LLA_OK) return 0;
+  return lla::decode_absorbed_supported(d->dtype, d->d_head, d->r_k, d->r_v, d_rope) ? 1 : 0;
+}
+
+int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                                 const void* k_rope, int32_t d_rope, int32_t layer, int32_t n_ctx,
+                                 const int32_t* ctx_lens, const float* q, int32_t loop_begin,
+                                 int32_t loop_count, float* out, void* workspace,
+                                 size_t workspace_bytes, const lla_decode_opts* opts, void* stream) {
+  int32_t st = check_dims(d);
+  if (st != LLA_OK) return st;
+  if (codec == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
+  if (n_ctx < 0 || n_ctx > d->n_max) return LLA_ERR_INVALID_ARG;
+  if (loop_begin < 0 || loop_count < 1 || static_cast<long long>(loop_begin) + loop_count > d->T)
+    return LLA_ERR_INVALID_ARG;
+  if (d_rope < 16 || d_rope >= d->d_head || d_rope % 16 != 0) return LLA_ERR_INVALID_ARG;
+  if (opts != nullptr && opts->num_splits < 0) return LLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {codec->mu_k, codec->w_up_k, codec->mu_v, codec->w_up_v,
+                        cache->c_k, cache->c_v, k_rope, q, out, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+  if (ctx_lens != nullptr && (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) != 0) return LLA_ERR_INVALID_ARG;
+  if (!lla::decode_absorbed_supported(d->dtype, d->d_head, d->r_k, d->r_v, d_rope))
+    return LLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(d->n_max) * d_rope >= (1LL << 31)) return LLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < lla_decode_absorbed_workspace_bytes(d, d_rope, n_ctx, loop_count, opts))
+    return LLA_ERR_WORKSPACE;
+
+  const Plan p = plan_absorbed(*d, n_ctx, loop_count, opts);
+  const size_t es = elem_bytes(*d);
+  const int Hc = latent_heads(*d);
+  const int K = d->T * d_in(*d);
+  const size_t units = static_cast<size_t>(d->batch) * d->H * loop_count;
+  const size_t qa_bytes = (units * lla::absorbed_query_floats(d->r_k, d_rope) * 4 + 255) / 256 * 256;
+  lla::DecodeArgs a;
+  a.c_k = static_cast<const char*>(cache->c_k) +
+          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * d->r_k * es;
+  a.c_v = static_cast<const char*>(cache->c_v) +
+          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * d->r_v * es;
+  a.w_up_k = static_cast<const char*>(codec->w_up_k) +
+             static_cast<size_t>(layer) * d->T * d->H * d->d_head * d->r_k * es;
+  a.w_up_v = static_cast<const char*>(codec->w_up_v) +
+             static_cast<size_t>(layer) * d->T * d->H * d->d_head * d->r_v * es;
+  a.mu_k = static_cast<const char*>(codec->mu_k) + static_cast<size_t>(layer) * Hc * K * es;
+  a.mu_v = static_cast<const char*>(codec->mu_v) + static_cast<size_t>(layer) * Hc * K * es;
+  a.rope32 = nullptr;
+  a.rope16 = nullptr;
+  a.q = q;
+  a.ctx_lens = ctx_lens;
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + qa_bytes);
+  a.out = out;
+  a.B = d->batch;
+  a.H = d->H;
+  a.Hc = Hc;
+  a.T = d->T;
+  a.L = loop_count;
+  a.loop_begin = loop_begin;
+  a.n_max = d->n_max;
+  a.n_ctx = n_ctx;
+  a.S = p.S;
+  a.split_len = p.split_len;
+  a.variant = d->variant;
+  const double scale = d->scale > 0.f ? d->scale : 1.0 / std::sqrt(static_cast<double>(d->d_head));
+  a.scale_log2e = static_cast<float>(scale * kLog2e);
+  const char* kr = static_cast<const char*>(k_rope) +
+                   static_cast<size_t>(layer) * d->batch * d->H * static_cast<size_t>(d->n_max) * d_rope * es;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!lla::launch_decode_absorbed(d->dtype, d->d_head, d->r_k, d->r_v, d_rope, a, kr,
+                                   static_cast<float*>(workspace), s))
+    return LLA_ERR_UNSUPPORTED;
+  st = hip_status();
+  if (st != LLA_OK) return st;
+  if (p.S == 1) return LLA_OK;  // the kernel finished the single split itself
   if (!lla::launch_combine(d->dtype, d->d_head, d->r_v, a, s)) return LLA_ERR_UNSUPPORTED;
   return hip_status();
 }

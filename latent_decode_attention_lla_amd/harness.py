@@ -61,6 +61,32 @@ class DeviceLatentStore:
                             loop_begin, loop_count, out, ws, ws.numel(), opts, stream)
         return out
 
+    def absorbed_workspace(self, n_ctx: int, loop_count: int, opts=None) -> torch.Tensor:
+        nb = lla.lla_decode_absorbed_workspace_bytes(self.dims, self.w.d_rope, n_ctx, loop_count, opts)
+        if self._ws is None or self._ws.numel() < nb:
+            self._ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode_absorbed(self, layer: int, loop_begin: int, loop_count: int,
+                        q: torch.Tensor | None = None, n_ctx: int | None = None,
+                        ctx_lens: torch.Tensor | None = None, opts=None,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Decoupled-RoPE absorbed decode over this store's latents and rotary keys."""
+        w = self.w
+        n_ctx = w.n if n_ctx is None else n_ctx
+        if q is None:
+            if loop_count == 1:
+                q = self.t["q"][layer, loop_begin]
+            else:
+                q = self.t["q"][layer, loop_begin:loop_begin + loop_count].permute(1, 2, 0, 3).contiguous()
+        if out is None:
+            out = torch.empty(w.batch, w.H, loop_count, w.d, dtype=torch.float32, device=self.device)
+        ws = self.absorbed_workspace(n_ctx, loop_count, opts)
+        lla.lla_decode_attn_absorbed(self.dims, self.codec, self.cache, self.t["k_rope"], w.d_rope,
+                                     layer, n_ctx, ctx_lens, q, loop_begin, loop_count, out, ws,
+                                     ws.numel(), opts, stream)
+        return out
+
     def encode(self, layer: int, x_k: torch.Tensor, x_v: torch.Tensor, pos_start: int,
                n_new: int, stream=None) -> None:
         lla.lla_encode(self.dims, self.codec, self.cache, layer, x_k, x_v, pos_start, n_new, stream)

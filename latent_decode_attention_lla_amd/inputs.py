@@ -14,6 +14,9 @@ Table 5):
 * ``encode_heavy``  T=4, D=1, H=16, d=128, (96, 160), bf16, batch 8, context 8192
 * ``lla2d_long``    LLA-2D, T=4, D=24, H=16, d=128, shared (96, 160), bf16, batch 16,
                     context 16384
+* ``absorbed_4x``   the Ouro-1.4B 4x geometry, T=4, D=24, H=16, d=128, (96, 160), bf16,
+                    decoupled decode with a 64-wide rotary branch (Appendix J, Table 14's
+                    d_rope), batch 8, context 32768 (Table 13's shortest context)
 
 Distributions: latents, queries and pre-RoPE K/V ~ N(0, 1); W_up,t ~ N(0, 1/r)
 (variance 1/r, so rebuilt keys have about unit variance); mu ~ N(0, 0.1) (variance).
@@ -22,6 +25,7 @@ of W_down, the structure the SVD initialisation produces) or Gaussian.
 
 Memory layouts (all row-major, shared with the C ABI):
   c_k  [D][B][Hc][n_max][r_k]     c_v  [D][B][Hc][n_max][r_v]
+  k_rope [D][B][H][n_max][d_rope] (rotary keys of the decoupled decode, ~ N(0, 1))
   w_down_k_t [D][Hc][r_k][T*d_in] (W_down transposed)   mu_k [D][Hc][T*d_in]
   w_up_k [D][T][H][d][r_k]        (same for v)
   q    [D][T][B][H][d]  (post-RoPE queries for every layer and loop)
@@ -51,6 +55,7 @@ class Workload:
     variant: str = "per_head"      # "per_head" or "2d"
     dtype: str = "bf16"            # "f32" or "bf16" (latents and codec weights)
     rope_base: float = 10000.0
+    d_rope: int = 0                # rotary-branch width of the decoupled (absorbed) decode
 
     @property
     def Hc(self) -> int:
@@ -79,6 +84,8 @@ WORKLOADS = {
                              batch=8, n=8192),
     "lla2d_long": Workload("lla2d_long", T=4, D=24, H=16, d=128, r_k=96, r_v=160,
                            batch=16, n=16384, variant="2d"),
+    "absorbed_4x": Workload("absorbed_4x", T=4, D=24, H=16, d=128, r_k=96, r_v=160,
+                            batch=8, n=32768, d_rope=64),
 }
 
 
@@ -114,6 +121,8 @@ def decode_inputs(w: Workload, seed: int, device="cpu", n_alloc: int | None = No
     }
     if with_q:
         out["q"] = _randn((w.D, w.T, w.batch, w.H, w.d), 1.0, torch.float32, g, device)
+    if w.d_rope > 0:  # drawn last, so the tensors above do not depend on it
+        out["k_rope"] = _randn((w.D, w.batch, w.H, n_max, w.d_rope), 1.0, dt, g, device)
     return out
 
 

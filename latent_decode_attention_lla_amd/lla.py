@@ -35,6 +35,8 @@ EXPORTED = (
     "lla_status_string", "lla_compression_ratio", "lla_cache_bytes_per_token",
     "lla_rope_table_bytes", "lla_rope_table_build", "lla_encode",
     "lla_decode_workspace_bytes", "lla_decode_attn", "lla_decode_num_splits",
+    "lla_decode_absorbed_workspace_bytes", "lla_decode_attn_absorbed",
+    "lla_decode_absorbed_supported",
 )
 
 
@@ -100,6 +102,15 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_attn.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, i32, vp, vp,
                                     i32, i32, vp, vp, sz, P(lla_decode_opts), vp]
     lib.lla_decode_attn.restype = i32
+    lib.lla_decode_absorbed_workspace_bytes.argtypes = [P(lla_dims), i32, i32, i32,
+                                                        P(lla_decode_opts)]
+    lib.lla_decode_absorbed_workspace_bytes.restype = sz
+    lib.lla_decode_attn_absorbed.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), vp, i32,
+                                             i32, i32, vp, vp, i32, i32, vp, vp, sz,
+                                             P(lla_decode_opts), vp]
+    lib.lla_decode_attn_absorbed.restype = i32
+    lib.lla_decode_absorbed_supported.argtypes = [P(lla_dims), i32]
+    lib.lla_decode_absorbed_supported.restype = i32
     _lib = lib
     return lib
 
@@ -190,6 +201,35 @@ def lla_decode_attn(dims: lla_dims, codec: lla_codec, cache: lla_cache, layer: i
         ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), layer, n_ctx,
         _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out), _ptr(workspace),
         workspace_bytes, ctypes.byref(opts) if opts is not None else None, _stream(stream)))
+
+
+def lla_decode_absorbed_workspace_bytes(dims: lla_dims, d_rope: int, n_ctx: int, loop_count: int,
+                                        opts=None) -> int:
+    return load().lla_decode_absorbed_workspace_bytes(
+        ctypes.byref(dims), d_rope, n_ctx, loop_count,
+        ctypes.byref(opts) if opts is not None else None)
+
+
+def lla_decode_absorbed_supported(dims: lla_dims, d_rope: int) -> bool:
+    return bool(load().lla_decode_absorbed_supported(ctypes.byref(dims), d_rope))
+
+
+def lla_decode_attn_absorbed(dims: lla_dims, codec: lla_codec, cache: lla_cache, k_rope,
+                             d_rope: int, layer: int, n_ctx: int, ctx_lens, q, loop_begin: int,
+                             loop_count: int, out, workspace, workspace_bytes: int, opts=None,
+                             stream=None) -> None:
+    _check("lla_decode_attn_absorbed", lla_decode_attn_absorbed_status(
+        dims, codec, cache, k_rope, d_rope, layer, n_ctx, ctx_lens, q, loop_begin, loop_count,
+        out, workspace, workspace_bytes, opts, _stream(stream)))
+
+
+def lla_decode_attn_absorbed_status(dims, codec, cache, k_rope, d_rope, layer, n_ctx, ctx_lens, q,
+                                    loop_begin, loop_count, out, workspace, workspace_bytes,
+                                    opts=None, stream=0) -> int:
+    return load().lla_decode_attn_absorbed(
+        ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), _ptr(k_rope), d_rope, layer,
+        n_ctx, _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out), _ptr(workspace),
+        workspace_bytes, ctypes.byref(opts) if opts is not None else None, stream)
 
 
 def lla_decode_attn_status(dims, codec, cache, layer, n_ctx, ctx_lens, q, loop_begin, loop_count,

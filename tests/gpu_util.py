@@ -52,6 +52,24 @@ def oracle_decode(store, layer: int, loop_begin: int, loop_count: int, seqs, n_c
                     "per_head" if w.variant == "per_head" else "2d")
 
 
+def oracle_decode_absorbed(store, layer: int, loop_begin: int, loop_count: int, seqs, n_ctx: int,
+                           ctx_lens=None, q=None):
+    """fp64 oracle of the decoupled (absorbed) decode on sequences ``seqs``."""
+    t = store.t
+    w = store.w
+    idx = torch.as_tensor(list(seqs), device=t["c_k"].device)
+    ck = f64(t["c_k"][layer].index_select(0, idx)[:, :, :n_ctx])
+    cv = f64(t["c_v"][layer].index_select(0, idx)[:, :, :n_ctx])
+    kr = f64(t["k_rope"][layer].index_select(0, idx)[:, :, :n_ctx])
+    qq = t["q"][layer, loop_begin:loop_begin + loop_count].permute(1, 2, 0, 3) if q is None else q
+    qq = f64(qq.index_select(0, idx))
+    lens = None if ctx_lens is None else [int(ctx_lens[i]) for i in seqs]
+    return O.decode_absorbed(ck, cv, kr, f64(t["w_up_k"][layer]), f64(t["mu_k"][layer]),
+                             f64(t["w_up_v"][layer]), f64(t["mu_v"][layer]), qq, w.d_rope,
+                             loop_begin, lens, None,
+                             "per_head" if w.variant == "per_head" else "2d")
+
+
 def max_abs(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
 
@@ -73,5 +91,6 @@ def rel_note(err: float, tol: float) -> str:
     return f"max-abs {err:.3e} (tolerance {tol:.0e}, {err / tol:.1%} of it)" if tol > 0 else f"{err:.3e}"
 
 
-__all__ = ["BF16_TOL", "F32_TOL", "ensure_built", "announce", "f64", "oracle_decode", "max_abs",
+__all__ = ["BF16_TOL", "F32_TOL", "ensure_built", "announce", "f64", "oracle_decode",
+           "oracle_decode_absorbed", "max_abs",
            "bf16_ulp", "seed_everything", "rel_note", "math"]
