@@ -38,12 +38,13 @@ _COMMON_SOURCES = ("lla_device.h", "lla_kernels.h", "lla_api.cpp")
 KERNEL_SOURCES = {
     "decode": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip",
                                  "decode_reconstruct.hip", "combine.hip", "rope_table.hip"),
+    "absorbed": _COMMON_SOURCES + ("decode_absorbed.hip", "combine.hip"),
     "encode": _COMMON_SOURCES + ("encode.hip",),
 }
 
 
 def kernel_source_hash(kind: str) -> str:
-    """Hash of the HIP/C++ sources behind one call kind ("decode" or "encode") with comments
+    """Hash of the HIP/C++ sources behind one call kind ("decode", "absorbed" or "encode") with comments
     and whitespace removed: it changes when that call's compiled code or launch plan can
     change, not when a comment or the other call's sources do."""
     import re
@@ -118,20 +119,32 @@ def cpu_baseline(w, seqs: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    sw = w.replace(batch=seqs)
+    # the decoupled decode's oracle rebuilds a 32768-token context per (head, loop): one
+    # layer is timed and the step scaled by D
+    layers = 1 if w.d_rope > 0 else w.D
+    sw = w.replace(batch=seqs, D=layers)
     t = decode_inputs(sw, seed=12345, device="cpu")
     t = {k: v.float().numpy().astype(np.float64) for k, v in t.items()}
+    variant = "per_head" if w.variant == "per_head" else "2d"
     t0 = time.perf_counter()
     for loop in range(w.T):
-        for layer in range(w.D):
-            O.decode(t["c_k"][layer], t["c_v"][layer], t["w_up_k"][layer], t["mu_k"][layer],
-                     t["w_up_v"][layer], t["mu_v"][layer], t["q"][layer, loop:loop + 1].transpose(1, 2, 0, 3),
-                     loop, None, w.rope_base, None, "per_head" if w.variant == "per_head" else "2d")
+        for layer in range(layers):
+            q = t["q"][layer, loop:loop + 1].transpose(1, 2, 0, 3)
+            if w.d_rope > 0:
+                O.decode_absorbed(t["c_k"][layer], t["c_v"][layer], t["k_rope"][layer],
+                                  t["w_up_k"][layer], t["mu_k"][layer], t["w_up_v"][layer],
+                                  t["mu_v"][layer], q, w.d_rope, loop, None, None, variant)
+            else:
+                O.decode(t["c_k"][layer], t["c_v"][layer], t["w_up_k"][layer], t["mu_k"][layer],
+                         t["w_up_v"][layer], t["mu_v"][layer], q, loop, None, w.rope_base, None,
+                         variant)
     dt = time.perf_counter() - t0
-    return {"value": seqs / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{seqs} sequence(s) x {w.H} heads x {w.D} layers x {w.T} loops at context "
-                      f"{w.n} (one full decode step for {seqs} of the {w.batch} sequences), fp64 "
-                      f"NumPy, {dt:.1f} s; host os.cpu_count()={os.cpu_count()}"}
+    step_s = dt * w.D / layers
+    scaled = "" if layers == w.D else f", timed on {layers} layer(s) and scaled by {w.D // layers}"
+    return {"value": seqs / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{seqs} sequence(s) x {w.H} heads x {layers} layer(s) x {w.T} loops at "
+                      f"context {w.n} (a decode step for {seqs} of the {w.batch} sequences{scaled}), "
+                      f"fp64 NumPy, {dt:.1f} s; host os.cpu_count()={os.cpu_count()}"}
 
 
 def step_shape(w):
@@ -152,6 +165,11 @@ def algorithmic(w, kind: str, L: int = 1, n_new: int = 0):
         tok = w.batch * w.Hc * w.n
         nbytes = (tok * (w.r_k + w.r_v) * es + 2 * w.batch * w.H * L * w.d * 4
                   + L * w.H * w.d * (w.r_k + w.r_v) * es + 2 * L * w.H * w.d * es)
+        if w.d_rope > 0:
+            # decoupled decode: the rotary keys are read too; scores and values on the
+            # vector ALU, 2 (r_k + d_rope + r_v) flop per (token, head)
+            nbytes += w.batch * w.H * w.n * w.d_rope * es
+            return nbytes, 2.0 * w.batch * w.H * w.n * L * (w.r_k + w.d_rope + w.r_v)
         if w.variant == "per_head":
             flops = 2.0 * w.batch * w.H * w.n * L * w.r_k * w.d
         else:
@@ -219,8 +237,13 @@ def main():
     path = {"auto": lla.LLA_PATH_AUTO, "reconstruct": lla.LLA_PATH_RECONSTRUCT,
             "rotary_fold": lla.LLA_PATH_ROTARY_FOLD}[args.path]
     opts = lla.make_opts(args.splits, path)
-    S = lla.lla_decode_num_splits(st.dims, w.n, 1, opts)
-    ws = st.workspace(w.n, 1, opts)
+    absorbed = w.d_rope > 0  # the decoupled-RoPE absorbed decode (one wave per head)
+    if absorbed:
+        S = lla.lla_decode_num_splits(st.dims, w.n, 1, lla.make_opts(args.splits, lla.LLA_PATH_RECONSTRUCT))
+        ws = st.absorbed_workspace(w.n, 1, opts)
+    else:
+        S = lla.lla_decode_num_splits(st.dims, w.n, 1, opts)
+        ws = st.workspace(w.n, 1, opts)
     out = torch.empty(w.batch, w.H, 1, w.d, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -246,8 +269,13 @@ def main():
                 q = st.t["q"][layer, loop]
                 if record is not None:
                     ev_dec[record * n_dec + k][0].record(stream)
-                lla.lla_decode_attn(st.dims, st.codec, st.cache, layer, w.n, None, q, loop, 1, out,
-                                    ws, ws.numel(), opts, sp)
+                if absorbed:
+                    lla.lla_decode_attn_absorbed(st.dims, st.codec, st.cache, st.t["k_rope"], w.d_rope,
+                                                 layer, w.n, None, q, loop, 1, out, ws, ws.numel(),
+                                                 opts, sp)
+                else:
+                    lla.lla_decode_attn(st.dims, st.codec, st.cache, layer, w.n, None, q, loop, 1,
+                                        out, ws, ws.numel(), opts, sp)
                 if record is not None:
                     ev_dec[record * n_dec + k][1].record(stream)
                 k += 1
@@ -278,10 +306,32 @@ def main():
     enc_bytes, enc_flops = algorithmic(w, "encode", n_new=n_new)
 
     dec_roof = roofline(dec_bytes, dec_flops, dec_ms,
-                        measured_traffic("decode", args.workload, args.path))
+                        measured_traffic("absorbed" if absorbed else "decode", args.workload,
+                                         args.path))
     enc_roof = roofline(enc_bytes, enc_flops, enc_ms,
                         measured_traffic("encode", args.workload, args.path))
     dominant = "decode" if dec_ms * n_dec >= enc_ms * n_enc else "encode"
+
+    reference = None
+    if absorbed:
+        # the same call shape on the full-RoPE paths, for the ratio the pages report
+        reference = {}
+        for name, pth in (("rotary_fold_full_rope", lla.LLA_PATH_AUTO), ("reconstruct", lla.LLA_PATH_RECONSTRUCT)):
+            o = lla.make_opts(0, pth)
+            wsr = st.workspace(w.n, 1, o)
+            q = st.t["q"][0, 0]
+            for _ in range(2):
+                lla.lla_decode_attn(st.dims, st.codec, st.cache, 0, w.n, None, q, 0, 1, out, wsr,
+                                    wsr.numel(), o, sp)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                lla.lla_decode_attn(st.dims, st.codec, st.cache, 0, w.n, None, q, 0, 1, out, wsr,
+                                    wsr.numel(), o, sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            reference[name] = {"avg_ms": round(ms, 5), "absorbed_speedup": round(ms / dec_ms, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -292,6 +342,8 @@ def main():
     step_desc = (f"encode a {n_new}-token prompt per sequence for one layer, then {w.T} decode calls"
                  if prefill else
                  f"encode the new token for {w.D} layers, then {w.D} x {w.T} decode calls")
+    if absorbed:
+        step_desc += f" (decoupled-RoPE absorbed decode, rotary branch {w.d_rope} wide)"
     res = {
         "metric": "LLA decode tokens/s (one decode step of the looped model over the latent "
                   "cache: the new token's encode plus D layers x T loops of latent-store "
@@ -311,9 +363,11 @@ def main():
         "config": {"workload": w.name, "T": w.T, "D": w.D, "H": w.H, "d_head": w.d, "r_k": w.r_k,
                    "r_v": w.r_v, "batch": w.batch, "context": w.n, "variant": w.variant,
                    "path": args.path, "splits": S, "step": step_desc,
-                   "decode_calls_per_step": n_dec, "encode_calls_per_step": n_enc},
+                   "decode_calls_per_step": n_dec, "encode_calls_per_step": n_enc,
+                   **({"d_rope": w.d_rope} if absorbed else {})},
         "roofline": dec_roof if dominant == "decode" else enc_roof,
-        "roofline_kernel": "lla_decode_attn" if dominant == "decode" else "lla_encode",
+        "roofline_kernel": ("lla_decode_attn_absorbed" if absorbed else "lla_decode_attn")
+                           if dominant == "decode" else "lla_encode",
         "cpu_baseline": cpu,
         "decode_call": {"avg_ms": round(dec_ms, 5), "median_ms": round(dec_med, 5),
                         "algorithmic_bytes": dec_bytes, "algorithmic_flops": dec_flops,
@@ -324,6 +378,7 @@ def main():
                         "algorithmic_flops": enc_flops,
                         "tokens_per_s": round(w.batch * n_new / (enc_ms * 1e-3), 1),
                         "roofline": enc_roof},
+        **({"reference_calls": reference} if reference is not None else {}),
         "wall_s_timed": round(wall, 3),
         "kernel_source_hash": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
     }

@@ -189,7 +189,7 @@ int32_t lla_decode_num_splits(const lla_dims* dims, int32_t n_ctx, int32_t loop_
  *   scale  : dims->scale, 0 = 1/sqrt(d_head).
  *   other arguments and errors as lla_decode_attn (the path field of opts is ignored);
  *   workspace >= lla_decode_absorbed_workspace_bytes(dims, d_rope, n_ctx, loop_count, opts)
- *   (it holds the folded queries and the split partials). */
+ *   (the split partials). */
 size_t lla_decode_absorbed_workspace_bytes(const lla_dims* dims, int32_t d_rope, int32_t n_ctx,
                                            int32_t loop_count, const lla_decode_opts* opts);
 int32_t lla_decode_attn_absorbed(const lla_dims* dims, const lla_codec* codec,

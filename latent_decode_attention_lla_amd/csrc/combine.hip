@@ -17,62 +17,93 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+constexpr int kLdsSplits = 32;  // partials of up to this many splits are staged in LDS
+
+// One workgroup of 256 threads per (b, h, t). Everything the unit needs from memory (its
+// split partials, its rows of W_up,v,t and mu_v,t) is requested at the start, so the
+// kernel pays one memory round trip: thread k owns output i = k / TPR and the TPR-th
+// slice of that row of W_up,v,t.
 template <typename T, int D, int RV>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  constexpr int TPR = 256 / D;      // threads per output row
+  constexpr int RS = RV / TPR;      // row entries per thread
+  static_assert(256 % D == 0 && RV % TPR == 0, "row slices");
+  constexpr int PS = 2 + RV;        // floats per split partial
+  __shared__ float part[kLdsSplits * PS];
+  __shared__ float wsplit[kLdsSplits];
   __shared__ float abar[RV];
+  __shared__ float red[2];
+
+  const int tid = threadIdx.x;
   const int unit = blockIdx.x;  // (b * H + h) * L + li
   const int li = unit % a.L;
-  const int bh = unit / a.L;
-  const int h = bh % a.H;
+  const int h = (unit / a.L) % a.H;
   const int t = a.loop_begin + li;
-  const float* p = a.part + static_cast<size_t>(unit) * a.S * (2 + RV);
+  const int S = a.S;
+  const float* p = a.part + static_cast<size_t>(unit) * S * PS;
+  const bool staged = S <= kLdsSplits;
 
-  float mx = kNegInf;
-  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, p[s * (2 + RV)]);
-  float total = 0.f;
-  if (mx != kNegInf) {
-    for (int s = 0; s < a.S; ++s) total += p[s * (2 + RV) + 1] * fast_exp2(p[s * (2 + RV)] - mx);
+  // (1) every load of the unit
+  if (staged) {
+    for (int k = tid; k < S * PS; k += 256) part[k] = p[k];
   }
-  const float inv = total > 0.f ? 1.f / total : 0.f;
-  for (int r = threadIdx.x; r < RV; r += blockDim.x) {
-    float v = 0.f;
-    if (mx != kNegInf) {
-      for (int s = 0; s < a.S; ++s) {
-        const float ms = p[s * (2 + RV)];
-        if (ms != kNegInf) v += p[s * (2 + RV) + 2 + r] * fast_exp2(ms - mx);
-      }
-    }
-    abar[r] = v * inv;
-  }
-  __syncthreads();
-
-  const T* wv = static_cast<const T*>(a.w_up_v) + static_cast<size_t>(t * a.H + h) * D * RV;
+  const int i = tid / TPR, sub = tid % TPR;
+  const T* wv = static_cast<const T*>(a.w_up_v) + static_cast<size_t>(t * a.H + h) * D * RV +
+                static_cast<size_t>(i) * RV + sub * RS;
+  float w[RS];
+  load_f32<RS>(wv, w);
   const size_t mu_off = a.variant == 0 ? static_cast<size_t>(h * a.T + t) * D
                                        : static_cast<size_t>(t * a.H + h) * D;
-  const T* muv = static_cast<const T*>(a.mu_v) + mu_off;
-  float* out = a.out + static_cast<size_t>(unit) * D;
-  for (int i = threadIdx.x; i < D; i += blockDim.x) {
-    float o = 0.f;
-    if (total > 0.f) {
-      static_assert(RV % 8 == 0, "r_v multiple of 8");
-#pragma unroll 4
-      for (int r0 = 0; r0 < RV; r0 += 8) {
-        float w[8];
-        load_f32<8>(wv + static_cast<size_t>(i) * RV + r0, w);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) o += abar[r0 + r] * w[r];
+  float mu1[1];
+  load_f32<1>(static_cast<const T*>(a.mu_v) + mu_off + i, mu1);
+  __syncthreads();
+
+  // (2) log-sum-exp weights of the splits, then the normalised latent
+  auto merge = [&](const float* src) {
+    if (tid == 0) {
+      float mx = kNegInf;
+      for (int s = 0; s < S; ++s) mx = fmaxf(mx, src[s * PS]);
+      float total = 0.f;
+      if (mx != kNegInf) {
+        for (int s = 0; s < S; ++s) {
+          const float ms = src[s * PS];
+          const float ws = ms != kNegInf ? fast_exp2(ms - mx) : 0.f;
+          if (s < kLdsSplits) wsplit[s] = ws;
+          total += src[s * PS + 1] * ws;
+        }
       }
-      float m1[1];
-      load_f32<1>(muv + i, m1);
-      o += m1[0];
+      red[0] = mx;
+      red[1] = total;
     }
-    out[i] = o;
-  }
+    __syncthreads();
+    const float mx = red[0], total = red[1];
+    const float inv = total > 0.f ? 1.f / total : 0.f;
+    for (int r = tid; r < RV; r += 256) {
+      float v = 0.f;
+      for (int s = 0; s < S; ++s) {
+        const float ms = src[s * PS];
+        const float ws = s < kLdsSplits ? wsplit[s] : (ms != kNegInf ? fast_exp2(ms - mx) : 0.f);
+        v += src[s * PS + 2 + r] * ws;
+      }
+      abar[r] = v * inv;
+    }
+    __syncthreads();
+    return total;
+  };
+  const float total = staged ? merge(part) : merge(p);
+
+  // (3) out = abar W_up,v,t^T + mu_v,t
+  float o = 0.f;
+#pragma unroll
+  for (int e = 0; e < RS; ++e) o += abar[sub * RS + e] * w[e];
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) o += shfl_xor(o, m);
+  if (sub == 0) a.out[static_cast<size_t>(unit) * D + i] = total > 0.f ? o + mu1[0] : 0.f;
 }
 
 template <typename T, int D, int RV>
 void launch(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((combine_kernel<T, D, RV>), dim3(a.B * a.H * a.L), dim3(D), 0, s, a);
+  hipLaunchKernelGGL((combine_kernel<T, D, RV>), dim3(a.B * a.H * a.L), dim3(256), 0, s, a);
 }
 
 }  // namespace

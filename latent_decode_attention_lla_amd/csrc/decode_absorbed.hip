@@ -13,12 +13,11 @@
 //   s_j = scale (q~ . c_j + beta + q[rotary] . k_rope,j)
 // so attention reads only the c_k, k_rope and c_v rows and rebuilds no key.
 //
-// absorbed_prep_kernel: q~, beta and the rotary query, scaled into the exp2 domain, for
-//   every (sequence, head, loop) into the workspace ([unit][QS] floats, QS = r_k + 4 + d_rope:
-//   q~, then beta and three zeros, then the rotary query).
-// decode_absorbed_kernel: one wave per (sequence, head, loop, split), its 64 lanes G
-//   groups of 64/G: lane (j, g) takes token j of each (64/G)-token tile and the g-th of G
-//   slices of each of its rows (c_k, k_rope, c_v). G = 4 for narrow latents; G = 8 for
+// decode_absorbed_kernel: one wave per (sequence, head, loop, split). Its prologue folds
+//   the query: q~, beta and the rotary query, scaled into the exp2 domain, go to LDS (the
+//   unit's W_up,k,t rows are read from L2, shared by the unit's splits). Its 64 lanes are G
+//   groups of 64/G: lane (j, g) takes token j of each (64/G)-token tile and every G-th
+//   8-byte unit of each of its rows (c_k, k_rope, c_v), starting at unit g. G = 4 for narrow latents; G = 8 for
 //   wide ones keeps a lane's share of the rows, the folded query and the value
 //   accumulator within the registers of two waves per SIMD. The slice dots are summed over
 //   the lane groups by butterflies (a DPP row rotation for 8, permlane swaps for 16 and
@@ -43,31 +42,35 @@ constexpr float kRescaleSlack = 8.0f;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// N consecutive elements of one row, kept as raw 32-bit words until they are used.
+// A lane group's share of one row: the row is cut into 8-byte units and group g takes
+// units g, g + G, g + 2 G, ..., so that one load instruction of the wave reads 8 G
+// contiguous bytes of each of its rows. Kept as raw 32-bit words until used; local
+// element e is row element ((e / EU) G + g) EU + e % EU, EU elements per unit.
 template <typename T, int N>
 struct Piece {
   static constexpr int BYTES = N * static_cast<int>(sizeof(T));
   static constexpr int WORDS = BYTES / 4;
+  static constexpr int UNITS = BYTES / 8;
   uint32_t w[WORDS];
 };
 
-// Load a piece (16-byte loads where the piece and the row stride allow, else 8-byte).
-template <typename T, int N, int ROW_BYTES>
-__device__ __forceinline__ void load_piece(Piece<T, N>& p, const char* src) {
-  constexpr int B = Piece<T, N>::BYTES;
-  if constexpr (B % 16 == 0 && ROW_BYTES % 16 == 0) {
+template <typename T>
+struct Unit { static constexpr int EU = 8 / static_cast<int>(sizeof(T)); };
+
+// row element of local element e for lane group g
+template <typename T, int G>
+__device__ __forceinline__ int row_elem(int e, int g) {
+  constexpr int EU = Unit<T>::EU;
+  return ((e / EU) * G + g) * EU + e % EU;
+}
+
+template <typename T, int N, int G>
+__device__ __forceinline__ void load_piece(Piece<T, N>& p, const char* row, int g) {
+  static_assert(Piece<T, N>::BYTES % 8 == 0, "whole 8-byte units");
 #pragma unroll
-    for (int k = 0; k < B / 16; ++k) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + k);
-      p.w[4 * k] = v.x; p.w[4 * k + 1] = v.y; p.w[4 * k + 2] = v.z; p.w[4 * k + 3] = v.w;
-    }
-  } else {
-    static_assert(B % 8 == 0 && ROW_BYTES % 8 == 0, "8-byte aligned row pieces");
-#pragma unroll
-    for (int k = 0; k < B / 8; ++k) {
-      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src) + k);
-      p.w[2 * k] = v.x; p.w[2 * k + 1] = v.y;
-    }
+  for (int k = 0; k < Piece<T, N>::UNITS; ++k) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row) + k * G + g);
+    p.w[2 * k] = v.x; p.w[2 * k + 1] = v.y;
   }
 }
 
@@ -88,40 +91,13 @@ __device__ __forceinline__ float load_scalar(const T* p) {
   else return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[0]);
 }
 
+// Folded query of one unit in LDS: q~ [RK], beta, then the rotary query [DR].
 template <int RK, int DR>
 struct QaLayout {
-  static constexpr int BETA = RK;       // beta, then three zeros (16-byte alignment)
-  static constexpr int ROT = RK + 4;    // rotary query
+  static constexpr int BETA = RK;
+  static constexpr int ROT = RK + 4;
   static constexpr int QS = RK + 4 + DR;
 };
-
-template <typename T, int D, int RK, int DR>
-__global__ __launch_bounds__(64) void absorbed_prep_kernel(DecodeArgs a, float* qa) {
-  using L = QaLayout<RK, DR>;
-  const int unit = blockIdx.x;  // (b * H + h) * L + li
-  const int li = unit % a.L;
-  const int h = (unit / a.L) % a.H;
-  const int t = a.loop_begin + li;
-  const int lane = threadIdx.x;
-  const float* q = a.q + static_cast<size_t>(unit) * D;
-  const T* W = static_cast<const T*>(a.w_up_k) + static_cast<size_t>(t * a.H + h) * D * RK;
-  const size_t mu_off = a.variant == 0 ? static_cast<size_t>(h * a.T + t) * D
-                                       : static_cast<size_t>(t * a.H + h) * D;
-  const T* mu = static_cast<const T*>(a.mu_k) + mu_off;
-  const float sc = a.scale_log2e;
-  float* o = qa + static_cast<size_t>(unit) * L::QS;
-  for (int r = lane; r < RK; r += 64) {
-    float acc = 0.f;
-    for (int i = DR; i < D; ++i) acc += q[i] * load_scalar(W + static_cast<size_t>(i) * RK + r);
-    o[r] = acc * sc;
-  }
-  float bp = 0.f;
-  for (int i = DR + lane; i < D; i += 64) bp += q[i] * load_scalar(mu + i);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) bp += shfl_xor(bp, m);
-  if (lane < 4) o[L::BETA + lane] = lane == 0 ? bp * sc : 0.f;
-  for (int i = lane; i < DR; i += 64) o[L::ROT + i] = q[i] * sc;
-}
 
 // v + (v of lane l ^ 8): rotate each 16-lane row by 8 (DPP row_ror:8)
 __device__ __forceinline__ float sum_xor8(float v) {
@@ -137,19 +113,20 @@ __device__ __forceinline__ float sum_groups(float v) {
 }
 
 template <typename T, int D, int RK, int RV, int DR, int G, int TPC>
-__global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const void* k_rope,
-                                                              const float* qa) {
+__global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const void* k_rope) {
   using L = QaLayout<RK, DR>;
   constexpr int TOK = 64 / G;                           // tokens per tile
   constexpr int NK = RK / G, NR = DR / G, NV = RV / G;  // row elements per lane group
   constexpr int ES = static_cast<int>(sizeof(T));
-  static_assert(RK % (4 * G) == 0 && DR % (4 * G) == 0 && RV % (2 * G) == 0, "shape");
+  static_assert((RK * ES) % (8 * G) == 0 && (DR * ES) % (8 * G) == 0 && (RV * ES) % (8 * G) == 0,
+                "rows cut into whole 8-byte units per lane group");
   struct Rows {
     Piece<T, NK> k[TPC];
     Piece<T, NR> r[TPC];
     Piece<T, NV> v[TPC];
   };
   __shared__ float abar[RV];
+  __shared__ float qs[QaLayout<RK, DR>::QS];
 
   const int lane = threadIdx.x;
   const int lo = lane % TOK, hi = lane / TOK;
@@ -169,21 +146,40 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
   const int nchunk = (ntok + TOK * TPC - 1) / (TOK * TPC);
   const int nfull = ntok / (TOK * TPC);
 
-  // this lane's slice of the folded query
-  const float* qv = qa + unit * L::QS;
+  // ---- fold the query: q~ = W_up,k,t[content]^T q[content], beta = q[content] . mu_k,t ----
+  {
+    const float* q = a.q + unit * D;
+    const T* W = static_cast<const T*>(a.w_up_k) + static_cast<size_t>(t * a.H + h) * D * RK;
+    const size_t mu_off = a.variant == 0 ? static_cast<size_t>(h * a.T + t) * D
+                                         : static_cast<size_t>(t * a.H + h) * D;
+    const T* mu = static_cast<const T*>(a.mu_k) + mu_off;
+    const float sc = a.scale_log2e;
+    for (int r = lane; r < RK; r += 64) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int i = DR; i < D; ++i) acc += q[i] * load_scalar(W + static_cast<size_t>(i) * RK + r);
+      qs[r] = acc * sc;
+    }
+    float bp = 0.f;
+    for (int i = DR + lane; i < D; i += 64) bp += q[i] * load_scalar(mu + i);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) bp += shfl_xor(bp, m);
+    if (lane == 0) qs[L::BETA] = bp * sc;
+    for (int i = lane; i < DR; i += 64) qs[L::ROT + i] = q[i] * sc;
+  }
+  __syncthreads();
+  // this lane's slice of the folded query, in its row-unit order
+  const float* qv = qs;
   float qk[NK], qr[NR];
 #pragma unroll
-  for (int e = 0; e < NK; ++e) qk[e] = qv[hi * NK + e];
+  for (int e = 0; e < NK; ++e) qk[e] = qv[row_elem<T, G>(e, hi)];
 #pragma unroll
-  for (int e = 0; e < NR; ++e) qr[e] = qv[L::ROT + hi * NR + e];
+  for (int e = 0; e < NR; ++e) qr[e] = qv[L::ROT + row_elem<T, G>(e, hi)];
   const float beta = hi == 0 ? qv[L::BETA] : 0.f;  // added once per token
 
-  const char* ck = static_cast<const char*>(a.c_k) +
-                   (static_cast<size_t>(b * a.Hc + hc) * a.n_max) * RK * ES + hi * NK * ES;
-  const char* kr = static_cast<const char*>(k_rope) +
-                   (static_cast<size_t>(b * a.H + h) * a.n_max) * DR * ES + hi * NR * ES;
-  const char* cv = static_cast<const char*>(a.c_v) +
-                   (static_cast<size_t>(b * a.Hc + hc) * a.n_max) * RV * ES + hi * NV * ES;
+  const char* ck = static_cast<const char*>(a.c_k) + (static_cast<size_t>(b * a.Hc + hc) * a.n_max) * RK * ES;
+  const char* kr = static_cast<const char*>(k_rope) + (static_cast<size_t>(b * a.H + h) * a.n_max) * DR * ES;
+  const char* cv = static_cast<const char*>(a.c_v) + (static_cast<size_t>(b * a.Hc + hc) * a.n_max) * RV * ES;
 
   auto load_chunk = [&](Rows& R, int c) {
     const int tok0 = s0 + c * TPC * TOK;
@@ -192,9 +188,9 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
     for (int tt = 0; tt < TPC; ++tt) {
       const int row0 = tok0 + TOK * tt + lo;
       const size_t row = static_cast<size_t>(clamp ? min(row0, s1 - 1) : row0);
-      load_piece<T, NK, RK * ES>(R.k[tt], ck + row * (RK * ES));
-      load_piece<T, NR, DR * ES>(R.r[tt], kr + row * (DR * ES));
-      load_piece<T, NV, RV * ES>(R.v[tt], cv + row * (RV * ES));
+      load_piece<T, NK, G>(R.k[tt], ck + row * (RK * ES), hi);
+      load_piece<T, NR, G>(R.r[tt], kr + row * (DR * ES), hi);
+      load_piece<T, NV, G>(R.v[tt], cv + row * (RV * ES), hi);
     }
   };
 
@@ -266,7 +262,7 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
     float* out = a.part + (unit * a.S + split) * (2 + RV);
     if (lo == 0) {
 #pragma unroll
-      for (int e = 0; e < NV; ++e) out[2 + hi * NV + e] = acc[e];
+      for (int e = 0; e < NV; ++e) out[2 + row_elem<T, G>(e, hi)] = acc[e];
       if (hi == 0) {
         out[0] = mx;
         out[1] = lsum;
@@ -279,7 +275,7 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   if (lo == 0) {
 #pragma unroll
-    for (int e = 0; e < NV; ++e) abar[hi * NV + e] = acc[e] * inv;
+    for (int e = 0; e < NV; ++e) abar[row_elem<T, G>(e, hi)] = acc[e] * inv;
   }
   __syncthreads();
   const T* Wv = static_cast<const T*>(a.w_up_v) + static_cast<size_t>(t * a.H + h) * D * RV;
@@ -302,20 +298,22 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
 }
 
 template <typename T, int D, int RK, int RV, int DR, int G, int TPC>
-void launch(const DecodeArgs& a, const void* k_rope, float* qa, hipStream_t s) {
-  const int units = a.B * a.H * a.L;
-  hipLaunchKernelGGL((absorbed_prep_kernel<T, D, RK, DR>), dim3(units), dim3(64), 0, s, a, qa);
+void launch(const DecodeArgs& a, const void* k_rope, hipStream_t s) {
   hipLaunchKernelGGL((decode_absorbed_kernel<T, D, RK, RV, DR, G, TPC>), dim3(a.S, a.H * a.L, a.B),
-                     dim3(64), 0, s, a, k_rope, static_cast<const float*>(qa));
+                     dim3(64), 0, s, a, k_rope);
 }
 
 }  // namespace
 
+#ifndef LLA_ABS_WIDE_TPC
+#define LLA_ABS_WIDE_TPC 2  // tiles per chunk for the wide (8 lane group) shapes
+#endif
+
 // (dtype, d, r_k, r_v, d_rope, lane groups, tiles per chunk)
-#define LLA_ABSORBED_SHAPES(X)         \
-  X(bf16_t, 1, 128, 96, 160, 32, 8, 2) \
-  X(bf16_t, 1, 128, 96, 160, 64, 8, 2) \
-  X(bf16_t, 1, 128, 96, 160, 96, 8, 2) \
+#define LLA_ABSORBED_SHAPES(X)                        \
+  X(bf16_t, 1, 128, 96, 160, 32, 8, LLA_ABS_WIDE_TPC) \
+  X(bf16_t, 1, 128, 96, 160, 64, 8, LLA_ABS_WIDE_TPC) \
+  X(bf16_t, 1, 128, 96, 160, 96, 8, LLA_ABS_WIDE_TPC) \
   X(bf16_t, 1, 128, 16, 32, 32, 4, 4)  \
   X(bf16_t, 1, 128, 16, 32, 64, 4, 2)  \
   X(bf16_t, 1, 64, 16, 32, 32, 4, 4)   \
@@ -330,13 +328,11 @@ bool decode_absorbed_supported(int dtype, int d, int r_k, int r_v, int d_rope) {
   return false;
 }
 
-size_t absorbed_query_floats(int r_k, int d_rope) { return static_cast<size_t>(r_k) + 4 + d_rope; }
-
 bool launch_decode_absorbed(int dtype, int d, int r_k, int r_v, int d_rope, const DecodeArgs& a,
-                            const void* k_rope, float* qa, hipStream_t s) {
+                            const void* k_rope, hipStream_t s) {
 #define X(T_, DT_, D_, RK_, RV_, DR_, G_, TPC_)                                    \
   if (dtype == DT_ && d == D_ && r_k == RK_ && r_v == RV_ && d_rope == DR_) {      \
-    launch<T_, D_, RK_, RV_, DR_, G_, TPC_>(a, k_rope, qa, s);                     \
+    launch<T_, D_, RK_, RV_, DR_, G_, TPC_>(a, k_rope, s);                         \
     return true;                                                                   \
   }
   LLA_ABSORBED_SHAPES(X)

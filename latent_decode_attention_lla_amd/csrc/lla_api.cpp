@@ -311,10 +311,8 @@ size_t lla_decode_absorbed_workspace_bytes(const lla_dims* d, int32_t d_rope, in
   if (check_dims(d) != LLA_OK || n_ctx < 0 || n_ctx > d->n_max || loop_count < 1) return 0;
   if (d_rope < 16 || d_rope >= d->d_head || d_rope % 16 != 0) return 0;
   const Plan p = plan_absorbed(*d, n_ctx, loop_count, opts);
-  const size_t units = static_cast<size_t>(d->batch) * d->H * loop_count;
-  const size_t qa = (units * lla::absorbed_query_floats(d->r_k, d_rope) * 4 + 255) / 256 * 256;
-  const size_t part = units * p.S * (2 + d->r_v) * 4;
-  return qa + (part + 255) / 256 * 256;
+  const size_t part = static_cast<size_t>(d->batch) * d->H * loop_count * p.S * (2 + d->r_v) * 4;
+  return (part + 255) / 256 * 256;
 }
 
 int32_t lla_decode_absorbed_supported(const lla_dims* d, int32_t d_rope) {
@@ -351,8 +349,6 @@ int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, cons
   const size_t es = elem_bytes(*d);
   const int Hc = latent_heads(*d);
   const int K = d->T * d_in(*d);
-  const size_t units = static_cast<size_t>(d->batch) * d->H * loop_count;
-  const size_t qa_bytes = (units * lla::absorbed_query_floats(d->r_k, d_rope) * 4 + 255) / 256 * 256;
   lla::DecodeArgs a;
   a.c_k = static_cast<const char*>(cache->c_k) +
           static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * d->r_k * es;
@@ -368,7 +364,7 @@ int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, cons
   a.rope16 = nullptr;
   a.q = q;
   a.ctx_lens = ctx_lens;
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + qa_bytes);
+  a.part = static_cast<float*>(workspace);
   a.out = out;
   a.B = d->batch;
   a.H = d->H;
@@ -387,8 +383,7 @@ int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, cons
                    static_cast<size_t>(layer) * d->batch * d->H * static_cast<size_t>(d->n_max) * d_rope * es;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!lla::launch_decode_absorbed(d->dtype, d->d_head, d->r_k, d->r_v, d_rope, a, kr,
-                                   static_cast<float*>(workspace), s))
+  if (!lla::launch_decode_absorbed(d->dtype, d->d_head, d->r_k, d->r_v, d_rope, a, kr, s))
     return LLA_ERR_UNSUPPORTED;
   st = hip_status();
   if (st != LLA_OK) return st;

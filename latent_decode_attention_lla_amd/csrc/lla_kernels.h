@@ -52,12 +52,10 @@ bool decode_fold_wide_supported(int dtype, int d, int r_k, int r_v);
 int fold_wide_heads_per_group(int d, int r_k, int r_v, bool shared);
 int fold_wide_waves_per_head();
 bool launch_combine(int dtype, int d, int r_v, const DecodeArgs& a, hipStream_t s);
-// Decoupled-RoPE absorbed decode: `k_rope` is the layer's rotary-key base, `qa` a
-// workspace of units * absorbed_query_floats(r_k, d_rope) floats for the folded queries.
+// Decoupled-RoPE absorbed decode: `k_rope` is the layer's rotary-key base.
 bool launch_decode_absorbed(int dtype, int d, int r_k, int r_v, int d_rope, const DecodeArgs& a,
-                            const void* k_rope, float* qa, hipStream_t s);
+                            const void* k_rope, hipStream_t s);
 bool decode_absorbed_supported(int dtype, int d, int r_k, int r_v, int d_rope);
-size_t absorbed_query_floats(int r_k, int d_rope);
 bool decode_reconstruct_supported(int dtype, int d, int r_k, int r_v);
 bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v);
 

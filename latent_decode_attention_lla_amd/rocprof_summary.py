@@ -68,7 +68,7 @@ def main(argv=None):
     t.add_argument("--sum", action="store_true")
     t.add_argument("--out")
     t.add_argument("--extra", default="{}", help="JSON merged into the output")
-    t.add_argument("--call", choices=["decode", "encode"],
+    t.add_argument("--call", choices=["decode", "absorbed", "encode"],
                    help="with --workload: record the call's source hash and algorithmic bytes")
     t.add_argument("--workload")
     a = p.parse_args(argv)
@@ -104,7 +104,7 @@ def main(argv=None):
         from latent_decode_attention_lla_amd.inputs import WORKLOADS
         w = WORKLOADS[a.workload]
         _, n_new, _ = bench.step_shape(w)
-        alg, _ = bench.algorithmic(w, a.call, n_new=n_new)
+        alg, _ = bench.algorithmic(w, "encode" if a.call == "encode" else "decode", n_new=n_new)
         res.update({"call": a.call, "workload": a.workload, "path": "auto",
                     "kernel_source_hash": bench.kernel_source_hash(a.call),
                     "algorithmic_bytes_per_launch": alg,
