@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "reconstruct", "rotary_fold"])
     p.add_argument("--splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-reference-calls", action="store_true",
+                   help="skip timing the full-RoPE paths beside the absorbed decode")
     p.add_argument("--cpu-sample-seqs", type=int, default=1)
     p.add_argument("--copy-calibration-gib", type=float, default=0.0,
                    help="only run a plain device copy of this size (for counter scaling)")
@@ -313,7 +315,7 @@ def main():
     dominant = "decode" if dec_ms * n_dec >= enc_ms * n_enc else "encode"
 
     reference = None
-    if absorbed:
+    if absorbed and not args.no_reference_calls:
         # the same call shape on the full-RoPE paths, for the ratio the pages report
         reference = {}
         for name, pth in (("rotary_fold_full_rope", lla.LLA_PATH_AUTO), ("reconstruct", lla.LLA_PATH_RECONSTRUCT)):
