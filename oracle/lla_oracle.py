@@ -30,7 +30,8 @@ printed on the pages, the full-rank special case against textbook attention, RoP
 invariants, softmax special cases, a scalar brute-force re-derivation, the LLA-2D
 block-diagonal reduction and the Eckart-Young property of the SVD initialisation;
 the decoupled decode against textbook attention on the original keys and values, a
-scalar brute force, and its reduction to the full-RoPE decode).
+scalar brute force, and its reduction to the full-RoPE decode; the uncompressed decode
+against textbook attention and against the latent decode of the same cache).
 """
 
 from __future__ import annotations
@@ -55,6 +56,8 @@ __all__ = [
     "absorbed_scale",
     "absorbed_keys",
     "decode_absorbed",
+    "teacher_rows",
+    "decode_teacher",
     "svd_init",
     "round_bf16",
     "encode_stored",
@@ -283,6 +286,43 @@ def decode_absorbed(c_k: np.ndarray, c_v: np.ndarray, k_rope: np.ndarray,
                 v_hat = reconstruct(cv, w_up_v[t, h], _mu_slice(mu_v, variant, t, h, H, d))
                 out[b, h, li] = attention(np.asarray(q[b, h, li], dtype=np.float64),
                                           absorbed_keys(kr, k_hat, d_rope), v_hat, scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Uncompressed decode: the teacher's loop-indexed cache (Section 3, "Problem setup":
+# every loop t keeps its own keys and values; Section 7, Table 5's "teacher" column).
+# ---------------------------------------------------------------------------
+
+def teacher_rows(cache: np.ndarray, t: int, b: int, h: int, nb: int) -> np.ndarray:
+    """The first nb cached rows of loop t, sequence b, head h: [nb, d] float64."""
+    return np.asarray(cache[t, b, h, :nb], dtype=np.float64)
+
+
+def decode_teacher(k_cache: np.ndarray, v_cache: np.ndarray, q: np.ndarray,
+                   loop_begin: int = 0, ctx_lens=None, scale: float | None = None) -> np.ndarray:
+    """Decode attention over the uncompressed per-loop cache.
+
+    k_cache [T, B, H, n, d] : keys of every loop, already rotated to their positions
+    v_cache [T, B, H, n, d] : values of every loop
+    q [B, H, L, d]          : rotated queries for loops loop_begin .. loop_begin+L-1
+    returns out [B, H, L, d] float64 (zeros for an empty context)
+    """
+    T, B, H, n, d = k_cache.shape
+    L = q.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if ctx_lens is None:
+        ctx_lens = [n] * B
+    out = np.zeros((B, H, L, d), dtype=np.float64)
+    for b in range(B):
+        nb = int(ctx_lens[b])
+        for h in range(H):
+            for li in range(L):
+                t = loop_begin + li
+                out[b, h, li] = attention(np.asarray(q[b, h, li], dtype=np.float64),
+                                          teacher_rows(k_cache, t, b, h, nb),
+                                          teacher_rows(v_cache, t, b, h, nb), scale)
     return out
 
 

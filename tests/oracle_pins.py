@@ -450,6 +450,48 @@ def pin_absorbed_equals_full_rope() -> float:
     return float(np.max(np.abs(got - ref)))
 
 
+def pin_teacher_textbook() -> float:
+    """Uncompressed decode against torch SDPA (fp64) on the same per-loop caches, ragged
+    contexts included (a masked tail)."""
+    T, B, H, n, d = 3, 2, 2, 9, 8
+    rng = _rng(91)
+    k = rng.standard_normal((T, B, H, n, d))
+    v = rng.standard_normal((T, B, H, n, d))
+    q = rng.standard_normal((B, H, T, d))
+    lens = [9, 4]
+    got = O.decode_teacher(k, v, q, 0, lens)
+    err = 0.0
+    for t in range(T):
+        for b in range(B):
+            kk = torch.from_numpy(k[t, b, :, :lens[b]])[None]
+            vv = torch.from_numpy(v[t, b, :, :lens[b]])[None]
+            qq = torch.from_numpy(q[b, :, t])[None, :, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[0, :, 0]
+            err = max(err, float(np.max(np.abs(got[b, :, t] - ref.numpy()))))
+    return err
+
+
+def pin_teacher_equals_latent_decode() -> float:
+    """The latent decode is the teacher's attention over the keys and values that the
+    codec rebuilds: materialise K_t = RoPE(c_k W_up,k,t^T + mu_k,t) (complex RoPE here)
+    and V_t, and the uncompressed decode of them equals the latent decode."""
+    a = _tiny(92, T=3, n=7)
+    T, H, d = a["w_up_k"].shape[0], a["w_up_k"].shape[1], a["w_up_k"].shape[2]
+    B, n = a["q"].shape[0], a["c_k"].shape[2]
+    k = np.empty((T, B, H, n, d))
+    v = np.empty((T, B, H, n, d))
+    for t in range(T):
+        for b in range(B):
+            for h in range(H):
+                kh = a["c_k"][b, h] @ a["w_up_k"][t, h].T + a["mu_k"][h][t * d:(t + 1) * d]
+                k[t, b, h] = _textbook_rope_complex(torch.from_numpy(kh), torch.arange(n), 10000.0).numpy()
+                v[t, b, h] = a["c_v"][b, h] @ a["w_up_v"][t, h].T + a["mu_v"][h][t * d:(t + 1) * d]
+    lens = [7, 3]
+    got = O.decode_teacher(k, v, a["q"], 0, lens)
+    ref = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"], a["q"], 0, lens)
+    return float(np.max(np.abs(got - ref)))
+
+
 ALL_PINS = {
     "closed_forms": (pin_closed_forms, 1e-9),
     "rope": (pin_rope, 1e-12),
@@ -463,4 +505,6 @@ ALL_PINS = {
     "absorbed_textbook": (pin_absorbed_textbook, 1e-12),
     "absorbed_brute_force": (pin_absorbed_brute_force, 1e-12),
     "absorbed_equals_full_rope": (pin_absorbed_equals_full_rope, 1e-12),
+    "teacher_textbook": (pin_teacher_textbook, 1e-12),
+    "teacher_equals_latent_decode": (pin_teacher_equals_latent_decode, 1e-12),
 }

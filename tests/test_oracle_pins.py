@@ -106,6 +106,10 @@ def _mut_absorbed_scale_content_only(d, d_rope):
     return 1.0 / np.sqrt(max(d - d_rope, 1))
 
 
+def _mut_teacher_next_loop(cache, t, b, h, nb):
+    return np.asarray(cache[(t + 1) % cache.shape[0], b, h, :nb], dtype=np.float64)
+
+
 _ORIG = {name: getattr(O, name) for name in
          ("apply_rope", "reconstruct", "attention", "_mu_slice", "rope_theta", "absorbed_keys")}
 
@@ -127,6 +131,7 @@ MUTANTS = {
     "absorbed_drops_rotary": ("absorbed_keys", _mut_absorbed_drops_rotary),
     "absorbed_content_rotated": ("absorbed_keys", _mut_absorbed_content_rotated),
     "absorbed_scale_content_only": ("absorbed_scale", _mut_absorbed_scale_content_only),
+    "teacher_next_loop": ("teacher_rows", _mut_teacher_next_loop),
 }
 
 
