@@ -38,13 +38,14 @@ _COMMON_SOURCES = ("lla_device.h", "lla_kernels.h", "lla_api.cpp")
 KERNEL_SOURCES = {
     "decode": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip",
                                  "decode_reconstruct.hip", "combine.hip", "rope_table.hip"),
-    "absorbed": _COMMON_SOURCES + ("decode_absorbed.hip", "combine.hip"),
+    "absorbed": _COMMON_SOURCES + ("decode_absorbed.hip", "decode_stream.h", "combine.hip"),
     "encode": _COMMON_SOURCES + ("encode.hip",),
+    "teacher": _COMMON_SOURCES + ("decode_teacher.hip", "decode_stream.h", "combine.hip"),
 }
 
 
 def kernel_source_hash(kind: str) -> str:
-    """Hash of the HIP/C++ sources behind one call kind ("decode", "absorbed" or "encode") with comments
+    """Hash of the HIP/C++ sources behind one call kind (a key of KERNEL_SOURCES) with comments
     and whitespace removed: it changes when that call's compiled code or launch plan can
     change, not when a comment or the other call's sources do."""
     import re
@@ -121,18 +122,25 @@ def cpu_baseline(w, seqs: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    # the decoupled decode's oracle rebuilds a 32768-token context per (head, loop): one
-    # layer is timed and the step scaled by D
-    layers = 1 if w.d_rope > 0 else w.D
+    # the decoupled decode's oracle rebuilds a 32768-token context per (head, loop), and
+    # the uncompressed cache of one sequence is 1.6 GB at 24 layers: a few layers are
+    # timed and the step scaled by D
+    layers = 1 if w.d_rope > 0 else (2 if w.teacher else w.D)
     sw = w.replace(batch=seqs, D=layers)
-    t = decode_inputs(sw, seed=12345, device="cpu")
+    if w.teacher:
+        from latent_decode_attention_lla_amd.inputs import teacher_inputs
+        t = teacher_inputs(sw, seed=12345, device="cpu")
+    else:
+        t = decode_inputs(sw, seed=12345, device="cpu")
     t = {k: v.float().numpy().astype(np.float64) for k, v in t.items()}
     variant = "per_head" if w.variant == "per_head" else "2d"
     t0 = time.perf_counter()
     for loop in range(w.T):
         for layer in range(layers):
             q = t["q"][layer, loop:loop + 1].transpose(1, 2, 0, 3)
-            if w.d_rope > 0:
+            if w.teacher:
+                O.decode_teacher(t["k_cache"][layer], t["v_cache"][layer], q, loop)
+            elif w.d_rope > 0:
                 O.decode_absorbed(t["c_k"][layer], t["c_v"][layer], t["k_rope"][layer],
                                   t["w_up_k"][layer], t["mu_k"][layer], t["w_up_v"][layer],
                                   t["mu_v"][layer], q, w.d_rope, loop, None, None, variant)
@@ -152,6 +160,8 @@ def cpu_baseline(w, seqs: int):
 def step_shape(w):
     """(prefill, tokens encoded per sequence, layers) of one step of workload ``w``."""
     prefill = w.name in ("ouro_layer_4x", "encode_heavy")
+    if w.teacher:  # the uncompressed cache has no encode
+        return False, 0, w.D
     return prefill, (w.n if prefill else 1), (1 if prefill else w.D)
 
 
@@ -163,6 +173,11 @@ def algorithmic(w, kind: str, L: int = 1, n_new: int = 0):
     encode: x_k and x_v read once, latents written once, W_down and mu read once;
             flops 2 T d_in (r_k + r_v) per (token, latent head)."""
     es = 2 if w.dtype == "bf16" else 4
+    if kind == "decode" and w.teacher:
+        # uncompressed decode: one loop's key and value rows read once, q and out;
+        # 4 d flop per (token, head) for the score and the weighted value
+        nbytes = 2 * w.batch * w.H * w.n * w.d * es + 2 * w.batch * w.H * L * w.d * 4
+        return nbytes, 4.0 * w.batch * w.H * w.n * L * w.d
     if kind == "decode":
         tok = w.batch * w.Hc * w.n
         nbytes = (tok * (w.r_k + w.r_v) * es + 2 * w.batch * w.H * L * w.d * 4
@@ -206,7 +221,7 @@ def main():
         return
 
     from latent_decode_attention_lla_amd import lla
-    from latent_decode_attention_lla_amd.harness import DeviceLatentStore
+    from latent_decode_attention_lla_amd.harness import DeviceLatentStore, DeviceTeacherCache
     from latent_decode_attention_lla_amd.inputs import WORKLOADS
 
     if not os.path.exists(lla.LIB_PATH):
@@ -222,25 +237,35 @@ def main():
     # sequence for one layer, then take one decode step over all loops of that layer.
     prefill, n_new, layers = step_shape(w)
     pos = 0 if prefill else w.n - 1
-    print(f"[bench] allocating {args.workload}: latents "
-          f"{w.D * w.batch * w.Hc * w.n * (w.r_k + w.r_v) * (2 if w.dtype == 'bf16' else 4) / 2**30:.1f} GiB",
-          file=sys.stderr, flush=True)
-    st = DeviceLatentStore(w, seed=3, device=dev)
-    # Encode-side codec and the finished per-loop K/V to encode for every layer used.
-    g = torch.Generator(device=dev).manual_seed(4)
-    K = w.T * w.d_in
-    dt = w.torch_dtype
-    st.t["w_down_k_t"] = (torch.randn(w.D, w.Hc, w.r_k, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
-    st.t["w_down_v_t"] = (torch.randn(w.D, w.Hc, w.r_v, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
-    st.codec = lla.make_codec(st.t["w_down_k_t"], st.t["mu_k"], st.t["w_up_k"], st.t["w_down_v_t"],
-                              st.t["mu_v"], st.t["w_up_v"], st.rope)
-    x_new = [torch.randn(layers, w.batch, n_new, w.Hc, w.T, w.d_in, generator=g, device=dev).to(dt)
-             for _ in range(2)]
+    es = 2 if w.dtype == "bf16" else 4
+    teacher = w.teacher  # the uncompressed per-loop cache, no codec
+    cache_gib = (2 * w.D * w.T * w.batch * w.H * w.n * w.d * es if teacher else
+                 w.D * w.batch * w.Hc * w.n * (w.r_k + w.r_v) * es) / 2**30
+    print(f"[bench] allocating {args.workload}: {'K/V cache' if teacher else 'latents'} "
+          f"{cache_gib:.1f} GiB", file=sys.stderr, flush=True)
     path = {"auto": lla.LLA_PATH_AUTO, "reconstruct": lla.LLA_PATH_RECONSTRUCT,
             "rotary_fold": lla.LLA_PATH_ROTARY_FOLD}[args.path]
     opts = lla.make_opts(args.splits, path)
     absorbed = w.d_rope > 0  # the decoupled-RoPE absorbed decode (one wave per head)
-    if absorbed:
+    if teacher:
+        st = DeviceTeacherCache(w, seed=3, device=dev)
+        x_new = None
+    else:
+        st = DeviceLatentStore(w, seed=3, device=dev)
+        # Encode-side codec and the finished per-loop K/V to encode for every layer used.
+        g = torch.Generator(device=dev).manual_seed(4)
+        K = w.T * w.d_in
+        dt = w.torch_dtype
+        st.t["w_down_k_t"] = (torch.randn(w.D, w.Hc, w.r_k, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
+        st.t["w_down_v_t"] = (torch.randn(w.D, w.Hc, w.r_v, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
+        st.codec = lla.make_codec(st.t["w_down_k_t"], st.t["mu_k"], st.t["w_up_k"], st.t["w_down_v_t"],
+                                  st.t["mu_v"], st.t["w_up_v"], st.rope)
+        x_new = [torch.randn(layers, w.batch, n_new, w.Hc, w.T, w.d_in, generator=g, device=dev).to(dt)
+                 for _ in range(2)]
+    if teacher:
+        S = lla.lla_decode_num_splits(st.dims, w.n, 1, lla.make_opts(args.splits, lla.LLA_PATH_RECONSTRUCT))
+        ws = st.workspace(w.n, 1, opts)
+    elif absorbed:
         S = lla.lla_decode_num_splits(st.dims, w.n, 1, lla.make_opts(args.splits, lla.LLA_PATH_RECONSTRUCT))
         ws = st.absorbed_workspace(w.n, 1, opts)
     else:
@@ -250,7 +275,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     n_dec = layers * w.T
-    n_enc = layers
+    n_enc = 0 if teacher else layers
     steps = max(args.steps, 1)
     ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n_dec * steps)]
@@ -258,7 +283,7 @@ def main():
               for _ in range(n_enc * steps)]
 
     def step(record):
-        for layer in range(layers):
+        for layer in range(n_enc):
             if record is not None:
                 ev_enc[record * n_enc + layer][0].record(stream)
             lla.lla_encode(st.dims, st.codec, st.cache, layer, x_new[0][layer], x_new[1][layer],
@@ -271,7 +296,10 @@ def main():
                 q = st.t["q"][layer, loop]
                 if record is not None:
                     ev_dec[record * n_dec + k][0].record(stream)
-                if absorbed:
+                if teacher:
+                    lla.lla_decode_attn_teacher(st.dims, st.t["k_cache"], st.t["v_cache"], layer, w.n,
+                                                None, q, loop, 1, out, ws, ws.numel(), opts, sp)
+                elif absorbed:
                     lla.lla_decode_attn_absorbed(st.dims, st.codec, st.cache, st.t["k_rope"], w.d_rope,
                                                  layer, w.n, None, q, loop, 1, out, ws, ws.numel(),
                                                  opts, sp)
@@ -302,17 +330,16 @@ def main():
         xs = sorted(a.elapsed_time(b) for a, b in evs[:len(evs)])
         return sum(xs) / len(xs), xs[len(xs) // 2]
 
+    dec_kind = "teacher" if teacher else ("absorbed" if absorbed else "decode")
     dec_ms, dec_med = avg(ev_dec[:n_dec * args.steps])
-    enc_ms, enc_med = avg(ev_enc[:n_enc * args.steps])
     dec_bytes, dec_flops = algorithmic(w, "decode")
-    enc_bytes, enc_flops = algorithmic(w, "encode", n_new=n_new)
-
-    dec_roof = roofline(dec_bytes, dec_flops, dec_ms,
-                        measured_traffic("absorbed" if absorbed else "decode", args.workload,
-                                         args.path))
-    enc_roof = roofline(enc_bytes, enc_flops, enc_ms,
-                        measured_traffic("encode", args.workload, args.path))
-    dominant = "decode" if dec_ms * n_dec >= enc_ms * n_enc else "encode"
+    dec_roof = roofline(dec_bytes, dec_flops, dec_ms, measured_traffic(dec_kind, args.workload, args.path))
+    if n_enc > 0:
+        enc_ms, enc_med = avg(ev_enc[:n_enc * args.steps])
+        enc_bytes, enc_flops = algorithmic(w, "encode", n_new=n_new)
+        enc_roof = roofline(enc_bytes, enc_flops, enc_ms,
+                            measured_traffic("encode", args.workload, args.path))
+    dominant = "decode" if n_enc == 0 or dec_ms * n_dec >= enc_ms * n_enc else "encode"
 
     reference = None
     if absorbed and not args.no_reference_calls:
@@ -344,13 +371,20 @@ def main():
     step_desc = (f"encode a {n_new}-token prompt per sequence for one layer, then {w.T} decode calls"
                  if prefill else
                  f"encode the new token for {w.D} layers, then {w.D} x {w.T} decode calls")
+    if teacher:
+        step_desc = (f"{w.D} x {w.T} uncompressed decode calls over the per-loop K/V cache (the "
+                     f"new token's K/V rows, {w.batch * w.T * w.H * w.d * 2 * es // 1024} KiB per "
+                     f"layer, are not written)")
     if absorbed:
         step_desc += f" (decoupled-RoPE absorbed decode, rotary branch {w.d_rope} wide)"
     res = {
-        "metric": "LLA decode tokens/s (one decode step of the looped model over the latent "
-                  "cache: the new token's encode plus D layers x T loops of latent-store "
-                  "attention), 1 GPU; HBM GB/s or MFMA TFLOP/s of the dominant kernel and "
-                  "fraction of peak",
+        "metric": ("uncompressed (teacher) decode tokens/s (D layers x T loops of attention over "
+                   "the per-loop K/V cache), 1 GPU, the reference for the latent store's ratio"
+                   if teacher else
+                   "LLA decode tokens/s (one decode step of the looped model over the latent "
+                   "cache: the new token's encode plus D layers x T loops of latent-store "
+                   "attention), 1 GPU; HBM GB/s or MFMA TFLOP/s of the dominant kernel and "
+                   "fraction of peak"),
         "value": round(value, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -362,20 +396,24 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian latents, codec maps and queries; no model weights)",
-        "config": {"workload": w.name, "T": w.T, "D": w.D, "H": w.H, "d_head": w.d, "r_k": w.r_k,
-                   "r_v": w.r_v, "batch": w.batch, "context": w.n, "variant": w.variant,
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "H": w.H, "d_head": w.d,
+                   **({"cache": "uncompressed per-loop K/V"} if teacher else
+                      {"r_k": w.r_k, "r_v": w.r_v, "variant": w.variant}),
+                   "batch": w.batch, "context": w.n,
                    "path": args.path, "splits": S, "step": step_desc,
                    "decode_calls_per_step": n_dec, "encode_calls_per_step": n_enc,
                    **({"d_rope": w.d_rope} if absorbed else {})},
         "roofline": dec_roof if dominant == "decode" else enc_roof,
-        "roofline_kernel": ("lla_decode_attn_absorbed" if absorbed else "lla_decode_attn")
+        "roofline_kernel": {"teacher": "lla_decode_attn_teacher", "absorbed": "lla_decode_attn_absorbed",
+                            "decode": "lla_decode_attn"}[dec_kind]
                            if dominant == "decode" else "lla_encode",
         "cpu_baseline": cpu,
         "decode_call": {"avg_ms": round(dec_ms, 5), "median_ms": round(dec_med, 5),
                         "algorithmic_bytes": dec_bytes, "algorithmic_flops": dec_flops,
                         "loop_step_tokens_per_s": round(w.batch / (dec_ms * 1e-3), 1),
                         "roofline": dec_roof},
-        "encode_call": {"avg_ms": round(enc_ms, 5), "median_ms": round(enc_med, 5),
+        "encode_call": None if n_enc == 0 else
+                       {"avg_ms": round(enc_ms, 5), "median_ms": round(enc_med, 5),
                         "tokens": w.batch * n_new, "algorithmic_bytes": enc_bytes,
                         "algorithmic_flops": enc_flops,
                         "tokens_per_s": round(w.batch * n_new / (enc_ms * 1e-3), 1),

@@ -201,6 +201,32 @@ int32_t lla_decode_attn_absorbed(const lla_dims* dims, const lla_codec* codec,
 /* 1 when a kernel is built for (dims' dtype, d_head, r_k, r_v, d_rope), else 0. */
 int32_t lla_decode_absorbed_supported(const lla_dims* dims, int32_t d_rope);
 
+/* Uncompressed decode over the loop-indexed cache that the latent store replaces (Section
+ * 3, "Teacher cache": every loop of every layer keeps its own key and value; Section 7,
+ * Table 5: the teacher's serving path). For every sequence b, head h and loop t:
+ *   out[b][h][t] = softmax_j(scale * q . k_cache[t][b][h][j]) v_cache[t][b][h]  over j < len_b.
+ *   k_cache : device [D][T][batch][H][n_max][d_head] in dims->dtype: keys of every loop,
+ *             already rotated to their positions. Written by the caller.
+ *   v_cache : device [D][T][batch][H][n_max][d_head] in dims->dtype: values of every loop.
+ *   q, out, ctx_lens, layer, n_ctx, loop_begin, loop_count: as lla_decode_attn.
+ *   scale   : dims->scale, 0 = 1/sqrt(d_head).
+ * Only T, D, H, batch, n_max, d_head, dtype and scale of dims are read (the codec fields
+ * r_k, r_v, variant and rope_base are ignored). Built shapes are listed by
+ * lla_decode_teacher_supported (d_head 64 or 128). num_splits of opts applies; its path
+ * field is ignored.
+ *   workspace >= lla_decode_teacher_workspace_bytes(dims, n_ctx, loop_count, opts)
+ *   (the split partials; may be 0 bytes, then workspace may be NULL).
+ * Errors as lla_decode_attn. */
+size_t lla_decode_teacher_workspace_bytes(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,
+                                          const lla_decode_opts* opts);
+int32_t lla_decode_attn_teacher(const lla_dims* dims, const void* k_cache, const void* v_cache,
+                                int32_t layer, int32_t n_ctx, const int32_t* ctx_lens,
+                                const float* q, int32_t loop_begin, int32_t loop_count,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                const lla_decode_opts* opts, void* stream);
+/* 1 when a kernel is built for (dims' dtype, d_head), else 0. */
+int32_t lla_decode_teacher_supported(const lla_dims* dims);
+
 #ifdef __cplusplus
 }
 #endif

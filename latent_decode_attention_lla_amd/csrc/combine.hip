@@ -7,7 +7,8 @@
 //   out = a W_up,v,t^T + mu_v,t
 // which equals sum_j softmax_j V_t[j] because the weights sum to one
 // ("Looped Latent Attention", Section 3 Eq. 3 and Appendix J "Absorbed attention").
-// An empty context (every split empty) gives zeros.
+// For a cache of uncompressed values the partials hold value rows and the merged row is
+// the output itself (no projection). An empty context (every split empty) gives zeros.
 #include "lla_device.h"
 #include "lla_kernels.h"
 
@@ -23,7 +24,7 @@ constexpr int kLdsSplits = 32;  // partials of up to this many splits are staged
 // split partials, its rows of W_up,v,t and mu_v,t) is requested at the start, so the
 // kernel pays one memory round trip: thread k owns output i = k / TPR and the TPR-th
 // slice of that row of W_up,v,t.
-template <typename T, int D, int RV>
+template <typename T, int D, int RV, bool PROJ>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int TPR = 256 / D;      // threads per output row
   constexpr int RS = RV / TPR;      // row entries per thread
@@ -48,14 +49,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     for (int k = tid; k < S * PS; k += 256) part[k] = p[k];
   }
   const int i = tid / TPR, sub = tid % TPR;
-  const T* wv = static_cast<const T*>(a.w_up_v) + static_cast<size_t>(t * a.H + h) * D * RV +
-                static_cast<size_t>(i) * RV + sub * RS;
   float w[RS];
-  load_f32<RS>(wv, w);
-  const size_t mu_off = a.variant == 0 ? static_cast<size_t>(h * a.T + t) * D
-                                       : static_cast<size_t>(t * a.H + h) * D;
-  float mu1[1];
-  load_f32<1>(static_cast<const T*>(a.mu_v) + mu_off + i, mu1);
+  float mu1[1] = {0.f};
+  if constexpr (PROJ) {
+    const T* wv = static_cast<const T*>(a.w_up_v) + static_cast<size_t>(t * a.H + h) * D * RV +
+                  static_cast<size_t>(i) * RV + sub * RS;
+    load_f32<RS>(wv, w);
+    const size_t mu_off = a.variant == 0 ? static_cast<size_t>(h * a.T + t) * D
+                                         : static_cast<size_t>(t * a.H + h) * D;
+    load_f32<1>(static_cast<const T*>(a.mu_v) + mu_off + i, mu1);
+  }
   __syncthreads();
 
   // (2) log-sum-exp weights of the splits, then the normalised latent
@@ -92,6 +95,10 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   };
   const float total = staged ? merge(part) : merge(p);
 
+  if constexpr (!PROJ) {  // the merged value itself (an uncompressed cache)
+    for (int r = tid; r < RV; r += 256) a.out[static_cast<size_t>(unit) * D + r] = abar[r];
+    return;
+  }
   // (3) out = abar W_up,v,t^T + mu_v,t
   float o = 0.f;
 #pragma unroll
@@ -101,9 +108,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (sub == 0) a.out[static_cast<size_t>(unit) * D + i] = total > 0.f ? o + mu1[0] : 0.f;
 }
 
-template <typename T, int D, int RV>
+template <typename T, int D, int RV, bool PROJ = true>
 void launch(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((combine_kernel<T, D, RV>), dim3(a.B * a.H * a.L), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((combine_kernel<T, D, RV, PROJ>), dim3(a.B * a.H * a.L), dim3(256), 0, s, a);
 }
 
 }  // namespace
@@ -118,6 +125,19 @@ bool launch_combine(int dtype, int d, int r_v, const DecodeArgs& a, hipStream_t 
     return true;                                 \
   }
   LLA_COMBINE_SHAPES(X)
+#undef X
+  return false;
+}
+
+// Merge the partials of an uncompressed decode (values of width d, no up-projection).
+bool launch_combine_identity(int dtype, int d, const DecodeArgs& a, hipStream_t s) {
+  (void)dtype;  // the partials are float whatever the cache type
+#define X(D_)                               \
+  if (d == D_) {                            \
+    launch<float, D_, D_, false>(a, s);     \
+    return true;                            \
+  }
+  X(64) X(128)
 #undef X
   return false;
 }

@@ -110,6 +110,25 @@ Plan plan_absorbed(const lla_dims& d, int n_ctx, int loop_count, const lla_decod
   return plan_splits(d, n_ctx, loop_count, &o);
 }
 
+// Uncompressed decode: only the attention shape matters (no codec fields).
+int32_t check_teacher_dims(const lla_dims* d) {
+  if (d == nullptr) return LLA_ERR_INVALID_ARG;
+  if (d->T < 1 || d->D < 1 || d->H < 1 || d->batch < 1 || d->n_max < 1) return LLA_ERR_INVALID_ARG;
+  if (d->d_head < 2 || d->d_head % 2 != 0) return LLA_ERR_INVALID_ARG;
+  if (d->dtype != LLA_F32 && d->dtype != LLA_BF16) return LLA_ERR_INVALID_ARG;
+  if (!(d->scale >= 0.f) || !std::isfinite(d->scale)) return LLA_ERR_INVALID_ARG;
+  if (!lla::decode_teacher_supported(d->dtype, d->d_head)) return LLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(d->n_max) * d->d_head >= (1LL << 31)) return LLA_ERR_UNSUPPORTED;
+  return LLA_OK;
+}
+
+// One wave per (sequence, head, loop, split), as the reconstruct kernel.
+Plan plan_teacher(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_opts* opts) {
+  lla_decode_opts o{0, LLA_PATH_RECONSTRUCT};
+  if (opts != nullptr) o.num_splits = opts->num_splits;
+  return plan_splits(d, n_ctx, loop_count, &o);  // reads batch and H only on this path
+}
+
 int32_t hip_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? LLA_OK : LLA_ERR_HIP;
@@ -389,6 +408,72 @@ int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, cons
   if (st != LLA_OK) return st;
   if (p.S == 1) return LLA_OK;  // the kernel finished the single split itself
   if (!lla::launch_combine(d->dtype, d->d_head, d->r_v, a, s)) return LLA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
+size_t lla_decode_teacher_workspace_bytes(const lla_dims* d, int32_t n_ctx, int32_t loop_count,
+                                          const lla_decode_opts* opts) {
+  if (check_teacher_dims(d) != LLA_OK || n_ctx < 0 || n_ctx > d->n_max || loop_count < 1) return 0;
+  const Plan p = plan_teacher(*d, n_ctx, loop_count, opts);
+  if (p.S == 1) return 0;  // a single split writes the output itself
+  const size_t part = static_cast<size_t>(d->batch) * d->H * loop_count * p.S * (2 + d->d_head) * 4;
+  return (part + 255) / 256 * 256;
+}
+
+int32_t lla_decode_teacher_supported(const lla_dims* d) {
+  return check_teacher_dims(d) == LLA_OK ? 1 : 0;
+}
+
+int32_t lla_decode_attn_teacher(const lla_dims* d, const void* k_cache, const void* v_cache,
+                                int32_t layer, int32_t n_ctx, const int32_t* ctx_lens,
+                                const float* q, int32_t loop_begin, int32_t loop_count,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                const lla_decode_opts* opts, void* stream) {
+  int32_t st = check_teacher_dims(d);
+  if (st != LLA_OK) return st;
+  if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
+  if (n_ctx < 0 || n_ctx > d->n_max) return LLA_ERR_INVALID_ARG;
+  if (loop_begin < 0 || loop_count < 1 || static_cast<long long>(loop_begin) + loop_count > d->T)
+    return LLA_ERR_INVALID_ARG;
+  if (opts != nullptr && opts->num_splits < 0) return LLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {k_cache, v_cache, q, out};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+  if (ctx_lens != nullptr && (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) != 0) return LLA_ERR_INVALID_ARG;
+  const size_t need = lla_decode_teacher_workspace_bytes(d, n_ctx, loop_count, opts);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace))) return LLA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return LLA_ERR_WORKSPACE;
+
+  const Plan p = plan_teacher(*d, n_ctx, loop_count, opts);
+  const size_t es = elem_bytes(*d);
+  const size_t layer_elems = static_cast<size_t>(d->T) * d->batch * d->H *
+                             static_cast<size_t>(d->n_max) * d->d_head;
+  lla::DecodeArgs a{};
+  a.c_k = static_cast<const char*>(k_cache) + static_cast<size_t>(layer) * layer_elems * es;
+  a.c_v = static_cast<const char*>(v_cache) + static_cast<size_t>(layer) * layer_elems * es;
+  a.q = q;
+  a.ctx_lens = ctx_lens;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.B = d->batch;
+  a.H = d->H;
+  a.Hc = d->H;
+  a.T = d->T;
+  a.L = loop_count;
+  a.loop_begin = loop_begin;
+  a.n_max = d->n_max;
+  a.n_ctx = n_ctx;
+  a.S = p.S;
+  a.split_len = p.split_len;
+  const double scale = d->scale > 0.f ? d->scale : 1.0 / std::sqrt(static_cast<double>(d->d_head));
+  a.scale_log2e = static_cast<float>(scale * kLog2e);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!lla::launch_decode_teacher(d->dtype, d->d_head, a, s)) return LLA_ERR_UNSUPPORTED;
+  st = hip_status();
+  if (st != LLA_OK) return st;
+  if (p.S == 1) return LLA_OK;
+  if (!lla::launch_combine_identity(d->dtype, d->d_head, a, s)) return LLA_ERR_UNSUPPORTED;
   return hip_status();
 }
 

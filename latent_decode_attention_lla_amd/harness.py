@@ -8,7 +8,7 @@ from __future__ import annotations
 import torch
 
 from . import lla
-from .inputs import Workload, decode_inputs
+from .inputs import Workload, decode_inputs, teacher_inputs
 
 
 def dims_for(w: Workload, n_max: int | None = None, batch: int | None = None) -> lla.lla_dims:
@@ -90,3 +90,41 @@ class DeviceLatentStore:
     def encode(self, layer: int, x_k: torch.Tensor, x_v: torch.Tensor, pos_start: int,
                n_new: int, stream=None) -> None:
         lla.lla_encode(self.dims, self.codec, self.cache, layer, x_k, x_v, pos_start, n_new, stream)
+
+
+class DeviceTeacherCache:
+    """An uncompressed per-loop key/value cache for one workload, resident on ``device``."""
+
+    def __init__(self, w: Workload, seed: int, device="cuda", n_alloc: int | None = None,
+                 tensors: dict | None = None, with_q: bool = True):
+        self.w = w
+        self.device = torch.device(device)
+        self.n_max = n_alloc or w.n
+        t = tensors if tensors is not None else teacher_inputs(w, seed, device, self.n_max, with_q)
+        self.t = {k: v.to(self.device).contiguous() for k, v in t.items()}
+        self.dims = dims_for(w, self.n_max)
+        self._ws = None
+
+    def workspace(self, n_ctx: int, loop_count: int, opts=None) -> torch.Tensor:
+        nb = lla.lla_decode_teacher_workspace_bytes(self.dims, n_ctx, loop_count, opts)
+        if self._ws is None or self._ws.numel() < nb:
+            self._ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode(self, layer: int, loop_begin: int, loop_count: int, q: torch.Tensor | None = None,
+               n_ctx: int | None = None, ctx_lens: torch.Tensor | None = None, opts=None,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        w = self.w
+        n_ctx = w.n if n_ctx is None else n_ctx
+        if q is None:
+            if loop_count == 1:
+                q = self.t["q"][layer, loop_begin]
+            else:
+                q = self.t["q"][layer, loop_begin:loop_begin + loop_count].permute(1, 2, 0, 3).contiguous()
+        if out is None:
+            out = torch.empty(w.batch, w.H, loop_count, w.d, dtype=torch.float32, device=self.device)
+        ws = self.workspace(n_ctx, loop_count, opts)
+        lla.lla_decode_attn_teacher(self.dims, self.t["k_cache"], self.t["v_cache"], layer, n_ctx,
+                                    ctx_lens, q, loop_begin, loop_count, out, ws, ws.numel(), opts,
+                                    stream)
+        return out

@@ -17,6 +17,10 @@ Table 5):
 * ``absorbed_4x``   the Ouro-1.4B 4x geometry, T=4, D=24, H=16, d=128, (96, 160), bf16,
                     decoupled decode with a 64-wide rotary branch (Appendix J, Table 14's
                     d_rope), batch 8, context 32768 (Table 13's shortest context)
+* ``teacher_4k``    the uncompressed loop-indexed cache the latent store replaces (Section
+                    3 "Teacher cache"; Table 5's teacher column): T=4, D=24, H=16, d=128,
+                    bf16 keys and values for every loop, batch 32 (the teacher's measured
+                    capacity at 4k), context 4096
 
 Distributions: latents, queries and pre-RoPE K/V ~ N(0, 1); W_up,t ~ N(0, 1/r)
 (variance 1/r, so rebuilt keys have about unit variance); mu ~ N(0, 0.1) (variance).
@@ -26,6 +30,8 @@ of W_down, the structure the SVD initialisation produces) or Gaussian.
 Memory layouts (all row-major, shared with the C ABI):
   c_k  [D][B][Hc][n_max][r_k]     c_v  [D][B][Hc][n_max][r_v]
   k_rope [D][B][H][n_max][d_rope] (rotary keys of the decoupled decode, ~ N(0, 1))
+  k_cache, v_cache [D][T][B][H][n_max][d] (the uncompressed cache, ~ N(0, 1); keys
+                  already rotated)
   w_down_k_t [D][Hc][r_k][T*d_in] (W_down transposed)   mu_k [D][Hc][T*d_in]
   w_up_k [D][T][H][d][r_k]        (same for v)
   q    [D][T][B][H][d]  (post-RoPE queries for every layer and loop)
@@ -56,6 +62,7 @@ class Workload:
     dtype: str = "bf16"            # "f32" or "bf16" (latents and codec weights)
     rope_base: float = 10000.0
     d_rope: int = 0                # rotary-branch width of the decoupled (absorbed) decode
+    teacher: bool = False          # an uncompressed per-loop cache (no codec)
 
     @property
     def Hc(self) -> int:
@@ -86,6 +93,8 @@ WORKLOADS = {
                            batch=16, n=16384, variant="2d"),
     "absorbed_4x": Workload("absorbed_4x", T=4, D=24, H=16, d=128, r_k=96, r_v=160,
                             batch=8, n=32768, d_rope=64),
+    "teacher_4k": Workload("teacher_4k", T=4, D=24, H=16, d=128, r_k=0, r_v=0, batch=32,
+                           n=4096, teacher=True),
 }
 
 
@@ -123,6 +132,25 @@ def decode_inputs(w: Workload, seed: int, device="cpu", n_alloc: int | None = No
         out["q"] = _randn((w.D, w.T, w.batch, w.H, w.d), 1.0, torch.float32, g, device)
     if w.d_rope > 0:  # drawn last, so the tensors above do not depend on it
         out["k_rope"] = _randn((w.D, w.batch, w.H, n_max, w.d_rope), 1.0, dt, g, device)
+    return out
+
+
+def teacher_inputs(w: Workload, seed: int, device="cpu", n_alloc: int | None = None,
+                   with_q: bool = True):
+    """Random uncompressed per-loop key and value caches and queries. Drawn one layer at a
+    time (each layer's float32 draw is converted to the storage dtype before the next), so a
+    full-size cache needs no float32 copy of itself."""
+    n_max = n_alloc or w.n
+    g = _gen(seed, device)
+    dt = w.torch_dtype
+    shape = (w.D, w.T, w.batch, w.H, n_max, w.d)
+    out = {"k_cache": torch.empty(shape, dtype=dt, device=device),
+           "v_cache": torch.empty(shape, dtype=dt, device=device)}
+    for name in ("k_cache", "v_cache"):
+        for layer in range(w.D):
+            out[name][layer].copy_(_randn(shape[1:], 1.0, dt, g, device))
+    if with_q:
+        out["q"] = _randn((w.D, w.T, w.batch, w.H, w.d), 1.0, torch.float32, g, device)
     return out
 
 

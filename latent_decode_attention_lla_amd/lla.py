@@ -37,6 +37,7 @@ EXPORTED = (
     "lla_decode_workspace_bytes", "lla_decode_attn", "lla_decode_num_splits",
     "lla_decode_absorbed_workspace_bytes", "lla_decode_attn_absorbed",
     "lla_decode_absorbed_supported",
+    "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
 )
 
 
@@ -111,6 +112,13 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_attn_absorbed.restype = i32
     lib.lla_decode_absorbed_supported.argtypes = [P(lla_dims), i32]
     lib.lla_decode_absorbed_supported.restype = i32
+    lib.lla_decode_teacher_workspace_bytes.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
+    lib.lla_decode_teacher_workspace_bytes.restype = sz
+    lib.lla_decode_attn_teacher.argtypes = [P(lla_dims), vp, vp, i32, i32, vp, vp, i32, i32, vp,
+                                            vp, sz, P(lla_decode_opts), vp]
+    lib.lla_decode_attn_teacher.restype = i32
+    lib.lla_decode_teacher_supported.argtypes = [P(lla_dims)]
+    lib.lla_decode_teacher_supported.restype = i32
     _lib = lib
     return lib
 
@@ -244,3 +252,30 @@ def lla_decode_attn_status(dims, codec, cache, layer, n_ctx, ctx_lens, q, loop_b
 def lla_encode_status(dims, codec, cache, layer, x_k, x_v, pos_start, n_new, stream=0) -> int:
     return load().lla_encode(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), layer,
                              _ptr(x_k), _ptr(x_v), pos_start, n_new, stream)
+
+
+def lla_decode_teacher_workspace_bytes(dims: lla_dims, n_ctx: int, loop_count: int,
+                                       opts=None) -> int:
+    return load().lla_decode_teacher_workspace_bytes(
+        ctypes.byref(dims), n_ctx, loop_count, ctypes.byref(opts) if opts is not None else None)
+
+
+def lla_decode_teacher_supported(dims: lla_dims) -> bool:
+    return bool(load().lla_decode_teacher_supported(ctypes.byref(dims)))
+
+
+def lla_decode_attn_teacher(dims: lla_dims, k_cache, v_cache, layer: int, n_ctx: int, ctx_lens, q,
+                            loop_begin: int, loop_count: int, out, workspace, workspace_bytes: int,
+                            opts=None, stream=None) -> None:
+    _check("lla_decode_attn_teacher", lla_decode_attn_teacher_status(
+        dims, k_cache, v_cache, layer, n_ctx, ctx_lens, q, loop_begin, loop_count, out, workspace,
+        workspace_bytes, opts, _stream(stream)))
+
+
+def lla_decode_attn_teacher_status(dims, k_cache, v_cache, layer, n_ctx, ctx_lens, q, loop_begin,
+                                   loop_count, out, workspace, workspace_bytes, opts=None,
+                                   stream=0) -> int:
+    return load().lla_decode_attn_teacher(
+        ctypes.byref(dims), _ptr(k_cache), _ptr(v_cache), layer, n_ctx, _ptr(ctx_lens), _ptr(q),
+        loop_begin, loop_count, _ptr(out), _ptr(workspace), workspace_bytes,
+        ctypes.byref(opts) if opts is not None else None, stream)

@@ -70,6 +70,22 @@ def oracle_decode_absorbed(store, layer: int, loop_begin: int, loop_count: int, 
                              "per_head" if w.variant == "per_head" else "2d")
 
 
+def oracle_decode_teacher(cache, layer: int, loop_begin: int, loop_count: int, seqs, n_ctx: int,
+                          ctx_lens=None, q=None, heads=None):
+    """fp64 oracle of the uncompressed decode on sequences ``seqs`` (and ``heads``, all by
+    default) of a DeviceTeacherCache. Returns [len(seqs)][len(heads)][loop_count][d]."""
+    t = cache.t
+    dev = t["k_cache"].device
+    idx = torch.as_tensor(list(seqs), device=dev)
+    hs = torch.as_tensor(list(range(cache.w.H)) if heads is None else list(heads), device=dev)
+    kc = t["k_cache"][layer].index_select(1, idx).index_select(2, hs)[:, :, :, :n_ctx]
+    vc = t["v_cache"][layer].index_select(1, idx).index_select(2, hs)[:, :, :, :n_ctx]
+    qq = t["q"][layer, loop_begin:loop_begin + loop_count].permute(1, 2, 0, 3) if q is None else q
+    qq = qq.index_select(0, idx).index_select(1, hs)
+    lens = None if ctx_lens is None else [int(ctx_lens[i]) for i in seqs]
+    return O.decode_teacher(f64(kc), f64(vc), f64(qq), loop_begin, lens, None)
+
+
 def max_abs(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
 
@@ -92,5 +108,5 @@ def rel_note(err: float, tol: float) -> str:
 
 
 __all__ = ["BF16_TOL", "F32_TOL", "ensure_built", "announce", "f64", "oracle_decode",
-           "oracle_decode_absorbed", "max_abs",
+           "oracle_decode_absorbed", "oracle_decode_teacher", "max_abs",
            "bf16_ulp", "seed_everything", "rel_note", "math"]

@@ -68,6 +68,23 @@ def test_workspace_and_splits_planning():
     assert lla.lla_decode_num_splits(small, 0, 1) == 1
 
 
+def test_teacher_workspace_planning():
+    """The uncompressed decode reads only the attention shape (no codec ranks); one split
+    needs no workspace, more need (max, sum, acc[d]) floats per split."""
+    dims = lla.make_dims(4, 24, 16, 128, 0, 0, 32, 4096)
+    assert lla.lla_decode_teacher_supported(dims)
+    # 512 (sequence, head) waves fill a quarter of the ~2048 wanted: four context splits
+    assert lla.lla_decode_teacher_workspace_bytes(dims, 4096, 1) == 32 * 16 * 4 * (2 + 128) * 4
+    assert lla.lla_decode_teacher_workspace_bytes(dims, 4096, 1, lla.make_opts(1)) == 0
+    forced = lla.make_opts(num_splits=5)
+    nb = lla.lla_decode_teacher_workspace_bytes(dims, 4096, 1, forced)
+    assert nb >= 32 * 16 * 5 * (2 + 128) * 4 and nb % 256 == 0
+    small = lla.make_dims(4, 1, 2, 64, 0, 0, 1, 1000, dtype=lla.LLA_F32)
+    assert lla.lla_decode_teacher_workspace_bytes(small, 1000, 4) > 0  # 8 units need splits
+    assert lla.lla_decode_teacher_workspace_bytes(small, 1001, 4) == 0  # n_ctx > n_max
+    assert not lla.lla_decode_teacher_supported(lla.make_dims(4, 1, 2, 96, 0, 0, 1, 64))
+
+
 def test_splits_count_the_kernels_waves_per_head():
     """About 2048 waves in flight: the wide fold kernel spends a pair of waves per head,
     the reconstruct kernel one."""
