@@ -33,8 +33,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 
-# Sources whose compiled code (or launch plan) a kernel's measured traffic depends on.
-_COMMON_SOURCES = ("lla_device.h", "lla_kernels.h", "lla_api.cpp")
+# Sources whose compiled code (or launch plan) a kernel's measured traffic depends on:
+# device helpers, launch arguments, split planning, and each call's kernels (host-side
+# validation and dispatch in lla_api.cpp do not change what a kernel reads).
+_COMMON_SOURCES = ("lla_device.h", "lla_args.h", "lla_plan.h")
 KERNEL_SOURCES = {
     "decode": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip",
                                  "decode_reconstruct.hip", "combine.hip", "rope_table.hip"),
@@ -263,7 +265,7 @@ def main():
         x_new = [torch.randn(layers, w.batch, n_new, w.Hc, w.T, w.d_in, generator=g, device=dev).to(dt)
                  for _ in range(2)]
     if teacher:
-        S = lla.lla_decode_num_splits(st.dims, w.n, 1, lla.make_opts(args.splits, lla.LLA_PATH_RECONSTRUCT))
+        S = lla.lla_decode_teacher_num_splits(st.dims, w.n, 1, opts)
         ws = st.workspace(w.n, 1, opts)
     elif absorbed:
         S = lla.lla_decode_num_splits(st.dims, w.n, 1, lla.make_opts(args.splits, lla.LLA_PATH_RECONSTRUCT))

@@ -226,6 +226,10 @@ int32_t lla_decode_attn_teacher(const lla_dims* dims, const void* k_cache, const
                                 const lla_decode_opts* opts, void* stream);
 /* 1 when a kernel is built for (dims' dtype, d_head), else 0. */
 int32_t lla_decode_teacher_supported(const lla_dims* dims);
+/* Number of context splits lla_decode_attn_teacher would use (after `opts`), for
+ * reporting; 0 on invalid arguments. */
+int32_t lla_decode_teacher_num_splits(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,
+                                      const lla_decode_opts* opts);
 
 #ifdef __cplusplus
 }

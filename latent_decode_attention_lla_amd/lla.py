@@ -38,6 +38,7 @@ EXPORTED = (
     "lla_decode_absorbed_workspace_bytes", "lla_decode_attn_absorbed",
     "lla_decode_absorbed_supported",
     "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
+    "lla_decode_teacher_num_splits",
 )
 
 
@@ -119,6 +120,8 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_attn_teacher.restype = i32
     lib.lla_decode_teacher_supported.argtypes = [P(lla_dims)]
     lib.lla_decode_teacher_supported.restype = i32
+    lib.lla_decode_teacher_num_splits.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
+    lib.lla_decode_teacher_num_splits.restype = i32
     _lib = lib
     return lib
 
@@ -262,6 +265,11 @@ def lla_decode_teacher_workspace_bytes(dims: lla_dims, n_ctx: int, loop_count: i
 
 def lla_decode_teacher_supported(dims: lla_dims) -> bool:
     return bool(load().lla_decode_teacher_supported(ctypes.byref(dims)))
+
+
+def lla_decode_teacher_num_splits(dims: lla_dims, n_ctx: int, loop_count: int, opts=None) -> int:
+    return load().lla_decode_teacher_num_splits(
+        ctypes.byref(dims), n_ctx, loop_count, ctypes.byref(opts) if opts is not None else None)
 
 
 def lla_decode_attn_teacher(dims: lla_dims, k_cache, v_cache, layer: int, n_ctx: int, ctx_lens, q,

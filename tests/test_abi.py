@@ -76,6 +76,8 @@ def test_teacher_workspace_planning():
     # 512 (sequence, head) waves fill a quarter of the ~2048 wanted: four context splits
     assert lla.lla_decode_teacher_workspace_bytes(dims, 4096, 1) == 32 * 16 * 4 * (2 + 128) * 4
     assert lla.lla_decode_teacher_workspace_bytes(dims, 4096, 1, lla.make_opts(1)) == 0
+    assert lla.lla_decode_teacher_num_splits(dims, 4096, 1) == 4
+    assert lla.lla_decode_teacher_num_splits(dims, 4097, 1) == 0
     forced = lla.make_opts(num_splits=5)
     nb = lla.lla_decode_teacher_workspace_bytes(dims, 4096, 1, forced)
     assert nb >= 32 * 16 * 5 * (2 + 128) * 4 and nb % 256 == 0
