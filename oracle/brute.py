@@ -76,3 +76,21 @@ def brute_decode_absorbed_one(c_k, c_v, k_rope, w_up_k_t, mu_k_t, w_up_v_t, mu_v
         out.append(math.fsum(w[j] * (_row_times_matT(c_v[j], w_up_v_t)[i] + mu_v_t[i])
                              for j in range(len(c_v))) / tot)
     return out
+
+
+def brute_reconstruct_key_one(c, w_up_t, mu_t, pos, base):
+    """One rebuilt key at slot `pos`: c [r], W_up,t [d][r], mu_t [d]; the pairs rotated
+    as complex numbers. Returns [d] as a list of floats."""
+    k = [a + b for a, b in zip(_row_times_matT(c, w_up_t), mu_t)]
+    d = len(k)
+    out = [0.0] * d
+    for i in range(d // 2):
+        theta = base ** (-(2.0 * i) / d)
+        z = complex(k[2 * i], k[2 * i + 1]) * cmath.exp(1j * (pos * theta))
+        out[2 * i], out[2 * i + 1] = z.real, z.imag
+    return out
+
+
+def brute_reconstruct_value_one(c, w_up_t, mu_t):
+    """One rebuilt value: c [r], W_up,t [d][r], mu_t [d] -> [d]."""
+    return [a + b for a, b in zip(_row_times_matT(c, w_up_t), mu_t)]

@@ -31,7 +31,9 @@ invariants, softmax special cases, a scalar brute-force re-derivation, the LLA-2
 block-diagonal reduction and the Eckart-Young property of the SVD initialisation;
 the decoupled decode against textbook attention on the original keys and values, a
 scalar brute force, and its reduction to the full-RoPE decode; the uncompressed decode
-against textbook attention and against the latent decode of the same cache).
+against textbook attention and against the latent decode of the same cache; the
+materialised reconstruction by a full-rank round trip, a scalar brute force and by
+feeding the uncompressed decode).
 """
 
 from __future__ import annotations
@@ -58,6 +60,7 @@ __all__ = [
     "decode_absorbed",
     "teacher_rows",
     "decode_teacher",
+    "reconstruct_cache",
     "svd_init",
     "round_bf16",
     "encode_stored",
@@ -324,6 +327,44 @@ def decode_teacher(k_cache: np.ndarray, v_cache: np.ndarray, q: np.ndarray,
                                           teacher_rows(k_cache, t, b, h, nb),
                                           teacher_rows(v_cache, t, b, h, nb), scale)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Materialised reconstruction for the streamed two-pass prefill: Appendix A, "Decoding
+# and caching" (pass 2 re-forwards with the codec's reconstruction, which the latent-
+# store decoder streams layer by layer) and Appendix J, "Eviction and long-context
+# prefill" (one layer's K/V rebuilt and freed at a time). Eq. 3 for every token of a
+# range, then RoPE on the keys at the slot index (Section 3, "RoPE and reconstruction").
+# ---------------------------------------------------------------------------
+
+def reconstruct_cache(c_k: np.ndarray, c_v: np.ndarray,
+                      w_up_k: np.ndarray, mu_k: np.ndarray,
+                      w_up_v: np.ndarray, mu_v: np.ndarray,
+                      loop_begin: int, loop_count: int, pos_start: int, n_tok: int,
+                      rope_base: float = 10000.0, variant: str = "per_head"):
+    """Keys and values of loops loop_begin .. loop_begin+loop_count-1 for the tokens in
+    slots pos_start .. pos_start+n_tok-1 of one layer's latent cache.
+
+    c_k [B, Hc, n, r_k], c_v [B, Hc, n, r_v]; w_up_* [T, H, d, r]; mu_* as in decode.
+    returns (k [L, B, H, n_tok, d], v [L, B, H, n_tok, d]) float64: k rotated by RoPE at
+    its slot index, v as rebuilt.
+    """
+    B = c_k.shape[0]
+    _, H, d, _ = np.asarray(w_up_k).shape
+    pos = np.arange(pos_start, pos_start + n_tok)
+    k = np.zeros((loop_count, B, H, n_tok, d), dtype=np.float64)
+    v = np.zeros((loop_count, B, H, n_tok, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            hc = h if variant == "per_head" else 0
+            ck = np.asarray(c_k[b, hc, pos_start:pos_start + n_tok], dtype=np.float64)
+            cv = np.asarray(c_v[b, hc, pos_start:pos_start + n_tok], dtype=np.float64)
+            for li in range(loop_count):
+                t = loop_begin + li
+                k_hat = reconstruct(ck, w_up_k[t, h], _mu_slice(mu_k, variant, t, h, H, d))
+                k[li, b, h] = apply_rope(k_hat, pos, rope_base)
+                v[li, b, h] = reconstruct(cv, w_up_v[t, h], _mu_slice(mu_v, variant, t, h, H, d))
+    return k, v
 
 
 # ---------------------------------------------------------------------------

@@ -492,6 +492,81 @@ def pin_teacher_equals_latent_decode() -> float:
     return float(np.max(np.abs(got - ref)))
 
 
+def pin_reconstruct_round_trip() -> float:
+    """Full-rank orthonormal codec (r = T*d, W_up,t the loop slices of W_down): the
+    materialised reconstruction of a slot range gives back the original per-loop keys
+    (rotated by complex multiplication at their slots) and values exactly."""
+    T, H, d, n, B = 3, 2, 4, 9, 2
+    rng = _rng(93)
+    xk = rng.standard_normal((B, H, n, T, d))
+    xv = rng.standard_normal((B, H, n, T, d))
+    r = T * d
+    ck, cv = np.empty((B, H, n, r)), np.empty((B, H, n, r))
+    wuk, wuv = np.empty((T, H, d, r)), np.empty((T, H, d, r))
+    muk, muv = rng.standard_normal((H, T * d)), rng.standard_normal((H, T * d))
+    for h in range(H):
+        wk, wv = _orthonormal(r, r, 300 + h), _orthonormal(r, r, 400 + h)
+        ck[:, h] = O.encode(O.stack_loops(xk[:, h]), muk[h], wk)
+        cv[:, h] = O.encode(O.stack_loops(xv[:, h]), muv[h], wv)
+        for t in range(T):
+            wuk[t, h], wuv[t, h] = wk[t * d:(t + 1) * d], wv[t * d:(t + 1) * d]
+    p0, nt, lb, lc = 3, 5, 1, 2
+    k, v = O.reconstruct_cache(ck, cv, wuk, muk, wuv, muv, lb, lc, p0, nt, 10000.0)
+    err = 0.0
+    for li in range(lc):
+        t = lb + li
+        kr = _textbook_rope_complex(torch.from_numpy(xk[:, :, p0:p0 + nt, t]),
+                                    torch.arange(p0, p0 + nt), 10000.0).numpy()
+        err = max(err, float(np.max(np.abs(k[li] - kr))),
+                  float(np.max(np.abs(v[li] - xv[:, :, p0:p0 + nt, t]))))
+    return err
+
+
+def pin_reconstruct_brute_force() -> float:
+    """Element by element against oracle/brute.py (scalar codec, complex RoPE), per head
+    and LLA-2D, a slot range that starts inside the cache."""
+    err = 0.0
+    for variant, seed, base in (("per_head", 94, 10000.0), ("2d", 95, 100.0)):
+        a = _tiny(seed, T=3, n=7, variant=variant)
+        T, H, d = a["w_up_k"].shape[0], a["w_up_k"].shape[1], a["w_up_k"].shape[2]
+        p0, nt = 2, 4
+        k, v = O.reconstruct_cache(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"],
+                                   a["mu_v"], 0, T, p0, nt, base, variant)
+        for b in range(a["c_k"].shape[0]):
+            for h in range(H):
+                hc = h if variant == "per_head" else 0
+                for t in range(T):
+                    if variant == "per_head":
+                        mk = a["mu_k"][h][t * d:(t + 1) * d]
+                        mv = a["mu_v"][h][t * d:(t + 1) * d]
+                    else:
+                        mk = a["mu_k"][0][(t * H + h) * d:(t * H + h + 1) * d]
+                        mv = a["mu_v"][0][(t * H + h) * d:(t * H + h + 1) * d]
+                    for j in range(nt):
+                        kb = brute.brute_reconstruct_key_one(list(a["c_k"][b, hc, p0 + j]),
+                                                             a["w_up_k"][t, h].tolist(), list(mk),
+                                                             p0 + j, base)
+                        vb = brute.brute_reconstruct_value_one(list(a["c_v"][b, hc, p0 + j]),
+                                                               a["w_up_v"][t, h].tolist(), list(mv))
+                        err = max(err, float(np.max(np.abs(k[t, b, h, j] - np.array(kb)))),
+                                  float(np.max(np.abs(v[t, b, h, j] - np.array(vb)))))
+    return err
+
+
+def pin_reconstruct_feeds_teacher() -> float:
+    """The full-memory path: reconstruct every slot, then the uncompressed decode of the
+    rebuilt cache equals the latent decode (both oracle functions, different routes)."""
+    a = _tiny(96, T=3, n=8)
+    T = a["w_up_k"].shape[0]
+    n = a["c_k"].shape[2]
+    k, v = O.reconstruct_cache(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"],
+                               a["mu_v"], 0, T, 0, n, 10000.0)
+    lens = [8, 5]
+    got = O.decode_teacher(k, v, a["q"], 0, lens)
+    ref = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"], a["q"], 0, lens)
+    return float(np.max(np.abs(got - ref)))
+
+
 ALL_PINS = {
     "closed_forms": (pin_closed_forms, 1e-9),
     "rope": (pin_rope, 1e-12),
@@ -507,4 +582,7 @@ ALL_PINS = {
     "absorbed_equals_full_rope": (pin_absorbed_equals_full_rope, 1e-12),
     "teacher_textbook": (pin_teacher_textbook, 1e-12),
     "teacher_equals_latent_decode": (pin_teacher_equals_latent_decode, 1e-12),
+    "reconstruct_round_trip": (pin_reconstruct_round_trip, 1e-12),
+    "reconstruct_brute_force": (pin_reconstruct_brute_force, 1e-12),
+    "reconstruct_feeds_teacher": (pin_reconstruct_feeds_teacher, 1e-12),
 }

@@ -110,8 +110,31 @@ def _mut_teacher_next_loop(cache, t, b, h, nb):
     return np.asarray(cache[(t + 1) % cache.shape[0], b, h, :nb], dtype=np.float64)
 
 
+def _mut_reconstruct_cache_positions_from_zero(c_k, c_v, w_up_k, mu_k, w_up_v, mu_v, loop_begin,
+                                               loop_count, pos_start, n_tok, rope_base=10000.0,
+                                               variant="per_head"):
+    """Rotates the rebuilt keys as if the range started at slot 0."""
+    k, v = _ORIG["reconstruct_cache"](c_k, c_v, w_up_k, mu_k, w_up_v, mu_v, loop_begin,
+                                      loop_count, pos_start, n_tok, rope_base, variant)
+    d = k.shape[-1]
+    phi = pos_start * O.rope_theta(d, rope_base)
+    back = np.empty_like(k)  # rotate every pair back by pos_start * theta
+    back[..., 0::2] = k[..., 0::2] * np.cos(phi) + k[..., 1::2] * np.sin(phi)
+    back[..., 1::2] = -k[..., 0::2] * np.sin(phi) + k[..., 1::2] * np.cos(phi)
+    return back, v
+
+
+def _mut_reconstruct_cache_rotates_values(c_k, c_v, w_up_k, mu_k, w_up_v, mu_v, loop_begin,
+                                          loop_count, pos_start, n_tok, rope_base=10000.0,
+                                          variant="per_head"):
+    k, v = _ORIG["reconstruct_cache"](c_k, c_v, w_up_k, mu_k, w_up_v, mu_v, loop_begin,
+                                      loop_count, pos_start, n_tok, rope_base, variant)
+    return k, O.apply_rope(v, np.arange(pos_start, pos_start + n_tok), rope_base)
+
+
 _ORIG = {name: getattr(O, name) for name in
-         ("apply_rope", "reconstruct", "attention", "_mu_slice", "rope_theta", "absorbed_keys")}
+         ("apply_rope", "reconstruct", "attention", "_mu_slice", "rope_theta", "absorbed_keys",
+          "reconstruct_cache")}
 
 MUTANTS = {
     "rope_sign": ("apply_rope", _mut_rope_sign),
@@ -132,6 +155,8 @@ MUTANTS = {
     "absorbed_content_rotated": ("absorbed_keys", _mut_absorbed_content_rotated),
     "absorbed_scale_content_only": ("absorbed_scale", _mut_absorbed_scale_content_only),
     "teacher_next_loop": ("teacher_rows", _mut_teacher_next_loop),
+    "reconstruct_cache_positions_from_zero": ("reconstruct_cache", _mut_reconstruct_cache_positions_from_zero),
+    "reconstruct_cache_rotates_values": ("reconstruct_cache", _mut_reconstruct_cache_rotates_values),
 }
 
 
