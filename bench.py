@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "absorbed": _COMMON_SOURCES + ("decode_absorbed.hip", "decode_stream.h", "combine.hip"),
     "encode": _COMMON_SOURCES + ("encode.hip",),
     "teacher": _COMMON_SOURCES + ("decode_teacher.hip", "decode_stream.h", "combine.hip"),
+    "reconstruct": _COMMON_SOURCES + ("reconstruct.hip", "lla_recon_args.h"),
 }
 
 
@@ -96,6 +97,8 @@ def parse():
     p.add_argument("--no-reference-calls", action="store_true",
                    help="skip timing the full-RoPE paths beside the absorbed decode")
     p.add_argument("--cpu-sample-seqs", type=int, default=1)
+    p.add_argument("--cpu-sample-tokens", type=int, default=16384,
+                   help="prompt tokens of the oracle's sample for the streamed-prefill workload")
     p.add_argument("--copy-calibration-gib", type=float, default=0.0,
                    help="only run a plain device copy of this size (for counter scaling)")
     return p.parse_args()
@@ -164,6 +167,8 @@ def step_shape(w):
     prefill = w.name in ("ouro_layer_4x", "encode_heavy")
     if w.teacher:  # the uncompressed cache has no encode
         return False, 0, w.D
+    if w.stream_prefill:  # every layer encodes the whole prompt
+        return True, w.n, w.D
     return prefill, (w.n if prefill else 1), (1 if prefill else w.D)
 
 
@@ -175,6 +180,13 @@ def algorithmic(w, kind: str, L: int = 1, n_new: int = 0):
     encode: x_k and x_v read once, latents written once, W_down and mu read once;
             flops 2 T d_in (r_k + r_v) per (token, latent head)."""
     es = 2 if w.dtype == "bf16" else 4
+    if kind == "reconstruct":
+        # every latent of the range read once, L loops of keys and values written once,
+        # W_up and mu slices; flops of rebuilding both axes on the matrix cores
+        tok = w.batch * n_new
+        nbytes = (tok * w.Hc * (w.r_k + w.r_v) * es + 2 * L * tok * w.H * w.d * es
+                  + L * w.H * w.d * (w.r_k + w.r_v) * es + 2 * L * w.H * w.d * es)
+        return nbytes, 2.0 * L * tok * w.H * w.d * (w.r_k + w.r_v)
     if kind == "decode" and w.teacher:
         # uncompressed decode: one loop's key and value rows read once, q and out;
         # 4 d flop per (token, head) for the score and the weighted value
@@ -199,6 +211,136 @@ def algorithmic(w, kind: str, L: int = 1, n_new: int = 0):
     nbytes = (2 * toks * K * es + toks * (w.r_k + w.r_v) * es + w.Hc * (w.r_k + w.r_v) * K * es
               + 2 * w.Hc * K * es)
     return nbytes, 2.0 * toks * K * (w.r_k + w.r_v)
+
+
+def cpu_baseline_prefill(w, tokens: int):
+    """The fp64 oracle's encode (Eq. 2) and materialised reconstruction of `tokens`
+    prompt tokens of one layer (every head, all T loops), scaled to the whole prompt and
+    all D layers."""
+    import numpy as np
+    from oracle import lla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    rng = np.random.default_rng(12345)
+    K = w.T * w.d_in
+    x = rng.standard_normal((tokens, w.Hc, K))
+    wd = [rng.standard_normal((w.Hc, K, r)) / math.sqrt(K) for r in (w.r_k, w.r_v)]
+    mu = [rng.standard_normal((w.Hc, K)) * math.sqrt(0.1) for _ in range(2)]
+    wu = [rng.standard_normal((w.T, w.H, w.d, r)) / math.sqrt(r) for r in (w.r_k, w.r_v)]
+    t0 = time.perf_counter()
+    c = []
+    for axis in range(2):
+        c.append(np.stack([O.encode(x[:, hc], mu[axis][hc], wd[axis][hc]) for hc in range(w.Hc)])[None])
+    O.reconstruct_cache(c[0], c[1], wu[0], mu[0], wu[1], mu[1], 0, w.T, 0, tokens, w.rope_base,
+                        "per_head" if w.variant == "per_head" else "2d")
+    dt = time.perf_counter() - t0
+    scale = (w.batch * w.n / tokens) * w.D
+    return {"value": w.batch * w.n / (dt * scale), "unit": "prompt tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{tokens} prompt tokens x {w.H} heads x 1 layer (encode of both axes, then "
+                      f"K/V rebuilt for all {w.T} loops), fp64 NumPy, {dt:.1f} s, scaled by "
+                      f"{scale:g} to the {w.n}-token prompt and {w.D} layers; host "
+                      f"os.cpu_count()={os.cpu_count()}"}
+
+
+def main_stream_prefill(args, w):
+    """One step = the streamed two-pass prefill of a prompt: for every layer in turn,
+    lla_encode of the prompt's per-loop K/V (the capture buffer is reused by every layer),
+    then lla_reconstruct of that layer's K/V for all T loops (the second pass's input; its
+    buffer is reused too). Peak memory is the latent cache plus one layer's captures and
+    one layer's rebuilt K/V."""
+    import torch
+    from latent_decode_attention_lla_amd import lla
+    from latent_decode_attention_lla_amd.harness import DeviceLatentStore
+    dev = torch.device("cuda:0")
+    es = 2 if w.dtype == "bf16" else 4
+    n = w.n
+    print(f"[bench] allocating {w.name}: latents "
+          f"{w.D * w.batch * w.Hc * n * (w.r_k + w.r_v) * es / 2**30:.1f} GiB", file=sys.stderr,
+          flush=True)
+    st = DeviceLatentStore(w, seed=3, device=dev, with_q=False)
+    g = torch.Generator(device=dev).manual_seed(4)
+    K = w.T * w.d_in
+    dt = w.torch_dtype
+    st.t["w_down_k_t"] = (torch.randn(w.D, w.Hc, w.r_k, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
+    st.t["w_down_v_t"] = (torch.randn(w.D, w.Hc, w.r_v, K, generator=g, device=dev) / math.sqrt(K)).to(dt)
+    st.codec = lla.make_codec(st.t["w_down_k_t"], st.t["mu_k"], st.t["w_up_k"], st.t["w_down_v_t"],
+                              st.t["mu_v"], st.t["w_up_v"], st.rope)
+    x = [torch.randn(w.batch, n, w.Hc, w.T, w.d_in, generator=g, device=dev).to(dt) for _ in range(2)]
+    kv = [torch.empty(w.T, w.batch, w.H, n, w.d, dtype=dt, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    steps = max(args.steps, 1)
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(w.D * steps)] for k in ("encode", "reconstruct")}
+
+    def step(record):
+        for layer in range(w.D):
+            if record is not None:
+                ev["encode"][record * w.D + layer][0].record(stream)
+            lla.lla_encode(st.dims, st.codec, st.cache, layer, x[0], x[1], 0, n, sp)
+            if record is not None:
+                ev["encode"][record * w.D + layer][1].record(stream)
+                ev["reconstruct"][record * w.D + layer][0].record(stream)
+            lla.lla_reconstruct(st.dims, st.codec, st.cache, layer, 0, w.T, 0, n, kv[0], kv[1], sp)
+            if record is not None:
+                ev["reconstruct"][record * w.D + layer][1].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s_ in range(args.steps):
+        step(s_)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    calls = {}
+    for kind in ("encode", "reconstruct"):
+        xs = sorted(a.elapsed_time(b) for a, b in ev[kind][:w.D * args.steps])
+        ms = sum(xs) / len(xs)
+        nb, fl = (algorithmic(w, "encode", n_new=n) if kind == "encode"
+                  else algorithmic(w, "reconstruct", L=w.T, n_new=n))
+        calls[kind] = {"avg_ms": round(ms, 5), "median_ms": round(xs[len(xs) // 2], 5),
+                       "algorithmic_bytes": nb, "algorithmic_flops": fl,
+                       "roofline": roofline(nb, fl, ms, measured_traffic(kind, w.name, "auto"))}
+    dominant = max(calls, key=lambda k: calls[k]["avg_ms"])
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_sample_tokens)
+    peak_gib = (w.D * w.batch * w.Hc * n * (w.r_k + w.r_v) * es
+                + 2 * w.batch * n * w.Hc * K * es + 2 * w.T * w.batch * w.H * n * w.d * es) / 2**30
+    one_shot_gib = (w.D * w.batch * w.Hc * n * (w.r_k + w.r_v) * es
+                    + w.D * (2 * w.batch * n * w.Hc * K * 4 + 2 * w.T * w.batch * w.H * n * w.d * es)) / 2**30
+    res = {
+        "metric": "LLA streamed two-pass prefill, prompt tokens/s (per layer in turn: encode of "
+                  "the prompt's per-loop K/V, then K/V rebuilt for all loops), 1 GPU; HBM GB/s of "
+                  "the dominant kernel and fraction of peak",
+        "value": round(w.batch * n / (ms_step * 1e-3), 1),
+        "unit": "prompt tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian per-loop K/V and codec maps; no model weights)",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "H": w.H, "d_head": w.d, "r_k": w.r_k,
+                   "r_v": w.r_v, "variant": w.variant, "batch": w.batch, "prompt": n,
+                   "step": f"{w.D} x (lla_encode of {n} tokens, lla_reconstruct of {w.T} loops)",
+                   "device_working_set_gib": round(peak_gib, 1),
+                   "one_shot_working_set_gib": round(one_shot_gib, 1)},
+        "roofline": calls[dominant]["roofline"],
+        "roofline_kernel": "lla_" + dominant,
+        "cpu_baseline": cpu,
+        "encode_call": calls["encode"],
+        "reconstruct_call": calls["reconstruct"],
+        "wall_s_timed": round(wall, 3),
+        "kernel_source_hash": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
+    }
+    print(json.dumps(res))
 
 
 def roofline(nbytes, flops, ms, traffic=None):
@@ -234,6 +376,9 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.stream_prefill:
+        main_stream_prefill(args, w)
+        return
     # Step shape: "append" workloads decode over an existing cache after appending one new
     # token per sequence; "prefill" workloads encode a whole prompt of n tokens per
     # sequence for one layer, then take one decode step over all loops of that layer.

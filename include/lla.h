@@ -201,6 +201,27 @@ int32_t lla_decode_attn_absorbed(const lla_dims* dims, const lla_codec* codec,
 /* 1 when a kernel is built for (dims' dtype, d_head, r_k, r_v, d_rope), else 0. */
 int32_t lla_decode_absorbed_supported(const lla_dims* dims, int32_t d_rope);
 
+/* Materialised reconstruction of a slot range of one layer (Section 3, Eq. 3 and "RoPE
+ * and reconstruction"): the second pass of the latent-store decoder's two-pass prefill,
+ * streamed one layer at a time (Appendix A, "Decoding and caching"; Appendix J,
+ * "Eviction and long-context prefill"). For loops t = loop_begin .. loop_begin +
+ * loop_count - 1, every sequence b, head h and slot j in [pos_start, pos_start + n_tok):
+ *   k_out[t - loop_begin][b][h][j] = RoPE_j(c_k[j] W_up,k,t^T + mu_k,t)
+ *   v_out[t - loop_begin][b][h][j] = c_v[j] W_up,v,t^T + mu_v,t
+ *   k_out, v_out : device [loop_count][batch][H][n_max][d_head] in dims->dtype (the
+ *                  layout of one layer of the uncompressed cache that
+ *                  lla_decode_attn_teacher reads); only the rows of the slot range are
+ *                  written. Either may be NULL (that axis is skipped), not both.
+ *                  bfloat16 outputs are rounded once, to nearest even.
+ *   codec  : w_up_*, mu_* of the axes asked for; rope_table when k_out is given.
+ *   requires 0 <= layer < D, 0 <= loop_begin, 1 <= loop_count, loop_begin + loop_count
+ *            <= T, 0 <= pos_start, 0 <= n_tok, pos_start + n_tok <= n_max.
+ * n_tok == 0 enqueues nothing. Errors as lla_decode_attn; shapes not built (r not in
+ * 16, 24, 32, 64, 96, 128, 160, 256) give LLA_ERR_UNSUPPORTED. */
+int32_t lla_reconstruct(const lla_dims* dims, const lla_codec* codec, const lla_cache* cache,
+                        int32_t layer, int32_t loop_begin, int32_t loop_count, int32_t pos_start,
+                        int32_t n_tok, void* k_out, void* v_out, void* stream);
+
 /* Uncompressed decode over the loop-indexed cache that the latent store replaces (Section
  * 3, "Teacher cache": every loop of every layer keeps its own key and value; Section 7,
  * Table 5: the teacher's serving path). For every sequence b, head h and loop t:

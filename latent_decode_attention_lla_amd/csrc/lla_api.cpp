@@ -407,4 +407,74 @@ int32_t lla_decode_attn_teacher(const lla_dims* d, const void* k_cache, const vo
   return hip_status();
 }
 
+int32_t lla_reconstruct(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                        int32_t layer, int32_t loop_begin, int32_t loop_count, int32_t pos_start,
+                        int32_t n_tok, void* k_out, void* v_out, void* stream) {
+  const int32_t st = check_dims(d);
+  if (st != LLA_OK) return st;
+  if (codec == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
+  if (loop_begin < 0 || loop_count < 1 || static_cast<long long>(loop_begin) + loop_count > d->T)
+    return LLA_ERR_INVALID_ARG;
+  if (pos_start < 0 || n_tok < 0 || static_cast<long long>(pos_start) + n_tok > d->n_max)
+    return LLA_ERR_INVALID_ARG;
+  if (k_out == nullptr && v_out == nullptr) return LLA_ERR_INVALID_ARG;
+  if (k_out != nullptr) {
+    const void* ptrs[] = {codec->w_up_k, codec->mu_k, codec->rope_table, cache->c_k, k_out};
+    for (const void* p : ptrs)
+      if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+    if (!lla::reconstruct_supported(d->dtype, d->d_head, d->r_k)) return LLA_ERR_UNSUPPORTED;
+  }
+  if (v_out != nullptr) {
+    const void* ptrs[] = {codec->w_up_v, codec->mu_v, cache->c_v, v_out};
+    for (const void* p : ptrs)
+      if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+    if (!lla::reconstruct_supported(d->dtype, d->d_head, d->r_v)) return LLA_ERR_UNSUPPORTED;
+  }
+  if (n_tok == 0) return LLA_OK;
+
+  const size_t es = elem_bytes(*d);
+  const int Hc = latent_heads(*d);
+  const int K = d->T * d_in(*d);
+  const size_t loop_elems = static_cast<size_t>(d->batch) * d->H * d->n_max * d->d_head;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int axis = 0; axis < 2; ++axis) {
+    void* out = axis == 0 ? k_out : v_out;
+    if (out == nullptr) continue;
+    const int r = axis == 0 ? d->r_k : d->r_v;
+    lla::ReconArgs a{};
+    a.c = static_cast<const char*>(axis == 0 ? cache->c_k : cache->c_v) +
+          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * r * es;
+    a.w_up = static_cast<const char*>(axis == 0 ? codec->w_up_k : codec->w_up_v) +
+             static_cast<size_t>(layer) * d->T * d->H * d->d_head * r * es;
+    a.mu = static_cast<const char*>(axis == 0 ? codec->mu_k : codec->mu_v) +
+           static_cast<size_t>(layer) * Hc * K * es;
+    a.rope32 = axis == 0 ? static_cast<const float*>(codec->rope_table) : nullptr;
+    a.B = d->batch;
+    a.H = d->H;
+    a.Hc = Hc;
+    a.T = d->T;
+    a.n_max = d->n_max;
+    a.pos_start = pos_start;
+    a.n_tok = n_tok;
+    a.variant = d->variant;
+    // Slots per workgroup: long chunks (up to 1024) amortise each wave's W_up load and keep
+    // its stores streaming; shorter ones keep about 1024 workgroups for short ranges.
+    const long long per_wg = static_cast<long long>(n_tok) * d->batch * d->H / 1024;
+    const long long chunk = (per_wg + 15) / 16 * 16;
+    a.chunk = static_cast<int>(chunk < 64 ? 64 : (chunk > 1024 ? 1024 : chunk));
+    const int max_l = lla::reconstruct_max_loops(d->dtype, d->d_head, r);
+    if (max_l < 1) return LLA_ERR_UNSUPPORTED;
+    for (int lb = 0; lb < loop_count; lb += max_l) {
+      a.L = loop_count - lb < max_l ? loop_count - lb : max_l;
+      a.loop_begin = loop_begin + lb;
+      a.out = static_cast<char*>(out) + static_cast<size_t>(lb) * loop_elems * es;
+      if (!lla::launch_reconstruct(d->dtype, d->d_head, r, a, s)) return LLA_ERR_UNSUPPORTED;
+      const int32_t hs = hip_status();
+      if (hs != LLA_OK) return hs;
+    }
+  }
+  return LLA_OK;
+}
+
 }  // extern "C"

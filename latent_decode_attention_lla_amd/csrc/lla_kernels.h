@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "lla_args.h"
+#include "lla_recon_args.h"
 
 namespace lla {
 
@@ -32,6 +33,12 @@ bool decode_teacher_supported(int dtype, int d);
 bool launch_combine_identity(int dtype, int d, const DecodeArgs& a, hipStream_t s);
 bool decode_reconstruct_supported(int dtype, int d, int r_k, int r_v);
 bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v);
+
+// Materialised reconstruction of one axis: a.L loops per launch, at most
+// reconstruct_max_loops(d, r) of them.
+bool launch_reconstruct(int dtype, int d, int r, const ReconArgs& a, hipStream_t s);
+bool reconstruct_supported(int dtype, int d, int r);
+int reconstruct_max_loops(int dtype, int d, int r);
 
 bool launch_encode(int dtype, int r, const EncodeArgs& a, hipStream_t s);
 bool encode_supported(int dtype, int r, int Kdim);

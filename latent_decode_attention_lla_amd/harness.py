@@ -87,6 +87,23 @@ class DeviceLatentStore:
                                      ws.numel(), opts, stream)
         return out
 
+    def reconstruct(self, layer: int, loop_begin: int, loop_count: int, pos_start: int = 0,
+                    n_tok: int | None = None, k_out: torch.Tensor | None = None,
+                    v_out: torch.Tensor | None = None, keys: bool = True, values: bool = True,
+                    stream=None):
+        """Rebuilt K/V of a slot range, [loop_count][B][H][n_max][d] in the cache dtype."""
+        w = self.w
+        n_tok = self.n_max - pos_start if n_tok is None else n_tok
+        shape = (loop_count, w.batch, w.H, self.n_max, w.d)
+        if keys and k_out is None:
+            k_out = torch.zeros(shape, dtype=w.torch_dtype, device=self.device)
+        if values and v_out is None:
+            v_out = torch.zeros(shape, dtype=w.torch_dtype, device=self.device)
+        lla.lla_reconstruct(self.dims, self.codec, self.cache, layer, loop_begin, loop_count,
+                            pos_start, n_tok, k_out if keys else None, v_out if values else None,
+                            stream)
+        return k_out, v_out
+
     def encode(self, layer: int, x_k: torch.Tensor, x_v: torch.Tensor, pos_start: int,
                n_new: int, stream=None) -> None:
         lla.lla_encode(self.dims, self.codec, self.cache, layer, x_k, x_v, pos_start, n_new, stream)

@@ -17,6 +17,10 @@ Table 5):
 * ``absorbed_4x``   the Ouro-1.4B 4x geometry, T=4, D=24, H=16, d=128, (96, 160), bf16,
                     decoupled decode with a 64-wide rotary branch (Appendix J, Table 14's
                     d_rope), batch 8, context 32768 (Table 13's shortest context)
+* ``prefill_64k``   the streamed two-pass prefill of one 65536-token prompt at the
+                    Ouro-1.4B 4x geometry (T=4, D=24, H=16, d=128, (96, 160), bf16): per
+                    layer, encode the prompt's per-loop K/V, then rebuild them for the
+                    second pass (Appendix J's 64k passkey cells; Table 12)
 * ``teacher_4k``    the uncompressed loop-indexed cache the latent store replaces (Section
                     3 "Teacher cache"; Table 5's teacher column): T=4, D=24, H=16, d=128,
                     bf16 keys and values for every loop, batch 32 (the teacher's measured
@@ -63,6 +67,7 @@ class Workload:
     rope_base: float = 10000.0
     d_rope: int = 0                # rotary-branch width of the decoupled (absorbed) decode
     teacher: bool = False          # an uncompressed per-loop cache (no codec)
+    stream_prefill: bool = False   # a step is the layer-by-layer two-pass prefill
 
     @property
     def Hc(self) -> int:
@@ -93,6 +98,8 @@ WORKLOADS = {
                            batch=16, n=16384, variant="2d"),
     "absorbed_4x": Workload("absorbed_4x", T=4, D=24, H=16, d=128, r_k=96, r_v=160,
                             batch=8, n=32768, d_rope=64),
+    "prefill_64k": Workload("prefill_64k", T=4, D=24, H=16, d=128, r_k=96, r_v=160, batch=1,
+                            n=65536, stream_prefill=True),
     "teacher_4k": Workload("teacher_4k", T=4, D=24, H=16, d=128, r_k=0, r_v=0, batch=32,
                            n=4096, teacher=True),
 }

@@ -38,7 +38,7 @@ EXPORTED = (
     "lla_decode_absorbed_workspace_bytes", "lla_decode_attn_absorbed",
     "lla_decode_absorbed_supported",
     "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
-    "lla_decode_teacher_num_splits",
+    "lla_decode_teacher_num_splits", "lla_reconstruct",
 )
 
 
@@ -122,6 +122,9 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_teacher_supported.restype = i32
     lib.lla_decode_teacher_num_splits.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
     lib.lla_decode_teacher_num_splits.restype = i32
+    lib.lla_reconstruct.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, i32, i32, i32,
+                                    i32, vp, vp, vp]
+    lib.lla_reconstruct.restype = i32
     _lib = lib
     return lib
 
@@ -287,3 +290,18 @@ def lla_decode_attn_teacher_status(dims, k_cache, v_cache, layer, n_ctx, ctx_len
         ctypes.byref(dims), _ptr(k_cache), _ptr(v_cache), layer, n_ctx, _ptr(ctx_lens), _ptr(q),
         loop_begin, loop_count, _ptr(out), _ptr(workspace), workspace_bytes,
         ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def lla_reconstruct(dims: lla_dims, codec: lla_codec, cache: lla_cache, layer: int,
+                    loop_begin: int, loop_count: int, pos_start: int, n_tok: int, k_out, v_out,
+                    stream=None) -> None:
+    _check("lla_reconstruct", lla_reconstruct_status(dims, codec, cache, layer, loop_begin,
+                                                     loop_count, pos_start, n_tok, k_out, v_out,
+                                                     _stream(stream)))
+
+
+def lla_reconstruct_status(dims, codec, cache, layer, loop_begin, loop_count, pos_start, n_tok,
+                           k_out, v_out, stream=0) -> int:
+    return load().lla_reconstruct(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache),
+                                  layer, loop_begin, loop_count, pos_start, n_tok, _ptr(k_out),
+                                  _ptr(v_out), stream)

@@ -68,7 +68,7 @@ def main(argv=None):
     t.add_argument("--sum", action="store_true")
     t.add_argument("--out")
     t.add_argument("--extra", default="{}", help="JSON merged into the output")
-    t.add_argument("--call", choices=["decode", "absorbed", "encode", "teacher"],
+    t.add_argument("--call", choices=["decode", "absorbed", "encode", "teacher", "reconstruct"],
                    help="with --workload: record the call's source hash and algorithmic bytes")
     t.add_argument("--workload")
     a = p.parse_args(argv)
@@ -104,7 +104,10 @@ def main(argv=None):
         from latent_decode_attention_lla_amd.inputs import WORKLOADS
         w = WORKLOADS[a.workload]
         _, n_new, _ = bench.step_shape(w)
-        alg, _ = bench.algorithmic(w, "encode" if a.call == "encode" else "decode", n_new=n_new)
+        if a.call == "reconstruct":
+            alg, _ = bench.algorithmic(w, "reconstruct", L=w.T, n_new=n_new)
+        else:
+            alg, _ = bench.algorithmic(w, "encode" if a.call == "encode" else "decode", n_new=n_new)
         res.update({"call": a.call, "workload": a.workload, "path": "auto",
                     "kernel_source_hash": bench.kernel_source_hash(a.call),
                     "algorithmic_bytes_per_launch": alg,
