@@ -33,7 +33,8 @@ the decoupled decode against textbook attention on the original keys and values,
 scalar brute force, and its reduction to the full-RoPE decode; the uncompressed decode
 against textbook attention and against the latent decode of the same cache; the
 materialised reconstruction by a full-rank round trip, a scalar brute force and by
-feeding the uncompressed decode).
+feeding the uncompressed decode; the paged cache by identity and permuted block tables,
+and eviction by textbook attention over the kept keys at their new positions).
 """
 
 from __future__ import annotations
@@ -61,6 +62,10 @@ __all__ = [
     "teacher_rows",
     "decode_teacher",
     "reconstruct_cache",
+    "PAGE",
+    "gather_pages",
+    "decode_paged",
+    "window_pages",
     "svd_init",
     "round_bf16",
     "encode_stored",
@@ -365,6 +370,56 @@ def reconstruct_cache(c_k: np.ndarray, c_v: np.ndarray,
                 k[li, b, h] = apply_rope(k_hat, pos, rope_base)
                 v[li, b, h] = reconstruct(cv, w_up_v[t, h], _mu_slice(mu_v, variant, t, h, H, d))
     return k, v
+
+
+# ---------------------------------------------------------------------------
+# Paged latent cache with token eviction: Appendix D (Table 9, StreamingLLM/H2O-style
+# eviction to a sink plus a recent window) and Appendix J, "Eviction and long-context
+# prefill" (the sequence axis composes with the loop axis; a 1024-token budget caps the
+# 1M-context cache). Readings: the cache is stored in pages of PAGE tokens listed per
+# sequence by a block table in logical order; what eviction keeps is the sink pages plus
+# the most recent pages; positions for RoPE are the logical slots of the kept cache (the
+# StreamingLLM convention, free here because latents are stored before RoPE).
+# ---------------------------------------------------------------------------
+
+PAGE = 16
+
+
+def gather_pages(pool: np.ndarray, block_table: np.ndarray, n: int) -> np.ndarray:
+    """Logical latent rows of every sequence: token j of sequence b is row j % PAGE of
+    page block_table[b][j // PAGE]. pool [P, Hc, PAGE, r] -> [B, Hc, n, r] float64."""
+    pool = np.asarray(pool)
+    block_table = np.asarray(block_table)
+    B = block_table.shape[0]
+    Hc, r = pool.shape[1], pool.shape[3]
+    out = np.zeros((B, Hc, n, r), dtype=np.float64)
+    for b in range(B):
+        for j in range(n):
+            out[b, :, j] = pool[int(block_table[b][j // PAGE]), :, j % PAGE]
+    return out
+
+
+def decode_paged(pool_k: np.ndarray, pool_v: np.ndarray, block_table: np.ndarray,
+                 w_up_k: np.ndarray, mu_k: np.ndarray, w_up_v: np.ndarray, mu_v: np.ndarray,
+                 q: np.ndarray, loop_begin: int = 0, ctx_lens=None, n_ctx: int | None = None,
+                 rope_base: float = 10000.0, scale: float | None = None,
+                 variant: str = "per_head") -> np.ndarray:
+    """Decode attention over a paged latent cache: the latent decode of the logical rows
+    the block table lists (RoPE at the logical slot)."""
+    if n_ctx is None:
+        n_ctx = np.asarray(block_table).shape[1] * PAGE
+    c_k = gather_pages(pool_k, block_table, n_ctx)
+    c_v = gather_pages(pool_v, block_table, n_ctx)
+    return decode(c_k, c_v, w_up_k, mu_k, w_up_v, mu_v, q, loop_begin, ctx_lens, rope_base,
+                  scale, variant)
+
+
+def window_pages(n_pages_written: int, sink_pages: int, window_pages: int) -> list:
+    """Logical pages eviction keeps once n_pages_written pages exist: the first sink_pages
+    pages and the window_pages most recent ones, in order (all of them while they fit)."""
+    if n_pages_written <= sink_pages + window_pages:
+        return list(range(n_pages_written))
+    return list(range(sink_pages)) + list(range(n_pages_written - window_pages, n_pages_written))
 
 
 # ---------------------------------------------------------------------------

@@ -567,6 +567,82 @@ def pin_reconstruct_feeds_teacher() -> float:
     return float(np.max(np.abs(got - ref)))
 
 
+def pin_paged_permuted() -> float:
+    """A dense latent cache scattered into pages in a random order (the pool built here by
+    reshaping, not by the oracle's gather): the paged decode equals the dense decode, per
+    head and LLA-2D, ragged contexts included."""
+    err = 0.0
+    for variant, seed in (("per_head", 97), ("2d", 98)):
+        a = _tiny(seed, T=2, n=48, variant=variant)
+        B, Hc, n, _ = a["c_k"].shape
+        npg = n // O.PAGE
+        rng = _rng(seed + 1)
+        perm = rng.permutation(B * npg + 3)[:B * npg]  # physical page of (b, p), spares unused
+        table = perm.reshape(B, npg)
+        pools = []
+        for key in ("c_k", "c_v"):
+            x = a[key]
+            pool = rng.standard_normal((B * npg + 3, Hc, O.PAGE, x.shape[3]))  # junk in spares
+            pages = x.reshape(B, Hc, npg, O.PAGE, x.shape[3]).transpose(0, 2, 1, 3, 4)
+            pool[table.reshape(-1)] = pages.reshape(B * npg, Hc, O.PAGE, x.shape[3])
+            pools.append(pool)
+        lens = [48, 21]
+        got = O.decode_paged(pools[0], pools[1], table, a["w_up_k"], a["mu_k"], a["w_up_v"],
+                             a["mu_v"], a["q"], 0, lens, None, 10000.0, None, variant)
+        ref = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"], a["q"],
+                       0, lens, 10000.0, None, variant)
+        err = max(err, float(np.max(np.abs(got - ref))))
+    return err
+
+
+def pin_eviction_window() -> float:
+    """StreamingLLM-style eviction: window_pages against hand-listed cases, then, with a
+    full-rank orthonormal codec, the paged decode over the kept pages (sink page plus the
+    newest pages) equals textbook attention (torch SDPA, fp64) over the kept tokens'
+    original keys and values, the keys rotated at their positions in the kept cache."""
+    err = 0.0
+    for args, want in (((3, 1, 4), [0, 1, 2]), ((5, 1, 4), [0, 1, 2, 3, 4]),
+                       ((10, 1, 4), [0, 6, 7, 8, 9]), ((9, 2, 3), [0, 1, 6, 7, 8])):
+        if O.window_pages(*args) != want:
+            err = max(err, 1.0)
+    T, H, d, B = 2, 2, 4, 1
+    r = T * d
+    written = 9  # pages written; kept: page 0 and pages 6..8
+    n_all = written * O.PAGE
+    rng = _rng(99)
+    xk = rng.standard_normal((B, H, n_all, T, d))
+    xv = rng.standard_normal((B, H, n_all, T, d))
+    muk, muv = rng.standard_normal((H, T * d)), rng.standard_normal((H, T * d))
+    wuk, wuv = np.empty((T, H, d, r)), np.empty((T, H, d, r))
+    pool_k = np.zeros((written + 2, H, O.PAGE, r))
+    pool_v = np.zeros((written + 2, H, O.PAGE, r))
+    phys = rng.permutation(written + 2)[:written]  # physical page of each logical page
+    for h in range(H):
+        wk, wv = _orthonormal(r, r, 500 + h), _orthonormal(r, r, 600 + h)
+        ck = O.encode(O.stack_loops(xk[0, h]), muk[h], wk)
+        cv = O.encode(O.stack_loops(xv[0, h]), muv[h], wv)
+        for pg in range(written):
+            pool_k[phys[pg], h] = ck[pg * O.PAGE:(pg + 1) * O.PAGE]
+            pool_v[phys[pg], h] = cv[pg * O.PAGE:(pg + 1) * O.PAGE]
+        for t in range(T):
+            wuk[t, h], wuv[t, h] = wk[t * d:(t + 1) * d], wv[t * d:(t + 1) * d]
+    kept = O.window_pages(written, 1, 3)
+    table = np.array([[phys[pg] for pg in kept]])
+    toks = np.concatenate([np.arange(pg * O.PAGE, (pg + 1) * O.PAGE) for pg in kept])
+    n_kept = len(toks) - 5  # the newest page only partly filled
+    toks = toks[:n_kept]
+    q = rng.standard_normal((B, H, T, d))
+    got = O.decode_paged(pool_k, pool_v, table, wuk, muk, wuv, muv, q, 0, [n_kept], None)
+    pos = torch.arange(n_kept)
+    for t in range(T):
+        k = _textbook_rope_complex(torch.from_numpy(xk[:, :, toks, t]), pos, 10000.0)
+        v = torch.from_numpy(xv[:, :, toks, t])
+        qt = torch.from_numpy(q[:, :, t])[:, :, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, k, v)[:, :, 0]
+        err = max(err, float(np.max(np.abs(got[:, :, t] - ref.numpy()))))
+    return err
+
+
 ALL_PINS = {
     "closed_forms": (pin_closed_forms, 1e-9),
     "rope": (pin_rope, 1e-12),
@@ -585,4 +661,6 @@ ALL_PINS = {
     "reconstruct_round_trip": (pin_reconstruct_round_trip, 1e-12),
     "reconstruct_brute_force": (pin_reconstruct_brute_force, 1e-12),
     "reconstruct_feeds_teacher": (pin_reconstruct_feeds_teacher, 1e-12),
+    "paged_permuted": (pin_paged_permuted, 1e-12),
+    "eviction_window": (pin_eviction_window, 1e-12),
 }

@@ -132,6 +132,23 @@ def _mut_reconstruct_cache_rotates_values(c_k, c_v, w_up_k, mu_k, w_up_v, mu_v, 
     return k, O.apply_rope(v, np.arange(pos_start, pos_start + n_tok), rope_base)
 
 
+def _mut_gather_pages_next_page(pool, block_table, n):
+    """Reads page j // PAGE + 1 of the table (wrapping)."""
+    pool = np.asarray(pool)
+    bt = np.asarray(block_table)
+    out = np.zeros((bt.shape[0], pool.shape[1], n, pool.shape[3]))
+    for b in range(bt.shape[0]):
+        for j in range(n):
+            out[b, :, j] = pool[int(bt[b][(j // O.PAGE + 1) % bt.shape[1]]), :, j % O.PAGE]
+    return out
+
+
+def _mut_window_keeps_oldest(n_pages_written, sink_pages, window_pages):
+    if n_pages_written <= sink_pages + window_pages:
+        return list(range(n_pages_written))
+    return list(range(sink_pages + window_pages))
+
+
 _ORIG = {name: getattr(O, name) for name in
          ("apply_rope", "reconstruct", "attention", "_mu_slice", "rope_theta", "absorbed_keys",
           "reconstruct_cache")}
@@ -157,6 +174,8 @@ MUTANTS = {
     "teacher_next_loop": ("teacher_rows", _mut_teacher_next_loop),
     "reconstruct_cache_positions_from_zero": ("reconstruct_cache", _mut_reconstruct_cache_positions_from_zero),
     "reconstruct_cache_rotates_values": ("reconstruct_cache", _mut_reconstruct_cache_rotates_values),
+    "gather_pages_next_page": ("gather_pages", _mut_gather_pages_next_page),
+    "window_keeps_oldest": ("window_pages", _mut_window_keeps_oldest),
 }
 
 
