@@ -30,8 +30,8 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-template <typename T, int D, int RK, int RV>
-__global__ __launch_bounds__(64) void decode_reconstruct_kernel(DecodeArgs a) {
+template <typename T, int D, int RK, int RV, bool PAGED>
+__global__ __launch_bounds__(64) void decode_reconstruct_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int KS = KStep<T, RK>::value;
   using M = Mfma<T, KS>;
   constexpr int E = M::E;
@@ -76,7 +76,8 @@ __global__ __launch_bounds__(64) void decode_reconstruct_kernel(DecodeArgs a) {
     load_f32<4>(q + 16 * m + 4 * hi, qv[m]);
   }
 
-  const size_t plane = static_cast<size_t>(b * a.Hc + hc) * a.n_max;
+  // dense: this (sequence, latent head)'s plane; paged: its rows of page 0 of the pool
+  const size_t plane = PAGED ? static_cast<size_t>(hc) * kPage : static_cast<size_t>(b * a.Hc + hc) * a.n_max;
   const T* ck = static_cast<const T*>(a.c_k) + plane * RK;
   const T* cv = static_cast<const T*>(a.c_v) + plane * RV;
 
@@ -90,11 +91,21 @@ __global__ __launch_bounds__(64) void decode_reconstruct_kernel(DecodeArgs a) {
     const bool valid = tok < s1;
     const int row = valid ? tok : s1 - 1;
 
+    // a tile (j0 a multiple of 16) is one page; its clamped rows stay in it
+    const T* ckt = ck;
+    const T* cvt = cv;
+    int prow = row;
+    if constexpr (PAGED) {
+      const size_t page = static_cast<size_t>(page_of(pg, b, __builtin_amdgcn_readfirstlane(j0 / kPage)));
+      ckt = ck + page * a.Hc * kPage * RK;
+      cvt = cv + page * a.Hc * kPage * RV;
+      prow = row - j0;
+    }
     typename M::Frag cf[NK];
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) cf[ks] = M::load(ck + static_cast<size_t>(row) * RK + ks * KS + hi * E);
+    for (int ks = 0; ks < NK; ++ks) cf[ks] = M::load(ckt + static_cast<size_t>(prow) * RK + ks * KS + hi * E);
     float vv[VS];
-    load_f32<VS>(cv + static_cast<size_t>(row) * RV + hi * VS, vv);
+    load_f32<VS>(cvt + static_cast<size_t>(prow) * RV + hi * VS, vv);
 
     const float* cs_row = a.rope32 + static_cast<size_t>(row) * D;  // (cos, sin) x D/2
     float part = 0.f;
@@ -149,10 +160,10 @@ __global__ __launch_bounds__(64) void decode_reconstruct_kernel(DecodeArgs a) {
   }
 }
 
-template <typename T, int D, int RK, int RV>
-void launch(const DecodeArgs& a, hipStream_t s) {
+template <typename T, int D, int RK, int RV, bool PAGED = false>
+void launch(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
   dim3 grid(a.S, a.H * a.L, a.B);
-  hipLaunchKernelGGL((decode_reconstruct_kernel<T, D, RK, RV>), grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_reconstruct_kernel<T, D, RK, RV, PAGED>), grid, dim3(64), 0, s, a, pg);
 }
 
 }  // namespace
@@ -179,11 +190,25 @@ bool decode_reconstruct_supported(int dtype, int d, int r_k, int r_v) {
 
 bool launch_decode_reconstruct(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                hipStream_t s) {
-#define X(D_, RK_, RV_)                                   \
-  if (d == D_ && r_k == RK_ && r_v == RV_) {              \
-    if (dtype == 0) launch<float, D_, RK_, RV_>(a, s);    \
-    else launch<bf16_t, D_, RK_, RV_>(a, s);              \
-    return true;                                          \
+#define X(D_, RK_, RV_)                                             \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                        \
+    if (dtype == 0) launch<float, D_, RK_, RV_>(a, PageArgs{}, s);  \
+    else launch<bf16_t, D_, RK_, RV_>(a, PageArgs{}, s);            \
+    return true;                                                    \
+  }
+  LLA_RECON_SHAPES(X)
+#undef X
+  return false;
+}
+
+bool launch_decode_reconstruct_paged(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
+                                     const PageArgs& pg, hipStream_t s) {
+  if (pg.table == nullptr) return false;
+#define X(D_, RK_, RV_)                                             \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                        \
+    if (dtype == 0) launch<float, D_, RK_, RV_, true>(a, pg, s);    \
+    else launch<bf16_t, D_, RK_, RV_, true>(a, pg, s);              \
+    return true;                                                    \
   }
   LLA_RECON_SHAPES(X)
 #undef X

@@ -23,7 +23,9 @@
 //
 // Workgroup: HPW waves = HPW heads of one (sequence, loop, context split); they walk the
 // same token range, TPC tiles of 16 tokens per chunk, with the next chunk's cache rows
-// and table tile loaded while the current one is computed. Each lane keeps an online
+// and table tile loaded while the current one is computed. With a paged cache a 16-token
+// tile is one page: its rows come from the page the block table names for it, and
+// everything else (positions, the table of angles) follows the logical token index. Each lane keeps an online
 // softmax for its token column; the running max is raised only when a score exceeds it
 // by more than 2^8 (scores live in the exp2 domain), which is exact because the same max
 // is used by the running sum and the accumulator.
@@ -105,12 +107,33 @@ __device__ __forceinline__ void load_rows(Rows<RK, RV, TPC>& R, const uint16_t* 
   }
 }
 
-template <int D, int RK, int RV, int HPW, int TPC>
+// Paged: the rows of tile tt start at kb[tt] / vb[tt] (the page's rows for this head),
+// row r of the chunk's tile tt being row r - 16 * ptile[tt] of its page.
+template <bool CLAMP, int RK, int RV, int TPC>
+__device__ __forceinline__ void load_rows_paged(Rows<RK, RV, TPC>& R, const uint16_t* const* kb,
+                                                const uint16_t* const* vb, const int* pt0,
+                                                int tok0, int s1, int lo, int hi) {
+#pragma unroll
+  for (int tt = 0; tt < TPC; ++tt) {
+    const int row = (CLAMP ? min(tok0 + 16 * tt + lo, s1 - 1) : tok0 + 16 * tt + lo) - pt0[tt];
+    const uint16_t* kp = kb[tt] + row * RK + 4 * hi;
+#pragma unroll
+    for (int m = 0; m < RK / 16; ++m) {
+      const u32x2 kk = stream_load(reinterpret_cast<const u32x2*>(kp + 16 * m));
+      R.k[tt][m] = make_uint2(kk.x, kk.y);
+    }
+    const uint16_t* vp = vb[tt] + row * RV + hi * (RV / 4);
+#pragma unroll
+    for (int m = 0; m < RV / 32; ++m) R.v[tt][m] = stream_load(reinterpret_cast<const u32x4*>(vp + 8 * m));
+  }
+}
+
+template <int D, int RK, int RV, int HPW, int TPC, bool PAGED>
 __global__ __launch_bounds__(64 * HPW)
 #if LLA_FOLD_WAVES_PER_EU
 __attribute__((amdgpu_waves_per_eu(LLA_FOLD_WAVES_PER_EU)))
 #endif
-void decode_rotary_fold_kernel(DecodeArgs a) {
+void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int NKS = D / 32;        // k-steps of 32 over the cos|sin index
   constexpr int NMT = RK / 16 + 1;   // row tiles of M^T: r_k latent rows + the mean row
   constexpr int NCK = RK / 16;       // 8-byte key-latent pieces per lane per tile
@@ -194,7 +217,8 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
     __syncthreads();
   }
 
-  const size_t plane = static_cast<size_t>(b * a.H + h) * a.n_max;
+  // dense: this head's plane; paged: this head's rows of page 0 of the pool
+  const size_t plane = PAGED ? static_cast<size_t>(h) * kPage : static_cast<size_t>(b * a.H + h) * a.n_max;
   const uint16_t* ck = reinterpret_cast<const uint16_t*>(a.c_k) + plane * RK;
   const uint16_t* cv = reinterpret_cast<const uint16_t*>(a.c_v) + plane * RV;
   const u32x4* tab_g = reinterpret_cast<const u32x4*>(a.rope16);
@@ -267,6 +291,24 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
 
   // Two row buffers used in turn: chunk c computes from one while chunk c + 1 loads into
   // the other; the table of chunk c + 1 goes through registers into the other LDS half.
+  // Paged rows: the page of a tile is looked up per tile (uniform across the workgroup;
+  // rows clamped to the context's last token lie in the last tile's page).
+  auto load_paged = [&](Rows<RK, RV, TPC>& R, int c, int tile0, int tok0, auto clamp) {
+    (void)c;
+    const uint16_t* kb[TPC];
+    const uint16_t* vb[TPC];
+    int pt0[TPC];
+#pragma unroll
+    for (int tt = 0; tt < TPC; ++tt) {
+      const int ptile = __builtin_amdgcn_readfirstlane(min(tile0 + tt, tile_max));
+      const size_t page = static_cast<size_t>(page_of(pg, b, ptile));
+      kb[tt] = ck + page * a.H * kPage * RK;
+      vb[tt] = cv + page * a.H * kPage * RV;
+      pt0[tt] = ptile * kPage;
+    }
+    load_rows_paged<decltype(clamp)::value, RK, RV, TPC>(R, kb, vb, pt0, tok0, s1, lo, hi);
+  };
+
   Rows<RK, RV, TPC> ra, rb;
   u32x4 tb[TPT];
   u32x4* tab0 = lds;
@@ -280,7 +322,8 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
         const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
         tb[k] = tab_g[static_cast<size_t>(tile0) * NKS * 64 + u];
       }
-      load_rows<false, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
+      if constexpr (PAGED) load_paged(R, c, tile0, tok0, std::false_type{});
+      else load_rows<false, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
     } else {
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
@@ -288,7 +331,8 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
         const int tile = min(tile0 + u / (NKS * 64), tile_max);
         tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];
       }
-      load_rows<true, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
+      if constexpr (PAGED) load_paged(R, c, tile0, tok0, std::true_type{});
+      else load_rows<true, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
     }
   };
   auto store_tab = [&](u32x4* dst) {
@@ -388,10 +432,11 @@ void decode_rotary_fold_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int RK, int RV, int HPW, int TPC>
-void launch(const DecodeArgs& a, hipStream_t s) {
+template <int D, int RK, int RV, int HPW, int TPC, bool PAGED = false>
+void launch(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
   dim3 grid(a.S, (a.H / HPW) * a.L, a.B);
-  hipLaunchKernelGGL((decode_rotary_fold_kernel<D, RK, RV, HPW, TPC>), grid, dim3(64 * HPW), 0, s, a);
+  hipLaunchKernelGGL((decode_rotary_fold_kernel<D, RK, RV, HPW, TPC, PAGED>), grid, dim3(64 * HPW), 0,
+                     s, a, pg);
 }
 
 }  // namespace
@@ -417,10 +462,23 @@ bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v) {
 bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                hipStream_t s) {
   if (dtype != 1 || a.H % LLA_FOLD_HPW != 0) return false;
-#define X(D_, RK_, RV_, TPC_)                       \
-  if (d == D_ && r_k == RK_ && r_v == RV_) {        \
-    launch<D_, RK_, RV_, LLA_FOLD_HPW, TPC_>(a, s); \
-    return true;                                    \
+#define X(D_, RK_, RV_, TPC_)                                  \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                   \
+    launch<D_, RK_, RV_, LLA_FOLD_HPW, TPC_>(a, PageArgs{}, s); \
+    return true;                                               \
+  }
+  LLA_FOLD_SHAPES(X)
+#undef X
+  return false;
+}
+
+bool launch_decode_rotary_fold_paged(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
+                                     const PageArgs& pg, hipStream_t s) {
+  if (dtype != 1 || a.H % LLA_FOLD_HPW != 0 || pg.table == nullptr) return false;
+#define X(D_, RK_, RV_, TPC_)                                  \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                   \
+    launch<D_, RK_, RV_, LLA_FOLD_HPW, TPC_, true>(a, pg, s);  \
+    return true;                                               \
   }
   LLA_FOLD_SHAPES(X)
 #undef X

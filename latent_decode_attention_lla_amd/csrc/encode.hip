@@ -42,8 +42,8 @@ __device__ __forceinline__ void store4(bf16_t* p, f32x4 v) {
   *reinterpret_cast<uint2*>(p) = w;
 }
 
-template <typename T, int R, int RG, int KSPLIT>
-__global__ __launch_bounds__(64 * KSPLIT) void encode_kernel(EncodeArgs a) {
+template <typename T, int R, int RG, int KSPLIT, bool PAGED = false>
+__global__ __launch_bounds__(64 * KSPLIT) void encode_kernel(EncodeArgs a, PageArgs pg) {
   constexpr int KS = KsOf<T>::value;
   using M = Mfma<T, KS>;
   constexpr int E = M::E;
@@ -158,8 +158,14 @@ __global__ __launch_bounds__(64 * KSPLIT) void encode_kernel(EncodeArgs a) {
     const int tok = j0 + 16 * nt + lo;
     const int b = tok / a.n_new;
     const int j = tok - b * a.n_new;
-    T* crow = static_cast<T*>(a.c) +
-              (static_cast<size_t>(b * a.Hc + hc) * a.n_max + a.pos_start + j) * R;
+    const int pos = a.pos_start + j;
+    T* crow;
+    if constexpr (PAGED) {  // row pos % 16 of the page the block table names for it
+      const size_t page = static_cast<size_t>(page_of(pg, b, pos / kPage));
+      crow = static_cast<T*>(a.c) + ((page * a.Hc + hc) * kPage + pos % kPage) * R;
+    } else {
+      crow = static_cast<T*>(a.c) + (static_cast<size_t>(b * a.Hc + hc) * a.n_max + pos) * R;
+    }
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       const int r4 = 16 * (rt0 + g) + 4 * hi;
@@ -468,12 +474,26 @@ void launch_stream(const EncodeArgs& a, hipStream_t s) {
                      dim3(64 * EsShape<R>::NW), 0, s, a, per);
 }
 
-template <typename T, int R, int RG, int KSPLIT>
-void launch(const EncodeArgs& a, hipStream_t s) {
+template <typename T, int R, int RG, int KSPLIT, bool PAGED = false>
+void launch(const EncodeArgs& a, hipStream_t s, const PageArgs& pg = PageArgs{}) {
   constexpr int NR = (R + 15) / 16;
   const long long total = static_cast<long long>(a.B) * a.n_new;
   dim3 grid(static_cast<unsigned>((total + 31) / 32), (NR + RG - 1) / RG, a.Hc);
-  hipLaunchKernelGGL((encode_kernel<T, R, RG, KSPLIT>), grid, dim3(64 * KSPLIT), 0, s, a);
+  hipLaunchKernelGGL((encode_kernel<T, R, RG, KSPLIT, PAGED>), grid, dim3(64 * KSPLIT), 0, s, a, pg);
+}
+
+// Paged cache: the few-token kernel for any token count (its rows are addressed per token).
+template <typename T, int R>
+void launch_shape_paged(const EncodeArgs& a, const PageArgs& pg, hipStream_t s) {
+  constexpr int NR = (R + 15) / 16;
+  const long long tiles = (static_cast<long long>(a.B) * a.n_new + 31) / 32;
+  if (tiles * a.Hc >= 1024) {
+    launch<T, R, NR, 1, true>(a, s, pg);
+  } else if (a.Kdim % (8 * KsOf<T>::value) == 0 && a.Kdim >= 8 * 256) {
+    launch<T, R, 1, 8, true>(a, s, pg);
+  } else {
+    launch<T, R, 1, 1, true>(a, s, pg);
+  }
 }
 
 // Long prompts: the register-resident W_down^T stream for per-head bfloat16 with a short
@@ -515,6 +535,19 @@ bool encode_supported(int dtype, int r, int Kdim) {
   const int ks = dtype == 0 ? 16 : 32;
   if (Kdim % ks != 0) return false;
 #define X(R_) if (r == R_) return true;
+  LLA_ENCODE_RANKS(X)
+#undef X
+  return false;
+}
+
+bool launch_encode_paged(int dtype, int r, const EncodeArgs& a, const PageArgs& pg, hipStream_t s) {
+  if (pg.table == nullptr) return false;
+#define X(R_)                                                \
+  if (r == R_) {                                             \
+    if (dtype == 0) launch_shape_paged<float, R_>(a, pg, s); \
+    else launch_shape_paged<bf16_t, R_>(a, pg, s);           \
+    return true;                                             \
+  }
   LLA_ENCODE_RANKS(X)
 #undef X
   return false;

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "lla_args.h"
+#include "lla_page_args.h"
 #include "lla_recon_args.h"
 
 namespace lla {
@@ -14,6 +15,12 @@ bool launch_decode_reconstruct(int dtype, int d, int r_k, int r_v, const DecodeA
                                hipStream_t s);
 bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                hipStream_t s);
+// Paged cache (pg.table non-null): c_k / c_v of the args are the layer's page pools.
+bool launch_decode_rotary_fold_paged(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
+                                     const PageArgs& pg, hipStream_t s);
+bool launch_decode_reconstruct_paged(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
+                                     const PageArgs& pg, hipStream_t s);
+bool launch_encode_paged(int dtype, int r, const EncodeArgs& a, const PageArgs& pg, hipStream_t s);
 // Wide latents (r_k >= 64): a pair of waves per head; `shared` selects LLA-2D (all heads
 // read one latent plane). H must be a multiple of fold_wide_heads_per_group(...).
 bool launch_decode_fold_wide(int dtype, int d, int r_k, int r_v, bool shared, const DecodeArgs& a,
