@@ -109,6 +109,19 @@ typedef struct {
   int32_t path;       /* lla_path */
 } lla_decode_opts;
 
+/* A paged latent cache (Appendix D, Table 9 and Appendix J, "Eviction and long-context
+ * prefill": token eviction composes with the latent codec). Latents live in pages of 16
+ * tokens; each layer's pool is cache.c_k [D][num_pages][Hc][16][r_k] (c_v likewise), and
+ * logical token j of sequence b is row j % 16 of page block_table[b * max_blocks + j / 16].
+ * Positions for RoPE are the logical slots j, so evicting pages and listing the kept ones
+ * in order (sinks, then the most recent pages) gives StreamingLLM's cache-relative
+ * positions without touching the stored latents, which are kept before RoPE. */
+typedef struct {
+  const int32_t* block_table; /* device int32 [batch][max_blocks], 4-byte aligned */
+  int32_t max_blocks;         /* max_blocks * 16 >= dims.n_max (the logical capacity) */
+  int32_t num_pages;          /* pages in each layer's pool */
+} lla_pages;
+
 /* Human-readable name of a status code. Never NULL. */
 const char* lla_status_string(int32_t status);
 
@@ -221,6 +234,29 @@ int32_t lla_decode_absorbed_supported(const lla_dims* dims, int32_t d_rope);
 int32_t lla_reconstruct(const lla_dims* dims, const lla_codec* codec, const lla_cache* cache,
                         int32_t layer, int32_t loop_begin, int32_t loop_count, int32_t pos_start,
                         int32_t n_tok, void* k_out, void* v_out, void* stream);
+
+/* lla_encode into a paged cache: the latents of logical tokens pos_start .. pos_start +
+ * n_new - 1 of every sequence are written to the rows their pages name. Arguments and
+ * errors as lla_encode, plus `pages` (validated as described at lla_pages). The block
+ * table's entries for the written logical pages must be pages of the pool; an entry
+ * outside [0, num_pages) is clamped into it (no access outside the pool, wrong rows). */
+int32_t lla_encode_paged(const lla_dims* dims, const lla_codec* codec, const lla_cache* cache,
+                         const lla_pages* pages, int32_t layer, const void* x_k, const void* x_v,
+                         int32_t pos_start, int32_t n_new, void* stream);
+
+/* lla_decode_attn over a paged cache (logical tokens 0 .. len_b - 1 through the block
+ * table; RoPE at the logical slot). Paths: the rotary fold for the shapes its narrow
+ * kernel serves (per-head bfloat16, r_k <= 32), else the reconstruct path; asking for the
+ * rotary fold elsewhere gives LLA_ERR_UNSUPPORTED. workspace >=
+ * lla_decode_paged_workspace_bytes(dims, n_ctx, loop_count, opts). Other arguments and
+ * errors as lla_decode_attn; block table entries as for lla_encode_paged. */
+size_t lla_decode_paged_workspace_bytes(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,
+                                        const lla_decode_opts* opts);
+int32_t lla_decode_attn_paged(const lla_dims* dims, const lla_codec* codec, const lla_cache* cache,
+                              const lla_pages* pages, int32_t layer, int32_t n_ctx,
+                              const int32_t* ctx_lens, const float* q, int32_t loop_begin,
+                              int32_t loop_count, float* out, void* workspace,
+                              size_t workspace_bytes, const lla_decode_opts* opts, void* stream);
 
 /* Uncompressed decode over the loop-indexed cache that the latent store replaces (Section
  * 3, "Teacher cache": every loop of every layer keeps its own key and value; Section 7,

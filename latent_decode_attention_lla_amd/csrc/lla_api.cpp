@@ -58,6 +58,33 @@ int32_t check_teacher_dims(const lla_dims* d) {
   return LLA_OK;
 }
 
+// Paged cache checks: the block table covers the logical capacity n_max, the pool is
+// non-empty, and the table is readable as int32.
+int32_t check_pages(const lla_dims& d, const lla_pages* pg) {
+  if (pg == nullptr || pg->block_table == nullptr) return LLA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(pg->block_table) & 3u) != 0) return LLA_ERR_INVALID_ARG;
+  if (pg->num_pages < 1 || pg->max_blocks < 1) return LLA_ERR_INVALID_ARG;
+  if (static_cast<long long>(pg->max_blocks) * lla::kPage < d.n_max) return LLA_ERR_INVALID_ARG;
+  if (static_cast<long long>(d.batch) * pg->max_blocks >= (1LL << 31)) return LLA_ERR_UNSUPPORTED;
+  return LLA_OK;
+}
+
+// The paged decode runs the narrow fold kernel or the reconstruct kernel (one wave per
+// head either way).
+int paged_path(const lla_dims& d, const lla_decode_opts* opts) {
+  const int want = opts ? opts->path : LLA_PATH_AUTO;
+  const bool narrow = fold_kind(d) == kFoldNarrow;
+  if (want == LLA_PATH_AUTO) return narrow ? LLA_PATH_ROTARY_FOLD : LLA_PATH_RECONSTRUCT;
+  if (want == LLA_PATH_ROTARY_FOLD && !narrow) return -1;
+  return want;
+}
+
+Plan plan_paged(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_opts* opts) {
+  lla_decode_opts o{0, LLA_PATH_RECONSTRUCT};  // one wave per (sequence, head, loop, split)
+  if (opts != nullptr) o.num_splits = opts->num_splits;
+  return plan_splits(d, n_ctx, loop_count, &o);
+}
+
 }  // namespace
 
 extern "C" {
@@ -475,6 +502,140 @@ int32_t lla_reconstruct(const lla_dims* d, const lla_codec* codec, const lla_cac
     }
   }
   return LLA_OK;
+}
+
+int32_t lla_encode_paged(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                         const lla_pages* pages, int32_t layer, const void* x_k, const void* x_v,
+                         int32_t pos_start, int32_t n_new, void* stream) {
+  int32_t st = check_dims(d);
+  if (st != LLA_OK) return st;
+  st = check_pages(*d, pages);
+  if (st != LLA_OK) return st;
+  if (codec == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
+  if (n_new < 0 || pos_start < 0 || static_cast<long long>(pos_start) + n_new > d->n_max)
+    return LLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_k, x_v, codec->w_down_k_t, codec->w_down_v_t, codec->mu_k, codec->mu_v,
+                        cache->c_k, cache->c_v};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+  const int Hc = latent_heads(*d);
+  const int K = d->T * d_in(*d);
+  if (!lla::encode_supported(d->dtype, d->r_k, K) || !lla::encode_supported(d->dtype, d->r_v, K))
+    return LLA_ERR_UNSUPPORTED;
+  if (n_new == 0) return LLA_OK;
+  if (static_cast<long long>(d->batch) * n_new >= (1LL << 31) - 64) return LLA_ERR_UNSUPPORTED;
+  const size_t es = elem_bytes(*d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const lla::PageArgs pg{pages->block_table, pages->max_blocks, pages->num_pages};
+  const int rs[2] = {d->r_k, d->r_v};
+  const void* xs[2] = {x_k, x_v};
+  const void* wds[2] = {codec->w_down_k_t, codec->w_down_v_t};
+  const void* mus[2] = {codec->mu_k, codec->mu_v};
+  void* cs[2] = {cache->c_k, cache->c_v};
+  for (int ax = 0; ax < 2; ++ax) {
+    const int r = rs[ax];
+    lla::EncodeArgs a;
+    a.x = xs[ax];
+    a.w_down_t = static_cast<const char*>(wds[ax]) + static_cast<size_t>(layer) * Hc * r * K * es;
+    a.mu = static_cast<const char*>(mus[ax]) + static_cast<size_t>(layer) * Hc * K * es;
+    a.c = static_cast<char*>(cs[ax]) +
+          static_cast<size_t>(layer) * pages->num_pages * Hc * static_cast<size_t>(lla::kPage) * r * es;
+    a.B = d->batch;
+    a.Hc = Hc;
+    a.Kdim = K;
+    a.n_new = n_new;
+    a.pos_start = pos_start;
+    a.n_max = d->n_max;
+    if (!lla::launch_encode_paged(d->dtype, r, a, pg, s)) return LLA_ERR_UNSUPPORTED;
+  }
+  return hip_status();
+}
+
+size_t lla_decode_paged_workspace_bytes(const lla_dims* d, int32_t n_ctx, int32_t loop_count,
+                                        const lla_decode_opts* opts) {
+  if (check_dims(d) != LLA_OK || n_ctx < 0 || n_ctx > d->n_max || loop_count < 1) return 0;
+  const Plan p = plan_paged(*d, n_ctx, loop_count, opts);
+  const size_t bytes = static_cast<size_t>(d->batch) * d->H * loop_count * p.S * (2 + d->r_v) * 4;
+  return (bytes + 255) / 256 * 256;
+}
+
+int32_t lla_decode_attn_paged(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                              const lla_pages* pages, int32_t layer, int32_t n_ctx,
+                              const int32_t* ctx_lens, const float* q, int32_t loop_begin,
+                              int32_t loop_count, float* out, void* workspace,
+                              size_t workspace_bytes, const lla_decode_opts* opts, void* stream) {
+  int32_t st = check_dims(d);
+  if (st != LLA_OK) return st;
+  st = check_pages(*d, pages);
+  if (st != LLA_OK) return st;
+  if (codec == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
+  if (n_ctx < 0 || n_ctx > d->n_max) return LLA_ERR_INVALID_ARG;
+  if (loop_begin < 0 || loop_count < 1 || static_cast<long long>(loop_begin) + loop_count > d->T)
+    return LLA_ERR_INVALID_ARG;
+  if (opts != nullptr && (opts->num_splits < 0 || opts->path < LLA_PATH_AUTO ||
+                          opts->path > LLA_PATH_ROTARY_FOLD))
+    return LLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {codec->mu_k, codec->w_up_k, codec->mu_v, codec->w_up_v, codec->rope_table,
+                        cache->c_k, cache->c_v, q, out, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+  if (ctx_lens != nullptr && (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) != 0) return LLA_ERR_INVALID_ARG;
+  const int path = paged_path(*d, opts);
+  if (path < 0) return LLA_ERR_UNSUPPORTED;
+  if (path == LLA_PATH_RECONSTRUCT &&
+      !lla::decode_reconstruct_supported(d->dtype, d->d_head, d->r_k, d->r_v))
+    return LLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < lla_decode_paged_workspace_bytes(d, n_ctx, loop_count, opts))
+    return LLA_ERR_WORKSPACE;
+
+  const Plan p = plan_paged(*d, n_ctx, loop_count, opts);
+  const size_t es = elem_bytes(*d);
+  const int Hc = latent_heads(*d);
+  const int K = d->T * d_in(*d);
+  const size_t pool_rows = static_cast<size_t>(pages->num_pages) * Hc * lla::kPage;
+  lla::DecodeArgs a;
+  a.c_k = static_cast<const char*>(cache->c_k) + static_cast<size_t>(layer) * pool_rows * d->r_k * es;
+  a.c_v = static_cast<const char*>(cache->c_v) + static_cast<size_t>(layer) * pool_rows * d->r_v * es;
+  a.w_up_k = static_cast<const char*>(codec->w_up_k) +
+             static_cast<size_t>(layer) * d->T * d->H * d->d_head * d->r_k * es;
+  a.w_up_v = static_cast<const char*>(codec->w_up_v) +
+             static_cast<size_t>(layer) * d->T * d->H * d->d_head * d->r_v * es;
+  a.mu_k = static_cast<const char*>(codec->mu_k) + static_cast<size_t>(layer) * Hc * K * es;
+  a.mu_v = static_cast<const char*>(codec->mu_v) + static_cast<size_t>(layer) * Hc * K * es;
+  a.rope32 = static_cast<const float*>(codec->rope_table);
+  a.rope16 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(codec->rope_table) +
+                                               static_cast<size_t>(d->n_max) * d->d_head * 4);
+  a.q = q;
+  a.ctx_lens = ctx_lens;
+  a.part = static_cast<float*>(workspace);
+  a.out = out;
+  a.B = d->batch;
+  a.H = d->H;
+  a.Hc = Hc;
+  a.T = d->T;
+  a.L = loop_count;
+  a.loop_begin = loop_begin;
+  a.n_max = d->n_max;
+  a.n_ctx = n_ctx;
+  a.S = p.S;
+  a.split_len = p.split_len;
+  a.variant = d->variant;
+  const double scale = d->scale > 0.f ? d->scale : 1.0 / std::sqrt(static_cast<double>(d->d_head));
+  a.scale_log2e = static_cast<float>(scale * kLog2e);
+  const lla::PageArgs pg{pages->block_table, pages->max_blocks, pages->num_pages};
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool ok = path == LLA_PATH_ROTARY_FOLD
+                      ? lla::launch_decode_rotary_fold_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s)
+                      : lla::launch_decode_reconstruct_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s);
+  if (!ok) return LLA_ERR_UNSUPPORTED;
+  st = hip_status();
+  if (st != LLA_OK) return st;
+  if (path == LLA_PATH_ROTARY_FOLD && p.S == 1) return LLA_OK;
+  if (!lla::launch_combine(d->dtype, d->d_head, d->r_v, a, s)) return LLA_ERR_UNSUPPORTED;
+  return hip_status();
 }
 
 }  // extern "C"

@@ -39,6 +39,7 @@ EXPORTED = (
     "lla_decode_absorbed_supported",
     "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
     "lla_decode_teacher_num_splits", "lla_reconstruct",
+    "lla_encode_paged", "lla_decode_paged_workspace_bytes", "lla_decode_attn_paged",
 )
 
 
@@ -65,6 +66,11 @@ class lla_codec(ctypes.Structure):
 
 class lla_cache(ctypes.Structure):
     _fields_ = [("c_k", ctypes.c_void_p), ("c_v", ctypes.c_void_p)]
+
+
+class lla_pages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
 
 
 class lla_decode_opts(ctypes.Structure):
@@ -125,6 +131,14 @@ def load() -> ctypes.CDLL:
     lib.lla_reconstruct.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, i32, i32, i32,
                                     i32, vp, vp, vp]
     lib.lla_reconstruct.restype = i32
+    lib.lla_encode_paged.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), P(lla_pages), i32, vp,
+                                     vp, i32, i32, vp]
+    lib.lla_encode_paged.restype = i32
+    lib.lla_decode_paged_workspace_bytes.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
+    lib.lla_decode_paged_workspace_bytes.restype = sz
+    lib.lla_decode_attn_paged.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), P(lla_pages), i32,
+                                          i32, vp, vp, i32, i32, vp, vp, sz, P(lla_decode_opts), vp]
+    lib.lla_decode_attn_paged.restype = i32
     _lib = lib
     return lib
 
@@ -305,3 +319,40 @@ def lla_reconstruct_status(dims, codec, cache, layer, loop_begin, loop_count, po
     return load().lla_reconstruct(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache),
                                   layer, loop_begin, loop_count, pos_start, n_tok, _ptr(k_out),
                                   _ptr(v_out), stream)
+
+
+def make_pages(block_table, max_blocks: int, num_pages: int) -> lla_pages:
+    return lla_pages(_ptr(block_table), max_blocks, num_pages)
+
+
+def lla_encode_paged(dims, codec, cache, pages, layer, x_k, x_v, pos_start, n_new, stream=None):
+    _check("lla_encode_paged", lla_encode_paged_status(dims, codec, cache, pages, layer, x_k, x_v,
+                                                       pos_start, n_new, _stream(stream)))
+
+
+def lla_encode_paged_status(dims, codec, cache, pages, layer, x_k, x_v, pos_start, n_new,
+                            stream=0) -> int:
+    return load().lla_encode_paged(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache),
+                                   ctypes.byref(pages), layer, _ptr(x_k), _ptr(x_v), pos_start,
+                                   n_new, stream)
+
+
+def lla_decode_paged_workspace_bytes(dims, n_ctx, loop_count, opts=None) -> int:
+    return load().lla_decode_paged_workspace_bytes(
+        ctypes.byref(dims), n_ctx, loop_count, ctypes.byref(opts) if opts is not None else None)
+
+
+def lla_decode_attn_paged(dims, codec, cache, pages, layer, n_ctx, ctx_lens, q, loop_begin,
+                          loop_count, out, workspace, workspace_bytes, opts=None, stream=None):
+    _check("lla_decode_attn_paged", lla_decode_attn_paged_status(
+        dims, codec, cache, pages, layer, n_ctx, ctx_lens, q, loop_begin, loop_count, out,
+        workspace, workspace_bytes, opts, _stream(stream)))
+
+
+def lla_decode_attn_paged_status(dims, codec, cache, pages, layer, n_ctx, ctx_lens, q, loop_begin,
+                                 loop_count, out, workspace, workspace_bytes, opts=None,
+                                 stream=0) -> int:
+    return load().lla_decode_attn_paged(
+        ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), ctypes.byref(pages), layer,
+        n_ctx, _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out), _ptr(workspace),
+        workspace_bytes, ctypes.byref(opts) if opts is not None else None, stream)
