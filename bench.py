@@ -44,6 +44,8 @@ KERNEL_SOURCES = {
     "encode": _COMMON_SOURCES + ("encode.hip",),
     "teacher": _COMMON_SOURCES + ("decode_teacher.hip", "decode_stream.h", "combine.hip"),
     "reconstruct": _COMMON_SOURCES + ("reconstruct.hip", "lla_recon_args.h"),
+    "paged": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_reconstruct.hip", "combine.hip",
+                                "lla_page_args.h"),
 }
 
 
@@ -135,6 +137,9 @@ def cpu_baseline(w, seqs: int):
     if w.teacher:
         from latent_decode_attention_lla_amd.inputs import teacher_inputs
         t = teacher_inputs(sw, seed=12345, device="cpu")
+    elif w.paged:
+        from latent_decode_attention_lla_amd.inputs import paged_decode_inputs
+        t = paged_decode_inputs(sw, seed=12345, device="cpu")
     else:
         t = decode_inputs(sw, seed=12345, device="cpu")
     t = {k: v.float().numpy().astype(np.float64) for k, v in t.items()}
@@ -145,6 +150,10 @@ def cpu_baseline(w, seqs: int):
             q = t["q"][layer, loop:loop + 1].transpose(1, 2, 0, 3)
             if w.teacher:
                 O.decode_teacher(t["k_cache"][layer], t["v_cache"][layer], q, loop)
+            elif w.paged:
+                O.decode_paged(t["c_k"][layer], t["c_v"][layer], t["block_table"], t["w_up_k"][layer],
+                               t["mu_k"][layer], t["w_up_v"][layer], t["mu_v"][layer], q, loop, None,
+                               w.n, w.rope_base, None, variant)
             elif w.d_rope > 0:
                 O.decode_absorbed(t["c_k"][layer], t["c_v"][layer], t["k_rope"][layer],
                                   t["w_up_k"][layer], t["mu_k"][layer], t["w_up_v"][layer],
@@ -398,7 +407,14 @@ def main():
         st = DeviceTeacherCache(w, seed=3, device=dev)
         x_new = None
     else:
-        st = DeviceLatentStore(w, seed=3, device=dev)
+        if w.paged:  # latents in shuffled pages of each layer's pool, a block table per sequence
+            from latent_decode_attention_lla_amd.inputs import paged_decode_inputs
+            st = DeviceLatentStore(w, seed=3, device=dev, tensors=paged_decode_inputs(w, 3, dev))
+            st.block_table = st.t["block_table"]
+            st.pages = lla.make_pages(st.block_table, st.block_table.shape[1],
+                                      st.t["c_k"].shape[1])
+        else:
+            st = DeviceLatentStore(w, seed=3, device=dev)
         # Encode-side codec and the finished per-loop K/V to encode for every layer used.
         g = torch.Generator(device=dev).manual_seed(4)
         K = w.T * w.d_in
@@ -415,6 +431,10 @@ def main():
     elif absorbed:
         S = lla.lla_decode_num_splits(st.dims, w.n, 1, lla.make_opts(args.splits, lla.LLA_PATH_RECONSTRUCT))
         ws = st.absorbed_workspace(w.n, 1, opts)
+    elif w.paged:
+        S = lla.lla_decode_num_splits(st.dims, w.n, 1, opts)
+        ws = torch.empty(max(lla.lla_decode_paged_workspace_bytes(st.dims, w.n, 1, opts), 256),
+                         dtype=torch.uint8, device=dev)
     else:
         S = lla.lla_decode_num_splits(st.dims, w.n, 1, opts)
         ws = st.workspace(w.n, 1, opts)
@@ -433,8 +453,12 @@ def main():
         for layer in range(n_enc):
             if record is not None:
                 ev_enc[record * n_enc + layer][0].record(stream)
-            lla.lla_encode(st.dims, st.codec, st.cache, layer, x_new[0][layer], x_new[1][layer],
-                           pos, n_new, sp)
+            if w.paged:
+                lla.lla_encode_paged(st.dims, st.codec, st.cache, st.pages, layer, x_new[0][layer],
+                                     x_new[1][layer], pos, n_new, sp)
+            else:
+                lla.lla_encode(st.dims, st.codec, st.cache, layer, x_new[0][layer],
+                               x_new[1][layer], pos, n_new, sp)
             if record is not None:
                 ev_enc[record * n_enc + layer][1].record(stream)
         k = 0
@@ -446,6 +470,9 @@ def main():
                 if teacher:
                     lla.lla_decode_attn_teacher(st.dims, st.t["k_cache"], st.t["v_cache"], layer, w.n,
                                                 None, q, loop, 1, out, ws, ws.numel(), opts, sp)
+                elif w.paged:
+                    lla.lla_decode_attn_paged(st.dims, st.codec, st.cache, st.pages, layer, w.n,
+                                              None, q, loop, 1, out, ws, ws.numel(), opts, sp)
                 elif absorbed:
                     lla.lla_decode_attn_absorbed(st.dims, st.codec, st.cache, st.t["k_rope"], w.d_rope,
                                                  layer, w.n, None, q, loop, 1, out, ws, ws.numel(),
@@ -477,7 +504,7 @@ def main():
         xs = sorted(a.elapsed_time(b) for a, b in evs[:len(evs)])
         return sum(xs) / len(xs), xs[len(xs) // 2]
 
-    dec_kind = "teacher" if teacher else ("absorbed" if absorbed else "decode")
+    dec_kind = "teacher" if teacher else ("absorbed" if absorbed else ("paged" if w.paged else "decode"))
     dec_ms, dec_med = avg(ev_dec[:n_dec * args.steps])
     dec_bytes, dec_flops = algorithmic(w, "decode")
     dec_roof = roofline(dec_bytes, dec_flops, dec_ms, measured_traffic(dec_kind, args.workload, args.path))
@@ -518,6 +545,8 @@ def main():
     step_desc = (f"encode a {n_new}-token prompt per sequence for one layer, then {w.T} decode calls"
                  if prefill else
                  f"encode the new token for {w.D} layers, then {w.D} x {w.T} decode calls")
+    if w.paged:
+        step_desc += " over a paged cache (16-token pages in a random order, block table per sequence)"
     if teacher:
         step_desc = (f"{w.D} x {w.T} uncompressed decode calls over the per-loop K/V cache (the "
                      f"new token's K/V rows, {w.batch * w.T * w.H * w.d * 2 * es // 1024} KiB per "
@@ -552,7 +581,7 @@ def main():
                    **({"d_rope": w.d_rope} if absorbed else {})},
         "roofline": dec_roof if dominant == "decode" else enc_roof,
         "roofline_kernel": {"teacher": "lla_decode_attn_teacher", "absorbed": "lla_decode_attn_absorbed",
-                            "decode": "lla_decode_attn"}[dec_kind]
+                            "paged": "lla_decode_attn_paged", "decode": "lla_decode_attn"}[dec_kind]
                            if dominant == "decode" else "lla_encode",
         "cpu_baseline": cpu,
         "decode_call": {"avg_ms": round(dec_ms, 5), "median_ms": round(dec_med, 5),

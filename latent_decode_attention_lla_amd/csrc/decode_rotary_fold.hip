@@ -107,22 +107,24 @@ __device__ __forceinline__ void load_rows(Rows<RK, RV, TPC>& R, const uint16_t* 
   }
 }
 
-// Paged: the rows of tile tt start at kb[tt] / vb[tt] (the page's rows for this head),
-// row r of the chunk's tile tt being row r - 16 * ptile[tt] of its page.
+// Paged: the rows of tile tt are those of the pool's page rows starting at element
+// offsets koff[tt] / voff[tt] (wave-uniform), row r of the chunk's tile tt being row
+// r - pt0[tt] of its page.
 template <bool CLAMP, int RK, int RV, int TPC>
-__device__ __forceinline__ void load_rows_paged(Rows<RK, RV, TPC>& R, const uint16_t* const* kb,
-                                                const uint16_t* const* vb, const int* pt0,
-                                                int tok0, int s1, int lo, int hi) {
+__device__ __forceinline__ void load_rows_paged(Rows<RK, RV, TPC>& R, const uint16_t* kpool,
+                                                const uint16_t* vpool, const size_t* koff,
+                                                const size_t* voff, const int* pt0, int tok0,
+                                                int s1, int lo, int hi) {
 #pragma unroll
   for (int tt = 0; tt < TPC; ++tt) {
     const int row = (CLAMP ? min(tok0 + 16 * tt + lo, s1 - 1) : tok0 + 16 * tt + lo) - pt0[tt];
-    const uint16_t* kp = kb[tt] + row * RK + 4 * hi;
+    const uint16_t* kp = kpool + koff[tt] + row * RK + 4 * hi;
 #pragma unroll
     for (int m = 0; m < RK / 16; ++m) {
       const u32x2 kk = stream_load(reinterpret_cast<const u32x2*>(kp + 16 * m));
       R.k[tt][m] = make_uint2(kk.x, kk.y);
     }
-    const uint16_t* vp = vb[tt] + row * RV + hi * (RV / 4);
+    const uint16_t* vp = vpool + voff[tt] + row * RV + hi * (RV / 4);
 #pragma unroll
     for (int m = 0; m < RV / 32; ++m) R.v[tt][m] = stream_load(reinterpret_cast<const u32x4*>(vp + 8 * m));
   }
@@ -291,29 +293,42 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
 
   // Two row buffers used in turn: chunk c computes from one while chunk c + 1 loads into
   // the other; the table of chunk c + 1 goes through registers into the other LDS half.
-  // Paged rows: the page of a tile is looked up per tile (uniform across the workgroup;
-  // rows clamped to the context's last token lie in the last tile's page).
-  auto load_paged = [&](Rows<RK, RV, TPC>& R, int c, int tile0, int tok0, auto clamp) {
-    (void)c;
-    const uint16_t* kb[TPC];
-    const uint16_t* vb[TPC];
+  // Paged rows: the pages of a chunk's tiles (uniform across the workgroup; rows clamped to
+  // the context's last token lie in the last tile's page) are read with scalar loads one
+  // chunk ahead of the rows that need them, so the lookup is off the loads' issue path.
+  struct Pages {
+    int p[TPC];
+  };
+  auto fetch_pages = [&](int c) {
+    Pages P;
+#pragma unroll
+    for (int tt = 0; tt < TPC; ++tt) {
+      const int ptile = min((s0 >> 4) + c * TPC + tt, tile_max);
+      P.p[tt] = page_of(pg, b, __builtin_amdgcn_readfirstlane(ptile));
+    }
+    return P;
+  };
+  const int h_u = __builtin_amdgcn_readfirstlane(h);  // the wave's head, in a scalar register
+  auto load_paged = [&](Rows<RK, RV, TPC>& R, const Pages& P, int tile0, int tok0, auto clamp) {
+    size_t koff[TPC], voff[TPC];
     int pt0[TPC];
 #pragma unroll
     for (int tt = 0; tt < TPC; ++tt) {
-      const int ptile = __builtin_amdgcn_readfirstlane(min(tile0 + tt, tile_max));
-      const size_t page = static_cast<size_t>(page_of(pg, b, ptile));
-      kb[tt] = ck + page * a.H * kPage * RK;
-      vb[tt] = cv + page * a.H * kPage * RV;
-      pt0[tt] = ptile * kPage;
+      const size_t rows = (static_cast<size_t>(P.p[tt]) * a.H + h_u) * kPage;  // page's first row
+      koff[tt] = rows * RK;
+      voff[tt] = rows * RV;
+      pt0[tt] = min(tile0 + tt, tile_max) * kPage;
     }
-    load_rows_paged<decltype(clamp)::value, RK, RV, TPC>(R, kb, vb, pt0, tok0, s1, lo, hi);
+    load_rows_paged<decltype(clamp)::value, RK, RV, TPC>(
+        R, reinterpret_cast<const uint16_t*>(a.c_k), reinterpret_cast<const uint16_t*>(a.c_v), koff,
+        voff, pt0, tok0, s1, lo, hi);
   };
 
   Rows<RK, RV, TPC> ra, rb;
   u32x4 tb[TPT];
   u32x4* tab0 = lds;
   u32x4* tab1 = lds + TAB_CHUNK;
-  auto load_chunk = [&](Rows<RK, RV, TPC>& R, int c) {
+  auto load_chunk = [&](Rows<RK, RV, TPC>& R, int c, const Pages& P) {
     const int tile0 = (s0 >> 4) + c * TPC;
     const int tok0 = s0 + c * TPC * 16;
     if (c < nfull) {
@@ -322,7 +337,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
         const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
         tb[k] = tab_g[static_cast<size_t>(tile0) * NKS * 64 + u];
       }
-      if constexpr (PAGED) load_paged(R, c, tile0, tok0, std::false_type{});
+      if constexpr (PAGED) load_paged(R, P, tile0, tok0, std::false_type{});
       else load_rows<false, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
     } else {
 #pragma unroll
@@ -331,7 +346,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
         const int tile = min(tile0 + u / (NKS * 64), tile_max);
         tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];
       }
-      if constexpr (PAGED) load_paged(R, c, tile0, tok0, std::true_type{});
+      if constexpr (PAGED) load_paged(R, P, tile0, tok0, std::true_type{});
       else load_rows<true, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
     }
   };
@@ -347,22 +362,29 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
     else compute_chunk(c, R, tcur, std::false_type{});
   };
 
+  Pages pa{}, pb{};
+  if constexpr (PAGED) {
+    pa = fetch_pages(0);
+    pb = fetch_pages(1);
+  }
   if (nchunk > 0) {
-    load_chunk(ra, 0);
+    load_chunk(ra, 0, pa);
     store_tab(tab0);
   }
   __syncthreads();
   for (int c = 0; c < nchunk; c += 2) {
     // even chunk: compute from (ra, tab0), prefetch into (rb, tab1)
     const bool more1 = c + 1 < nchunk;
-    if (more1) load_chunk(rb, c + 1);
+    if (more1) load_chunk(rb, c + 1, pb);
+    if constexpr (PAGED) pa = fetch_pages(c + 2);
     compute(c, ra, tab0);
     if (more1) store_tab(tab1);
     __syncthreads();
     if (!more1) break;
     // odd chunk: compute from (rb, tab1), prefetch into (ra, tab0)
     const bool more2 = c + 2 < nchunk;
-    if (more2) load_chunk(ra, c + 2);
+    if (more2) load_chunk(ra, c + 2, pa);
+    if constexpr (PAGED) pb = fetch_pages(c + 3);
     compute(c + 1, rb, tab1);
     if (more2) store_tab(tab0);
     __syncthreads();

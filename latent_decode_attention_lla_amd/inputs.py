@@ -21,6 +21,8 @@ Table 5):
                     Ouro-1.4B 4x geometry (T=4, D=24, H=16, d=128, (96, 160), bf16): per
                     layer, encode the prompt's per-loop K/V, then rebuild them for the
                     second pass (Appendix J's 64k passkey cells; Table 12)
+* ``paged_21x``     ``capacity_21x`` stored in a paged cache: 16-token pages of each
+                    layer's pool in a random order, found through a block table
 * ``teacher_4k``    the uncompressed loop-indexed cache the latent store replaces (Section
                     3 "Teacher cache"; Table 5's teacher column): T=4, D=24, H=16, d=128,
                     bf16 keys and values for every loop, batch 32 (the teacher's measured
@@ -68,6 +70,7 @@ class Workload:
     d_rope: int = 0                # rotary-branch width of the decoupled (absorbed) decode
     teacher: bool = False          # an uncompressed per-loop cache (no codec)
     stream_prefill: bool = False   # a step is the layer-by-layer two-pass prefill
+    paged: bool = False            # latents in shuffled 16-token pages (a block table)
 
     @property
     def Hc(self) -> int:
@@ -98,6 +101,8 @@ WORKLOADS = {
                            batch=16, n=16384, variant="2d"),
     "absorbed_4x": Workload("absorbed_4x", T=4, D=24, H=16, d=128, r_k=96, r_v=160,
                             batch=8, n=32768, d_rope=64),
+    "paged_21x": Workload("paged_21x", T=4, D=24, H=16, d=128, r_k=16, r_v=32, batch=768,
+                          n=4096, paged=True),
     "prefill_64k": Workload("prefill_64k", T=4, D=24, H=16, d=128, r_k=96, r_v=160, batch=1,
                             n=65536, stream_prefill=True),
     "teacher_4k": Workload("teacher_4k", T=4, D=24, H=16, d=128, r_k=0, r_v=0, batch=32,
@@ -139,6 +144,28 @@ def decode_inputs(w: Workload, seed: int, device="cpu", n_alloc: int | None = No
         out["q"] = _randn((w.D, w.T, w.batch, w.H, w.d), 1.0, torch.float32, g, device)
     if w.d_rope > 0:  # drawn last, so the tensors above do not depend on it
         out["k_rope"] = _randn((w.D, w.batch, w.H, n_max, w.d_rope), 1.0, dt, g, device)
+    return out
+
+
+def paged_decode_inputs(w: Workload, seed: int, device="cpu"):
+    """decode_inputs with the latents drawn straight into page pools [D][P][Hc][16][r]
+    (P = batch * ceil(n / 16) pages) and a block table [batch][ceil(n / 16)] int32 that
+    deals the pages out in a random order."""
+    npg = (w.n + 15) // 16
+    P = w.batch * npg
+    g = _gen(seed, device)
+    dt = w.torch_dtype
+    out = {
+        "c_k": _randn((w.D, P, w.Hc, 16, w.r_k), 1.0, dt, g, device),
+        "c_v": _randn((w.D, P, w.Hc, 16, w.r_v), 1.0, dt, g, device),
+        "w_up_k": _randn((w.D, w.T, w.H, w.d, w.r_k), 1.0 / math.sqrt(w.r_k), dt, g, device),
+        "w_up_v": _randn((w.D, w.T, w.H, w.d, w.r_v), 1.0 / math.sqrt(w.r_v), dt, g, device),
+        "mu_k": _randn((w.D, w.Hc, w.T * w.d_in), math.sqrt(0.1), dt, g, device),
+        "mu_v": _randn((w.D, w.Hc, w.T * w.d_in), math.sqrt(0.1), dt, g, device),
+        "q": _randn((w.D, w.T, w.batch, w.H, w.d), 1.0, torch.float32, g, device),
+    }
+    perm = torch.randperm(P, generator=g, device=device)
+    out["block_table"] = perm.reshape(w.batch, npg).to(torch.int32)
     return out
 
 

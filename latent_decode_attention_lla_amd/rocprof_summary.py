@@ -68,7 +68,7 @@ def main(argv=None):
     t.add_argument("--sum", action="store_true")
     t.add_argument("--out")
     t.add_argument("--extra", default="{}", help="JSON merged into the output")
-    t.add_argument("--call", choices=["decode", "absorbed", "encode", "teacher", "reconstruct"],
+    t.add_argument("--call", choices=["decode", "absorbed", "encode", "teacher", "reconstruct", "paged"],
                    help="with --workload: record the call's source hash and algorithmic bytes")
     t.add_argument("--workload")
     a = p.parse_args(argv)
