@@ -15,17 +15,19 @@
 //
 // decode_absorbed_kernel: one wave per (sequence, head, loop, split). Its prologue folds
 //   the query: q~, beta and the rotary query, scaled into the exp2 domain, go to LDS (the
-//   unit's W_up,k,t rows are read from L2, shared by the unit's splits). Its 64 lanes are G
-//   groups of 64/G: lane (j, g) takes token j of each (64/G)-token tile and every G-th
-//   8-byte unit of each of its rows (c_k, k_rope, c_v), starting at unit g. G = 4 for narrow latents; G = 8 for
-//   wide ones keeps a lane's share of the rows, the folded query and the value
-//   accumulator within the registers of two waves per SIMD. The slice dots are summed over
-//   the lane groups by butterflies (a DPP row rotation for 8, permlane swaps for 16 and
-//   32). The per-column online softmax (max raised only past a 2^8 slack, exact) and the
-//   value-latent accumulation follow the other decode kernels; one split finishes with the
-//   value up-projection in the epilogue, more go through combine_kernel. The rows of the
-//   next TPC tiles are loaded (non-temporal) while the current ones are computed, and
-//   chunks wholly inside the context skip the clamping and masking.
+//   unit's W_up,k,t rows are read from L2, shared by the unit's splits). A token's c_v,
+//   c_k and k_rope rows are cut into 16-byte pieces, numbered c_v first, then c_k, then
+//   k_rope, and 16 consecutive lanes take the token's pieces j, j + 16, j + 32, ... (one
+//   load instruction per round), so a round reads whole rows, or long runs of them, of 4
+//   consecutive tokens. A lane's key pieces meet the matching slice of the folded query,
+//   the 16 partial dots of a token are summed with DPP, and the per-token-slot online
+//   softmax (max raised only past a 2^8 slack, exact) accumulates every piece with the
+//   token's weight; only the value pieces are kept. One split finishes with the value
+//   up-projection in the epilogue, more go through combine_kernel. The rows of the next
+//   TPC tiles are loaded (non-temporal) while the current ones are computed, and chunks
+//   wholly inside the context skip the clamping and masking. (Lanes that each took every
+//   G-th 8-byte unit of a row read 8 G contiguous bytes per row and instruction and ran at
+//   5.2 TB/s; whole rows per round run at 6.8 TB/s.)
 #include <type_traits>
 
 #include "decode_stream.h"
@@ -50,24 +52,31 @@ struct QaLayout {
   static constexpr int QS = RK + 4 + DR;
 };
 
-template <typename T, int D, int RK, int RV, int DR, int G, int TPC>
+// Row-piece layout: a token's c_v, c_k and k_rope rows are cut into 16-byte pieces,
+// numbered c_v first, then c_k, then k_rope, and the token's 16 consecutive lanes take
+// pieces j, j + 16, j + 32, ... (one load instruction per round). A round thus reads whole
+// rows or long runs of them for 4 consecutive tokens, instead of 8 G contiguous bytes of
+// each row. A lane's score pieces meet the matching slice of the folded query; the 16
+// partial dots of a token are summed with DPP; every piece is also accumulated with the
+// softmax weight, and only the value pieces are kept at the end.
+template <typename T, int D, int RK, int RV, int DR, int TPC>
 __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const void* k_rope) {
   using L = QaLayout<RK, DR>;
-  constexpr int TOK = 64 / G;                           // tokens per tile
-  constexpr int NK = RK / G, NR = DR / G, NV = RV / G;  // row elements per lane group
   constexpr int ES = static_cast<int>(sizeof(T));
-  static_assert((RK * ES) % (8 * G) == 0 && (DR * ES) % (8 * G) == 0 && (RV * ES) % (8 * G) == 0,
-                "rows cut into whole 8-byte units per lane group");
+  constexpr int EPL = 16 / ES;                  // row elements per 16-byte piece
+  constexpr int GP = 16, TOK = 64 / GP;         // lanes per token, tokens per tile
+  constexpr int NPV = RV / EPL, NPK = RK / EPL, NPR = DR / EPL;
+  constexpr int NP = NPV + NPK + NPR;
+  constexpr int NRND = (NP + GP - 1) / GP;      // pieces per lane (rounds)
+  static_assert(RV % EPL == 0 && RK % EPL == 0 && DR % EPL == 0, "whole 16-byte pieces");
   struct Rows {
-    Piece<T, NK> k[TPC];
-    Piece<T, NR> r[TPC];
-    Piece<T, NV> v[TPC];
+    u32x4 x[TPC][NRND];
   };
   __shared__ float abar[RV];
   __shared__ float qs[QaLayout<RK, DR>::QS];
 
   const int lane = threadIdx.x;
-  const int lo = lane % TOK, hi = lane / TOK;
+  const int tok = lane / GP, j = lane % GP;
   const int split = blockIdx.x;
   const int h = blockIdx.y / a.L;
   const int li = blockIdx.y - h * a.L;
@@ -84,7 +93,7 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
   const int nchunk = (ntok + TOK * TPC - 1) / (TOK * TPC);
   const int nfull = ntok / (TOK * TPC);
 
-  // ---- fold the query: q~ = W_up,k,t[content]^T q[content], beta = q[content] . mu_k,t ----
+  // ---- fold the query (as decode_absorbed_kernel) ----------------------------------------
   {
     const float* q = a.q + unit * D;
     const T* W = static_cast<const T*>(a.w_up_k) + static_cast<size_t>(t * a.H + h) * D * RK;
@@ -106,36 +115,58 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
     for (int i = lane; i < DR; i += 64) qs[L::ROT + i] = q[i] * sc;
   }
   __syncthreads();
-  // this lane's slice of the folded query, in its row-unit order
-  const float* qv = qs;
-  float qk[NK], qr[NR];
-#pragma unroll
-  for (int e = 0; e < NK; ++e) qk[e] = qv[row_elem<T, G>(e, hi)];
-#pragma unroll
-  for (int e = 0; e < NR; ++e) qr[e] = qv[L::ROT + row_elem<T, G>(e, hi)];
-  const float beta = hi == 0 ? qv[L::BETA] : 0.f;  // added once per token
 
+  // ---- this lane's pieces: source, row stride and the query slice they meet --------------
   const char* ck = static_cast<const char*>(a.c_k) + (static_cast<size_t>(b * a.Hc + hc) * a.n_max) * RK * ES;
   const char* kr = static_cast<const char*>(k_rope) + (static_cast<size_t>(b * a.H + h) * a.n_max) * DR * ES;
   const char* cv = static_cast<const char*>(a.c_v) + (static_cast<size_t>(b * a.Hc + hc) * a.n_max) * RV * ES;
+  const char* src[NRND];
+  int stride[NRND];
+  bool live[NRND];
+  float qp[NRND][EPL];
+#pragma unroll
+  for (int u = 0; u < NRND; ++u) {
+    const int p = j + GP * u;
+    live[u] = p < NP;
+    if (p < NPV) {
+      src[u] = cv + p * 16;
+      stride[u] = RV * ES;
+    } else if (p < NPV + NPK) {
+      src[u] = ck + (p - NPV) * 16;
+      stride[u] = RK * ES;
+    } else {
+      src[u] = kr + (min(p, NP - 1) - NPV - NPK) * 16;
+      stride[u] = DR * ES;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float qv = 0.f;
+      if (p >= NPV && p < NPV + NPK) qv = qs[(p - NPV) * EPL + e];
+      else if (p >= NPV + NPK && p < NP) qv = qs[L::ROT + (p - NPV - NPK) * EPL + e];
+      qp[u][e] = qv;
+    }
+  }
+  const float beta = j == 0 ? qs[L::BETA] : 0.f;  // added once per token
 
   auto load_chunk = [&](Rows& R, int c) {
     const int tok0 = s0 + c * TPC * TOK;
     const bool clamp = c >= nfull;
 #pragma unroll
     for (int tt = 0; tt < TPC; ++tt) {
-      const int row0 = tok0 + TOK * tt + lo;
+      const int row0 = tok0 + TOK * tt + tok;
       const size_t row = static_cast<size_t>(clamp ? min(row0, s1 - 1) : row0);
-      load_piece<T, NK, G>(R.k[tt], ck + row * (RK * ES), hi);
-      load_piece<T, NR, G>(R.r[tt], kr + row * (DR * ES), hi);
-      load_piece<T, NV, G>(R.v[tt], cv + row * (RV * ES), hi);
+#pragma unroll
+      for (int u = 0; u < NRND; ++u)
+        R.x[tt][u] = live[u] ? load16(src[u] + row * stride[u]) : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
   float m_run = kMaxInit, l_run = 0.f;
-  float acc[NV];
+  float acc[NRND][EPL];
 #pragma unroll
-  for (int e = 0; e < NV; ++e) acc[e] = 0.f;
+  for (int u = 0; u < NRND; ++u)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[u][e] = 0.f;
 
   auto compute_chunk = [&](int c, const Rows& R, auto full) {
     constexpr bool FULL = decltype(full)::value;
@@ -143,25 +174,29 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
     for (int tt = 0; tt < TPC; ++tt) {
       float part = beta;
 #pragma unroll
-      for (int e = 0; e < NK; ++e) part += qk[e] * elem(R.k[tt], e);
+      for (int u = 0; u < NRND; ++u)
 #pragma unroll
-      for (int e = 0; e < NR; ++e) part += qr[e] * elem(R.r[tt], e);
-      part = sum_groups<G>(part);
-      const int tok = s0 + (c * TPC + tt) * TOK + lo;
-      const float s = (FULL || tok < s1) ? part : kNegInf;
+        for (int e = 0; e < EPL; ++e) part += qp[u][e] * elem16<T>(R.x[tt][u], e);
+      part = sum_lanes<GP>(part);
+      const int tk = s0 + (c * TPC + tt) * TOK + tok;
+      const float s = (FULL || tk < s1) ? part : kNegInf;
       const bool raise = s > m_run + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(raise) != 0) {
         const float m_new = raise ? s : m_run;
         const float alpha = raise ? fast_exp2(m_run - m_new) : 1.f;
         l_run *= alpha;
 #pragma unroll
-        for (int e = 0; e < NV; ++e) acc[e] *= alpha;
+        for (int u = 0; u < NRND; ++u)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[u][e] *= alpha;
         m_run = m_new;
       }
-      const float p = fast_exp2(s - m_run);
-      l_run += p;
+      const float pw = fast_exp2(s - m_run);
+      l_run += pw;
 #pragma unroll
-      for (int e = 0; e < NV; ++e) acc[e] += p * elem(R.v[tt], e);
+      for (int u = 0; u < NRND; ++u)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[u][e] += pw * elem16<T>(R.x[tt][u], e);
     }
   };
   auto compute = [&](int c, const Rows& R) {
@@ -169,7 +204,6 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
     else compute_chunk(c, R, std::false_type{});
   };
 
-  // two row buffers used in turn: chunk c computes from one while chunk c + 1 loads
   Rows ra, rb;
   if (nchunk > 0) load_chunk(ra, 0);
   for (int c = 0; c < nchunk; c += 2) {
@@ -180,28 +214,36 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
     compute(c + 1, rb);
   }
 
-  // ---- merge the TOK token columns --------------------------------------------------
+  // ---- merge the TOK token slots -------------------------------------------------------
   float mx = m_run;
 #pragma unroll
-  for (int msk = 1; msk < TOK; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
+  for (int msk = GP; msk < 64; msk <<= 1) mx = fmaxf(mx, shfl_xor(mx, msk));
   const float scl = fast_exp2(m_run - mx);
   float lsum = l_run * scl;
 #pragma unroll
-  for (int msk = 1; msk < TOK; msk <<= 1) lsum += shfl_xor(lsum, msk);
+  for (int msk = GP; msk < 64; msk <<= 1) lsum += shfl_xor(lsum, msk);
 #pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    float v = acc[e] * scl;
+  for (int u = 0; u < NRND; ++u)
 #pragma unroll
-    for (int msk = 1; msk < TOK; msk <<= 1) v += shfl_xor(v, msk);
-    acc[e] = v;
-  }
+    for (int e = 0; e < EPL; ++e) {
+      float v = acc[u][e] * scl;
+#pragma unroll
+      for (int msk = GP; msk < 64; msk <<= 1) v += shfl_xor(v, msk);
+      acc[u][e] = v;
+    }
 
   if (a.S > 1) {
     float* out = a.part + (unit * a.S + split) * (2 + RV);
-    if (lo == 0) {
+    if (tok == 0) {
 #pragma unroll
-      for (int e = 0; e < NV; ++e) out[2 + row_elem<T, G>(e, hi)] = acc[e];
-      if (hi == 0) {
+      for (int u = 0; u < NRND; ++u) {
+        const int p = j + GP * u;
+        if (p < NPV) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) out[2 + p * EPL + e] = acc[u][e];
+        }
+      }
+      if (j == 0) {
         out[0] = mx;
         out[1] = lsum;
       }
@@ -209,11 +251,16 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
     return;
   }
 
-  // ---- single split: out = (acc / sum) W_up,v,t^T + mu_v,t -----------------------------
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  if (lo == 0) {
+  if (tok == 0) {
 #pragma unroll
-    for (int e = 0; e < NV; ++e) abar[row_elem<T, G>(e, hi)] = acc[e] * inv;
+    for (int u = 0; u < NRND; ++u) {
+      const int p = j + GP * u;
+      if (p < NPV) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) abar[p * EPL + e] = acc[u][e] * inv;
+      }
+    }
   }
   __syncthreads();
   const T* Wv = static_cast<const T*>(a.w_up_v) + static_cast<size_t>(t * a.H + h) * D * RV;
@@ -235,31 +282,31 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
   }
 }
 
-template <typename T, int D, int RK, int RV, int DR, int G, int TPC>
+#ifndef LLA_ABS_TPC
+#define LLA_ABS_TPC 4  // tiles of 4 tokens per chunk; two chunks are in flight
+#endif
+
+template <typename T, int D, int RK, int RV, int DR>
 void launch(const DecodeArgs& a, const void* k_rope, hipStream_t s) {
-  hipLaunchKernelGGL((decode_absorbed_kernel<T, D, RK, RV, DR, G, TPC>), dim3(a.S, a.H * a.L, a.B),
+  hipLaunchKernelGGL((decode_absorbed_kernel<T, D, RK, RV, DR, LLA_ABS_TPC>), dim3(a.S, a.H * a.L, a.B),
                      dim3(64), 0, s, a, k_rope);
 }
 
 }  // namespace
 
-#ifndef LLA_ABS_WIDE_TPC
-#define LLA_ABS_WIDE_TPC 2  // tiles per chunk for the wide (8 lane group) shapes
-#endif
-
-// (dtype, d, r_k, r_v, d_rope, lane groups, tiles per chunk)
-#define LLA_ABSORBED_SHAPES(X)                        \
-  X(bf16_t, 1, 128, 96, 160, 32, 8, LLA_ABS_WIDE_TPC) \
-  X(bf16_t, 1, 128, 96, 160, 64, 8, LLA_ABS_WIDE_TPC) \
-  X(bf16_t, 1, 128, 96, 160, 96, 8, LLA_ABS_WIDE_TPC) \
-  X(bf16_t, 1, 128, 16, 32, 32, 4, 4)  \
-  X(bf16_t, 1, 128, 16, 32, 64, 4, 2)  \
-  X(bf16_t, 1, 64, 16, 32, 32, 4, 4)   \
-  X(float, 0, 64, 16, 24, 16, 4, 2)    \
-  X(float, 0, 64, 16, 24, 32, 4, 2)
+// (element type, dtype code, d, r_k, r_v, d_rope)
+#define LLA_ABSORBED_SHAPES(X)          \
+  X(bf16_t, 1, 128, 96, 160, 32)        \
+  X(bf16_t, 1, 128, 96, 160, 64)        \
+  X(bf16_t, 1, 128, 96, 160, 96)        \
+  X(bf16_t, 1, 128, 16, 32, 32)         \
+  X(bf16_t, 1, 128, 16, 32, 64)         \
+  X(bf16_t, 1, 64, 16, 32, 32)          \
+  X(float, 0, 64, 16, 24, 16)           \
+  X(float, 0, 64, 16, 24, 32)
 
 bool decode_absorbed_supported(int dtype, int d, int r_k, int r_v, int d_rope) {
-#define X(T_, DT_, D_, RK_, RV_, DR_, G_, TPC_) \
+#define X(T_, DT_, D_, RK_, RV_, DR_) \
   if (dtype == DT_ && d == D_ && r_k == RK_ && r_v == RV_ && d_rope == DR_) return true;
   LLA_ABSORBED_SHAPES(X)
 #undef X
@@ -268,10 +315,10 @@ bool decode_absorbed_supported(int dtype, int d, int r_k, int r_v, int d_rope) {
 
 bool launch_decode_absorbed(int dtype, int d, int r_k, int r_v, int d_rope, const DecodeArgs& a,
                             const void* k_rope, hipStream_t s) {
-#define X(T_, DT_, D_, RK_, RV_, DR_, G_, TPC_)                                    \
-  if (dtype == DT_ && d == D_ && r_k == RK_ && r_v == RV_ && d_rope == DR_) {      \
-    launch<T_, D_, RK_, RV_, DR_, G_, TPC_>(a, k_rope, s);                         \
-    return true;                                                                   \
+#define X(T_, DT_, D_, RK_, RV_, DR_)                                         \
+  if (dtype == DT_ && d == D_ && r_k == RK_ && r_v == RV_ && d_rope == DR_) { \
+    launch<T_, D_, RK_, RV_, DR_>(a, k_rope, s);                              \
+    return true;                                                              \
   }
   LLA_ABSORBED_SHAPES(X)
 #undef X
