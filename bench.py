@@ -44,8 +44,8 @@ KERNEL_SOURCES = {
     "encode": _COMMON_SOURCES + ("encode.hip",),
     "teacher": _COMMON_SOURCES + ("decode_teacher.hip", "decode_stream.h", "combine.hip"),
     "reconstruct": _COMMON_SOURCES + ("reconstruct.hip", "lla_recon_args.h"),
-    "paged": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_reconstruct.hip", "combine.hip",
-                                "lla_page_args.h"),
+    "paged": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip",
+                                "decode_reconstruct.hip", "combine.hip", "lla_page_args.h"),
 }
 
 

@@ -59,9 +59,9 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D, int RK, int RV, int HPW, int NH, bool SHARED>
+template <int D, int RK, int RV, int HPW, int NH, bool SHARED, bool PAGED = false>
 __global__ __launch_bounds__(64 * NH * HPW) __attribute__((amdgpu_waves_per_eu(NH == 2 ? 2 : 1)))
-void decode_fold_wide_kernel(DecodeArgs a) {
+void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int NKS = D / 32;
   constexpr int NCK = RK / 16;            // latent row tiles of M^T
   // NH == 2: half 0 owns latent row tiles [0, NR0), half 1 owns [NR0, NCK) and the mean row.
@@ -167,8 +167,11 @@ void decode_fold_wide_kernel(DecodeArgs a) {
     __syncthreads();
   }
 
-  const size_t plane = SHARED ? static_cast<size_t>(b) * a.n_max
-                              : static_cast<size_t>(b * a.H + h) * a.n_max;
+  // dense: this head's plane (LLA-2D: the sequence's); paged: the pool (pages are added
+  // per tile)
+  const size_t plane = PAGED ? 0
+                             : (SHARED ? static_cast<size_t>(b) * a.n_max
+                                       : static_cast<size_t>(b * a.H + h) * a.n_max);
   const char* ck = reinterpret_cast<const char*>(a.c_k) + plane * RK * 2;
   const char* cv = reinterpret_cast<const char*>(a.c_v) + plane * RV * 2;
   const char* tab_g = reinterpret_cast<const char*>(a.rope16);
@@ -227,12 +230,16 @@ void decode_fold_wide_kernel(DecodeArgs a) {
       const int slot = (isk ? r : r - NIK) * 64 + lane;
       const int row = min(slot / sp, 15);
       const int col = min(slot % sp, sl - 1) * 16;
-      const size_t poff = SHARED ? 0 : static_cast<size_t>(pl - hw) * a.n_max;
+      // dense: plane pl's rows start poff rows after this head's; paged: head pl's rows
+      // of a page start hrow rows into it
+      const size_t poff = PAGED ? static_cast<size_t>(SHARED ? 0 : hg * HPW + pl) * kPage
+                                : (SHARED ? 0 : static_cast<size_t>(pl - hw) * a.n_max);
       rbytes[k] = isk ? RK * 2 : RV * 2;
       srow[k] = row;
-      step[k] = static_cast<size_t>(16) * rbytes[k];
+      step[k] = PAGED ? static_cast<size_t>(a.Hc) * kPage * rbytes[k]  // one page
+                      : static_cast<size_t>(16) * rbytes[k];
       sbase[k] = (isk ? ck + poff * (RK * 2) : cv + poff * (RV * 2)) + col;
-      nxt[k] = sbase[k] + static_cast<size_t>(s0 + row) * rbytes[k];
+      nxt[k] = sbase[k] + static_cast<size_t>(PAGED ? row : s0 + row) * rbytes[k];
     }
   }
 
@@ -240,8 +247,30 @@ void decode_fold_wide_kernel(DecodeArgs a) {
     __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                      (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
   };
+  // Paged: the page of the next tile to issue is read (scalar load) one issue ahead.
+  auto page_for = [&](int tl) {
+    return PAGED ? page_of(pg, b, __builtin_amdgcn_readfirstlane(min((s0 >> 4) + tl, tile_max))) : 0;
+  };
+  int page_next = page_for(0);
   auto issue = [&](int tl) {
     u32x4* stage = ring + (tl % NB) * STAGE_BLOCKS * 64;
+    if constexpr (PAGED) {
+      const size_t page = static_cast<size_t>(page_next);
+      const int ptok0 = min((s0 >> 4) + tl, tile_max) * kPage;  // the page's first token
+#pragma unroll
+      for (int k = 0; k < NIW; ++k) {
+        const char* src;
+        if (rbytes[k] == 0) {
+          src = sbase[k] + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * NKS * 1024;
+        } else {
+          const int tok = min(s0 + 16 * tl + srow[k], s1 - 1);
+          src = sbase[k] + page * step[k] + static_cast<size_t>(tok - ptok0) * rbytes[k];
+        }
+        dma(src, stage + blk[k] * 64);
+      }
+      page_next = page_for(tl + 1);
+      return;
+    }
     if (tl < nfull) {
 #pragma unroll
       for (int k = 0; k < NIW; ++k) {
@@ -415,18 +444,19 @@ void decode_fold_wide_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int RK, int RV, int HPW, int NH, bool SHARED>
-void launch(const DecodeArgs& a, hipStream_t s) {
+template <int D, int RK, int RV, int HPW, int NH, bool SHARED, bool PAGED = false>
+void launch(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
   if constexpr (!SHARED) {
     dim3 grid(a.S, (a.H / HPW) * a.L, a.B);
-    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, NH, SHARED>), grid, dim3(64 * NH * HPW), 0, s, a);
+    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, NH, SHARED, PAGED>), grid,
+                       dim3(64 * NH * HPW), 0, s, a, pg);
   } else {
     // (b, loop, split) units dealt to XCDs so that one unit's head groups share an XCD
     const long long units = static_cast<long long>(a.B) * a.L * a.S;
     const long long rounds = (units + kXcds - 1) / kXcds;
     const long long blocks = rounds * kXcds * (a.H / HPW);
-    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, NH, SHARED>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(64 * NH * HPW), 0, s, a);
+    hipLaunchKernelGGL((decode_fold_wide_kernel<D, RK, RV, HPW, NH, SHARED, PAGED>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(64 * NH * HPW), 0, s, a, pg);
   }
 }
 
@@ -471,11 +501,27 @@ int fold_wide_heads_per_group(int d, int r_k, int r_v, bool shared) {
 bool launch_decode_fold_wide(int dtype, int d, int r_k, int r_v, bool shared, const DecodeArgs& a,
                              hipStream_t s) {
   if (dtype != 1 || a.H % fold_wide_heads_per_group(d, r_k, r_v, shared) != 0) return false;
-#define X(D_, RK_, RV_, HP_, H2_)                          \
-  if (d == D_ && r_k == RK_ && r_v == RV_) {               \
-    if (shared) launch<D_, RK_, RV_, H2_, LLA_WIDE_NH, true>(a, s);  \
-    else launch<D_, RK_, RV_, HP_, LLA_WIDE_NH, false>(a, s);        \
-    return true;                                           \
+#define X(D_, RK_, RV_, HP_, H2_)                                        \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                             \
+    if (shared) launch<D_, RK_, RV_, H2_, LLA_WIDE_NH, true>(a, PageArgs{}, s);  \
+    else launch<D_, RK_, RV_, HP_, LLA_WIDE_NH, false>(a, PageArgs{}, s);        \
+    return true;                                                         \
+  }
+  LLA_WIDE_SHAPES(X)
+#undef X
+  return false;
+}
+
+bool launch_decode_fold_wide_paged(int dtype, int d, int r_k, int r_v, bool shared,
+                                   const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
+  if (dtype != 1 || pg.table == nullptr ||
+      a.H % fold_wide_heads_per_group(d, r_k, r_v, shared) != 0)
+    return false;
+#define X(D_, RK_, RV_, HP_, H2_)                                          \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                               \
+    if (shared) launch<D_, RK_, RV_, H2_, LLA_WIDE_NH, true, true>(a, pg, s);      \
+    else launch<D_, RK_, RV_, HP_, LLA_WIDE_NH, false, true>(a, pg, s);            \
+    return true;                                                           \
   }
   LLA_WIDE_SHAPES(X)
 #undef X

@@ -69,18 +69,19 @@ int32_t check_pages(const lla_dims& d, const lla_pages* pg) {
   return LLA_OK;
 }
 
-// The paged decode runs the narrow fold kernel or the reconstruct kernel (one wave per
-// head either way).
+// The paged decode runs the same kernel as the dense one: a fold kernel where one is built
+// for the shape, else the reconstruct kernel.
 int paged_path(const lla_dims& d, const lla_decode_opts* opts) {
   const int want = opts ? opts->path : LLA_PATH_AUTO;
-  const bool narrow = fold_kind(d) == kFoldNarrow;
-  if (want == LLA_PATH_AUTO) return narrow ? LLA_PATH_ROTARY_FOLD : LLA_PATH_RECONSTRUCT;
-  if (want == LLA_PATH_ROTARY_FOLD && !narrow) return -1;
+  const bool fold = fold_kind(d) != kFoldNone;
+  if (want == LLA_PATH_AUTO) return fold ? LLA_PATH_ROTARY_FOLD : LLA_PATH_RECONSTRUCT;
+  if (want == LLA_PATH_ROTARY_FOLD && !fold) return -1;
   return want;
 }
 
 Plan plan_paged(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_opts* opts) {
-  lla_decode_opts o{0, LLA_PATH_RECONSTRUCT};  // one wave per (sequence, head, loop, split)
+  lla_decode_opts o{0, paged_path(d, opts) == LLA_PATH_ROTARY_FOLD ? LLA_PATH_ROTARY_FOLD
+                                                                    : LLA_PATH_RECONSTRUCT};
   if (opts != nullptr) o.num_splits = opts->num_splits;
   return plan_splits(d, n_ctx, loop_count, &o);
 }
@@ -627,9 +628,15 @@ int32_t lla_decode_attn_paged(const lla_dims* d, const lla_codec* codec, const l
   const lla::PageArgs pg{pages->block_table, pages->max_blocks, pages->num_pages};
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool ok = path == LLA_PATH_ROTARY_FOLD
-                      ? lla::launch_decode_rotary_fold_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s)
-                      : lla::launch_decode_reconstruct_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s);
+  bool ok;
+  if (path == LLA_PATH_ROTARY_FOLD) {
+    ok = fold_kind(*d) == kFoldNarrow
+             ? lla::launch_decode_rotary_fold_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s)
+             : lla::launch_decode_fold_wide_paged(d->dtype, d->d_head, d->r_k, d->r_v,
+                                                  d->variant == LLA_2D, a, pg, s);
+  } else {
+    ok = lla::launch_decode_reconstruct_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s);
+  }
   if (!ok) return LLA_ERR_UNSUPPORTED;
   st = hip_status();
   if (st != LLA_OK) return st;

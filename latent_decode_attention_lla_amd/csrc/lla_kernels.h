@@ -18,6 +18,8 @@ bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeA
 // Paged cache (pg.table non-null): c_k / c_v of the args are the layer's page pools.
 bool launch_decode_rotary_fold_paged(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                      const PageArgs& pg, hipStream_t s);
+bool launch_decode_fold_wide_paged(int dtype, int d, int r_k, int r_v, bool shared,
+                                   const DecodeArgs& a, const PageArgs& pg, hipStream_t s);
 bool launch_decode_reconstruct_paged(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                      const PageArgs& pg, hipStream_t s);
 bool launch_encode_paged(int dtype, int r, const EncodeArgs& a, const PageArgs& pg, hipStream_t s);

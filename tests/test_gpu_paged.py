@@ -40,13 +40,17 @@ def _oracle_paged(st, layer, loop_begin, loop_count, seqs, n_ctx, ctx_lens=None)
     ("capacity_21x", {}, lla.LLA_PATH_AUTO, 3),
     ("capacity_21x", {"r_k": 32, "r_v": 64}, lla.LLA_PATH_AUTO, 0),
     ("capacity_21x", {}, lla.LLA_PATH_RECONSTRUCT, 0),
-    ("ouro_layer_4x", {}, lla.LLA_PATH_RECONSTRUCT, 2),     # wide latents: reconstruct path
-    ("tiny_f32", {}, lla.LLA_PATH_AUTO, 0),
+    ("ouro_layer_4x", {}, lla.LLA_PATH_AUTO, 2),            # wide fold, a pair of waves per head
+    ("ouro_layer_4x", {}, lla.LLA_PATH_AUTO, 0),
+    ("ouro_layer_4x", {}, lla.LLA_PATH_RECONSTRUCT, 2),
+    ("tiny_f32", {}, lla.LLA_PATH_AUTO, 0),                # float32: reconstruct path
+    ("lla2d_long", {}, lla.LLA_PATH_AUTO, 0),               # wide fold, shared latent plane
+    ("lla2d_long", {}, lla.LLA_PATH_AUTO, 3),
     ("lla2d_long", {}, lla.LLA_PATH_RECONSTRUCT, 0),
 ])
 def test_shuffled_pool_matches_dense_and_oracle(name, over, path, splits):
-    """The dense decode runs with the path the paged decode takes (the narrow rotary fold
-    or the reconstruct kernel), so the two must agree bit for bit."""
+    """The dense and paged decodes run the same kernel (narrow fold, wide fold or
+    reconstruct) on the same rows, so they must agree bit for bit."""
     w = WORKLOADS[name].replace(batch=3, n=300, D=2, **({"H": 4} if name != "tiny_f32" else {}),
                                 **over)
     st = DeviceLatentStore(w, seed=71)
@@ -67,10 +71,11 @@ def test_shuffled_pool_matches_dense_and_oracle(name, over, path, splits):
     assert same
 
 
-def test_pages_past_the_context_are_not_read():
+@pytest.mark.parametrize("name", ["capacity_21x", "ouro_layer_4x", "lla2d_long"])
+def test_pages_past_the_context_are_not_read(name):
     """Pages of the pool the table does not name for a token below len_b hold NaN (spares
     and the rows past each length): outputs stay finite; an empty context gives zeros."""
-    w = WORKLOADS["capacity_21x"].replace(batch=4, n=160, D=1, H=4)
+    w = WORKLOADS[name].replace(batch=4, n=160, D=1, H=4)
     st = DeviceLatentStore(w, seed=73)
     lens = [160, 77, 1, 0]
     for b, n_b in enumerate(lens):
@@ -86,7 +91,7 @@ def test_pages_past_the_context_are_not_read():
             assert np.all(got[3] == 0.0)
             ref = _oracle_paged(st, 0, 0, 4, range(3), w.n, lens[:3])
             err = max_abs(got[:3], ref)
-            announce(f"paged NaN tails path={path} splits={splits}: {rel_note(err, BF16_TOL)}")
+            announce(f"paged NaN tails {name} path={path} splits={splits}: {rel_note(err, BF16_TOL)}")
             assert err <= BF16_TOL
 
 
@@ -167,12 +172,13 @@ def test_streaming_eviction_sink_and_window():
     assert err <= BF16_TOL
 
 
-def test_capacity_21x_full_launch_paged_sampled():
-    """Batch 768 at context 4096, 16 heads, r = (16, 32), shuffled pages: one (layer, loop)
-    call as the bench times it; bit-identical to the dense cache, sampled sequences against
-    the oracle."""
-    w = WORKLOADS["capacity_21x"].replace(D=1)
-    announce("paged capacity_21x full launch, B=768 n=4096")
+@pytest.mark.parametrize("name,seqs", [("capacity_21x", [0, 383, 767]), ("ouro_layer_4x", [0, 31])])
+def test_full_launch_paged_sampled(name, seqs):
+    """The 21.3x capacity shape (768 x 4096, narrow fold) and the Ouro-1.4B 4x layer
+    (32 x 4096, wide fold) with shuffled pages: one (layer, loop) call as the bench times
+    it; bit-identical to the dense cache, sampled sequences against the oracle."""
+    w = WORKLOADS[name].replace(D=1)
+    announce(f"paged {name} full launch, B={w.batch} n={w.n}")
     st = DeviceLatentStore(w, seed=79)
     dense = st.decode(0, 2, 1).clone()
     st.paginate(seed=80)
@@ -181,7 +187,6 @@ def test_capacity_21x_full_launch_paged_sampled():
     out = st.decode_paged(0, 2, 1)
     torch.cuda.synchronize()
     assert torch.equal(out, dense)
-    seqs = [0, 383, 767]
     ref = _oracle_paged(st, 0, 2, 1, seqs, w.n)
     err = max_abs(f64(out[seqs]), ref)
     announce(f"  sampled: {rel_note(err, BF16_TOL)}")
@@ -205,10 +210,10 @@ def test_invalid_arguments():
     assert call(lla.make_pages(0, 4, st.pages.num_pages)) == lla.LLA_ERR_INVALID_ARG
     assert call(lla.make_pages(st.block_table.data_ptr() + 2, 4, 8)) == lla.LLA_ERR_INVALID_ARG
     assert call(lla.make_pages(st.block_table, 4, 0)) == lla.LLA_ERR_INVALID_ARG
-    w4 = WORKLOADS["ouro_layer_4x"].replace(batch=1, n=64, D=1, H=2)
+    w4 = WORKLOADS["tiny_f32"].replace(batch=1, n=64, D=1)  # float32: no fold kernel
     s4 = DeviceLatentStore(w4, seed=83)
     s4.paginate(seed=84)
-    o4 = torch.empty(1, 2, 1, w4.d, device="cuda")
+    o4 = torch.empty(1, w4.H, 1, w4.d, device="cuda")
     got = lla.lla_decode_attn_paged_status(s4.dims, s4.codec, s4.cache, s4.pages, 0, w4.n, None,
                                            s4.t["q"][0, 0], 0, 1, o4, ws, ws.numel(),
                                            lla.make_opts(0, lla.LLA_PATH_ROTARY_FOLD))
