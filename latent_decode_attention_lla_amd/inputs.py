@@ -23,6 +23,8 @@ Table 5):
                     second pass (Appendix J's 64k passkey cells; Table 12)
 * ``paged_21x``     ``capacity_21x`` stored in a paged cache: 16-token pages of each
                     layer's pool in a random order, found through a block table
+* ``paged_ouro_4x`` the Ouro-1.4B 4x geometry (96, 160) for all 24 layers, 32 sequences at
+                    context 4096, in a paged cache (the wide fold kernel)
 * ``teacher_4k``    the uncompressed loop-indexed cache the latent store replaces (Section
                     3 "Teacher cache"; Table 5's teacher column): T=4, D=24, H=16, d=128,
                     bf16 keys and values for every loop, batch 32 (the teacher's measured
@@ -103,6 +105,8 @@ WORKLOADS = {
                             batch=8, n=32768, d_rope=64),
     "paged_21x": Workload("paged_21x", T=4, D=24, H=16, d=128, r_k=16, r_v=32, batch=768,
                           n=4096, paged=True),
+    "paged_ouro_4x": Workload("paged_ouro_4x", T=4, D=24, H=16, d=128, r_k=96, r_v=160,
+                              batch=32, n=4096, paged=True),
     "prefill_64k": Workload("prefill_64k", T=4, D=24, H=16, d=128, r_k=96, r_v=160, batch=1,
                             n=65536, stream_prefill=True),
     "teacher_4k": Workload("teacher_4k", T=4, D=24, H=16, d=128, r_k=0, r_v=0, batch=32,
