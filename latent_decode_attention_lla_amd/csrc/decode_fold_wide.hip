@@ -78,7 +78,9 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int RING_UNITS =
       LLA_WIDE_STAGES * ((SHARED ? 1 : HPW) * (((16 * (RK / 8 + 1) + 63) / 64) + ((16 * (RV / 8 + 1) + 63) / 64)) + D / 32) * 64;
   constexpr int LDS_UNITS_RING = RING_UNITS + (XCH_FLOATS + 3) / 4;
-  constexpr int LDS_UNITS = LDS_UNITS_RING > STAGE_UNITS ? LDS_UNITS_RING : STAGE_UNITS;
+  constexpr int PAGE_UNITS = PAGED ? kMaxSplitPages * 4 / 16 : 0;  // the split's page indices
+  constexpr int LDS_UNITS = LDS_UNITS_RING + PAGE_UNITS > STAGE_UNITS ? LDS_UNITS_RING + PAGE_UNITS
+                                                                      : STAGE_UNITS;
   static_assert(RK % 16 == 0 && RV % 16 == 0 && VSH % 4 == 0 && D % 32 == 0, "shape");
 
   __shared__ u32x4 lds[LDS_UNITS];
@@ -247,26 +249,45 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
     __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                      (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
   };
-  // Paged: the page of the next tile to issue is read (scalar load) one issue ahead.
+  // Paged: the pages of the split's tiles are read into LDS once, before the ring starts
+  // (a vector load inside the ring would wait for every transfer issued before it).
+  int* split_pages = reinterpret_cast<int*>(lds + LDS_UNITS_RING);
+  if constexpr (PAGED) {
+    for (int i = static_cast<int>(threadIdx.x); i < ntile; i += 64 * NW)
+      split_pages[i] = page_of(pg, b, (s0 >> 4) + i);
+    __syncthreads();
+  }
   auto page_for = [&](int tl) {
-    return PAGED ? page_of(pg, b, __builtin_amdgcn_readfirstlane(min((s0 >> 4) + tl, tile_max))) : 0;
+    return PAGED ? __builtin_amdgcn_readfirstlane(split_pages[min(tl, ntile - 1)]) : 0;
   };
-  int page_next = page_for(0);
+  int page_next = ntile > 0 ? page_for(0) : 0;
   auto issue = [&](int tl) {
     u32x4* stage = ring + (tl % NB) * STAGE_BLOCKS * 64;
     if constexpr (PAGED) {
       const size_t page = static_cast<size_t>(page_next);
-      const int ptok0 = min((s0 >> 4) + tl, tile_max) * kPage;  // the page's first token
+      if (tl < nfull) {  // rows unclamped: the slot's row within the page is its own
 #pragma unroll
-      for (int k = 0; k < NIW; ++k) {
-        const char* src;
-        if (rbytes[k] == 0) {
-          src = sbase[k] + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * NKS * 1024;
-        } else {
-          const int tok = min(s0 + 16 * tl + srow[k], s1 - 1);
-          src = sbase[k] + page * step[k] + static_cast<size_t>(tok - ptok0) * rbytes[k];
+        for (int k = 0; k < NIW; ++k) {
+          if (rbytes[k] == 0) {
+            dma(nxt[k], stage + blk[k] * 64);
+            nxt[k] += step[k];
+          } else {
+            dma(nxt[k] + page * step[k], stage + blk[k] * 64);
+          }
         }
-        dma(src, stage + blk[k] * 64);
+      } else {
+        const int ptok0 = min((s0 >> 4) + tl, tile_max) * kPage;  // the page's first token
+#pragma unroll
+        for (int k = 0; k < NIW; ++k) {
+          const char* src;
+          if (rbytes[k] == 0) {
+            src = sbase[k] + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * NKS * 1024;
+          } else {
+            const int tok = min(s0 + 16 * tl + srow[k], s1 - 1);
+            src = sbase[k] + page * step[k] + static_cast<size_t>(tok - ptok0) * rbytes[k];
+          }
+          dma(src, stage + blk[k] * 64);
+        }
       }
       page_next = page_for(tl + 1);
       return;

@@ -7,6 +7,9 @@
 namespace lla {
 
 constexpr int kPage = 16;  // tokens per page (one 16-token tile of the decode kernels)
+// Pages of one context split that the wide fold kernel keeps in LDS; the planner keeps
+// paged splits of that kernel within it.
+constexpr int kMaxSplitPages = 256;
 
 // A layer's pool is [num_pages][Hc][kPage][r]; logical token j of sequence b lives in row
 // j % kPage of page table[b * max_blocks + j / kPage]. A null table means the dense layout.

@@ -87,9 +87,9 @@ class DeviceLatentStore:
                                      ws.numel(), opts, stream)
         return out
 
-    def paginate(self, seed: int, spare_pages: int = 0):
-        """Move this store's dense latent cache into a shuffled page pool: logical page p of
-        sequence b goes to a random physical page (spare pages are filled with NaN, so a
+    def paginate(self, seed: int, spare_pages: int = 0, shuffle: bool = True):
+        """Move this store's dense latent cache into a page pool: logical page p of
+        sequence b goes to a random physical page (in order with shuffle=False) (spare pages are filled with NaN, so a
         read of a page the table does not name shows). Sets self.pages / self.block_table
         and replaces c_k, c_v by the pools [D][num_pages][Hc][16][r]; the dense tensors stay
         in self.dense."""
@@ -97,7 +97,8 @@ class DeviceLatentStore:
         npg = (self.n_max + 15) // 16
         num_pages = w.batch * npg + spare_pages
         g = torch.Generator(device="cpu").manual_seed(seed)
-        perm = torch.randperm(num_pages, generator=g)[:w.batch * npg]
+        perm = (torch.randperm(num_pages, generator=g) if shuffle
+                else torch.arange(num_pages))[:w.batch * npg]
         table = perm.reshape(w.batch, npg).to(torch.int32)
         self.dense = {"c_k": self.t["c_k"], "c_v": self.t["c_v"]}
         for key in ("c_k", "c_v"):
