@@ -432,9 +432,9 @@ def main():
         S = lla.lla_decode_num_splits(st.dims, w.n, 1, lla.make_opts(args.splits, lla.LLA_PATH_RECONSTRUCT))
         ws = st.absorbed_workspace(w.n, 1, opts)
     elif w.paged:
-        nb = lla.lla_decode_paged_workspace_bytes(st.dims, w.n, 1, opts)
-        S = max(1, nb // (w.batch * w.H * (2 + w.r_v) * 4))  # the paged plan's splits
-        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        S = lla.lla_decode_paged_num_splits(st.dims, w.n, 1, opts)
+        ws = torch.empty(max(lla.lla_decode_paged_workspace_bytes(st.dims, w.n, 1, opts), 256),
+                         dtype=torch.uint8, device=dev)
     else:
         S = lla.lla_decode_num_splits(st.dims, w.n, 1, opts)
         ws = st.workspace(w.n, 1, opts)

@@ -259,6 +259,10 @@ int32_t lla_decode_attn_paged(const lla_dims* dims, const lla_codec* codec, cons
                               const int32_t* ctx_lens, const float* q, int32_t loop_begin,
                               int32_t loop_count, float* out, void* workspace,
                               size_t workspace_bytes, const lla_decode_opts* opts, void* stream);
+/* Number of context splits lla_decode_attn_paged would use (after `opts`), for reporting;
+ * 0 on invalid arguments. */
+int32_t lla_decode_paged_num_splits(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,
+                                    const lla_decode_opts* opts);
 
 /* Uncompressed decode over the loop-indexed cache that the latent store replaces (Section
  * 3, "Teacher cache": every loop of every layer keeps its own key and value; Section 7,

@@ -568,6 +568,12 @@ size_t lla_decode_paged_workspace_bytes(const lla_dims* d, int32_t n_ctx, int32_
   return (bytes + 255) / 256 * 256;
 }
 
+int32_t lla_decode_paged_num_splits(const lla_dims* d, int32_t n_ctx, int32_t loop_count,
+                                    const lla_decode_opts* opts) {
+  if (check_dims(d) != LLA_OK || n_ctx < 0 || n_ctx > d->n_max || loop_count < 1) return 0;
+  return plan_paged(*d, n_ctx, loop_count, opts).S;
+}
+
 int32_t lla_decode_attn_paged(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
                               const lla_pages* pages, int32_t layer, int32_t n_ctx,
                               const int32_t* ctx_lens, const float* q, int32_t loop_begin,

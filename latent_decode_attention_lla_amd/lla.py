@@ -38,7 +38,7 @@ EXPORTED = (
     "lla_decode_absorbed_workspace_bytes", "lla_decode_attn_absorbed",
     "lla_decode_absorbed_supported",
     "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
-    "lla_decode_teacher_num_splits", "lla_reconstruct",
+    "lla_decode_teacher_num_splits", "lla_decode_paged_num_splits", "lla_reconstruct",
     "lla_encode_paged", "lla_decode_paged_workspace_bytes", "lla_decode_attn_paged",
 )
 
@@ -128,6 +128,8 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_teacher_supported.restype = i32
     lib.lla_decode_teacher_num_splits.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
     lib.lla_decode_teacher_num_splits.restype = i32
+    lib.lla_decode_paged_num_splits.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
+    lib.lla_decode_paged_num_splits.restype = i32
     lib.lla_reconstruct.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, i32, i32, i32,
                                     i32, vp, vp, vp]
     lib.lla_reconstruct.restype = i32
@@ -286,6 +288,11 @@ def lla_decode_teacher_supported(dims: lla_dims) -> bool:
 
 def lla_decode_teacher_num_splits(dims: lla_dims, n_ctx: int, loop_count: int, opts=None) -> int:
     return load().lla_decode_teacher_num_splits(
+        ctypes.byref(dims), n_ctx, loop_count, ctypes.byref(opts) if opts is not None else None)
+
+
+def lla_decode_paged_num_splits(dims: lla_dims, n_ctx: int, loop_count: int, opts=None) -> int:
+    return load().lla_decode_paged_num_splits(
         ctypes.byref(dims), n_ctx, loop_count, ctypes.byref(opts) if opts is not None else None)
 
 

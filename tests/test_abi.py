@@ -98,6 +98,20 @@ def test_splits_count_the_kernels_waves_per_head():
         assert lla.lla_decode_num_splits(dims, n, 1, recon) == 2 * wide
 
 
+def test_paged_splits_of_the_wide_fold_span_at_most_4096_tokens():
+    """The wide fold kernel keeps a split's page indices in LDS (256 pages of 16 tokens);
+    the narrow fold and reconstruct paths plan like the dense cache."""
+    wide = lla.make_dims(4, 1, 16, 128, 96, 160, 32, 32768)
+    assert lla.lla_decode_num_splits(wide, 32768, 1) == 2
+    assert lla.lla_decode_paged_num_splits(wide, 32768, 1) == 8
+    assert lla.lla_decode_paged_num_splits(wide, 4096, 1) == lla.lla_decode_num_splits(wide, 4096, 1)
+    assert lla.lla_decode_paged_num_splits(wide, 32769, 1) == 0  # n_ctx > n_max
+    narrow = lla.make_dims(4, 1, 16, 128, 32, 32, 32, 32768)
+    assert lla.lla_decode_paged_num_splits(narrow, 32768, 1) == lla.lla_decode_num_splits(narrow, 32768, 1)
+    nb = lla.lla_decode_paged_workspace_bytes(wide, 32768, 1)
+    assert nb == 32 * 16 * 8 * (2 + 160) * 4
+
+
 # Argument validation with fake (never dereferenced) addresses. Every case below must be
 # rejected on the host; they are skipped where a GPU is visible so that a validation bug
 # can never turn into a launch with bogus pointers.
