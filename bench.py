@@ -38,13 +38,13 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 # validation and dispatch in lla_api.cpp do not change what a kernel reads).
 _COMMON_SOURCES = ("lla_device.h", "lla_args.h", "lla_plan.h")
 KERNEL_SOURCES = {
-    "decode": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip",
+    "decode": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip", "decode_lla2d.hip",
                                  "decode_reconstruct.hip", "combine.hip", "rope_table.hip"),
     "absorbed": _COMMON_SOURCES + ("decode_absorbed.hip", "decode_stream.h", "combine.hip"),
     "encode": _COMMON_SOURCES + ("encode.hip",),
     "teacher": _COMMON_SOURCES + ("decode_teacher.hip", "decode_stream.h", "combine.hip"),
     "reconstruct": _COMMON_SOURCES + ("reconstruct.hip", "lla_recon_args.h"),
-    "paged": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip",
+    "paged": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip", "decode_lla2d.hip",
                                 "decode_reconstruct.hip", "combine.hip", "lla_page_args.h"),
 }
 

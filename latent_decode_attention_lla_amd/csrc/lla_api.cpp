@@ -269,8 +269,10 @@ int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cac
   if (path == LLA_PATH_ROTARY_FOLD) {
     ok = fold_kind(*d) == kFoldNarrow
              ? lla::launch_decode_rotary_fold(d->dtype, d->d_head, d->r_k, d->r_v, a, s)
-             : lla::launch_decode_fold_wide(d->dtype, d->d_head, d->r_k, d->r_v,
-                                            d->variant == LLA_2D, a, s);
+             : (d->variant == LLA_2D &&
+                lla::launch_decode_lla2d(d->dtype, d->d_head, d->r_k, d->r_v, a, s)) ||
+                   lla::launch_decode_fold_wide(d->dtype, d->d_head, d->r_k, d->r_v,
+                                                d->variant == LLA_2D, a, s);
   } else {
     ok = lla::launch_decode_reconstruct(d->dtype, d->d_head, d->r_k, d->r_v, a, s);
   }
@@ -645,8 +647,10 @@ int32_t lla_decode_attn_paged(const lla_dims* d, const lla_codec* codec, const l
   if (path == LLA_PATH_ROTARY_FOLD) {
     ok = fold_kind(*d) == kFoldNarrow
              ? lla::launch_decode_rotary_fold_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s)
-             : lla::launch_decode_fold_wide_paged(d->dtype, d->d_head, d->r_k, d->r_v,
-                                                  d->variant == LLA_2D, a, pg, s);
+             : (d->variant == LLA_2D &&
+                lla::launch_decode_lla2d_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s)) ||
+                   lla::launch_decode_fold_wide_paged(d->dtype, d->d_head, d->r_k, d->r_v,
+                                                      d->variant == LLA_2D, a, pg, s);
   } else {
     ok = lla::launch_decode_reconstruct_paged(d->dtype, d->d_head, d->r_k, d->r_v, a, pg, s);
   }

@@ -25,6 +25,13 @@ bool launch_decode_reconstruct_paged(int dtype, int d, int r_k, int r_v, const D
 bool launch_encode_paged(int dtype, int r, const EncodeArgs& a, const PageArgs& pg, hipStream_t s);
 // Wide latents (r_k >= 64): a pair of waves per head; `shared` selects LLA-2D (all heads
 // read one latent plane). H must be a multiple of fold_wide_heads_per_group(...).
+// LLA-2D decode with the value side on the matrix cores, one wave per head (bfloat16; d 128
+// with (r_k, r_v) of (96, 160) or (64, 64), H a multiple of the heads per
+// workgroup); where it is not built the wide fold kernel runs LLA-2D.
+bool decode_lla2d_supported(int dtype, int d, int r_k, int r_v, int H);
+bool launch_decode_lla2d(int dtype, int d, int r_k, int r_v, const DecodeArgs& a, hipStream_t s);
+bool launch_decode_lla2d_paged(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
+                               const PageArgs& pg, hipStream_t s);
 bool launch_decode_fold_wide(int dtype, int d, int r_k, int r_v, bool shared, const DecodeArgs& a,
                              hipStream_t s);
 bool decode_fold_wide_supported(int dtype, int d, int r_k, int r_v);

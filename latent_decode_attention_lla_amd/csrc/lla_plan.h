@@ -64,8 +64,11 @@ int resolve_path(const lla_dims& d, const lla_decode_opts* opts) {
   return want;
 }
 
+// Waves the chosen kernel spends per (sequence, head, loop, split): a pair for the wide
+// fold kernel, one for the LLA-2D kernel and the others.
 int waves_per_unit(const lla_dims& d, const lla_decode_opts* opts) {
-  if (resolve_path(d, opts) == LLA_PATH_ROTARY_FOLD && fold_kind(d) == kFoldWide)
+  if (resolve_path(d, opts) == LLA_PATH_ROTARY_FOLD && fold_kind(d) == kFoldWide &&
+      !(d.variant == LLA_2D && lla::decode_lla2d_supported(d.dtype, d.d_head, d.r_k, d.r_v, d.H)))
     return lla::fold_wide_waves_per_head();
   return 1;
 }

@@ -89,13 +89,13 @@ def test_teacher_workspace_planning():
 
 def test_splits_count_the_kernels_waves_per_head():
     """About 2048 waves in flight: the wide fold kernel spends a pair of waves per head,
-    the reconstruct kernel one."""
+    the LLA-2D and reconstruct kernels one."""
     recon = lla.make_opts(0, lla.LLA_PATH_RECONSTRUCT)
-    for B, n, variant, wide in ((32, 4096, lla.LLA_PER_HEAD, 2), (8, 8192, lla.LLA_PER_HEAD, 8),
-                                (16, 16384, lla.LLA_2D, 4)):
+    for B, n, variant, fold, rec in ((32, 4096, lla.LLA_PER_HEAD, 2, 4), (8, 8192, lla.LLA_PER_HEAD, 8, 16),
+                                     (16, 16384, lla.LLA_2D, 8, 8)):
         dims = lla.make_dims(4, 1, 16, 128, 96, 160, B, n, variant)
-        assert lla.lla_decode_num_splits(dims, n, 1) == wide
-        assert lla.lla_decode_num_splits(dims, n, 1, recon) == 2 * wide
+        assert lla.lla_decode_num_splits(dims, n, 1) == fold
+        assert lla.lla_decode_num_splits(dims, n, 1, recon) == rec
 
 
 def test_paged_splits_of_the_wide_fold_span_at_most_4096_tokens():
