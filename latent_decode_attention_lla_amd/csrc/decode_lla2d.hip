@@ -95,7 +95,6 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int NIK = (16 * KSP + 63) / 64;
   constexpr int NIV = (16 * VSP + 63) / 64;
   constexpr int STAGE_BLOCKS = NIK + NIV + NKS;  // 1 KiB blocks
-  constexpr int NIW = (STAGE_BLOCKS + NW - 1) / NW;
   constexpr int RING_UNITS = kStages * STAGE_BLOCKS * 64;
   constexpr int XCH_UNITS = 0;
   constexpr int P_UNITS = 2 * 16 * 16 * 2 / 16;
@@ -105,7 +104,7 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   static_assert(NW * 16 * WT_STRIDE * 2 / 16 <= RING_UNITS, "prologue staging fits the ring");
   static_assert(HG * RV + 2 * HG <= RING_UNITS * 4, "epilogue staging fits the ring");
   static_assert(RK % 16 == 0 && RV % 16 == 0 && D % 32 == 0 && HG <= 16, "shape");
-  static_assert(NIW <= 31, "vmcnt range");
+  static_assert((NIK + NW - 1) / NW + (NIV + NW - 1) / NW + (NKS + NW - 1) / NW <= 31, "vmcnt range");
 
   __shared__ u32x4 lds[LDS_UNITS];
   uint16_t* ptile = reinterpret_cast<uint16_t*>(lds + RING_UNITS + XCH_UNITS);  // [2][16][16]
@@ -194,35 +193,34 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   const char* cv = reinterpret_cast<const char*>(a.c_v) + plane * RV * 2;
   const char* tab_g = reinterpret_cast<const char*>(a.rope16);
   const int tile_max = s1 > 0 ? (s1 - 1) >> 4 : 0;
-  // Per block slot k of this wave (the slot's block, its row size and plane base are
-  // wave-uniform): this lane's byte offset within the plane (row * row size + column) or,
-  // for a table block, within the 16-token table tile. Sources are a uniform base plus a
-  // 32-bit lane offset, so the loads use scalar base addressing.
-  int blk[NIW], srow[NIW], rbytes[NIW];
-  uint32_t loff[NIW];
-  const char* pbase[NIW];
+  // Block slots of this wave by kind: NSK key, NSV value and NST table slots; slot j of a
+  // kind loads block min(wave + NW j, blocks of the kind - 1) of it (a repeated block is
+  // loaded by two waves to the same place). Per slot this lane keeps the token row it
+  // loads and its byte offset in the tile (row * row size + column).
+  constexpr int NSK = (NIK + NW - 1) / NW, NSV = (NIV + NW - 1) / NW, NST = (NKS + NW - 1) / NW;
+  int kblk[NSK], krow[NSK], vblk[NSV], vrow[NSV], tblk[NST];
+  uint32_t koff[NSK], voff[NSV], toff[NST];
 #pragma unroll
-  for (int k = 0; k < NIW; ++k) {
-    int bi = wave + NW * k;
-    if (bi >= STAGE_BLOCKS) bi = wave;  // even out the per-wave count with a repeated block
-    blk[k] = bi;
-    if (bi >= NIK + NIV) {
-      const int ks = bi - NIK - NIV;
-      rbytes[k] = 0;
-      srow[k] = 0;
-      pbase[k] = tab_g;
-      loff[k] = static_cast<uint32_t>(ks * 1024 + lane * 16);
-    } else {
-      const bool isk = bi < NIK;
-      const int sp = isk ? KSP : VSP, sl = isk ? KSL : VSL;
-      const int sidx = (isk ? bi : bi - NIK) * 64 + lane;
-      const int row = min(sidx / sp, 15);
-      const int col = min(sidx % sp, sl - 1) * 16;
-      rbytes[k] = isk ? RK * 2 : RV * 2;
-      srow[k] = row;
-      pbase[k] = isk ? ck : cv;
-      loff[k] = static_cast<uint32_t>(row * rbytes[k] + col);
-    }
+  for (int j = 0; j < NSK; ++j) {
+    const int bi = min(wave + NW * j, NIK - 1);
+    const int sidx = bi * 64 + lane;
+    kblk[j] = bi;
+    krow[j] = min(sidx / KSP, 15);
+    koff[j] = static_cast<uint32_t>(krow[j] * (RK * 2) + min(sidx % KSP, KSL - 1) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < NSV; ++j) {
+    const int bi = min(wave + NW * j, NIV - 1);
+    const int sidx = bi * 64 + lane;
+    vblk[j] = NIK + bi;
+    vrow[j] = min(sidx / VSP, 15);
+    voff[j] = static_cast<uint32_t>(vrow[j] * (RV * 2) + min(sidx % VSP, VSL - 1) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < NST; ++j) {
+    const int bi = min(wave + NW * j, NKS - 1);
+    tblk[j] = NIK + NIV + bi;
+    toff[j] = static_cast<uint32_t>(bi * 1024 + lane * 16);
   }
   auto dma = [&](const char* src, u32x4* dst) {
     __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -238,27 +236,36 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
     return PAGED ? __builtin_amdgcn_readfirstlane(split_pages[min(tl, ntile - 1)]) : 0;
   };
   int page_next = PAGED && ntile > 0 ? page_for(0) : 0;  // read one issue ahead
-  // tiles past the last (the ring's run-out) load the last tile's rows again
+  // Sources are a wave-uniform base plus this lane's 32-bit offset. Tiles past the last
+  // (the ring's run-out) load the last tile's rows again.
   auto issue = [&](int tl) {
     u32x4* stage = lds + (tl % kStages) * STAGE_BLOCKS * 64;
-    const int tile = (s0 >> 4) + tl;  // table tile of a full tile
-    const int page = page_next;
+    const char* tb = tab_g + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * (NKS * 1024);
 #pragma unroll
-    for (int k = 0; k < NIW; ++k) {
-      // uniform base of the tile's rows (or table tile) plus this lane's 32-bit offset
-      const char* base;
-      uint32_t off = loff[k];
-      if (rbytes[k] == 0) {
-        base = pbase[k] + static_cast<size_t>(min(tile, tile_max)) * (NKS * 1024);
-      } else {
-        base = pbase[k] + static_cast<size_t>(PAGED ? 16 * page : s0 + 16 * tl) * rbytes[k];
-        if (tl >= nfull) {  // rows past the context end clamp to its last token (zero weight)
-          const int tok = min(s0 + 16 * tl + srow[k], s1 - 1);
-          if constexpr (PAGED) off += static_cast<uint32_t>(((tok & 15) - srow[k]) * rbytes[k]);
-          else base = pbase[k] + static_cast<size_t>(tok - srow[k]) * rbytes[k];
-        }
+    for (int j = 0; j < NST; ++j) dma(tb + toff[j], stage + tblk[j] * 64);
+    // first row of the tile (tiles past the last: of the last tile) in the sequence's plane,
+    // or the first row of the tile's page in the pool
+    const int tlc = min(tl, ntile - 1);
+    const size_t row0 = PAGED ? static_cast<size_t>(16) * page_next : static_cast<size_t>(s0 + 16 * tlc);
+    const char* kb = ck + row0 * (RK * 2);
+    const char* vb = cv + row0 * (RV * 2);
+    if (tl < nfull) {
+#pragma unroll
+      for (int j = 0; j < NSK; ++j) dma(kb + koff[j], stage + kblk[j] * 64);
+#pragma unroll
+      for (int j = 0; j < NSV; ++j) dma(vb + voff[j], stage + vblk[j] * 64);
+    } else {  // rows past the context end clamp to its last token (they get zero weight)
+      const int t0 = s0 + 16 * tlc;
+#pragma unroll
+      for (int j = 0; j < NSK; ++j) {
+        const int d = min(t0 + krow[j], s1 - 1) - t0 - krow[j];  // <= 0 rows
+        dma(kb + static_cast<uint32_t>(static_cast<int>(koff[j]) + d * (RK * 2)), stage + kblk[j] * 64);
       }
-      dma(base + off, stage + blk[k] * 64);
+#pragma unroll
+      for (int j = 0; j < NSV; ++j) {
+        const int d = min(t0 + vrow[j], s1 - 1) - t0 - vrow[j];
+        dma(vb + static_cast<uint32_t>(static_cast<int>(voff[j]) + d * (RV * 2)), stage + vblk[j] * 64);
+      }
     }
     if constexpr (PAGED) page_next = page_for(tl + 1);
   };
@@ -274,20 +281,24 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
     const char* vreg = reinterpret_cast<const char*>(lds + (cc % kStages) * STAGE_BLOCKS * 64 + NIK * 64);
     const f32x4 al = *reinterpret_cast<const f32x4*>(alpha_buf + (cc & 1) * 16 + 4 * hi);
     const i16x4 pa = *reinterpret_cast<const i16x4*>(ptile + (cc & 1) * 256 + lo * 16 + 4 * hi);
+    // all of this wave's value fragments are read before the first product (a value tile
+    // past the last reads the last one and is not used)
+    i16x4 vb[VT];
 #pragma unroll
     for (int k = 0; k < VT; ++k) {
-      const int rt = wave + NW * k;
-      if (rt < NRT) {
-        const char* col = vreg + (16 * rt + lo) * 2 + 4 * hi * (VSP * 16);
-        i16x4 vb;
+      const char* col = vreg + (16 * min(wave + NW * k, NRT - 1) + lo) * 2 + 4 * hi * (VSP * 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vb[i] = *reinterpret_cast<const short*>(col + i * (VSP * 16));
+      for (int i = 0; i < 4; ++i) vb[k][i] = *reinterpret_cast<const short*>(col + i * (VSP * 16));
+    }
+#pragma unroll
+    for (int k = 0; k < VT; ++k) {
+      if (wave + NW * k < NRT) {
         f32x4 acc = vacc[k];
         acc[0] *= al[0];
         acc[1] *= al[1];
         acc[2] *= al[2];
         acc[3] *= al[3];
-        vacc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc, 0, 0, 0);
+        vacc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[k], acc, 0, 0, 0);
       }
     }
   };
@@ -342,7 +353,7 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
         // tile c has landed once only tile c + 1's loads are outstanding; the barrier then
         // publishes every wave's blocks of tile c and the weights of tile c - 1, and tells
         // that tile c - 2's stage is free for tile c + 2
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NIW) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NSK + NSV + NST) : "memory");
         ring_barrier();
         issue(c + 2);
         if (c > 0) value_step(c - 1);
