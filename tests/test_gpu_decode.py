@@ -217,6 +217,23 @@ def test_lla2d_ragged_poisoned(path):
         assert max_abs(got[:3], ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("variant", ["per_head", "lla2d"])
+@pytest.mark.parametrize("d,r_k,r_v", [(128, 64, 64), (128, 128, 128), (64, 256, 256)])
+def test_bf16_table8_ranks_every_output(d, r_k, r_v, variant):
+    """The other rank points the fold kernels are built for (Table 8's ranks, and a
+    64-wide head with wide latents), per head and LLA-2D, on the folded path: a ragged
+    tail tile, one and several splits, all 4 loops."""
+    base = WORKLOADS["lla2d_long" if variant == "lla2d" else "ouro_layer_4x"]
+    w = base.replace(D=1, batch=2, n=200, d=d, r_k=r_k, r_v=r_v, H=16 if variant == "lla2d" else 4)
+    st = DeviceLatentStore(w, seed=21)
+    for splits in (1, 3):
+        out = st.decode(0, 0, 4, opts=lla.make_opts(splits, FOLD))
+        ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n)
+        err = max_abs(f64(out), ref)
+        announce(f"{variant} d={d} ranks=({r_k}, {r_v}) splits={splits}: {rel_note(err, BF16_TOL)}")
+        assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("path", BF16_PATHS)
 def test_bf16_ragged_contexts_poisoned_tail(path):
     """Ragged per-sequence lengths with NaN in every cache row past a sequence's length."""
