@@ -214,6 +214,27 @@ int32_t lla_decode_attn_absorbed(const lla_dims* dims, const lla_codec* codec,
 /* 1 when a kernel is built for (dims' dtype, d_head, r_k, r_v, d_rope), else 0. */
 int32_t lla_decode_absorbed_supported(const lla_dims* dims, int32_t d_rope);
 
+/* lla_decode_attn_absorbed over a paged cache (see lla_pages): cache.c_k and cache.c_v are
+ * the latent pools and k_rope is the rotary-key pool, device
+ * [D][num_pages][H][16][d_rope] in the cache dtype: the rotary key of logical token j of
+ * sequence b and head h is row j % 16 of head h's rows in page
+ * block_table[b * max_blocks + j / 16], written by the caller (rotated at the logical
+ * slot j, like the latents' RoPE positions). Same result as the dense call on the
+ * gathered rows. A context split spans at most 4096 tokens, so num_splits of opts may be
+ * raised to that. workspace >= lla_decode_absorbed_paged_workspace_bytes(...). Other
+ * arguments and errors as lla_decode_attn_absorbed, plus `pages` (validated as described
+ * at lla_pages; table entries outside the pool are clamped into it). */
+size_t lla_decode_absorbed_paged_workspace_bytes(const lla_dims* dims, int32_t d_rope,
+                                                 int32_t n_ctx, int32_t loop_count,
+                                                 const lla_decode_opts* opts);
+int32_t lla_decode_attn_absorbed_paged(const lla_dims* dims, const lla_codec* codec,
+                                       const lla_cache* cache, const lla_pages* pages,
+                                       const void* k_rope, int32_t d_rope, int32_t layer,
+                                       int32_t n_ctx, const int32_t* ctx_lens, const float* q,
+                                       int32_t loop_begin, int32_t loop_count, float* out,
+                                       void* workspace, size_t workspace_bytes,
+                                       const lla_decode_opts* opts, void* stream);
+
 /* Materialised reconstruction of a slot range of one layer (Section 3, Eq. 3 and "RoPE
  * and reconstruction"): the second pass of the latent-store decoder's two-pass prefill,
  * streamed one layer at a time (Appendix A, "Decoding and caching"; Appendix J,

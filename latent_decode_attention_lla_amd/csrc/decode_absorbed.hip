@@ -28,6 +28,10 @@
 //   wholly inside the context skip the clamping and masking. (Lanes that each took every
 //   G-th 8-byte unit of a row read 8 G contiguous bytes per row and instruction and ran at
 //   5.2 TB/s; whole rows per round run at 6.8 TB/s.)
+//   With a paged cache a chunk (16 tokens) is one page: the latent rows and the rotary keys
+//   of its tokens come from the page the block table names for it (the split's page
+//   indices are read into LDS first), at the same offsets within the page as the dense
+//   rows within a tile, so the arithmetic is the dense one.
 #include <type_traits>
 
 #include "decode_stream.h"
@@ -59,8 +63,9 @@ struct QaLayout {
 // each row. A lane's score pieces meet the matching slice of the folded query; the 16
 // partial dots of a token are summed with DPP; every piece is also accumulated with the
 // softmax weight, and only the value pieces are kept at the end.
-template <typename T, int D, int RK, int RV, int DR, int TPC>
-__global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const void* k_rope) {
+template <typename T, int D, int RK, int RV, int DR, int TPC, bool PAGED>
+__global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const void* k_rope,
+                                                             PageArgs pg) {
   using L = QaLayout<RK, DR>;
   constexpr int ES = static_cast<int>(sizeof(T));
   constexpr int EPL = 16 / ES;                  // row elements per 16-byte piece
@@ -69,11 +74,13 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
   constexpr int NP = NPV + NPK + NPR;
   constexpr int NRND = (NP + GP - 1) / GP;      // pieces per lane (rounds)
   static_assert(RV % EPL == 0 && RK % EPL == 0 && DR % EPL == 0, "whole 16-byte pieces");
+  static_assert(!PAGED || TPC * TOK == kPage, "a chunk is one page");
   struct Rows {
     u32x4 x[TPC][NRND];
   };
   __shared__ float abar[RV];
   __shared__ float qs[QaLayout<RK, DR>::QS];
+  __shared__ int split_pages[PAGED ? kMaxSplitPages : 1];  // page of each chunk of the split
 
   const int lane = threadIdx.x;
   const int tok = lane / GP, j = lane % GP;
@@ -117,11 +124,16 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
   __syncthreads();
 
   // ---- this lane's pieces: source, row stride and the query slice they meet --------------
-  const char* ck = static_cast<const char*>(a.c_k) + (static_cast<size_t>(b * a.Hc + hc) * a.n_max) * RK * ES;
-  const char* kr = static_cast<const char*>(k_rope) + (static_cast<size_t>(b * a.H + h) * a.n_max) * DR * ES;
-  const char* cv = static_cast<const char*>(a.c_v) + (static_cast<size_t>(b * a.Hc + hc) * a.n_max) * RV * ES;
+  // dense: the (b, hc) latent plane and the (b, h) rotary-key plane; paged: the head's rows
+  // within a page of the pool (a page holds Hc latent heads' and H rotary heads' 16 rows)
+  const size_t lrow = PAGED ? static_cast<size_t>(hc) * kPage : static_cast<size_t>(b * a.Hc + hc) * a.n_max;
+  const size_t rrow = PAGED ? static_cast<size_t>(h) * kPage : static_cast<size_t>(b * a.H + h) * a.n_max;
+  const char* ck = static_cast<const char*>(a.c_k) + lrow * RK * ES;
+  const char* kr = static_cast<const char*>(k_rope) + rrow * DR * ES;
+  const char* cv = static_cast<const char*>(a.c_v) + lrow * RV * ES;
   const char* src[NRND];
   int stride[NRND];
+  size_t pstep[NRND];  // bytes from one page of the pool to the next
   bool live[NRND];
   float qp[NRND][EPL];
 #pragma unroll
@@ -131,12 +143,15 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
     if (p < NPV) {
       src[u] = cv + p * 16;
       stride[u] = RV * ES;
+      pstep[u] = static_cast<size_t>(a.Hc) * kPage * RV * ES;
     } else if (p < NPV + NPK) {
       src[u] = ck + (p - NPV) * 16;
       stride[u] = RK * ES;
+      pstep[u] = static_cast<size_t>(a.Hc) * kPage * RK * ES;
     } else {
       src[u] = kr + (min(p, NP - 1) - NPV - NPK) * 16;
       stride[u] = DR * ES;
+      pstep[u] = static_cast<size_t>(a.H) * kPage * DR * ES;
     }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
@@ -148,16 +163,25 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
   }
   const float beta = j == 0 ? qs[L::BETA] : 0.f;  // added once per token
 
+  if constexpr (PAGED) {
+    for (int i = lane; i < min(nchunk, kMaxSplitPages); i += 64)
+      split_pages[i] = page_of(pg, b, (s0 >> 4) + i);
+    __syncthreads();
+  }
   auto load_chunk = [&](Rows& R, int c) {
     const int tok0 = s0 + c * TPC * TOK;
     const bool clamp = c >= nfull;
+    // paged: the chunk's page; rows are then counted from its first token
+    const size_t page =
+        PAGED ? static_cast<size_t>(__builtin_amdgcn_readfirstlane(split_pages[min(c, kMaxSplitPages - 1)])) : 0;
 #pragma unroll
     for (int tt = 0; tt < TPC; ++tt) {
       const int row0 = tok0 + TOK * tt + tok;
-      const size_t row = static_cast<size_t>(clamp ? min(row0, s1 - 1) : row0);
+      const int rc = clamp ? min(row0, s1 - 1) : row0;
+      const size_t row = static_cast<size_t>(PAGED ? rc - tok0 : rc);
 #pragma unroll
       for (int u = 0; u < NRND; ++u)
-        R.x[tt][u] = live[u] ? load16(src[u] + row * stride[u]) : u32x4{0u, 0u, 0u, 0u};
+        R.x[tt][u] = live[u] ? load16(src[u] + page * pstep[u] + row * stride[u]) : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -286,10 +310,10 @@ __global__ __launch_bounds__(64) void decode_absorbed_kernel(DecodeArgs a, const
 #define LLA_ABS_TPC 4  // tiles of 4 tokens per chunk; two chunks are in flight
 #endif
 
-template <typename T, int D, int RK, int RV, int DR>
-void launch(const DecodeArgs& a, const void* k_rope, hipStream_t s) {
-  hipLaunchKernelGGL((decode_absorbed_kernel<T, D, RK, RV, DR, LLA_ABS_TPC>), dim3(a.S, a.H * a.L, a.B),
-                     dim3(64), 0, s, a, k_rope);
+template <typename T, int D, int RK, int RV, int DR, bool PAGED>
+void launch(const DecodeArgs& a, const void* k_rope, const PageArgs& pg, hipStream_t s) {
+  hipLaunchKernelGGL((decode_absorbed_kernel<T, D, RK, RV, DR, LLA_ABS_TPC, PAGED>),
+                     dim3(a.S, a.H * a.L, a.B), dim3(64), 0, s, a, k_rope, pg);
 }
 
 }  // namespace
@@ -317,7 +341,21 @@ bool launch_decode_absorbed(int dtype, int d, int r_k, int r_v, int d_rope, cons
                             const void* k_rope, hipStream_t s) {
 #define X(T_, DT_, D_, RK_, RV_, DR_)                                         \
   if (dtype == DT_ && d == D_ && r_k == RK_ && r_v == RV_ && d_rope == DR_) { \
-    launch<T_, D_, RK_, RV_, DR_>(a, k_rope, s);                              \
+    launch<T_, D_, RK_, RV_, DR_, false>(a, k_rope, PageArgs{}, s);           \
+    return true;                                                              \
+  }
+  LLA_ABSORBED_SHAPES(X)
+#undef X
+  return false;
+}
+
+bool launch_decode_absorbed_paged(int dtype, int d, int r_k, int r_v, int d_rope,
+                                  const DecodeArgs& a, const void* k_rope, const PageArgs& pg,
+                                  hipStream_t s) {
+  if (pg.table == nullptr) return false;
+#define X(T_, DT_, D_, RK_, RV_, DR_)                                         \
+  if (dtype == DT_ && d == D_ && r_k == RK_ && r_v == RV_ && d_rope == DR_) { \
+    launch<T_, D_, RK_, RV_, DR_, true>(a, k_rope, pg, s);                    \
     return true;                                                              \
   }
   LLA_ABSORBED_SHAPES(X)

@@ -93,6 +93,18 @@ Plan plan_paged(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_o
   return p;
 }
 
+// Absorbed decode over a paged cache: the absorbed plan, with a split's page indices
+// (at most kMaxSplitPages) kept in LDS.
+Plan plan_absorbed_paged(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_opts* opts) {
+  Plan p = plan_absorbed(d, n_ctx, loop_count, opts);
+  constexpr int kMaxLen = lla::kMaxSplitPages * lla::kPage;
+  if (p.split_len > kMaxLen) {
+    p.split_len = kMaxLen;
+    p.S = (n_ctx + kMaxLen - 1) / kMaxLen;
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,13 +312,23 @@ int32_t lla_decode_absorbed_supported(const lla_dims* d, int32_t d_rope) {
   return lla::decode_absorbed_supported(d->dtype, d->d_head, d->r_k, d->r_v, d_rope) ? 1 : 0;
 }
 
-int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
-                                 const void* k_rope, int32_t d_rope, int32_t layer, int32_t n_ctx,
-                                 const int32_t* ctx_lens, const float* q, int32_t loop_begin,
-                                 int32_t loop_count, float* out, void* workspace,
-                                 size_t workspace_bytes, const lla_decode_opts* opts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Dense (pages == nullptr) and paged absorbed decode: validation, launch arguments, the
+// kernel and the split merge.
+int32_t absorbed_call(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                      const lla_pages* pages, const void* k_rope, int32_t d_rope, int32_t layer,
+                      int32_t n_ctx, const int32_t* ctx_lens, const float* q, int32_t loop_begin,
+                      int32_t loop_count, float* out, void* workspace, size_t workspace_bytes,
+                      const lla_decode_opts* opts, void* stream) {
   int32_t st = check_dims(d);
   if (st != LLA_OK) return st;
+  if (pages != nullptr) {
+    st = check_pages(*d, pages);
+    if (st != LLA_OK) return st;
+  }
   if (codec == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
   if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
   if (n_ctx < 0 || n_ctx > d->n_max) return LLA_ERR_INVALID_ARG;
@@ -322,18 +344,23 @@ int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, cons
   if (!lla::decode_absorbed_supported(d->dtype, d->d_head, d->r_k, d->r_v, d_rope))
     return LLA_ERR_UNSUPPORTED;
   if (static_cast<long long>(d->n_max) * d_rope >= (1LL << 31)) return LLA_ERR_UNSUPPORTED;
-  if (workspace_bytes < lla_decode_absorbed_workspace_bytes(d, d_rope, n_ctx, loop_count, opts))
-    return LLA_ERR_WORKSPACE;
+  const size_t need = pages ? lla_decode_absorbed_paged_workspace_bytes(d, d_rope, n_ctx, loop_count, opts)
+                            : lla_decode_absorbed_workspace_bytes(d, d_rope, n_ctx, loop_count, opts);
+  if (workspace_bytes < need) return LLA_ERR_WORKSPACE;
 
-  const Plan p = plan_absorbed(*d, n_ctx, loop_count, opts);
+  const Plan p = pages ? plan_absorbed_paged(*d, n_ctx, loop_count, opts)
+                       : plan_absorbed(*d, n_ctx, loop_count, opts);
   const size_t es = elem_bytes(*d);
   const int Hc = latent_heads(*d);
   const int K = d->T * d_in(*d);
+  // rows per layer: dense, batch x Hc planes of n_max rows; paged, the pool's pages
+  const size_t lrows = pages ? static_cast<size_t>(pages->num_pages) * Hc * lla::kPage
+                             : static_cast<size_t>(d->batch) * Hc * d->n_max;
+  const size_t rrows = pages ? static_cast<size_t>(pages->num_pages) * d->H * lla::kPage
+                             : static_cast<size_t>(d->batch) * d->H * d->n_max;
   lla::DecodeArgs a;
-  a.c_k = static_cast<const char*>(cache->c_k) +
-          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * d->r_k * es;
-  a.c_v = static_cast<const char*>(cache->c_v) +
-          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * d->r_v * es;
+  a.c_k = static_cast<const char*>(cache->c_k) + static_cast<size_t>(layer) * lrows * d->r_k * es;
+  a.c_v = static_cast<const char*>(cache->c_v) + static_cast<size_t>(layer) * lrows * d->r_v * es;
   a.w_up_k = static_cast<const char*>(codec->w_up_k) +
              static_cast<size_t>(layer) * d->T * d->H * d->d_head * d->r_k * es;
   a.w_up_v = static_cast<const char*>(codec->w_up_v) +
@@ -359,17 +386,56 @@ int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, cons
   a.variant = d->variant;
   const double scale = d->scale > 0.f ? d->scale : 1.0 / std::sqrt(static_cast<double>(d->d_head));
   a.scale_log2e = static_cast<float>(scale * kLog2e);
-  const char* kr = static_cast<const char*>(k_rope) +
-                   static_cast<size_t>(layer) * d->batch * d->H * static_cast<size_t>(d->n_max) * d_rope * es;
+  const char* kr = static_cast<const char*>(k_rope) + static_cast<size_t>(layer) * rrows * d_rope * es;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!lla::launch_decode_absorbed(d->dtype, d->d_head, d->r_k, d->r_v, d_rope, a, kr, s))
-    return LLA_ERR_UNSUPPORTED;
+  bool ok;
+  if (pages != nullptr) {
+    const lla::PageArgs pg{pages->block_table, pages->max_blocks, pages->num_pages};
+    ok = lla::launch_decode_absorbed_paged(d->dtype, d->d_head, d->r_k, d->r_v, d_rope, a, kr, pg, s);
+  } else {
+    ok = lla::launch_decode_absorbed(d->dtype, d->d_head, d->r_k, d->r_v, d_rope, a, kr, s);
+  }
+  if (!ok) return LLA_ERR_UNSUPPORTED;
   st = hip_status();
   if (st != LLA_OK) return st;
   if (p.S == 1) return LLA_OK;  // the kernel finished the single split itself
   if (!lla::launch_combine(d->dtype, d->d_head, d->r_v, a, s)) return LLA_ERR_UNSUPPORTED;
   return hip_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lla_decode_attn_absorbed(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                                 const void* k_rope, int32_t d_rope, int32_t layer, int32_t n_ctx,
+                                 const int32_t* ctx_lens, const float* q, int32_t loop_begin,
+                                 int32_t loop_count, float* out, void* workspace,
+                                 size_t workspace_bytes, const lla_decode_opts* opts, void* stream) {
+  return absorbed_call(d, codec, cache, nullptr, k_rope, d_rope, layer, n_ctx, ctx_lens, q,
+                       loop_begin, loop_count, out, workspace, workspace_bytes, opts, stream);
+}
+
+size_t lla_decode_absorbed_paged_workspace_bytes(const lla_dims* d, int32_t d_rope, int32_t n_ctx,
+                                                 int32_t loop_count, const lla_decode_opts* opts) {
+  if (check_dims(d) != LLA_OK || n_ctx < 0 || n_ctx > d->n_max || loop_count < 1) return 0;
+  if (d_rope < 16 || d_rope >= d->d_head || d_rope % 16 != 0) return 0;
+  const Plan p = plan_absorbed_paged(*d, n_ctx, loop_count, opts);
+  const size_t part = static_cast<size_t>(d->batch) * d->H * loop_count * p.S * (2 + d->r_v) * 4;
+  return (part + 255) / 256 * 256;
+}
+
+int32_t lla_decode_attn_absorbed_paged(const lla_dims* d, const lla_codec* codec,
+                                       const lla_cache* cache, const lla_pages* pages,
+                                       const void* k_rope, int32_t d_rope, int32_t layer,
+                                       int32_t n_ctx, const int32_t* ctx_lens, const float* q,
+                                       int32_t loop_begin, int32_t loop_count, float* out,
+                                       void* workspace, size_t workspace_bytes,
+                                       const lla_decode_opts* opts, void* stream) {
+  if (pages == nullptr) return LLA_ERR_INVALID_ARG;
+  return absorbed_call(d, codec, cache, pages, k_rope, d_rope, layer, n_ctx, ctx_lens, q,
+                       loop_begin, loop_count, out, workspace, workspace_bytes, opts, stream);
 }
 
 size_t lla_decode_teacher_workspace_bytes(const lla_dims* d, int32_t n_ctx, int32_t loop_count,

@@ -42,6 +42,11 @@ bool launch_combine(int dtype, int d, int r_v, const DecodeArgs& a, hipStream_t 
 bool launch_decode_absorbed(int dtype, int d, int r_k, int r_v, int d_rope, const DecodeArgs& a,
                             const void* k_rope, hipStream_t s);
 bool decode_absorbed_supported(int dtype, int d, int r_k, int r_v, int d_rope);
+// Paged instance: c_k, c_v and k_rope are the layer's pools (a chunk of 16 tokens is one
+// page); at most kMaxSplitPages pages per split.
+bool launch_decode_absorbed_paged(int dtype, int d, int r_k, int r_v, int d_rope,
+                                  const DecodeArgs& a, const void* k_rope, const PageArgs& pg,
+                                  hipStream_t s);
 // Uncompressed decode: c_k / c_v of the args are the layer's per-loop key and value
 // caches [T][B][H][n_max][d]; combine with `project` false merges its partials.
 bool launch_decode_teacher(int dtype, int d, const DecodeArgs& a, hipStream_t s);

@@ -91,8 +91,9 @@ class DeviceLatentStore:
         """Move this store's dense latent cache into a page pool: logical page p of
         sequence b goes to a random physical page (in order with shuffle=False) (spare pages are filled with NaN, so a
         read of a page the table does not name shows). Sets self.pages / self.block_table
-        and replaces c_k, c_v by the pools [D][num_pages][Hc][16][r]; the dense tensors stay
-        in self.dense."""
+        and replaces c_k, c_v by the pools [D][num_pages][Hc][16][r] (and k_rope, when the
+        store has rotary keys, by [D][num_pages][H][16][d_rope]); the dense tensors stay in
+        self.dense."""
         w = self.w
         npg = (self.n_max + 15) // 16
         num_pages = w.batch * npg + spare_pages
@@ -100,17 +101,18 @@ class DeviceLatentStore:
         perm = (torch.randperm(num_pages, generator=g) if shuffle
                 else torch.arange(num_pages))[:w.batch * npg]
         table = perm.reshape(w.batch, npg).to(torch.int32)
-        self.dense = {"c_k": self.t["c_k"], "c_v": self.t["c_v"]}
-        for key in ("c_k", "c_v"):
-            x = self.t[key]  # [D][B][Hc][n][r]
-            r = x.shape[-1]
+        keys = [k for k in ("c_k", "c_v", "k_rope") if k in self.t]
+        self.dense = {k: self.t[k] for k in keys}
+        for key in keys:
+            x = self.t[key]  # [D][B][heads][n][r]
+            nh, r = x.shape[2], x.shape[-1]
             pad = npg * 16 - x.shape[3]
             if pad:
                 x = torch.cat([x, torch.zeros(*x.shape[:3], pad, r, dtype=x.dtype, device=x.device)], 3)
-            pool = torch.full((w.D, num_pages, w.Hc, 16, r), float("nan"), dtype=x.dtype,
+            pool = torch.full((w.D, num_pages, nh, 16, r), float("nan"), dtype=x.dtype,
                               device=self.device)
-            pages = x.reshape(w.D, w.batch, w.Hc, npg, 16, r).permute(0, 1, 3, 2, 4, 5)
-            pool[:, perm.to(self.device)] = pages.reshape(w.D, w.batch * npg, w.Hc, 16, r)
+            pages = x.reshape(w.D, w.batch, nh, npg, 16, r).permute(0, 1, 3, 2, 4, 5)
+            pool[:, perm.to(self.device)] = pages.reshape(w.D, w.batch * npg, nh, 16, r)
             self.t[key] = pool
         self.block_table = table.to(self.device)
         self.pages = lla.make_pages(self.block_table, npg, num_pages)
@@ -133,6 +135,26 @@ class DeviceLatentStore:
         lla.lla_decode_attn_paged(self.dims, self.codec, self.cache, self.pages, layer, n_ctx,
                                   ctx_lens, q, loop_begin, loop_count, out, ws, ws.numel(), opts,
                                   stream)
+        return out
+
+    def decode_absorbed_paged(self, layer: int, loop_begin: int, loop_count: int, q=None,
+                              n_ctx=None, ctx_lens=None, opts=None, out=None,
+                              stream=None) -> torch.Tensor:
+        """Decoupled-RoPE absorbed decode over the paged cache (after paginate)."""
+        w = self.w
+        n_ctx = w.n if n_ctx is None else n_ctx
+        if q is None:
+            if loop_count == 1:
+                q = self.t["q"][layer, loop_begin]
+            else:
+                q = self.t["q"][layer, loop_begin:loop_begin + loop_count].permute(1, 2, 0, 3).contiguous()
+        if out is None:
+            out = torch.empty(w.batch, w.H, loop_count, w.d, dtype=torch.float32, device=self.device)
+        nb = lla.lla_decode_absorbed_paged_workspace_bytes(self.dims, w.d_rope, n_ctx, loop_count, opts)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=self.device)
+        lla.lla_decode_attn_absorbed_paged(self.dims, self.codec, self.cache, self.pages,
+                                           self.t["k_rope"], w.d_rope, layer, n_ctx, ctx_lens, q,
+                                           loop_begin, loop_count, out, ws, ws.numel(), opts, stream)
         return out
 
     def reconstruct(self, layer: int, loop_begin: int, loop_count: int, pos_start: int = 0,

@@ -36,7 +36,8 @@ EXPORTED = (
     "lla_rope_table_bytes", "lla_rope_table_build", "lla_encode",
     "lla_decode_workspace_bytes", "lla_decode_attn", "lla_decode_num_splits",
     "lla_decode_absorbed_workspace_bytes", "lla_decode_attn_absorbed",
-    "lla_decode_absorbed_supported",
+    "lla_decode_absorbed_supported", "lla_decode_absorbed_paged_workspace_bytes",
+    "lla_decode_attn_absorbed_paged",
     "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
     "lla_decode_teacher_num_splits", "lla_decode_paged_num_splits", "lla_reconstruct",
     "lla_encode_paged", "lla_decode_paged_workspace_bytes", "lla_decode_attn_paged",
@@ -119,6 +120,13 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_attn_absorbed.restype = i32
     lib.lla_decode_absorbed_supported.argtypes = [P(lla_dims), i32]
     lib.lla_decode_absorbed_supported.restype = i32
+    lib.lla_decode_absorbed_paged_workspace_bytes.argtypes = [P(lla_dims), i32, i32, i32,
+                                                              P(lla_decode_opts)]
+    lib.lla_decode_absorbed_paged_workspace_bytes.restype = sz
+    lib.lla_decode_attn_absorbed_paged.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache),
+                                                   P(lla_pages), vp, i32, i32, i32, vp, vp, i32,
+                                                   i32, vp, vp, sz, P(lla_decode_opts), vp]
+    lib.lla_decode_attn_absorbed_paged.restype = i32
     lib.lla_decode_teacher_workspace_bytes.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
     lib.lla_decode_teacher_workspace_bytes.restype = sz
     lib.lla_decode_attn_teacher.argtypes = [P(lla_dims), vp, vp, i32, i32, vp, vp, i32, i32, vp,
@@ -259,6 +267,31 @@ def lla_decode_attn_absorbed_status(dims, codec, cache, k_rope, d_rope, layer, n
     return load().lla_decode_attn_absorbed(
         ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), _ptr(k_rope), d_rope, layer,
         n_ctx, _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out), _ptr(workspace),
+        workspace_bytes, ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def lla_decode_absorbed_paged_workspace_bytes(dims: lla_dims, d_rope: int, n_ctx: int,
+                                              loop_count: int, opts=None) -> int:
+    return load().lla_decode_absorbed_paged_workspace_bytes(
+        ctypes.byref(dims), d_rope, n_ctx, loop_count,
+        ctypes.byref(opts) if opts is not None else None)
+
+
+def lla_decode_attn_absorbed_paged(dims, codec, cache, pages, k_rope, d_rope: int, layer: int,
+                                   n_ctx: int, ctx_lens, q, loop_begin: int, loop_count: int, out,
+                                   workspace, workspace_bytes: int, opts=None, stream=None) -> None:
+    _check("lla_decode_attn_absorbed_paged", lla_decode_attn_absorbed_paged_status(
+        dims, codec, cache, pages, k_rope, d_rope, layer, n_ctx, ctx_lens, q, loop_begin,
+        loop_count, out, workspace, workspace_bytes, opts, _stream(stream)))
+
+
+def lla_decode_attn_absorbed_paged_status(dims, codec, cache, pages, k_rope, d_rope, layer, n_ctx,
+                                          ctx_lens, q, loop_begin, loop_count, out, workspace,
+                                          workspace_bytes, opts=None, stream=0) -> int:
+    return load().lla_decode_attn_absorbed_paged(
+        ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache),
+        ctypes.byref(pages) if pages is not None else None, _ptr(k_rope), d_rope, layer, n_ctx,
+        _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out), _ptr(workspace),
         workspace_bytes, ctypes.byref(opts) if opts is not None else None, stream)
 
 

@@ -414,6 +414,23 @@ def decode_paged(pool_k: np.ndarray, pool_v: np.ndarray, block_table: np.ndarray
                   scale, variant)
 
 
+def decode_absorbed_paged(pool_k: np.ndarray, pool_v: np.ndarray, pool_rope: np.ndarray,
+                          block_table: np.ndarray, w_up_k: np.ndarray, mu_k: np.ndarray,
+                          w_up_v: np.ndarray, mu_v: np.ndarray, q: np.ndarray, d_rope: int,
+                          loop_begin: int = 0, ctx_lens=None, n_ctx: int | None = None,
+                          scale: float | None = None, variant: str = "per_head") -> np.ndarray:
+    """Decoupled-RoPE decode over a paged cache: the latent rows and the rotary keys
+    (pool_rope [P, H, PAGE, d_rope]) of the logical tokens the block table lists, then the
+    decode of `decode_absorbed`."""
+    if n_ctx is None:
+        n_ctx = np.asarray(block_table).shape[1] * PAGE
+    c_k = gather_pages(pool_k, block_table, n_ctx)
+    c_v = gather_pages(pool_v, block_table, n_ctx)
+    k_rope = gather_pages(pool_rope, block_table, n_ctx)
+    return decode_absorbed(c_k, c_v, k_rope, w_up_k, mu_k, w_up_v, mu_v, q, d_rope, loop_begin,
+                           ctx_lens, scale, variant)
+
+
 def window_pages(n_pages_written: int, sink_pages: int, window_pages: int) -> list:
     """Logical pages eviction keeps once n_pages_written pages exist: the first sink_pages
     pages and the window_pages most recent ones, in order (all of them while they fit)."""

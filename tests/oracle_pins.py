@@ -595,6 +595,36 @@ def pin_paged_permuted() -> float:
     return err
 
 
+def pin_absorbed_paged_permuted() -> float:
+    """The decoupled decode over a cache scattered into shuffled pages (latents and rotary
+    keys, pools built here by reshaping, junk in spare pages) equals the dense decoupled
+    decode, per head and LLA-2D, ragged contexts included."""
+    err = 0.0
+    for variant, seed, d_rope in (("per_head", 91, 2), ("2d", 92, 4)):
+        a = _tiny(seed, T=2, n=48, variant=variant)
+        B, Hc, n, _ = a["c_k"].shape
+        H = a["w_up_k"].shape[1]
+        npg = n // O.PAGE
+        rng = _rng(seed + 1)
+        kr = rng.standard_normal((B, H, n, d_rope))
+        table = rng.permutation(B * npg + 2)[:B * npg].reshape(B, npg)
+        pools = []
+        for x in (a["c_k"], a["c_v"], kr):
+            X = x.shape[1]
+            pool = rng.standard_normal((B * npg + 2, X, O.PAGE, x.shape[3]))
+            pages = x.reshape(B, X, npg, O.PAGE, x.shape[3]).transpose(0, 2, 1, 3, 4)
+            pool[table.reshape(-1)] = pages.reshape(B * npg, X, O.PAGE, x.shape[3])
+            pools.append(pool)
+        lens = [48, 19]
+        got = O.decode_absorbed_paged(pools[0], pools[1], pools[2], table, a["w_up_k"], a["mu_k"],
+                                      a["w_up_v"], a["mu_v"], a["q"], d_rope, 0, lens, None, None,
+                                      variant)
+        ref = O.decode_absorbed(a["c_k"], a["c_v"], kr, a["w_up_k"], a["mu_k"], a["w_up_v"],
+                                a["mu_v"], a["q"], d_rope, 0, lens, None, variant)
+        err = max(err, float(np.max(np.abs(got - ref))))
+    return err
+
+
 def pin_eviction_window() -> float:
     """StreamingLLM-style eviction: window_pages against hand-listed cases, then, with a
     full-rank orthonormal codec, the paged decode over the kept pages (sink page plus the
@@ -663,4 +693,5 @@ ALL_PINS = {
     "reconstruct_feeds_teacher": (pin_reconstruct_feeds_teacher, 1e-12),
     "paged_permuted": (pin_paged_permuted, 1e-12),
     "eviction_window": (pin_eviction_window, 1e-12),
+    "absorbed_paged_permuted": (pin_absorbed_paged_permuted, 1e-12),
 }

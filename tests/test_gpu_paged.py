@@ -219,3 +219,92 @@ def test_invalid_arguments():
                                            lla.make_opts(0, lla.LLA_PATH_ROTARY_FOLD))
     assert got == lla.LLA_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# decoupled-RoPE absorbed decode over a paged cache (latents and rotary keys in pages)
+# ---------------------------------------------------------------------------
+
+def _oracle_absorbed_paged(st, layer, loop_begin, loop_count, seqs, n_ctx, ctx_lens=None):
+    t, w = st.t, st.w
+    idx = torch.as_tensor(list(seqs), device=st.device)
+    table = st.block_table.index_select(0, idx).cpu().numpy()
+    q = t["q"][layer, loop_begin:loop_begin + loop_count].permute(1, 2, 0, 3).index_select(0, idx)
+    lens = None if ctx_lens is None else [int(ctx_lens[i]) for i in seqs]
+    return O.decode_absorbed_paged(f64(t["c_k"][layer]), f64(t["c_v"][layer]), f64(t["k_rope"][layer]),
+                                   table, f64(t["w_up_k"][layer]), f64(t["mu_k"][layer]),
+                                   f64(t["w_up_v"][layer]), f64(t["mu_v"][layer]), f64(q), w.d_rope,
+                                   loop_begin, lens, n_ctx, None,
+                                   "per_head" if w.variant == "per_head" else "2d")
+
+
+@pytest.mark.parametrize("name,d_rope,splits", [
+    ("ouro_layer_4x", 64, 0),
+    ("ouro_layer_4x", 32, 3),
+    ("capacity_21x", 32, 0),
+    ("capacity_21x", 64, 2),
+    ("tiny_f32", 16, 0),
+    ("tiny_f32", 32, 3),
+    ("lla2d_long", 64, 2),
+])
+def test_absorbed_shuffled_pool_matches_dense_and_oracle(name, d_rope, splits):
+    """The dense and paged absorbed decodes run the same arithmetic on the same rows (the
+    rotary keys through the same pages as the latents): bit for bit equal, and equal to
+    the oracle's decode over the gathered pages. Ragged contexts, NaN in spare pages."""
+    w = WORKLOADS[name].replace(batch=3, n=300, D=2, d_rope=d_rope,
+                                **({"H": 4} if name != "tiny_f32" else {}))
+    st = DeviceLatentStore(w, seed=81)
+    lens = [300, 141, 1]
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    opts = lla.make_opts(splits)
+    dense = st.decode_absorbed(1, 0, w.T, ctx_lens=ctx, opts=opts).clone()
+    st.paginate(seed=82, spare_pages=4)
+    paged = st.decode_absorbed_paged(1, 0, w.T, ctx_lens=ctx, opts=opts)
+    torch.cuda.synchronize()
+    ref = _oracle_absorbed_paged(st, 1, 0, w.T, range(3), w.n, lens)
+    tol = F32_TOL if w.dtype == "f32" else BF16_TOL
+    err = max_abs(f64(paged), ref)
+    same = torch.equal(paged, dense)
+    announce(f"absorbed paged {name} d_rope={d_rope} splits={splits}: {rel_note(err, tol)}; "
+             f"bit-identical to dense: {same}")
+    assert err <= tol
+    assert same
+
+
+def test_absorbed_full_launch_paged_matches_dense():
+    """The absorbed 4x launch (8 x 16 heads, context 32768, 64-wide rotary branch) on a
+    shuffled pool equals the dense cache bit for bit; one sequence against the oracle."""
+    w = WORKLOADS["absorbed_4x"].replace(D=1)
+    announce("absorbed_4x paged full launch, B=8 n=32768")
+    st = DeviceLatentStore(w, seed=83)
+    dense = st.decode_absorbed(0, 2, 1).clone()
+    st.paginate(seed=84, spare_pages=3)
+    paged = st.decode_absorbed_paged(0, 2, 1)
+    torch.cuda.synchronize()
+    same = torch.equal(paged, dense)
+    ref = _oracle_absorbed_paged(st, 0, 2, 1, [5], w.n)
+    err = max_abs(f64(paged[[5]]), ref)
+    announce(f"  bit-identical to dense: {same}; sequence 5: {rel_note(err, BF16_TOL)}")
+    assert same
+    assert err <= BF16_TOL
+
+
+def test_absorbed_paged_invalid_arguments():
+    w = WORKLOADS["ouro_layer_4x"].replace(batch=2, n=64, D=1, H=4, d_rope=64)
+    st = DeviceLatentStore(w, seed=85)
+    st.paginate(seed=86)
+    out = torch.empty(w.batch, w.H, 1, w.d, device="cuda")
+    nb = lla.lla_decode_absorbed_paged_workspace_bytes(st.dims, 64, w.n, 1)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    q = st.t["q"][0, 0]
+    args = (st.dims, st.codec, st.cache)
+    tail = (st.t["k_rope"], 64, 0, w.n, None, q, 0, 1, out, ws, ws.numel())
+    assert lla.lla_decode_attn_absorbed_paged_status(*args, st.pages, *tail) == lla.LLA_OK
+    assert lla.lla_decode_attn_absorbed_paged_status(*args, None, *tail) == lla.LLA_ERR_INVALID_ARG
+    bad = lla.make_pages(st.block_table, 1, st.pages.num_pages)  # max_blocks * 16 < n_max
+    assert lla.lla_decode_attn_absorbed_paged_status(*args, bad, *tail) == lla.LLA_ERR_INVALID_ARG
+    tail48 = (st.t["k_rope"], 48) + tail[2:]
+    assert lla.lla_decode_attn_absorbed_paged_status(*args, st.pages, *tail48) == lla.LLA_ERR_UNSUPPORTED
+    small = (st.t["k_rope"], 64, 0, w.n, None, q, 0, 1, out, ws, nb - 256)
+    if nb >= 256:
+        assert lla.lla_decode_attn_absorbed_paged_status(*args, st.pages, *small) == lla.LLA_ERR_WORKSPACE

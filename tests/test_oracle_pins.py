@@ -143,6 +143,21 @@ def _mut_gather_pages_next_page(pool, block_table, n):
     return out
 
 
+def _mut_absorbed_paged_rope_unrouted(pool_k, pool_v, pool_rope, block_table, w_up_k, mu_k,
+                                      w_up_v, mu_v, q, d_rope, loop_begin=0, ctx_lens=None,
+                                      n_ctx=None, scale=None, variant="per_head"):
+    """Takes the rotary keys from pages in logical order, bypassing the block table."""
+    bt = np.asarray(block_table)
+    if n_ctx is None:
+        n_ctx = bt.shape[1] * O.PAGE
+    ident = np.arange(bt.size).reshape(bt.shape)
+    c_k = O.gather_pages(pool_k, bt, n_ctx)
+    c_v = O.gather_pages(pool_v, bt, n_ctx)
+    k_rope = O.gather_pages(pool_rope, ident, n_ctx)
+    return O.decode_absorbed(c_k, c_v, k_rope, w_up_k, mu_k, w_up_v, mu_v, q, d_rope, loop_begin,
+                             ctx_lens, scale, variant)
+
+
 def _mut_window_keeps_oldest(n_pages_written, sink_pages, window_pages):
     if n_pages_written <= sink_pages + window_pages:
         return list(range(n_pages_written))
@@ -176,6 +191,7 @@ MUTANTS = {
     "reconstruct_cache_rotates_values": ("reconstruct_cache", _mut_reconstruct_cache_rotates_values),
     "gather_pages_next_page": ("gather_pages", _mut_gather_pages_next_page),
     "window_keeps_oldest": ("window_pages", _mut_window_keeps_oldest),
+    "absorbed_paged_rope_unrouted": ("decode_absorbed_paged", _mut_absorbed_paged_rope_unrouted),
 }
 
 
