@@ -79,6 +79,17 @@ __device__ __forceinline__ float max16(float v) {
   return dpp_max<0x140>(v);  // row_mirror
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [N - 3, N] (its loads of one tile): tile c has
+// landed once only the n loads of tile c + 1 are outstanding
+template <int N>
+__device__ __forceinline__ void wait_loads(int n) {
+  static_assert(N >= 3 && N <= 63, "vmcnt range");
+  if (n >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  else if (n == N - 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N - 1) : "memory");
+  else if (n == N - 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N - 2) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N - 3) : "memory");
+}
+
 template <int D, int RK, int RV, int HG, bool PAGED>
 __global__ __launch_bounds__(64 * HG) __attribute__((amdgpu_waves_per_eu(LLA_2D_WAVES_PER_EU)))
 void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
@@ -105,6 +116,10 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   static_assert(HG * RV + 2 * HG <= RING_UNITS * 4, "epilogue staging fits the ring");
   static_assert(RK % 16 == 0 && RV % 16 == 0 && D % 32 == 0 && HG <= 16, "shape");
   static_assert((NIK + NW - 1) / NW + (NIV + NW - 1) / NW + (NKS + NW - 1) / NW <= 31, "vmcnt range");
+  // the last wave issues the fewest loads per tile, NIK / NW + NIV / NW + NKS / NW, at
+  // least NSLOT - 3 (the range wait_loads covers)
+  static_assert((NIK + NW - 1) / NW + (NIV + NW - 1) / NW + (NKS + NW - 1) / NW -
+                        (NIK / NW + NIV / NW + NKS / NW) <= 3, "load counts");
 
   __shared__ u32x4 lds[LDS_UNITS];
   uint16_t* ptile = reinterpret_cast<uint16_t*>(lds + RING_UNITS + XCH_UNITS);  // [2][16][16]
@@ -194,10 +209,19 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   const char* tab_g = reinterpret_cast<const char*>(a.rope16);
   const int tile_max = s1 > 0 ? (s1 - 1) >> 4 : 0;
   // Block slots of this wave by kind: NSK key, NSV value and NST table slots; slot j of a
-  // kind loads block min(wave + NW j, blocks of the kind - 1) of it (a repeated block is
-  // loaded by two waves to the same place). Per slot this lane keeps the token row it
+  // kind loads block wave + NW j of it, if the kind has that many blocks (waves with fewer
+  // blocks issue fewer loads per tile: nload). Per slot this lane keeps the token row it
   // loads and its byte offset in the tile (row * row size + column).
   constexpr int NSK = (NIK + NW - 1) / NW, NSV = (NIV + NW - 1) / NW, NST = (NKS + NW - 1) / NW;
+  constexpr int NSLOT = NSK + NSV + NST;
+  auto has = [&](int j, int blocks) { return wave + NW * j < blocks; };  // wave-uniform
+  int nload = 0;
+#pragma unroll
+  for (int j = 0; j < NSK; ++j) nload += has(j, NIK);
+#pragma unroll
+  for (int j = 0; j < NSV; ++j) nload += has(j, NIV);
+#pragma unroll
+  for (int j = 0; j < NST; ++j) nload += has(j, NKS);
   int kblk[NSK], krow[NSK], vblk[NSV], vrow[NSV], tblk[NST];
   uint32_t koff[NSK], voff[NSV], toff[NST];
 #pragma unroll
@@ -242,7 +266,8 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
     u32x4* stage = lds + (tl % kStages) * STAGE_BLOCKS * 64;
     const char* tb = tab_g + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * (NKS * 1024);
 #pragma unroll
-    for (int j = 0; j < NST; ++j) dma(tb + toff[j], stage + tblk[j] * 64);
+    for (int j = 0; j < NST; ++j)
+      if (has(j, NKS)) dma(tb + toff[j], stage + tblk[j] * 64);
     // first row of the tile (tiles past the last: of the last tile) in the sequence's plane,
     // or the first row of the tile's page in the pool
     const int tlc = min(tl, ntile - 1);
@@ -251,20 +276,24 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
     const char* vb = cv + row0 * (RV * 2);
     if (tl < nfull) {
 #pragma unroll
-      for (int j = 0; j < NSK; ++j) dma(kb + koff[j], stage + kblk[j] * 64);
+      for (int j = 0; j < NSK; ++j)
+        if (has(j, NIK)) dma(kb + koff[j], stage + kblk[j] * 64);
 #pragma unroll
-      for (int j = 0; j < NSV; ++j) dma(vb + voff[j], stage + vblk[j] * 64);
+      for (int j = 0; j < NSV; ++j)
+        if (has(j, NIV)) dma(vb + voff[j], stage + vblk[j] * 64);
     } else {  // rows past the context end clamp to its last token (they get zero weight)
       const int t0 = s0 + 16 * tlc;
 #pragma unroll
       for (int j = 0; j < NSK; ++j) {
         const int d = min(t0 + krow[j], s1 - 1) - t0 - krow[j];  // <= 0 rows
-        dma(kb + static_cast<uint32_t>(static_cast<int>(koff[j]) + d * (RK * 2)), stage + kblk[j] * 64);
+        if (has(j, NIK))
+          dma(kb + static_cast<uint32_t>(static_cast<int>(koff[j]) + d * (RK * 2)), stage + kblk[j] * 64);
       }
 #pragma unroll
       for (int j = 0; j < NSV; ++j) {
         const int d = min(t0 + vrow[j], s1 - 1) - t0 - vrow[j];
-        dma(vb + static_cast<uint32_t>(static_cast<int>(voff[j]) + d * (RV * 2)), stage + vblk[j] * 64);
+        if (has(j, NIV))
+          dma(vb + static_cast<uint32_t>(static_cast<int>(voff[j]) + d * (RV * 2)), stage + vblk[j] * 64);
       }
     }
     if constexpr (PAGED) page_next = page_for(tl + 1);
@@ -353,7 +382,7 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
         // tile c has landed once only tile c + 1's loads are outstanding; the barrier then
         // publishes every wave's blocks of tile c and the weights of tile c - 1, and tells
         // that tile c - 2's stage is free for tile c + 2
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NSK + NSV + NST) : "memory");
+        wait_loads<NSLOT>(nload);
         ring_barrier();
         issue(c + 2);
         if (c > 0) value_step(c - 1);
