@@ -110,6 +110,18 @@ def test_paged_splits_of_the_wide_fold_span_at_most_4096_tokens():
     assert lla.lla_decode_paged_num_splits(narrow, 32768, 1) == lla.lla_decode_num_splits(narrow, 32768, 1)
     nb = lla.lla_decode_paged_workspace_bytes(wide, 32768, 1)
     assert nb == 32 * 16 * 8 * (2 + 160) * 4
+    # LLA-2D: one wave per head (its own kernel), splits of the paged cache capped alike
+    l2d = lla.make_dims(4, 1, 16, 128, 96, 160, 2, 65536, lla.LLA_2D)
+    assert lla.lla_decode_num_splits(l2d, 65536, 1) == 64  # 2048 waves / 32 heads
+    assert lla.lla_decode_paged_num_splits(l2d, 65536, 1) == 64
+    assert lla.lla_decode_paged_num_splits(l2d, 65536, 1, lla.make_opts(2)) == 16  # 4096-token cap
+    assert lla.lla_decode_num_splits(l2d, 65536, 1, lla.make_opts(2)) == 2
+    # the absorbed decode's paged plan has the same cap
+    absd = lla.make_dims(4, 1, 16, 128, 96, 160, 8, 32768)
+    assert (lla.lla_decode_absorbed_paged_workspace_bytes(absd, 64, 32768, 1, lla.make_opts(1))
+            == 8 * 16 * 8 * (2 + 160) * 4)
+    assert (lla.lla_decode_absorbed_workspace_bytes(absd, 64, 32768, 1, lla.make_opts(1))
+            == 8 * 16 * 1 * (2 + 160) * 4)
 
 
 # Argument validation with fake (never dereferenced) addresses. Every case below must be
