@@ -220,7 +220,10 @@ int32_t lla_decode_absorbed_supported(const lla_dims* dims, int32_t d_rope);
  * sequence b and head h is row j % 16 of head h's rows in page
  * block_table[b * max_blocks + j / 16], written by the caller (rotated at the logical
  * slot j, like the latents' RoPE positions). Same result as the dense call on the
- * gathered rows. A context split spans at most 4096 tokens, so num_splits of opts may be
+ * gathered rows. Unlike the latents, whose RoPE is applied at decode time at the current
+ * logical slot, the stored rotary keys keep the positions they were rotated at: after an
+ * eviction moves kept tokens to new logical slots, the caller re-rotates their rotary
+ * keys if it wants cache-relative positions for them too. A context split spans at most 4096 tokens, so num_splits of opts may be
  * raised to that. workspace >= lla_decode_absorbed_paged_workspace_bytes(...). Other
  * arguments and errors as lla_decode_attn_absorbed, plus `pages` (validated as described
  * at lla_pages; table entries outside the pool are clamped into it). */
