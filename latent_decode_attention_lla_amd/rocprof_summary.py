@@ -6,6 +6,12 @@ under profiles/.
       --fetch F.db --write W.db --copy-fetch CF.db --copy-write CW.db \
       --copy-bytes N --kernel decode_rotary_fold --out traffic.json
 
+``counters`` prints every counter of a --pmc run averaged per dispatch, for the kernels
+whose names contain one of the given fragments:
+
+  python -m latent_decode_attention_lla_amd.rocprof_summary counters RUN_results.db \
+      --kernel decode_rotary_fold
+
 ``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the named kernel by
 what the same counters read for a plain device copy of N bytes read and N bytes written
 (the copy kernel whose counters are largest in the copy runs), and reports HBM bytes per
@@ -60,6 +66,9 @@ def main(argv=None):
     k = sp.add_parser("kernels")
     k.add_argument("db")
     k.add_argument("--top", type=int, default=12)
+    cn = sp.add_parser("counters")
+    cn.add_argument("db")
+    cn.add_argument("--kernel", required=True)
     t = sp.add_parser("traffic")
     for name in ("fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument(f"--{name}", required=True)
@@ -79,6 +88,17 @@ def main(argv=None):
         for r in rows[:a.top]:
             print(f"| {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | {r['max_us']:.2f} | "
                   f"{r['total_ms']:.3f} | {r['pct']:.2f} | `{r['kernel'][:120]}` |")
+        return
+    if a.cmd == "counters":
+        con = sqlite3.connect(a.db)
+        names = [r[0] for r in con.execute("select distinct counter_name from counters_collection")]
+        subs = [x for x in a.kernel.split(",") if x]
+        print("| counter | per dispatch | dispatches | kernel |")
+        print("|---|---:|---:|---|")
+        for c in sorted(names):
+            for k, (n, v) in sorted(counter_per_kernel(a.db, c).items()):
+                if any(x in k for x in subs):
+                    print(f"| {c} | {v:.4g} | {n} | `{k[:100]}` |")
         return
     fk, (fn, fv) = _pick(counter_per_kernel(a.fetch, "FETCH_SIZE"), a.kernel, a.sum)
     wk, (wn, wv) = _pick(counter_per_kernel(a.write, "WRITE_SIZE"), a.kernel, a.sum)
