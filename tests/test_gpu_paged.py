@@ -122,13 +122,14 @@ def test_paged_encode_matches_dense_encode(name, n_new):
         announce(f"paged encode {name} n_new={n_new} {axis}: worst {ratio:.3g} (ulp or abs)")
 
 
-def test_streaming_eviction_sink_and_window():
+@pytest.mark.parametrize("name", ["capacity_21x", "ouro_layer_4x", "lla2d_long"])
+def test_streaming_eviction_sink_and_window(name):
     """A sequence grows page by page through lla_encode_paged; once sink + window pages
     are full, the oldest window page is evicted and its physical page reused. The block
     table then lists O.window_pages' logical pages, the stored latents are those of the
     kept tokens, and lla_decode_attn_paged over them (positions = slots of the kept cache)
-    matches the oracle."""
-    w = WORKLOADS["capacity_21x"].replace(batch=2, n=16 * 6, D=1, H=4)
+    matches the oracle: narrow fold, wide fold and the LLA-2D kernel."""
+    w = WORKLOADS[name].replace(batch=2, n=16 * 6, D=1, H=4)
     sink, window, written_pages = 1, 4, 11
     codec = encode_codec_orthonormal(w, seed=78)
     st = _store_for_encode(w, codec, seed=78, sentinel=0.0)
@@ -170,16 +171,18 @@ def test_streaming_eviction_sink_and_window():
     out = st.decode_paged(0, 0, 4, n_ctx=n_kept, ctx_lens=ctx)
     ref = _oracle_paged(st, 0, 0, 4, range(w.batch), n_kept, [n_kept, n_kept - 5])
     err = max_abs(f64(out), ref)
-    announce(f"streaming eviction (sink {sink}, window {window} pages, {written_pages} written): "
+    announce(f"streaming eviction {name} (sink {sink}, window {window} pages, {written_pages} written): "
              f"{rel_note(err, BF16_TOL)}")
     assert err <= BF16_TOL
 
 
-@pytest.mark.parametrize("name,seqs", [("capacity_21x", [0, 383, 767]), ("ouro_layer_4x", [0, 31])])
+@pytest.mark.parametrize("name,seqs", [("capacity_21x", [0, 383, 767]), ("ouro_layer_4x", [0, 31]),
+                                       ("lla2d_long", [0, 15])])
 def test_full_launch_paged_sampled(name, seqs):
-    """The 21.3x capacity shape (768 x 4096, narrow fold) and the Ouro-1.4B 4x layer
-    (32 x 4096, wide fold) with shuffled pages: one (layer, loop) call as the bench times
-    it; bit-identical to the dense cache, sampled sequences against the oracle."""
+    """The 21.3x capacity shape (768 x 4096, narrow fold), the Ouro-1.4B 4x layer
+    (32 x 4096, wide fold) and LLA-2D at 16 x 16384 (LLA-2D kernel) with shuffled pages:
+    one (layer, loop) call as the bench times it; bit-identical to the dense cache,
+    sampled sequences against the oracle."""
     w = WORKLOADS[name].replace(D=1)
     announce(f"paged {name} full launch, B={w.batch} n={w.n}")
     st = DeviceLatentStore(w, seed=79)
