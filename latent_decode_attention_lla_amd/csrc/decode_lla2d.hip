@@ -107,11 +107,10 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int NIV = (16 * VSP + 63) / 64;
   constexpr int STAGE_BLOCKS = NIK + NIV + NKS;  // 1 KiB blocks
   constexpr int RING_UNITS = kStages * STAGE_BLOCKS * 64;
-  constexpr int XCH_UNITS = 0;
   constexpr int P_UNITS = 2 * 16 * 16 * 2 / 16;
   constexpr int AL_UNITS = 2 * 16 * 4 / 16;
   constexpr int PAGE_UNITS = PAGED ? kMaxSplitPages * 4 / 16 : 0;  // the split's page indices
-  constexpr int LDS_UNITS = RING_UNITS + XCH_UNITS + P_UNITS + AL_UNITS + PAGE_UNITS;
+  constexpr int LDS_UNITS = RING_UNITS + P_UNITS + AL_UNITS + PAGE_UNITS;
   static_assert(NW * 16 * WT_STRIDE * 2 / 16 <= RING_UNITS, "prologue staging fits the ring");
   static_assert(HG * RV + 2 * HG <= RING_UNITS * 4, "epilogue staging fits the ring");
   static_assert(RK % 16 == 0 && RV % 16 == 0 && D % 32 == 0 && HG <= 16, "shape");
@@ -122,9 +121,9 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
                         (NIK / NW + NIV / NW + NKS / NW) <= 3, "load counts");
 
   __shared__ u32x4 lds[LDS_UNITS];
-  uint16_t* ptile = reinterpret_cast<uint16_t*>(lds + RING_UNITS + XCH_UNITS);  // [2][16][16]
-  float* alpha_buf = reinterpret_cast<float*>(lds + RING_UNITS + XCH_UNITS + P_UNITS);  // [2][16]
-  int* split_pages = reinterpret_cast<int*>(lds + RING_UNITS + XCH_UNITS + P_UNITS + AL_UNITS);
+  uint16_t* ptile = reinterpret_cast<uint16_t*>(lds + RING_UNITS);                 // [2][16][16]
+  float* alpha_buf = reinterpret_cast<float*>(lds + RING_UNITS + P_UNITS);           // [2][16]
+  int* split_pages = reinterpret_cast<int*>(lds + RING_UNITS + P_UNITS + AL_UNITS);  // [pages]
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
