@@ -234,6 +234,20 @@ def test_bf16_table8_ranks_every_output(d, r_k, r_v, variant):
         assert err <= BF16_TOL
 
 
+@pytest.mark.parametrize("name", ["capacity_21x", "ouro_layer_4x", "lla2d_long"])
+@pytest.mark.parametrize("T", [2, 8])
+def test_bf16_other_loop_counts(name, T):
+    """Loop counts other than Ouro's 4 (the codec's stacked contraction is T d_in long
+    and W_up, mu are sliced per loop): every loop in one call, folded path, two splits."""
+    w = WORKLOADS[name].replace(D=1, batch=2, n=150, T=T, H=4)
+    st = DeviceLatentStore(w, seed=31)
+    out = st.decode(0, 0, T, opts=lla.make_opts(2, FOLD))
+    ref = oracle_decode(st, 0, 0, T, range(w.batch), w.n)
+    err = max_abs(f64(out), ref)
+    announce(f"{name} T={T}: {rel_note(err, BF16_TOL)}")
+    assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("path", BF16_PATHS)
 def test_bf16_ragged_contexts_poisoned_tail(path):
     """Ragged per-sequence lengths with NaN in every cache row past a sequence's length."""
