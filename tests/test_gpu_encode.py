@@ -211,6 +211,8 @@ def test_encode_heavy_full_svd_codec():
     ("ouro_layer_4x", 2, 8197, False,       # stream with K = 256, r = 256 (8 waves) and 24
      {"d": 64, "H": 4, "r_k": 256, "r_v": 24}),
     ("lla2d_long", 5, 13109, True, {}),     # LLA-2D: ring kernel, contraction 8192
+    ("ouro_layer_4x", 2, 2049, False, {"T": 8}),  # per head, contraction 1024: ring kernel
+    ("ouro_layer_4x", 2, 3001, False, {"T": 2}),  # per head, contraction 256: stream, 8 steps
 ])
 def test_encode_long_prompt_ragged(name, batch, n_new, sampled, over):
     """Long prompts take the streaming encodes; token counts that are not a multiple of
