@@ -150,6 +150,11 @@ def cpu_baseline(w, seqs: int):
             q = t["q"][layer, loop:loop + 1].transpose(1, 2, 0, 3)
             if w.teacher:
                 O.decode_teacher(t["k_cache"][layer], t["v_cache"][layer], q, loop)
+            elif w.paged and w.d_rope > 0:
+                O.decode_absorbed_paged(t["c_k"][layer], t["c_v"][layer], t["k_rope"][layer],
+                                        t["block_table"], t["w_up_k"][layer], t["mu_k"][layer],
+                                        t["w_up_v"][layer], t["mu_v"][layer], q, w.d_rope, loop,
+                                        None, w.n, None, variant)
             elif w.paged:
                 O.decode_paged(t["c_k"][layer], t["c_v"][layer], t["block_table"], t["w_up_k"][layer],
                                t["mu_k"][layer], t["w_up_v"][layer], t["mu_v"][layer], q, loop, None,
@@ -429,8 +434,11 @@ def main():
         S = lla.lla_decode_teacher_num_splits(st.dims, w.n, 1, opts)
         ws = st.workspace(w.n, 1, opts)
     elif absorbed:
-        S = lla.lla_decode_num_splits(st.dims, w.n, 1, lla.make_opts(args.splits, lla.LLA_PATH_RECONSTRUCT))
-        ws = st.absorbed_workspace(w.n, 1, opts)
+        # the workspace holds one (max, sum, r_v accumulators) partial per split
+        nb = (lla.lla_decode_absorbed_paged_workspace_bytes if w.paged else
+              lla.lla_decode_absorbed_workspace_bytes)(st.dims, w.d_rope, w.n, 1, opts)
+        S = nb // (w.batch * w.H * (2 + w.r_v) * 4)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
     elif w.paged:
         S = lla.lla_decode_paged_num_splits(st.dims, w.n, 1, opts)
         ws = torch.empty(max(lla.lla_decode_paged_workspace_bytes(st.dims, w.n, 1, opts), 256),
@@ -470,6 +478,10 @@ def main():
                 if teacher:
                     lla.lla_decode_attn_teacher(st.dims, st.t["k_cache"], st.t["v_cache"], layer, w.n,
                                                 None, q, loop, 1, out, ws, ws.numel(), opts, sp)
+                elif w.paged and absorbed:
+                    lla.lla_decode_attn_absorbed_paged(st.dims, st.codec, st.cache, st.pages,
+                                                       st.t["k_rope"], w.d_rope, layer, w.n, None,
+                                                       q, loop, 1, out, ws, ws.numel(), opts, sp)
                 elif w.paged:
                     lla.lla_decode_attn_paged(st.dims, st.codec, st.cache, st.pages, layer, w.n,
                                               None, q, loop, 1, out, ws, ws.numel(), opts, sp)
@@ -521,16 +533,26 @@ def main():
         reference = {}
         for name, pth in (("rotary_fold_full_rope", lla.LLA_PATH_AUTO), ("reconstruct", lla.LLA_PATH_RECONSTRUCT)):
             o = lla.make_opts(0, pth)
-            wsr = st.workspace(w.n, 1, o)
             q = st.t["q"][0, 0]
+            if w.paged:
+                wsr = torch.empty(max(lla.lla_decode_paged_workspace_bytes(st.dims, w.n, 1, o), 256),
+                                  dtype=torch.uint8, device=dev)
+            else:
+                wsr = st.workspace(w.n, 1, o)
+
+            def ref_call():
+                if w.paged:
+                    lla.lla_decode_attn_paged(st.dims, st.codec, st.cache, st.pages, 0, w.n, None,
+                                              q, 0, 1, out, wsr, wsr.numel(), o, sp)
+                else:
+                    lla.lla_decode_attn(st.dims, st.codec, st.cache, 0, w.n, None, q, 0, 1, out,
+                                        wsr, wsr.numel(), o, sp)
             for _ in range(2):
-                lla.lla_decode_attn(st.dims, st.codec, st.cache, 0, w.n, None, q, 0, 1, out, wsr,
-                                    wsr.numel(), o, sp)
+                ref_call()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(5):
-                lla.lla_decode_attn(st.dims, st.codec, st.cache, 0, w.n, None, q, 0, 1, out, wsr,
-                                    wsr.numel(), o, sp)
+                ref_call()
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / 5
@@ -580,8 +602,9 @@ def main():
                    "decode_calls_per_step": n_dec, "encode_calls_per_step": n_enc,
                    **({"d_rope": w.d_rope} if absorbed else {})},
         "roofline": dec_roof if dominant == "decode" else enc_roof,
-        "roofline_kernel": {"teacher": "lla_decode_attn_teacher", "absorbed": "lla_decode_attn_absorbed",
-                            "paged": "lla_decode_attn_paged", "decode": "lla_decode_attn"}[dec_kind]
+        "roofline_kernel": ("lla_decode_attn_absorbed_paged" if absorbed and w.paged else
+                            {"teacher": "lla_decode_attn_teacher", "absorbed": "lla_decode_attn_absorbed",
+                             "paged": "lla_decode_attn_paged", "decode": "lla_decode_attn"}[dec_kind])
                            if dominant == "decode" else "lla_encode",
         "cpu_baseline": cpu,
         "decode_call": {"avg_ms": round(dec_ms, 5), "median_ms": round(dec_med, 5),

@@ -25,6 +25,8 @@ Table 5):
                     layer's pool in a random order, found through a block table
 * ``paged_ouro_4x`` the Ouro-1.4B 4x geometry (96, 160) for all 24 layers, 32 sequences at
                     context 4096, in a paged cache (the wide fold kernel)
+* ``paged_absorbed_4x`` ``absorbed_4x`` over a paged cache: latents and rotary keys in
+                    shuffled 16-token pages under one block table per sequence
 * ``teacher_4k``    the uncompressed loop-indexed cache the latent store replaces (Section
                     3 "Teacher cache"; Table 5's teacher column): T=4, D=24, H=16, d=128,
                     bf16 keys and values for every loop, batch 32 (the teacher's measured
@@ -107,6 +109,8 @@ WORKLOADS = {
                           n=4096, paged=True),
     "paged_ouro_4x": Workload("paged_ouro_4x", T=4, D=24, H=16, d=128, r_k=96, r_v=160,
                               batch=32, n=4096, paged=True),
+    "paged_absorbed_4x": Workload("paged_absorbed_4x", T=4, D=24, H=16, d=128, r_k=96,
+                                  r_v=160, batch=8, n=32768, d_rope=64, paged=True),
     "prefill_64k": Workload("prefill_64k", T=4, D=24, H=16, d=128, r_k=96, r_v=160, batch=1,
                             n=65536, stream_prefill=True),
     "teacher_4k": Workload("teacher_4k", T=4, D=24, H=16, d=128, r_k=0, r_v=0, batch=32,
@@ -154,7 +158,8 @@ def decode_inputs(w: Workload, seed: int, device="cpu", n_alloc: int | None = No
 def paged_decode_inputs(w: Workload, seed: int, device="cpu"):
     """decode_inputs with the latents drawn straight into page pools [D][P][Hc][16][r]
     (P = batch * ceil(n / 16) pages) and a block table [batch][ceil(n / 16)] int32 that
-    deals the pages out in a random order."""
+    deals the pages out in a random order; with a rotary branch, its keys in a pool
+    [D][P][H][16][d_rope] under the same table."""
     npg = (w.n + 15) // 16
     P = w.batch * npg
     g = _gen(seed, device)
@@ -170,6 +175,8 @@ def paged_decode_inputs(w: Workload, seed: int, device="cpu"):
     }
     perm = torch.randperm(P, generator=g, device=device)
     out["block_table"] = perm.reshape(w.batch, npg).to(torch.int32)
+    if w.d_rope > 0:  # rotary keys of the decoupled decode, paged like the latents
+        out["k_rope"] = _randn((w.D, P, w.H, 16, w.d_rope), 1.0, dt, g, device)
     return out
 
 
