@@ -67,6 +67,27 @@ def _oracle_latents(st, layer, x, axis, dtype):
     return out, delta
 
 
+def _svd_codec(w, xk, xv, seed):
+    """Codec maps of one layer from the SVD initialisation (Section 3) of a seeded
+    4096-token calibration subsample of the prompt's per-loop K/V."""
+    rng = np.random.default_rng(seed)
+    calib = rng.choice(w.batch * w.n, size=4096, replace=False)
+    codec = {}
+    for axis, x in (("k", xk), ("v", xv)):
+        r = w.r_k if axis == "k" else w.r_v
+        xs = f64(x.reshape(w.batch * w.n, w.H, w.T * w.d)[torch.as_tensor(calib, device=x.device)])
+        wd = np.empty((1, w.H, w.T * w.d, r))
+        wu = np.empty((1, w.T, w.H, w.d, r))
+        mu = np.empty((1, w.H, w.T * w.d))
+        for h in range(w.H):
+            m, W, Wu = O.svd_init(xs[:, h], r, w.T, w.d)
+            wd[0, h], mu[0, h], wu[0, :, h] = W, m, Wu
+        codec[f"w_down_{axis}"] = torch.from_numpy(wd)
+        codec[f"w_up_{axis}"] = torch.from_numpy(wu)
+        codec[f"mu_{axis}"] = torch.from_numpy(mu)
+    return codec
+
+
 def _check_latents(got, ref_delta, dtype):
     ref, delta = ref_delta
     if dtype == "bf16":
@@ -176,22 +197,7 @@ def test_encode_heavy_full_svd_codec():
     w = WORKLOADS["encode_heavy"]
     announce("encode_heavy full: SVD codec, encode 8x8192, decode at 8192")
     xk, xv = encode_x(w, w.n, seed=10, device="cuda", correlated=True)
-    rng = np.random.default_rng(10)
-    calib = rng.choice(w.batch * w.n, size=4096, replace=False)
-    codec = {}
-    for axis, x in (("k", xk), ("v", xv)):
-        r = w.r_k if axis == "k" else w.r_v
-        xs = f64(x.reshape(w.batch * w.n, w.H, w.T * w.d)[torch.as_tensor(calib, device="cuda")])
-        wd = np.empty((1, w.H, w.T * w.d, r))
-        wu = np.empty((1, w.T, w.H, w.d, r))
-        mu = np.empty((1, w.H, w.T * w.d))
-        for h in range(w.H):
-            m, W, Wu = O.svd_init(xs[:, h], r, w.T, w.d)
-            wd[0, h], mu[0, h], wu[0, :, h] = W, m, Wu
-        codec[f"w_down_{axis}"] = torch.from_numpy(wd)
-        codec[f"w_up_{axis}"] = torch.from_numpy(wu)
-        codec[f"mu_{axis}"] = torch.from_numpy(mu)
-    st = _store_for_encode(w, codec, seed=10)
+    st = _store_for_encode(w, _svd_codec(w, xk, xv, seed=10), seed=10)
     st.encode(0, xk, xv, 0, w.n)
     torch.cuda.synchronize()
     seqs = [3]
