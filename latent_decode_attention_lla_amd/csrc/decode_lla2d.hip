@@ -90,6 +90,23 @@ __device__ __forceinline__ void wait_loads(int n) {
   else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N - 3) : "memory");
 }
 
+#ifndef LLA_2D_WAVE_SPECIALIZE
+#define LLA_2D_WAVE_SPECIALIZE 1
+#endif
+
+// f(std::integral_constant<int, w>) for a wave-uniform w in [I, N): the tile loop compiled
+// once per wave of the workgroup, so which ring blocks and value tiles a wave owns are
+// compile-time constants
+template <int I, int N, class F>
+__device__ __forceinline__ void with_wave(int w, F& f) {
+  if constexpr (I + 1 < N) {
+    if (w == I) f(std::integral_constant<int, I>{});
+    else with_wave<I + 1, N>(w, f);
+  } else {
+    f(std::integral_constant<int, I>{});
+  }
+}
+
 template <int D, int RK, int RV, int HG, bool PAGED>
 __global__ __launch_bounds__(64 * HG) __attribute__((amdgpu_waves_per_eu(LLA_2D_WAVES_PER_EU)))
 void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
@@ -209,18 +226,10 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   const int tile_max = s1 > 0 ? (s1 - 1) >> 4 : 0;
   // Block slots of this wave by kind: NSK key, NSV value and NST table slots; slot j of a
   // kind loads block wave + NW j of it, if the kind has that many blocks (waves with fewer
-  // blocks issue fewer loads per tile: nload). Per slot this lane keeps the token row it
-  // loads and its byte offset in the tile (row * row size + column).
+  // blocks issue fewer loads per tile). Per slot this lane keeps the token row it loads and
+  // its byte offset in the tile (row * row size + column).
   constexpr int NSK = (NIK + NW - 1) / NW, NSV = (NIV + NW - 1) / NW, NST = (NKS + NW - 1) / NW;
   constexpr int NSLOT = NSK + NSV + NST;
-  auto has = [&](int j, int blocks) { return wave + NW * j < blocks; };  // wave-uniform
-  int nload = 0;
-#pragma unroll
-  for (int j = 0; j < NSK; ++j) nload += has(j, NIK);
-#pragma unroll
-  for (int j = 0; j < NSV; ++j) nload += has(j, NIV);
-#pragma unroll
-  for (int j = 0; j < NST; ++j) nload += has(j, NKS);
   int kblk[NSK], krow[NSK], vblk[NSV], vrow[NSV], tblk[NST];
   uint32_t koff[NSK], voff[NSV], toff[NST];
 #pragma unroll
@@ -261,7 +270,9 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   int page_next = PAGED && ntile > 0 ? page_for(0) : 0;  // read one issue ahead
   // Sources are a wave-uniform base plus this lane's 32-bit offset. Tiles past the last
   // (the ring's run-out) load the last tile's rows again.
-  auto issue = [&](int tl) {
+  auto issue = [&](auto wc, int tl) {
+    const int W = wc;
+    auto has = [&](int j, int blocks) { return W + NW * j < blocks; };
     u32x4* stage = lds + (tl % kStages) * STAGE_BLOCKS * 64;
     const char* tb = tab_g + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * (NKS * 1024);
 #pragma unroll
@@ -305,7 +316,8 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   for (int k = 0; k < VT; ++k) vacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // value product of tile cc: rescale by the tile's alphas, then acc += P(cc) C_v(cc)
-  auto value_step = [&](int cc) {
+  auto value_step = [&](auto wc, int cc) {
+    const int W = wc;
     const char* vreg = reinterpret_cast<const char*>(lds + (cc % kStages) * STAGE_BLOCKS * 64 + NIK * 64);
     const f32x4 al = *reinterpret_cast<const f32x4*>(alpha_buf + (cc & 1) * 16 + 4 * hi);
     const i16x4 pa = *reinterpret_cast<const i16x4*>(ptile + (cc & 1) * 256 + lo * 16 + 4 * hi);
@@ -314,13 +326,13 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
     i16x4 vb[VT];
 #pragma unroll
     for (int k = 0; k < VT; ++k) {
-      const char* col = vreg + (16 * min(wave + NW * k, NRT - 1) + lo) * 2 + 4 * hi * (VSP * 16);
+      const char* col = vreg + (16 * min(W + NW * k, NRT - 1) + lo) * 2 + 4 * hi * (VSP * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) vb[k][i] = *reinterpret_cast<const short*>(col + i * (VSP * 16));
     }
 #pragma unroll
     for (int k = 0; k < VT; ++k) {
-      if (wave + NW * k < NRT) {
+      if (W + NW * k < NRT) {
         f32x4 acc = vacc[k];
         acc[0] *= al[0];
         acc[1] *= al[1];
@@ -374,19 +386,34 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   if (threadIdx.x < 32) alpha_buf[threadIdx.x] = 1.f;
   for (int i = static_cast<int>(threadIdx.x); i < 2 * (16 - HG) * 16; i += 64 * HG)
     ptile[(i / ((16 - HG) * 16)) * 256 + HG * 16 + i % ((16 - HG) * 16)] = 0;
-  if (ntile > 0) {
-    issue(0);
-    issue(1);
+  auto ring_loop = [&](auto wc) {
+    const int W = wc;
+    int nl = 0;  // this wave's loads per tile
+#pragma unroll
+    for (int j = 0; j < NSK; ++j) nl += W + NW * j < NIK;
+#pragma unroll
+    for (int j = 0; j < NSV; ++j) nl += W + NW * j < NIV;
+#pragma unroll
+    for (int j = 0; j < NST; ++j) nl += W + NW * j < NKS;
+    issue(wc, 0);
+    issue(wc, 1);
     for (int c = 0; c <= ntile; ++c) {
         // tile c has landed once only tile c + 1's loads are outstanding; the barrier then
         // publishes every wave's blocks of tile c and the weights of tile c - 1, and tells
         // that tile c - 2's stage is free for tile c + 2
-        wait_loads<NSLOT>(nload);
+        wait_loads<NSLOT>(nl);
         ring_barrier();
-        issue(c + 2);
-        if (c > 0) value_step(c - 1);
+        issue(wc, c + 2);
+        if (c > 0) value_step(wc, c - 1);
         if (c < ntile) score_step(c);
     }
+  };
+  if (ntile > 0) {
+#if LLA_2D_WAVE_SPECIALIZE
+    with_wave<0, NW>(wave, ring_loop);
+#else
+    ring_loop(wave);
+#endif
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in the reused LDS
   __syncthreads();
