@@ -485,8 +485,13 @@ void launch(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
 
 }  // namespace
 
+// Heads per workgroup: LLA_2D_HG when H is a multiple of it (one workgroup per CU, the
+// stage's rows shared by more heads), else LLA_2D_HG_MIN, which H must be a multiple of.
 #ifndef LLA_2D_HG
-#define LLA_2D_HG 4  // heads per workgroup
+#define LLA_2D_HG 8
+#endif
+#ifndef LLA_2D_HG_MIN
+#define LLA_2D_HG_MIN 4
 #endif
 // M^T of (r_k + 16) x d float16 stays in one wave's registers: r_k <= 96 at d = 128
 #define LLA_2D_SHAPES(X) \
@@ -494,7 +499,7 @@ void launch(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
   X(128, 64, 64)
 
 bool decode_lla2d_supported(int dtype, int d, int r_k, int r_v, int H) {
-  if (!LLA_2D_ENABLE || dtype != 1 || H % LLA_2D_HG != 0) return false;
+  if (!LLA_2D_ENABLE || dtype != 1 || H % LLA_2D_HG_MIN != 0) return false;
 #define X(D_, RK_, RV_) \
   if (d == D_ && r_k == RK_ && r_v == RV_) return true;
   LLA_2D_SHAPES(X)
@@ -506,7 +511,10 @@ bool launch_decode_lla2d(int dtype, int d, int r_k, int r_v, const DecodeArgs& a
   if (a.variant != 1 || !decode_lla2d_supported(dtype, d, r_k, r_v, a.H)) return false;
 #define X(D_, RK_, RV_)                                      \
   if (d == D_ && r_k == RK_ && r_v == RV_) {                 \
-    launch<D_, RK_, RV_, LLA_2D_HG, false>(a, PageArgs{}, s); \
+    if (a.H % LLA_2D_HG == 0)                                \
+      launch<D_, RK_, RV_, LLA_2D_HG, false>(a, PageArgs{}, s); \
+    else                                                     \
+      launch<D_, RK_, RV_, LLA_2D_HG_MIN, false>(a, PageArgs{}, s); \
     return true;                                             \
   }
   LLA_2D_SHAPES(X)
@@ -520,7 +528,10 @@ bool launch_decode_lla2d_paged(int dtype, int d, int r_k, int r_v, const DecodeA
     return false;
 #define X(D_, RK_, RV_)                                \
   if (d == D_ && r_k == RK_ && r_v == RV_) {           \
-    launch<D_, RK_, RV_, LLA_2D_HG, true>(a, pg, s);   \
+    if (a.H % LLA_2D_HG == 0)                          \
+      launch<D_, RK_, RV_, LLA_2D_HG, true>(a, pg, s); \
+    else                                               \
+      launch<D_, RK_, RV_, LLA_2D_HG_MIN, true>(a, pg, s); \
     return true;                                       \
   }
   LLA_2D_SHAPES(X)
