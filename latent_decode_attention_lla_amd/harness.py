@@ -14,7 +14,7 @@ from .inputs import Workload, decode_inputs, teacher_inputs
 def dims_for(w: Workload, n_max: int | None = None, batch: int | None = None) -> lla.lla_dims:
     return lla.make_dims(w.T, w.D, w.H, w.d, w.r_k, w.r_v, batch or w.batch, n_max or w.n,
                          lla.LLA_PER_HEAD if w.variant == "per_head" else lla.LLA_2D,
-                         lla.LLA_F32 if w.dtype == "f32" else lla.LLA_BF16, w.rope_base, 0.0)
+                         lla.LLA_F32 if w.dtype == "f32" else lla.LLA_BF16, w.rope_base, w.scale)
 
 
 class DeviceLatentStore:

@@ -71,6 +71,7 @@ class Workload:
     variant: str = "per_head"      # "per_head" or "2d"
     dtype: str = "bf16"            # "f32" or "bf16" (latents and codec weights)
     rope_base: float = 10000.0
+    scale: float = 0.0             # score scale; 0 selects 1/sqrt(d)
     d_rope: int = 0                # rotary-branch width of the decoupled (absorbed) decode
     teacher: bool = False          # an uncompressed per-loop cache (no codec)
     stream_prefill: bool = False   # a step is the layer-by-layer two-pass prefill

@@ -33,6 +33,11 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
+def oracle_scale(w):
+    """The score scale a workload asks for (None: the oracle's default 1/sqrt(d))."""
+    return None if w.scale == 0.0 else float(w.scale)
+
+
 def oracle_decode(store, layer: int, loop_begin: int, loop_count: int, seqs, n_ctx: int,
                   ctx_lens=None, q=None):
     """fp64 oracle on sequences ``seqs`` of a DeviceLatentStore's cache (stored values)."""
@@ -48,7 +53,7 @@ def oracle_decode(store, layer: int, loop_begin: int, loop_count: int, seqs, n_c
     qq = f64(qq.index_select(0, idx))
     lens = None if ctx_lens is None else [int(ctx_lens[i]) for i in seqs]
     return O.decode(ck, cv, f64(t["w_up_k"][layer]), f64(t["mu_k"][layer]), f64(t["w_up_v"][layer]),
-                    f64(t["mu_v"][layer]), qq, loop_begin, lens, w.rope_base, None,
+                    f64(t["mu_v"][layer]), qq, loop_begin, lens, w.rope_base, oracle_scale(w),
                     "per_head" if w.variant == "per_head" else "2d")
 
 
@@ -66,7 +71,7 @@ def oracle_decode_absorbed(store, layer: int, loop_begin: int, loop_count: int, 
     lens = None if ctx_lens is None else [int(ctx_lens[i]) for i in seqs]
     return O.decode_absorbed(ck, cv, kr, f64(t["w_up_k"][layer]), f64(t["mu_k"][layer]),
                              f64(t["w_up_v"][layer]), f64(t["mu_v"][layer]), qq, w.d_rope,
-                             loop_begin, lens, None,
+                             loop_begin, lens, oracle_scale(w),
                              "per_head" if w.variant == "per_head" else "2d")
 
 
@@ -83,7 +88,7 @@ def oracle_decode_teacher(cache, layer: int, loop_begin: int, loop_count: int, s
     qq = t["q"][layer, loop_begin:loop_begin + loop_count].permute(1, 2, 0, 3) if q is None else q
     qq = qq.index_select(0, idx).index_select(1, hs)
     lens = None if ctx_lens is None else [int(ctx_lens[i]) for i in seqs]
-    return O.decode_teacher(f64(kc), f64(vc), f64(qq), loop_begin, lens, None)
+    return O.decode_teacher(f64(kc), f64(vc), f64(qq), loop_begin, lens, oracle_scale(cache.w))
 
 
 def max_abs(a, b) -> float:

@@ -294,6 +294,62 @@ def pin_special_cases() -> float:
     return err
 
 
+def pin_large_alpha_limit() -> float:
+    """q = alpha * K~_t[j*] for a late token j*: as alpha grows the softmax concentrates on
+    j*, so the output tends to that token's rebuilt value V_t[j*] (attention is unchanged,
+    Figure 1 caption; the value side of Eq. 3). The scores are formed here independently
+    (explicit reconstruction, RoPE by complex multiplication); the oracle's output must lie
+    within the bound (1 - a_j*) max_j |V_t[j] - V_t[j*]| <= sum_{j != j*} exp(s_j - s_j*)
+    max_j |V_t[j] - V_t[j*]| of V_t[j*], and at alpha = 32 it must equal V_t[j*] to 1e-9.
+    The largest scores are then several hundred, so the pin also needs a softmax that does
+    not overflow."""
+    worst = 0.0
+    for variant, seed in (("per_head", 57), ("2d", 58)):
+        a = _tiny(seed, T=2, H=2, d=16, n=40, r_k=6, r_v=5, B=2, variant=variant)
+        T, H, d = 2, 2, 16
+        n = a["c_k"].shape[2]
+        scale = 1.0 / math.sqrt(d)
+        pos = torch.arange(n)
+        for alpha in (8.0, 32.0):
+            q = np.zeros_like(a["q"])
+            expect = np.zeros_like(a["q"])
+            bound = np.zeros(a["q"].shape[:3])
+            for b in range(2):
+                for h in range(H):
+                    hc = h if variant == "per_head" else 0
+                    for t in range(T):
+                        if variant == "per_head":
+                            mk, mv = a["mu_k"][h][t * d:(t + 1) * d], a["mu_v"][h][t * d:(t + 1) * d]
+                        else:
+                            mk = a["mu_k"][0][(t * H + h) * d:(t * H + h + 1) * d]
+                            mv = a["mu_v"][0][(t * H + h) * d:(t * H + h + 1) * d]
+                        k_hat = a["c_k"][b, hc] @ a["w_up_k"][t, h].T + mk
+                        v_hat = a["c_v"][b, hc] @ a["w_up_v"][t, h].T + mv
+                        k_rot = _textbook_rope_complex(torch.from_numpy(k_hat), pos, 10000.0).numpy()
+                        # j*: among the last 8 tokens, the one whose own score beats every
+                        # other token's by the widest margin
+                        gram = k_rot @ k_rot.T
+                        cand = range(n - 8, n)
+                        margin = [min(gram[j, j] - gram[i, j] for i in range(n) if i != j) for j in cand]
+                        js = list(cand)[int(np.argmax(margin))]
+                        assert max(margin) > 0.0
+                        q[b, h, t] = alpha * k_rot[js]
+                        s = scale * (k_rot @ q[b, h, t])
+                        rest = np.exp(np.delete(s, js) - s[js]).sum()
+                        spread = np.max(np.abs(v_hat - v_hat[js]))
+                        expect[b, h, t] = v_hat[js]
+                        bound[b, h, t] = rest * spread + 1e-12
+            got = O.decode(a["c_k"], a["c_v"], a["w_up_k"], a["mu_k"], a["w_up_v"], a["mu_v"], q,
+                           0, None, 10000.0, None, variant)
+            dev = np.max(np.abs(got - expect), axis=-1)
+            if not np.all(np.isfinite(dev)):
+                return float("inf")
+            worst = max(worst, float(np.max(dev - bound)))
+            if alpha == 32.0:  # the limit is reached: o_t equals V_t[j*] to 1e-9
+                worst = max(worst, float(np.max(dev)) - 1e-9)
+    return max(worst, 0.0)
+
+
 def pin_lla2d_block_diagonal() -> float:
     """LLA-2D with a block-diagonal codec (head h owns latent columns h*r_h ..) must equal
     per-head LLA with rank r_h (Section 3, "The LLA-2D variant": one latent per token
@@ -681,6 +737,7 @@ ALL_PINS = {
     "full_rank_textbook": (pin_full_rank_textbook, 1e-12),
     "brute_force": (pin_brute_force, 1e-12),
     "special_cases": (pin_special_cases, 1e-12),
+    "large_alpha_limit": (pin_large_alpha_limit, 1e-12),
     "lla2d_block_diagonal": (pin_lla2d_block_diagonal, 1e-12),
     "round_bf16": (pin_round_bf16, 0.0),
     "absorbed_textbook": (pin_absorbed_textbook, 1e-12),

@@ -190,20 +190,25 @@ def test_lla2d_full_launch_sampled(path):
 
 
 @pytest.mark.parametrize("path", BF16_PATHS)
-@pytest.mark.parametrize("batch,n,splits", [(2, 200, 0), (2, 200, 1), (2, 200, 3), (3, 17, 1), (9, 64, 2)])
-def test_lla2d_small_every_output(path, batch, n, splits):
-    w = WORKLOADS["lla2d_long"].replace(D=1, batch=batch, n=n)
+@pytest.mark.parametrize("H,batch,n,splits", [
+    (16, 2, 200, 0), (16, 2, 200, 1), (16, 2, 200, 3), (16, 3, 17, 1), (16, 9, 64, 2),
+    # H not a multiple of 8: the LLA-2D kernel's 4-heads-per-workgroup instance, one and
+    # three splits (H = 12: three workgroups per (sequence, loop, split))
+    (4, 2, 200, 1), (4, 2, 200, 3), (12, 2, 200, 1), (12, 3, 200, 3)])
+def test_lla2d_small_every_output(path, H, batch, n, splits):
+    w = WORKLOADS["lla2d_long"].replace(D=1, batch=batch, n=n, H=H)
     st = DeviceLatentStore(w, seed=6)
     out = st.decode(0, 0, 4, opts=lla.make_opts(splits, path))
     ref = oracle_decode(st, 0, 0, 4, range(batch), n)
     err = max_abs(f64(out), ref)
-    announce(f"lla2d B={batch} n={n} splits={splits} path={path}: {rel_note(err, BF16_TOL)}")
+    announce(f"lla2d H={H} B={batch} n={n} splits={splits} path={path}: {rel_note(err, BF16_TOL)}")
     assert err <= BF16_TOL
 
 
 @pytest.mark.parametrize("path", BF16_PATHS)
-def test_lla2d_ragged_poisoned(path):
-    w = WORKLOADS["lla2d_long"].replace(D=1, batch=4, n=150)
+@pytest.mark.parametrize("H", [16, 4, 12])
+def test_lla2d_ragged_poisoned(path, H):
+    w = WORKLOADS["lla2d_long"].replace(D=1, batch=4, n=150, H=H)
     st = DeviceLatentStore(w, seed=7, n_alloc=160)
     lens = [150, 33, 1, 0]
     for b, n_b in enumerate(lens):

@@ -44,9 +44,12 @@ def _oracle_paged(st, layer, loop_begin, loop_count, seqs, n_ctx, ctx_lens=None)
     ("ouro_layer_4x", {}, lla.LLA_PATH_AUTO, 0),
     ("ouro_layer_4x", {}, lla.LLA_PATH_RECONSTRUCT, 2),
     ("tiny_f32", {}, lla.LLA_PATH_AUTO, 0),                # float32: reconstruct path
-    ("lla2d_long", {}, lla.LLA_PATH_AUTO, 0),               # wide fold, shared latent plane
+    ("lla2d_long", {}, lla.LLA_PATH_AUTO, 0),               # LLA-2D kernel, 4 heads per workgroup
     ("lla2d_long", {}, lla.LLA_PATH_AUTO, 3),
     ("lla2d_long", {}, lla.LLA_PATH_RECONSTRUCT, 0),
+    ("lla2d_long", {"H": 16}, lla.LLA_PATH_AUTO, 1),        # LLA-2D kernel, 8 heads per workgroup
+    ("lla2d_long", {"H": 16}, lla.LLA_PATH_AUTO, 3),
+    ("lla2d_long", {"H": 12}, lla.LLA_PATH_AUTO, 3),        # 4 heads per workgroup, 3 groups
     ("lla2d_long", {"r_k": 64, "r_v": 64}, lla.LLA_PATH_AUTO, 2),     # LLA-2D kernel, other ranks
     ("lla2d_long", {"r_k": 128, "r_v": 128}, lla.LLA_PATH_AUTO, 0),   # wide fold, shared plane
     ("ouro_layer_4x", {"r_k": 64, "r_v": 64}, lla.LLA_PATH_AUTO, 3),  # wide fold, per head
@@ -54,8 +57,8 @@ def _oracle_paged(st, layer, loop_begin, loop_count, seqs, n_ctx, ctx_lens=None)
 def test_shuffled_pool_matches_dense_and_oracle(name, over, path, splits):
     """The dense and paged decodes run the same kernel (narrow fold, wide fold or
     reconstruct) on the same rows, so they must agree bit for bit."""
-    w = WORKLOADS[name].replace(batch=3, n=300, D=2, **({"H": 4} if name != "tiny_f32" else {}),
-                                **over)
+    heads = {} if name == "tiny_f32" or "H" in over else {"H": 4}
+    w = WORKLOADS[name].replace(batch=3, n=300, D=2, **heads, **over)
     st = DeviceLatentStore(w, seed=71)
     lens = [300, 133, 1]
     ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")

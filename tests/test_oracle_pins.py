@@ -59,6 +59,15 @@ def _mut_attention_softmax_over_wrong_axis(q, k, v, scale):
     return a[::-1] @ v
 
 
+def _mut_attention_no_max_shift(q, k, v, scale):
+    """Softmax without subtracting the largest score: overflows for large scores."""
+    if k.shape[0] == 0:
+        return np.zeros(v.shape[-1])
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(scale * (k @ q))
+        return (e / e.sum()) @ v
+
+
 def _mut_mu_slice_2d_head_major(mu, variant, t, h, H, d):
     if variant == "per_head":
         return mu[h, t * d:(t + 1) * d]
@@ -177,6 +186,7 @@ MUTANTS = {
     "encode_no_centering": ("encode", _mut_encode_no_center),
     "attention_no_scale": ("attention", _mut_attention_no_scale),
     "attention_reversed_weights": ("attention", _mut_attention_softmax_over_wrong_axis),
+    "attention_no_max_shift": ("attention", _mut_attention_no_max_shift),
     "mu_2d_head_major": ("_mu_slice", _mut_mu_slice_2d_head_major),
     "mu_wrong_loop": ("_mu_slice", _mut_mu_slice_wrong_loop),
     "svd_no_centering": ("svd_init", _mut_svd_no_center),
