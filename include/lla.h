@@ -21,7 +21,8 @@
  * Conventions shared by every entry point
  *   - All pointers named as device pointers must point to HIP device memory (or memory
  *     the device can address) and be 16-byte aligned. The caller owns every buffer; the
- *     library allocates nothing and keeps no state beyond cached device properties.
+ *     library allocates nothing and keeps no state beyond cached device properties and
+ *     the fixed scratch array of lla_decode_attn_noalloc.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and is
  *     asynchronous: no host synchronisation happens inside the library.
  *   - Arguments are validated on the host before anything is enqueued. A rejected call
@@ -317,6 +318,25 @@ int32_t lla_decode_teacher_supported(const lla_dims* dims);
  * reporting; 0 on invalid arguments. */
 int32_t lla_decode_teacher_num_splits(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,
                                       const lla_decode_opts* opts);
+
+/* lla_decode_attn without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The split partials go to a device array of LLA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on, from the first such call on that GPU until
+ * the process ends; the call itself allocates nothing. Arguments, results and errors are
+ * those of lla_decode_attn with `workspace` taken from that array, except:
+ *   - LLA_ERR_WORKSPACE when lla_decode_workspace_bytes(dims, n_ctx, loop_count, opts)
+ *     exceeds LLA_NOALLOC_SCRATCH_BYTES (fewer splits in opts, or a smaller batch, fit);
+ *   - LLA_ERR_HIP when the array's device address cannot be found on the current device.
+ * The array is shared by every call on one GPU: two calls whose kernels may overlap on
+ * that GPU (different streams, or different host threads) race and can give wrong
+ * results. Serialise them on one stream. */
+#define LLA_NOALLOC_SCRATCH_BYTES (8u << 20)
+int32_t lla_decode_attn_noalloc(const lla_dims* dims, const lla_codec* codec,
+                                const lla_cache* cache, int32_t layer, int32_t n_ctx,
+                                const int32_t* ctx_lens, const float* q, int32_t loop_begin,
+                                int32_t loop_count, float* out, const lla_decode_opts* opts,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -212,11 +212,14 @@ size_t lla_decode_workspace_bytes(const lla_dims* d, int32_t n_ctx, int32_t loop
   return (bytes + 255) / 256 * 256;
 }
 
-int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
-                        int32_t layer, int32_t n_ctx, const int32_t* ctx_lens, const float* q,
-                        int32_t loop_begin, int32_t loop_count, float* out, void* workspace,
-                        size_t workspace_bytes, const lla_decode_opts* opts, void* stream) {
-  int32_t st = check_dims(d);
+}  // extern "C"
+
+// Every check of lla_decode_attn except those of the workspace; host-side only.
+int32_t lla::check_decode_args(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                               int32_t layer, int32_t n_ctx, const int32_t* ctx_lens,
+                               const float* q, int32_t loop_begin, int32_t loop_count,
+                               const float* out, const lla_decode_opts* opts) {
+  const int32_t st = check_dims(d);
   if (st != LLA_OK) return st;
   if (codec == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
   if (layer < 0 || layer >= d->D) return LLA_ERR_INVALID_ARG;
@@ -227,18 +230,31 @@ int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cac
                           opts->path > LLA_PATH_ROTARY_FOLD))
     return LLA_ERR_INVALID_ARG;
   const void* ptrs[] = {codec->mu_k, codec->w_up_k, codec->mu_v, codec->w_up_v, codec->rope_table,
-                        cache->c_k, cache->c_v, q, out, workspace};
+                        cache->c_k, cache->c_v, q, out};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
   if (ctx_lens != nullptr && (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) != 0) return LLA_ERR_INVALID_ARG;
-
   const int path = resolve_path(*d, opts);
   if (path == LLA_PATH_ROTARY_FOLD) {
     if (!fold_ok(*d)) return LLA_ERR_UNSUPPORTED;
   } else if (!lla::decode_reconstruct_supported(d->dtype, d->d_head, d->r_k, d->r_v)) {
     return LLA_ERR_UNSUPPORTED;
   }
+  return LLA_OK;
+}
+
+extern "C" {
+
+int32_t lla_decode_attn(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                        int32_t layer, int32_t n_ctx, const int32_t* ctx_lens, const float* q,
+                        int32_t loop_begin, int32_t loop_count, float* out, void* workspace,
+                        size_t workspace_bytes, const lla_decode_opts* opts, void* stream) {
+  int32_t st = lla::check_decode_args(d, codec, cache, layer, n_ctx, ctx_lens, q, loop_begin,
+                                      loop_count, out, opts);
+  if (st != LLA_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace)) return LLA_ERR_INVALID_ARG;
   if (workspace_bytes < lla_decode_workspace_bytes(d, n_ctx, loop_count, opts)) return LLA_ERR_WORKSPACE;
+  const int path = resolve_path(*d, opts);
 
   const Plan p = plan_splits(*d, n_ctx, loop_count, opts);
   const size_t es = elem_bytes(*d);

@@ -67,3 +67,15 @@ bool encode_supported(int dtype, int r, int Kdim);
 void launch_rope_table(int d, int n_max, double base, float* t32, uint16_t* t16, hipStream_t s);
 
 }  // namespace lla
+
+#include "lla.h"
+
+namespace lla {
+
+// Argument checks of lla_decode_attn other than its workspace (host only; lla_api.cpp).
+int32_t check_decode_args(const lla_dims* d, const lla_codec* codec, const lla_cache* cache,
+                          int32_t layer, int32_t n_ctx, const int32_t* ctx_lens, const float* q,
+                          int32_t loop_begin, int32_t loop_count, const float* out,
+                          const lla_decode_opts* opts);
+
+}  // namespace lla

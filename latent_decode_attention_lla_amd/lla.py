@@ -41,7 +41,11 @@ EXPORTED = (
     "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
     "lla_decode_teacher_num_splits", "lla_decode_paged_num_splits", "lla_reconstruct",
     "lla_encode_paged", "lla_decode_paged_workspace_bytes", "lla_decode_attn_paged",
+    "lla_decode_attn_noalloc",
 )
+
+# bytes of the fixed split-partial array lla_decode_attn_noalloc uses (include/lla.h)
+LLA_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class LLAError(RuntimeError):
@@ -110,6 +114,9 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_num_splits.restype = i32
     lib.lla_decode_attn.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, i32, vp, vp,
                                     i32, i32, vp, vp, sz, P(lla_decode_opts), vp]
+    lib.lla_decode_attn_noalloc.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, i32, vp,
+                                            vp, i32, i32, vp, P(lla_decode_opts), vp]
+    lib.lla_decode_attn_noalloc.restype = i32
     lib.lla_decode_attn.restype = i32
     lib.lla_decode_absorbed_workspace_bytes.argtypes = [P(lla_dims), i32, i32, i32,
                                                         P(lla_decode_opts)]
@@ -239,6 +246,16 @@ def lla_decode_attn(dims: lla_dims, codec: lla_codec, cache: lla_cache, layer: i
         ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), layer, n_ctx,
         _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out), _ptr(workspace),
         workspace_bytes, ctypes.byref(opts) if opts is not None else None, _stream(stream)))
+
+
+def lla_decode_attn_noalloc(dims: lla_dims, codec: lla_codec, cache: lla_cache, layer: int,
+                            n_ctx: int, ctx_lens, q, loop_begin: int, loop_count: int, out,
+                            opts=None, stream=None) -> None:
+    """lla_decode_attn with the split partials in the library's fixed device array."""
+    _check("lla_decode_attn_noalloc", load().lla_decode_attn_noalloc(
+        ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), layer, n_ctx,
+        _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out),
+        ctypes.byref(opts) if opts is not None else None, _stream(stream)))
 
 
 def lla_decode_absorbed_workspace_bytes(dims: lla_dims, d_rope: int, n_ctx: int, loop_count: int,
