@@ -7,33 +7,34 @@
 // reconstruction": RoPE of the reconstructed key at the slot index): for head h the score
 // of token j is c_j . G_j + G_j[r_k], G_j = CS_j M_h, where M_h is built from q, W_up,k,(t,h)
 // and the (t, h) slice of mu_k, and CS_j holds cos and sin of the slot's angles. G^T is an
-// f16 MFMA product with all of M_h^T in one wave's registers (the value side needs only a
-// few accumulator registers here), so a head's scores need no exchange between waves; the
-// wave keeps one running max for its head.
+// f16 MFMA product with all of M_h^T in one wave's registers, so a head's scores need no
+// exchange between waves; the wave keeps one running max for its head.
 //
 // Value side (Appendix J, "Absorbed attention": the attention weights sum to one, so the
 // weighted value latent can be up-projected once): per 16-token tile the softmax weights of
 // the workgroup's heads are written to LDS as bfloat16, and acc[h][r] += sum_j p[h][j] c_v[j][r]
 // is one v_mfma_f32_16x16x16_bf16 per 16 value entries, spread over the workgroup's waves.
 // The running sum adds the same rounded weights, so the result is an exact weighted mean
-// with weights rounded to bfloat16. The value product of tile c runs in the iteration of
-// tile c + 1, after the barrier that publishes tile c + 1's rows, so each tile costs one
-// workgroup barrier and the matrix-core work of one tile overlaps the vector work of the
-// next.
+// with weights rounded to bfloat16.
 //
-// Workgroup: HG heads (one wave each) of one (sequence, loop, split). Cache rows and
-// cos/sin tiles stream through a 4-stage direct-to-LDS ring two tiles ahead; the value
-// rows of a stage are still read one iteration after its scores. Workgroups of one
-// (sequence, loop, split) sit on the same XCD, so the shared latent rows come from HBM once.
-// With a paged cache a 16-token tile is one page of the pool, named by the block table
-// (the split's page indices are read into LDS before the ring starts); positions and the
-// table of angles follow the logical token index, so the arithmetic is the dense one.
+// Workgroup: HG heads (one wave each) of one (sequence, loop, split). Cache rows and cos/sin
+// tiles stream through a direct-to-LDS ring of kStages stages, kAhead tiles ahead. Each wave
+// runs its tiles as a three-deep software pipeline, one workgroup barrier per tile:
+//   iteration c:  score MFMAs and latent dot of tile c (operands read in iteration c - 1)
+//                 softmax of tile c - 1 (its score carried in a register), P tile c - 1 out
+//                 value product of tile c - 2 (every head's weights published by the barrier)
+//                 operands of tile c + 1 read from LDS into registers
+// so the matrix-core chain of one tile, the vector tail of the previous one and the LDS
+// latency of the next one overlap inside a wave instead of following one another. Keys sit
+// in LDS as [row-tile pair][entry group][token] 16-byte units and the rows of M^T are
+// ordered to match, so a wave's key reads are linear 1 KiB runs. Workgroups of one (sequence, loop, split) sit on the same XCD,
+// so the shared latent rows come from HBM once. With a paged cache a 16-token tile is one
+// page of the pool, named by the block table (the split's page indices are read into LDS
+// first); positions and the angles follow the logical token index, so the arithmetic is
+// the dense one.
 #include "lla_device.h"
 #include "lla_kernels.h"
 
-#ifndef LLA_2D_WAVES_PER_EU
-#define LLA_2D_WAVES_PER_EU 2
-#endif
 #ifndef LLA_2D_ENABLE
 #define LLA_2D_ENABLE 1  // 0 leaves dense LLA-2D to the wide fold kernel
 #endif
@@ -43,10 +44,14 @@ namespace lla {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kMaxInit = -1.0e30f;  // finite stand-in for -inf: the first valid score raises it
+constexpr float kMaxInit = -1.0e30f;   // finite stand-in for -inf: the first valid score raises it
 constexpr float kRescaleSlack = 8.0f;  // raise the running max only when exceeded by 2^8
 constexpr int kXcds = 8;
-constexpr int kStages = 4;  // ring depth: two tiles in flight, one computed, one read late
+#ifndef LLA_2D_AHEAD
+#define LLA_2D_AHEAD 3
+#endif
+constexpr int kAhead = LLA_2D_AHEAD;     // tile c + kAhead is requested in iteration c
+constexpr int kStages = kAhead + 3;      // tiles c - 2 .. c + kAhead live in iteration c
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -56,11 +61,18 @@ __device__ __forceinline__ f32x4 mfma_f16(const f16x8_t& a, const f16x8_t& b, f3
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Barrier inside the ring loop: only this wave's LDS traffic has to be complete (the
-// ring's direct-to-LDS loads are waited for explicitly with vmcnt), and a
-// __syncthreads() fence would wait for every load in flight.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Barrier inside the ring loop. The ring's direct-to-LDS loads are waited for explicitly
+// with vmcnt before it, and every LDS write another wave reads after it (the P tile, the
+// rescale factors) is waited for right after it is made, so LDS reads of the next tile's
+// operands may still be in flight here; a __syncthreads() fence would also wait for every
+// load in flight.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// LDS written by this wave's lanes is read back by other lanes of the same wave: the
+// wave's LDS operations complete in order, so waiting for its own writes is enough.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
 }
 
 // max over the 16 lanes of each row group (DPP: swap neighbours, swap pairs, mirror
@@ -79,68 +91,63 @@ __device__ __forceinline__ float max16(float v) {
   return dpp_max<0x140>(v);  // row_mirror
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n in [N - 3, N] (its loads of one tile): tile c has
-// landed once only the n loads of tile c + 1 are outstanding
 template <int N>
-__device__ __forceinline__ void wait_loads(int n) {
-  static_assert(N >= 3 && N <= 63, "vmcnt range");
-  if (n >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-  else if (n == N - 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N - 1) : "memory");
-  else if (n == N - 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N - 2) : "memory");
-  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N - 3) : "memory");
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-#ifndef LLA_2D_WAVE_SPECIALIZE
-#define LLA_2D_WAVE_SPECIALIZE 1
-#endif
-
-// f(std::integral_constant<int, w>) for a wave-uniform w in [I, N): the tile loop compiled
-// once per wave of the workgroup, so which ring blocks and value tiles a wave owns are
-// compile-time constants
-template <int I, int N, class F>
-__device__ __forceinline__ void with_wave(int w, F& f) {
-  if constexpr (I + 1 < N) {
-    if (w == I) f(std::integral_constant<int, I>{});
-    else with_wave<I + 1, N>(w, f);
-  } else {
-    f(std::integral_constant<int, I>{});
-  }
-}
+template <int D, int RK, int RV, int HG>
+struct Shape {
+  static constexpr int NW = HG;                   // waves: one per head
+  static constexpr int NKS = D / 32;              // K steps of the score MFMA
+  static constexpr int NCK = RK / 16;             // latent row tiles of M^T
+  static constexpr int NT = NCK + 1;              // MFMA row tiles: the latent rows and the mean row
+  static constexpr int NRT = RV / 16;             // value tiles of 16 entries
+  static constexpr int VT = (NRT + NW - 1) / NW;  // value tiles per wave (wave w: w, w + NW, ..)
+  // stage layout, in 16-byte units: keys by (row-tile pair, entry group, token), values
+  // row-major, then the cos/sin tile (NKS fragments of 1 KiB). A value row is padded to VSP
+  // units with VSP % 8 in {2, 6}, so the four token rows one lane group reads start 8 or
+  // 24 banks apart.
+  static constexpr int KEY_UNITS = NCK * 32;      // [row-tile pair][4 entry groups][token]
+  static constexpr int VSL = RV / 8;
+  static constexpr int VSP = (VSL + 1) % 8 == 2 || (VSL + 1) % 8 == 6 ? VSL + 1
+                             : (VSL + 2) % 8 == 2 || (VSL + 2) % 8 == 6 ? VSL + 2
+                             : (VSL + 3) % 8 == 2 || (VSL + 3) % 8 == 6 ? VSL + 3 : VSL + 4;
+  static constexpr int VAL_UNITS = 16 * VSP;
+  static constexpr int KEY_BLOCKS = (KEY_UNITS + 63) / 64;
+  static constexpr int VAL_BLOCKS = (VAL_UNITS + 63) / 64;
+  static constexpr int BLOCKS = KEY_BLOCKS + VAL_BLOCKS + NKS;  // 1 KiB DMA blocks per tile
+  static constexpr int STAGE_UNITS = BLOCKS * 64;
+  static constexpr int VAL_OFF = KEY_BLOCKS * 64;               // units
+  static constexpr int TAB_OFF = (KEY_BLOCKS + VAL_BLOCKS) * 64;
+  // DMA blocks per wave and tile, the same for every wave: slot j of wave w loads block
+  // min(w + NW j, BLOCKS - 1), so surplus slots re-load the last block into the same bytes
+  static constexpr int NSLOT = (BLOCKS + NW - 1) / NW;
+  static constexpr int WT_STRIDE = D + 8;                       // float16 row stride of the W staging
+  static constexpr int STAGING_UNITS = NW * 16 * WT_STRIDE * 2 / 16;
+  static_assert(RK % 32 == 0, "row tiles come in pairs");
+  static_assert(RK % 16 == 0 && RV % 16 == 0 && D % 64 == 0 && HG <= 16, "shape");
+};
 
 template <int D, int RK, int RV, int HG, bool PAGED>
-__global__ __launch_bounds__(64 * HG) __attribute__((amdgpu_waves_per_eu(LLA_2D_WAVES_PER_EU)))
+__global__ __launch_bounds__(64 * HG) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
-  constexpr int NW = HG;                   // waves: one per head
-  constexpr int NKS = D / 32;              // K steps of the score MFMA
-  constexpr int NCK = RK / 16;             // latent row tiles of M^T
-  constexpr int NT = NCK + 1;              // MFMA row tiles: the latent rows and the mean row
-  constexpr int NRT = RV / 16;             // value tiles of 16 entries
-  constexpr int VT = (NRT + NW - 1) / NW;  // value tiles per wave (wave w owns w, w + NW, ..)
-  constexpr int WT_STRIDE = D + 8;
-  // ring stage: key rows (16 x KSP slots of 16 B, one padding slot), value rows, cos/sin tile
-  constexpr int KSL = RK / 8, KSP = KSL + 1;
-  constexpr int VSL = RV / 8, VSP = VSL + 1;
-  constexpr int NIK = (16 * KSP + 63) / 64;
-  constexpr int NIV = (16 * VSP + 63) / 64;
-  constexpr int STAGE_BLOCKS = NIK + NIV + NKS;  // 1 KiB blocks
-  constexpr int RING_UNITS = kStages * STAGE_BLOCKS * 64;
-  constexpr int P_UNITS = 2 * 16 * 16 * 2 / 16;
-  constexpr int AL_UNITS = 2 * 16 * 4 / 16;
-  constexpr int PAGE_UNITS = PAGED ? kMaxSplitPages * 4 / 16 : 0;  // the split's page indices
-  constexpr int LDS_UNITS = RING_UNITS + P_UNITS + AL_UNITS + PAGE_UNITS;
-  static_assert(NW * 16 * WT_STRIDE * 2 / 16 <= RING_UNITS, "prologue staging fits the ring");
+  using S = Shape<D, RK, RV, HG>;
+  constexpr int NW = S::NW, NKS = S::NKS, NCK = S::NCK, NT = S::NT, NRT = S::NRT, VT = S::VT;
+  constexpr int RING_UNITS = kStages * S::STAGE_UNITS;
+  constexpr int P_UNITS = 2 * 16 * 16 * 2 / 16;   // two P tiles [16 heads][16 tokens] bf16
+  constexpr int AL_UNITS = 2 * 16 * 4 / 16;       // two rows of per-head rescale factors
+  constexpr int PAGE_UNITS = PAGED ? kMaxSplitPages * 4 / 16 : 0;
+  constexpr int LDS_UNITS = RING_UNITS + S::STAGING_UNITS + P_UNITS + AL_UNITS + PAGE_UNITS;
   static_assert(HG * RV + 2 * HG <= RING_UNITS * 4, "epilogue staging fits the ring");
-  static_assert(RK % 16 == 0 && RV % 16 == 0 && D % 32 == 0 && HG <= 16, "shape");
-  static_assert((NIK + NW - 1) / NW + (NIV + NW - 1) / NW + (NKS + NW - 1) / NW <= 31, "vmcnt range");
-  // the last wave issues the fewest loads per tile, NIK / NW + NIV / NW + NKS / NW, at
-  // least NSLOT - 3 (the range wait_loads covers)
-  static_assert((NIK + NW - 1) / NW + (NIV + NW - 1) / NW + (NKS + NW - 1) / NW -
-                        (NIK / NW + NIV / NW + NKS / NW) <= 3, "load counts");
 
   __shared__ u32x4 lds[LDS_UNITS];
-  uint16_t* ptile = reinterpret_cast<uint16_t*>(lds + RING_UNITS);                 // [2][16][16]
-  float* alpha_buf = reinterpret_cast<float*>(lds + RING_UNITS + P_UNITS);           // [2][16]
-  int* split_pages = reinterpret_cast<int*>(lds + RING_UNITS + P_UNITS + AL_UNITS);  // [pages]
+  uint16_t* staging = reinterpret_cast<uint16_t*>(lds + RING_UNITS);
+  // P tiles [2][token / 4][16 heads][token % 4]: a lane's 4 weights of one head are 8 bytes
+  uint16_t* ptile = reinterpret_cast<uint16_t*>(lds + RING_UNITS + S::STAGING_UNITS);
+  float* alpha_buf = reinterpret_cast<float*>(lds + RING_UNITS + S::STAGING_UNITS + P_UNITS);  // [2][16]
+  int* split_pages = reinterpret_cast<int*>(lds + RING_UNITS + S::STAGING_UNITS + P_UNITS + AL_UNITS);
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -169,90 +176,67 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   const int ntok = max(0, s1 - s0);
   const int ntile = (ntok + 15) >> 4;
   const int nfull = ntok >> 4;
+  const int tile_max = s1 > 0 ? (s1 - 1) >> 4 : 0;
 
-  // ---- M^T fragments of this head (scaled by scale * log2 e), via an LDS transpose ----
+  // ---- this head's codec rows and query, requested before the ring's first tiles -------
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w_up_k) + static_cast<size_t>(t * a.H + h) * D * RK;
   const uint16_t* mu = reinterpret_cast<const uint16_t*>(a.mu_k) + static_cast<size_t>(t * a.H + h) * D;
   const float* q = a.q + (static_cast<size_t>(b * a.H + h) * a.L + li) * D;
-  const float sc = a.scale_log2e;
-  uint16_t* wt = reinterpret_cast<uint16_t*>(lds) + wave * 16 * WT_STRIDE;
-  f16x8_t mf[NT][NKS];
+  // Row r of M^T's row tile m holds latent entry 32 (m / 2) + 8 (r / 4) + 4 (m % 2) + r % 4,
+  // so the 4 rows of tile m in lane group hi and those of tile m ^ 1 are 8 consecutive
+  // entries of one token: one 16-byte key unit per lane and tile pair.
+  u32x2 wreg[NCK][D / 64][4];  // W[lane + 64 k][entries of tile m's rows 4 g .. 4 g + 3]
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {  // latent row tiles, then the mean row (tile NCK)
+  for (int i = 0; i < NCK; ++i)
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
-      const int c = lane + 64 * k;  // model dimension
-      if (i < NCK) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(c) * RK + 16 * i);
-        const u32x4 x0 = src[0], x1 = src[1];
-        const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int k = 0; k < D / 64; ++k)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          wt[(2 * j) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] & 0xffffu);
-          wt[(2 * j + 1) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] >> 16);
-        }
-      } else {
-        // the mean row alone in its tile (row 0), the other rows zero
-        wt[c] = mu[c];
+      for (int g4 = 0; g4 < 4; ++g4)
+        wreg[i][k][g4] = *reinterpret_cast<const u32x2*>(
+            W + static_cast<size_t>(lane + 64 * k) * RK + 32 * (i / 2) + 8 * g4 + 4 * (i % 2));
+  // this lane's 8 rotary pairs of each half: p0 = 32 ks2 + 8 hi
+  float4 qreg[NKS / 2][4];
 #pragma unroll
-        for (int j = 1; j < 16; ++j) wt[j * WT_STRIDE + c] = 0;
-      }
-    }
-    __syncthreads();
+  for (int ks2 = 0; ks2 < NKS / 2; ++ks2)
 #pragma unroll
-    for (int ks2 = 0; ks2 < NKS / 2; ++ks2) {
-      const int p0 = 32 * ks2 + 8 * hi;  // rotary pair index
-      const u32x4* wrow = reinterpret_cast<const u32x4*>(wt + lo * WT_STRIDE + 2 * p0);
-      const u32x4 y0 = wrow[0], y1 = wrow[1];
-      const uint32_t wp[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+    for (int e = 0; e < 4; ++e)
+      qreg[ks2][e] = *reinterpret_cast<const float4*>(q + 2 * (32 * ks2 + 8 * hi) + 4 * e);
+  u32x4 mreg[NKS / 2][2];  // mu[2 p0 .. 2 p0 + 15] (used by the lanes holding the mean row)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x0 = __uint_as_float(wp[e] << 16);
-        const float x1 = __uint_as_float(wp[e] & 0xffff0000u);
-        const float2 qp = *reinterpret_cast<const float2*>(q + 2 * (p0 + e));
-        mf[i][ks2][e] = static_cast<_Float16>((qp.x * x0 + qp.y * x1) * sc);
-        mf[i][ks2 + NKS / 2][e] = static_cast<_Float16>((qp.y * x0 - qp.x * x1) * sc);
-      }
-    }
-    __syncthreads();
+  for (int ks2 = 0; ks2 < NKS / 2; ++ks2) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(mu + 2 * (32 * ks2 + 8 * hi));
+    mreg[ks2][0] = src[0];
+    mreg[ks2][1] = src[1];
   }
 
-  // ---- ring set-up: per block slot of this wave, its source and the step per tile ----
-  // dense: the sequence's plane; paged: the pool (a page's 16 rows are contiguous, Hc = 1)
+  // ---- ring: per DMA slot of this wave, the lane's byte offset in the tile and its row ----
+  // block k of a stage is issued by wave k % NW; keys: block P, lane (hi, lo) -> entries
+  // 32 P + 8 hi .. + 7 of token lo; values: unit u -> row u / VSP, slot u % VSP (the padding
+  // slot re-reads the row's last slot); table: fragment k - KEY_BLOCKS - VAL_BLOCKS.
   const size_t plane = PAGED ? 0 : static_cast<size_t>(b) * a.n_max;
   const char* ck = reinterpret_cast<const char*>(a.c_k) + plane * RK * 2;
   const char* cv = reinterpret_cast<const char*>(a.c_v) + plane * RV * 2;
   const char* tab_g = reinterpret_cast<const char*>(a.rope16);
-  const int tile_max = s1 > 0 ? (s1 - 1) >> 4 : 0;
-  // Block slots of this wave by kind: NSK key, NSV value and NST table slots; slot j of a
-  // kind loads block wave + NW j of it, if the kind has that many blocks (waves with fewer
-  // blocks issue fewer loads per tile). Per slot this lane keeps the token row it loads and
-  // its byte offset in the tile (row * row size + column).
-  constexpr int NSK = (NIK + NW - 1) / NW, NSV = (NIV + NW - 1) / NW, NST = (NKS + NW - 1) / NW;
-  constexpr int NSLOT = NSK + NSV + NST;
-  int kblk[NSK], krow[NSK], vblk[NSV], vrow[NSV], tblk[NST];
-  uint32_t koff[NSK], voff[NSV], toff[NST];
+  int srow[S::NSLOT];
+  uint32_t soff[S::NSLOT];
+  int skind[S::NSLOT];  // 0 keys, 1 values, 2 table (wave-uniform)
 #pragma unroll
-  for (int j = 0; j < NSK; ++j) {
-    const int bi = min(wave + NW * j, NIK - 1);
-    const int sidx = bi * 64 + lane;
-    kblk[j] = bi;
-    krow[j] = min(sidx / KSP, 15);
-    koff[j] = static_cast<uint32_t>(krow[j] * (RK * 2) + min(sidx % KSP, KSL - 1) * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < NSV; ++j) {
-    const int bi = min(wave + NW * j, NIV - 1);
-    const int sidx = bi * 64 + lane;
-    vblk[j] = NIK + bi;
-    vrow[j] = min(sidx / VSP, 15);
-    voff[j] = static_cast<uint32_t>(vrow[j] * (RV * 2) + min(sidx % VSP, VSL - 1) * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < NST; ++j) {
-    const int bi = min(wave + NW * j, NKS - 1);
-    tblk[j] = NIK + NIV + bi;
-    toff[j] = static_cast<uint32_t>(bi * 1024 + lane * 16);
+  for (int j = 0; j < S::NSLOT; ++j) {
+    const int blk = min(wave + NW * j, S::BLOCKS - 1);
+    skind[j] = blk < S::KEY_BLOCKS ? 0 : (blk < S::KEY_BLOCKS + S::VAL_BLOCKS ? 1 : 2);
+    const int u = blk * 64 + lane;
+    if (blk < S::KEY_BLOCKS) {  // block = row-tile pair P, lane = (entry group hi, token lo)
+      srow[j] = lo;
+      soff[j] = static_cast<uint32_t>(lo * RK * 2 + (32 * blk + 8 * hi) * 2);
+    } else if (blk < S::KEY_BLOCKS + S::VAL_BLOCKS) {
+      const int uv = u - S::VAL_OFF;
+      const int row = min(uv / S::VSP, 15);
+      srow[j] = row;
+      soff[j] = static_cast<uint32_t>(row * RV * 2 + min(uv % S::VSP, S::VSL - 1) * 16);
+    } else {
+      srow[j] = 0;
+      soff[j] = static_cast<uint32_t>((blk - S::KEY_BLOCKS - S::VAL_BLOCKS) * 1024 + lane * 16);
+    }
   }
   auto dma = [&](const char* src, u32x4* dst) {
     __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -263,181 +247,281 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
       split_pages[i] = page_of(pg, b, (s0 >> 4) + i);
     __syncthreads();
   }
-  // page of tile tl of the split (tiles past the last use the last one's)
-  auto page_for = [&](int tl) {
-    return PAGED ? __builtin_amdgcn_readfirstlane(split_pages[min(tl, ntile - 1)]) : 0;
-  };
-  int page_next = PAGED && ntile > 0 ? page_for(0) : 0;  // read one issue ahead
-  // Sources are a wave-uniform base plus this lane's 32-bit offset. Tiles past the last
-  // (the ring's run-out) load the last tile's rows again.
-  auto issue = [&](auto wc, int tl) {
-    const int W = wc;
-    auto has = [&](int j, int blocks) { return W + NW * j < blocks; };
-    u32x4* stage = lds + (tl % kStages) * STAGE_BLOCKS * 64;
-    const char* tb = tab_g + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * (NKS * 1024);
+  // Tile tl of the split into stage stg; tiles past the last load the last tile again.
+  // Tiles wholly inside the context take sources from a wave-uniform base plus the lane's
+  // fixed offset; the others clamp rows past the context end to its last row.
+  auto issue = [&](int tl, int stg) {
+    u32x4* stage = lds + stg * S::STAGE_UNITS;
+    if (tl < nfull) {
+      size_t row0;
+      if constexpr (PAGED) row0 = static_cast<size_t>(16) * __builtin_amdgcn_readfirstlane(split_pages[tl]);
+      else row0 = static_cast<size_t>(s0 + 16 * tl);
+      const char* base[3] = {ck + row0 * (RK * 2), cv + row0 * (RV * 2),
+                             tab_g + static_cast<size_t>((s0 >> 4) + tl) * (NKS * 1024)};
 #pragma unroll
-    for (int j = 0; j < NST; ++j)
-      if (has(j, NKS)) dma(tb + toff[j], stage + tblk[j] * 64);
-    // first row of the tile (tiles past the last: of the last tile) in the sequence's plane,
-    // or the first row of the tile's page in the pool
+      for (int j = 0; j < S::NSLOT; ++j)
+        dma(base[skind[j]] + soff[j], stage + min(wave + NW * j, S::BLOCKS - 1) * 64);
+      return;
+    }
     const int tlc = min(tl, ntile - 1);
-    const size_t row0 = PAGED ? static_cast<size_t>(16) * page_next : static_cast<size_t>(s0 + 16 * tlc);
+    const char* tb = tab_g + static_cast<size_t>(min((s0 >> 4) + tl, tile_max)) * (NKS * 1024);
+    size_t row0;
+    if constexpr (PAGED) row0 = static_cast<size_t>(16) * __builtin_amdgcn_readfirstlane(split_pages[tlc]);
+    else row0 = static_cast<size_t>(s0 + 16 * tlc);
     const char* kb = ck + row0 * (RK * 2);
     const char* vb = cv + row0 * (RV * 2);
-    if (tl < nfull) {
+    const int rmax = s1 - 1 - (s0 + 16 * tlc);  // rows past the context end re-read its last row
 #pragma unroll
-      for (int j = 0; j < NSK; ++j)
-        if (has(j, NIK)) dma(kb + koff[j], stage + kblk[j] * 64);
-#pragma unroll
-      for (int j = 0; j < NSV; ++j)
-        if (has(j, NIV)) dma(vb + voff[j], stage + vblk[j] * 64);
-    } else {  // rows past the context end clamp to its last token (they get zero weight)
-      const int t0 = s0 + 16 * tlc;
-#pragma unroll
-      for (int j = 0; j < NSK; ++j) {
-        const int d = min(t0 + krow[j], s1 - 1) - t0 - krow[j];  // <= 0 rows
-        if (has(j, NIK))
-          dma(kb + static_cast<uint32_t>(static_cast<int>(koff[j]) + d * (RK * 2)), stage + kblk[j] * 64);
-      }
-#pragma unroll
-      for (int j = 0; j < NSV; ++j) {
-        const int d = min(t0 + vrow[j], s1 - 1) - t0 - vrow[j];
-        if (has(j, NIV))
-          dma(vb + static_cast<uint32_t>(static_cast<int>(voff[j]) + d * (RV * 2)), stage + vblk[j] * 64);
-      }
-    }
-    if constexpr (PAGED) page_next = page_for(tl + 1);
-  };
-
-  float m_run = kMaxInit;  // this head's running max (exp2 domain), the same in every lane
-  float l_run = 0.f;       // this lane's token column's share of the running sum
-  f32x4 vacc[VT];          // acc[heads 4 hi .. 4 hi + 3][value entry 16 rt + lo]
-#pragma unroll
-  for (int k = 0; k < VT; ++k) vacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // value product of tile cc: rescale by the tile's alphas, then acc += P(cc) C_v(cc)
-  auto value_step = [&](auto wc, int cc) {
-    const int W = wc;
-    const char* vreg = reinterpret_cast<const char*>(lds + (cc % kStages) * STAGE_BLOCKS * 64 + NIK * 64);
-    const f32x4 al = *reinterpret_cast<const f32x4*>(alpha_buf + (cc & 1) * 16 + 4 * hi);
-    const i16x4 pa = *reinterpret_cast<const i16x4*>(ptile + (cc & 1) * 256 + lo * 16 + 4 * hi);
-    // all of this wave's value fragments are read before the first product (a value tile
-    // past the last reads the last one and is not used)
-    i16x4 vb[VT];
-#pragma unroll
-    for (int k = 0; k < VT; ++k) {
-      const char* col = vreg + (16 * min(W + NW * k, NRT - 1) + lo) * 2 + 4 * hi * (VSP * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vb[k][i] = *reinterpret_cast<const short*>(col + i * (VSP * 16));
-    }
-#pragma unroll
-    for (int k = 0; k < VT; ++k) {
-      if (W + NW * k < NRT) {
-        f32x4 acc = vacc[k];
-        acc[0] *= al[0];
-        acc[1] *= al[1];
-        acc[2] *= al[2];
-        acc[3] *= al[3];
-        vacc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[k], acc, 0, 0, 0);
-      }
+    for (int j = 0; j < S::NSLOT; ++j) {
+      u32x4* dst = stage + min(wave + NW * j, S::BLOCKS - 1) * 64;
+      const int d = min(srow[j], rmax) - srow[j];
+      if (skind[j] == 0)
+        dma(kb + static_cast<uint32_t>(static_cast<int>(soff[j]) + d * (RK * 2)), dst);
+      else if (skind[j] == 1)
+        dma(vb + static_cast<uint32_t>(static_cast<int>(soff[j]) + d * (RV * 2)), dst);
+      else
+        dma(tb + soff[j], dst);
     }
   };
 
-  // scores of tile c for this head, softmax weights into the P tile
-  auto score_step = [&](int c) {
-    const u32x4* st = lds + (c % kStages) * STAGE_BLOCKS * 64;
-    const char* kreg = reinterpret_cast<const char*>(st);
-    const u32x4* treg = st + (NIK + NIV) * 64;
-    f32x4 g[NT];
+  // ---- M^T fragments of this head (scaled by scale * log2 e), via a wave-local transpose --
+  const float sc = a.scale_log2e;
+  uint16_t* wt = staging + wave * 16 * S::WT_STRIDE;
+  f16x8_t mf[NT][NKS];
+  auto fold_row = [&](const u32x4 (&wp)[2], int ks2, int tile) {
+    // wp holds (W[2p], W[2p + 1]) for this lane's 8 pairs p0 .. p0 + 7 of half ks2
+    const uint32_t w8[8] = {wp[0].x, wp[0].y, wp[0].z, wp[0].w, wp[1].x, wp[1].y, wp[1].z, wp[1].w};
+    const float qf[16] = {qreg[ks2][0].x, qreg[ks2][0].y, qreg[ks2][0].z, qreg[ks2][0].w,
+                          qreg[ks2][1].x, qreg[ks2][1].y, qreg[ks2][1].z, qreg[ks2][1].w,
+                          qreg[ks2][2].x, qreg[ks2][2].y, qreg[ks2][2].z, qreg[ks2][2].w,
+                          qreg[ks2][3].x, qreg[ks2][3].y, qreg[ks2][3].z, qreg[ks2][3].w};
 #pragma unroll
-    for (int i = 0; i < NT; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const f16x8_t bf = __builtin_bit_cast(f16x8_t, treg[ks * 64 + lane]);
-#pragma unroll
-      for (int i = 0; i < NT; ++i) g[i] = mfma_f16(mf[i][ks], bf, g[i]);
+    for (int e = 0; e < 8; ++e) {
+      const float x0 = __uint_as_float(w8[e] << 16);
+      const float x1 = __uint_as_float(w8[e] & 0xffff0000u);
+      mf[tile][ks2][e] = static_cast<_Float16>((qf[2 * e] * x0 + qf[2 * e + 1] * x1) * sc);
+      mf[tile][ks2 + NKS / 2][e] = static_cast<_Float16>((qf[2 * e + 1] * x0 - qf[2 * e] * x1) * sc);
     }
-    // element 0 of the last tile: the mean row for hi = 0, a zero row elsewhere
-    float pp = g[NT - 1][0];
+  };
+
+  auto prologue_and_loop = [&]() {
+    constexpr int NL = S::NSLOT;  // DMA loads per wave and tile
+    static_assert(NL * (kAhead - 2) <= 63, "vmcnt range");
 #pragma unroll
-    for (int m = 0; m < NCK; ++m) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(kreg + lo * (KSP * 16) + 32 * m + 8 * hi);
-      pp += __uint_as_float(w.x << 16) * g[m][0] + __uint_as_float(w.x & 0xffff0000u) * g[m][1] +
-            __uint_as_float(w.y << 16) * g[m][2] + __uint_as_float(w.y & 0xffff0000u) * g[m][3];
+    for (int k = 0; k < kAhead; ++k) issue(k, k);
+
+#pragma unroll
+    for (int i = 0; i < NCK; ++i) {
+#pragma unroll
+      for (int k = 0; k < D / 64; ++k) {
+        const int c = lane + 64 * k;
+        const uint32_t w8[8] = {wreg[i][k][0].x, wreg[i][k][0].y, wreg[i][k][1].x, wreg[i][k][1].y,
+                                wreg[i][k][2].x, wreg[i][k][2].y, wreg[i][k][3].x, wreg[i][k][3].y};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          wt[(2 * j) * S::WT_STRIDE + c] = static_cast<uint16_t>(w8[j] & 0xffffu);
+          wt[(2 * j + 1) * S::WT_STRIDE + c] = static_cast<uint16_t>(w8[j] >> 16);
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int ks2 = 0; ks2 < NKS / 2; ++ks2) {
+        const u32x4* wrow = reinterpret_cast<const u32x4*>(wt + lo * S::WT_STRIDE + 2 * (32 * ks2 + 8 * hi));
+        const u32x4 wp[2] = {wrow[0], wrow[1]};
+        fold_row(wp, ks2, i);
+      }
+      wave_lds_sync();  // the reads are done before the next row tile overwrites the staging
     }
-    const float full = sum_xor32(sum_xor16(pp));
-    const float s = lo < s1 - s0 - 16 * c ? full : kNegInf;
-    float alpha = 1.f;
-    // the head's max is raised (to the tile's max) only when a score exceeds it by 2^8;
-    // every lane of the wave holds the same head, so the branch is uniform
-    if (__builtin_amdgcn_ballot_w64(s > m_run + kRescaleSlack) != 0) {
-      const float mt = max16(s);
-      alpha = fast_exp2(m_run - mt);
-      l_run *= alpha;
-      m_run = mt;
+    // the mean row: row 0 of its tile is mu, the other 15 rows are zero
+#pragma unroll
+    for (int ks2 = 0; ks2 < NKS / 2; ++ks2) {
+      fold_row(mreg[ks2], ks2, NCK);
+      if (lo != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mf[NCK][ks2][e] = static_cast<_Float16>(0.f);
+          mf[NCK][ks2 + NKS / 2][e] = static_cast<_Float16>(0.f);
+        }
+      }
     }
-    const uint16_t pb = __builtin_bit_cast(uint16_t, static_cast<__bf16>(fast_exp2(s - m_run)));
-    l_run += bf16_to_f32(pb);
-    if (hi == 0) ptile[(c & 1) * 256 + hw * 16 + lo] = pb;
-    if (lane == 0) alpha_buf[(c & 1) * 16 + hw] = alpha;
+
+    // ---- the pipelined tile loop ----
+    float m_run = kMaxInit;  // this head's running max (exp2 domain), the same in every lane
+    float l_run = 0.f;       // this lane's token column's share of the running sum
+    f32x4 vacc[VT];          // acc[heads 4 hi .. 4 hi + 3][value entry 16 rt + lo]
+#pragma unroll
+    for (int k = 0; k < VT; ++k) vacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f16x8_t bq[NKS];   // cos/sin fragments of the next tile to score
+    u32x4 kq[NCK / 2]; // its key latents: entries 32 P + 8 hi .. + 7 of token lo
+    float s_prev = kNegInf;  // the previous tile's score of token lo (exp2 domain)
+
+    auto read_operands = [&](int stg) {
+      const u32x4* st = lds + stg * S::STAGE_UNITS;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) bq[ks] = __builtin_bit_cast(f16x8_t, st[S::TAB_OFF + ks * 64 + lane]);
+#pragma unroll
+      for (int pr = 0; pr < NCK / 2; ++pr) kq[pr] = st[pr * 64 + lane];
+    };
+    // score of tile c from the operands in registers; the value returned is the full score
+    // of token lo in every lane (or -inf past the context end)
+    auto score = [&](int c) {
+      f32x4 g[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) g[i] = mfma_f16(mf[i][ks], bq[ks], g[i]);
+      // element 0 of the last tile: the mean row for hi = 0, a zero row elsewhere
+      float pp = g[NT - 1][0];
+#pragma unroll
+      for (int m = 0; m < NCK; ++m) {
+        const u32x2 w = (m % 2 == 0) ? u32x2{kq[m / 2].x, kq[m / 2].y} : u32x2{kq[m / 2].z, kq[m / 2].w};
+        pp += __uint_as_float(w.x << 16) * g[m][0] + __uint_as_float(w.x & 0xffff0000u) * g[m][1] +
+              __uint_as_float(w.y << 16) * g[m][2] + __uint_as_float(w.y & 0xffff0000u) * g[m][3];
+      }
+      const float full = sum_xor32(sum_xor16(pp));
+      return lo < s1 - s0 - 16 * c ? full : kNegInf;
+    };
+    // softmax weights of tile c from its scores, into P tile c and its rescale factor
+    auto tail = [&](int par, float s) {
+      float alpha = 1.f;
+      // the head's max is raised (to the tile's max) only when a score exceeds it by 2^8;
+      // every lane of the wave holds the same head, so the branch is uniform
+      if (__builtin_amdgcn_ballot_w64(s > m_run + kRescaleSlack) != 0) {
+        const float mt = max16(s);
+        alpha = fast_exp2(m_run - mt);
+        l_run *= alpha;
+        m_run = mt;
+      }
+      const uint16_t pb = __builtin_bit_cast(uint16_t, static_cast<__bf16>(fast_exp2(s - m_run)));
+      l_run += bf16_to_f32(pb);
+      if (hi == 0) ptile[par * 256 + (lo >> 2) * 64 + hw * 4 + (lo & 3)] = pb;
+      if (lane == 0) alpha_buf[par * 16 + hw] = alpha;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible to the next barrier's readers
+    };
+    // value product of tile c: rescale by the tile's alphas, then acc += P(c) C_v(c)
+    auto value_step = [&](int stg, int par) {
+      const char* vreg = reinterpret_cast<const char*>(lds + stg * S::STAGE_UNITS + S::VAL_OFF);
+      const f32x4 al = *reinterpret_cast<const f32x4*>(alpha_buf + par * 16 + 4 * hi);
+      const i16x4 pa = *reinterpret_cast<const i16x4*>(ptile + par * 256 + hi * 64 + lo * 4);
+      // B fragment (tokens 4 hi .. 4 hi + 3 of entry 16 rt + lo) by a transposing read: lane
+      // (hi, 4 k + j) names entries 16 rt + 4 j .. + 3 of token 4 hi + k, and lane (hi, lo)
+      // receives short lo % 4 of the chunks lanes (hi, 4 k + lo / 4) name, k = 0 .. 3
+      i16x4 vb[VT];
+#pragma unroll
+      for (int k = 0; k < VT; ++k) {
+        const char* chunk = vreg + (4 * hi + (lo >> 2)) * (S::VSP * 16) +
+                            (16 * min(wave + NW * k, NRT - 1) + 4 * (lo & 3)) * 2;
+        vb[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(chunk));
+      }
+#pragma unroll
+      for (int k = 0; k < VT; ++k) {
+        if (wave + NW * k < NRT) {
+          f32x4 acc = vacc[k];
+          acc[0] *= al[0];
+          acc[1] *= al[1];
+          acc[2] *= al[2];
+          acc[3] *= al[3];
+          vacc[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[k], acc, 0, 0, 0);
+        }
+      }
+    };
+
+    // One pipeline step for tile c whose stage is K (a compile-time constant in the
+    // unrolled steady loop, where K = c % kStages and the P buffers alternate with c).
+    auto step = [&](int c, int K) {
+      wait_vmcnt<NL * (kAhead - 2)>();
+      ring_barrier();
+      issue(c + kAhead, (K + kAhead) % kStages);
+      const float s_cur = score(c);
+      tail((K + 1) & 1, s_prev);                      // tile c - 1
+      value_step((K + kStages - 2) % kStages, K & 1);  // tile c - 2
+      read_operands((K + 1) % kStages);                // tile c + 1
+      s_prev = s_cur;
+    };
+    static_assert(kStages % 2 == 0, "P buffer parity follows the stage index");
+
+    // tiles 0 and 1 have landed once only tiles 2 .. kAhead - 1 are outstanding
+    wait_vmcnt<NL * (kAhead - 2)>();
+    ring_barrier();
+    read_operands(0);
+    // c = 0
+    issue(kAhead, kAhead % kStages);
+    float s_cur = score(0);
+    if (ntile > 1) read_operands(1);
+    s_prev = s_cur;
+    if (ntile > 1) {
+      // c = 1: no value product yet
+      wait_vmcnt<NL * (kAhead - 2)>();
+      ring_barrier();
+      issue(1 + kAhead, (1 + kAhead) % kStages);
+      s_cur = score(1);
+      tail(0, s_prev);
+      read_operands(2);
+      s_prev = s_cur;
+      // steady state, unrolled by the ring depth so that every stage index is a constant
+      int c = 2;
+      for (; c + kStages <= ntile; c += kStages) {
+#pragma unroll
+        for (int k = 0; k < kStages; ++k) step(c + k, (2 + k) % kStages);
+      }
+      for (; c < ntile; ++c) step(c, c % kStages);
+    }
+    // drain: the softmax of the last tile, then the last value products
+    ring_barrier();
+    tail((ntile - 1) & 1, s_prev);
+    if (ntile > 1) value_step((ntile - 2) % kStages, (ntile - 2) & 1);
+    ring_barrier();
+    value_step((ntile - 1) % kStages, (ntile - 1) & 1);
+
+    // ---- epilogue: the head's sum, the accumulated latent through LDS ----
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in the reused LDS
+    __syncthreads();
+    float* abar = reinterpret_cast<float*>(lds);  // [HG][RV]
+#pragma unroll
+    for (int k = 0; k < VT; ++k) {
+      const int rt = wave + NW * k;
+      if (rt < NRT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * hi + i < HG) abar[(4 * hi + i) * RV + 16 * rt + lo] = vacc[k][i];
+      }
+    }
+    float lsum = l_run;
+#pragma unroll
+    for (int msk = 1; msk < 16; msk <<= 1) lsum += shfl_xor(lsum, msk);
+    float* stats = abar + HG * RV;  // [HG][2]: max, sum
+    if (lane == 0) {
+      stats[2 * hw] = m_run;
+      stats[2 * hw + 1] = lsum;
+    }
   };
 
   // heads past HG: unit alphas and zero weights, so their accumulator rows stay zero
   if (threadIdx.x < 32) alpha_buf[threadIdx.x] = 1.f;
-  for (int i = static_cast<int>(threadIdx.x); i < 2 * (16 - HG) * 16; i += 64 * HG)
-    ptile[(i / ((16 - HG) * 16)) * 256 + HG * 16 + i % ((16 - HG) * 16)] = 0;
-  auto ring_loop = [&](auto wc) {
-    const int W = wc;
-    int nl = 0;  // this wave's loads per tile
-#pragma unroll
-    for (int j = 0; j < NSK; ++j) nl += W + NW * j < NIK;
-#pragma unroll
-    for (int j = 0; j < NSV; ++j) nl += W + NW * j < NIV;
-#pragma unroll
-    for (int j = 0; j < NST; ++j) nl += W + NW * j < NKS;
-    issue(wc, 0);
-    issue(wc, 1);
-    for (int c = 0; c <= ntile; ++c) {
-        // tile c has landed once only tile c + 1's loads are outstanding; the barrier then
-        // publishes every wave's blocks of tile c and the weights of tile c - 1, and tells
-        // that tile c - 2's stage is free for tile c + 2
-        wait_loads<NSLOT>(nl);
-        ring_barrier();
-        issue(wc, c + 2);
-        if (c > 0) value_step(wc, c - 1);
-        if (c < ntile) score_step(c);
-    }
-  };
-  if (ntile > 0) {
-#if LLA_2D_WAVE_SPECIALIZE
-    with_wave<0, NW>(wave, ring_loop);
-#else
-    ring_loop(wave);
-#endif
+  for (int i = static_cast<int>(threadIdx.x); i < 2 * (16 - HG) * 16; i += 64 * HG) {
+    const int par = i / ((16 - HG) * 16), rem = i % ((16 - HG) * 16);
+    const int hd = HG + rem / 16, tok = rem % 16;
+    ptile[par * 256 + (tok >> 2) * 64 + hd * 4 + (tok & 3)] = 0;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in the reused LDS
+  // an empty split leaves a zero accumulator and sum
+  if (ntile <= 0) {
+    float* abar = reinterpret_cast<float*>(lds);
+    for (int i = lane; i < RV; i += 64) abar[hw * RV + i] = 0.f;
+    if (lane == 0) {
+      abar[HG * RV + 2 * hw] = kMaxInit;
+      abar[HG * RV + 2 * hw + 1] = 0.f;
+    }
+  } else {
+    __syncthreads();  // the P padding rows and alphas are set before any wave reads them
+    prologue_and_loop();
+  }
   __syncthreads();
 
-  // ---- epilogue: the head's sum, the accumulated latent through LDS ----
-  float lsum = l_run;
-#pragma unroll
-  for (int msk = 1; msk < 16; msk <<= 1) lsum += shfl_xor(lsum, msk);
-  float* abar = reinterpret_cast<float*>(lds);  // [HG][RV]
-  float* stats = abar + HG * RV;                // [HG][2]: max, sum
-#pragma unroll
-  for (int k = 0; k < VT; ++k) {
-    const int rt = wave + NW * k;
-    if (rt < NRT) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * hi + i < HG) abar[(4 * hi + i) * RV + 16 * rt + lo] = vacc[k][i];
-    }
-  }
-  if (lane == 0) {
-    stats[2 * hw] = m_run;
-    stats[2 * hw + 1] = lsum;
-  }
-  __syncthreads();
+  const float* abar = reinterpret_cast<const float*>(lds);
+  const float* stats = abar + HG * RV;
   const float* arow = abar + hw * RV;
   const size_t uidx = static_cast<size_t>(b * a.H + h) * a.L + li;
   if (a.S > 1) {
