@@ -48,10 +48,12 @@ constexpr float kMaxInit = -1.0e30f;   // finite stand-in for -inf: the first va
 constexpr float kRescaleSlack = 8.0f;  // raise the running max only when exceeded by 2^8
 constexpr int kXcds = 8;
 #ifndef LLA_2D_AHEAD
-#define LLA_2D_AHEAD 3
+#define LLA_2D_AHEAD 5
 #endif
 constexpr int kAhead = LLA_2D_AHEAD;     // tile c + kAhead is requested in iteration c
-constexpr int kStages = kAhead + 3;      // tiles c - 2 .. c + kAhead live in iteration c
+// tiles c - 2 .. c + kAhead live in iteration c; an even count keeps the P buffer parity
+// a function of the stage index
+constexpr int kStages = (kAhead + 4) / 2 * 2;
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -136,8 +138,8 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   using S = Shape<D, RK, RV, HG>;
   constexpr int NW = S::NW, NKS = S::NKS, NCK = S::NCK, NT = S::NT, NRT = S::NRT, VT = S::VT;
   constexpr int RING_UNITS = kStages * S::STAGE_UNITS;
-  constexpr int P_UNITS = 2 * 16 * 16 * 2 / 16;   // two P tiles [16 heads][16 tokens] bf16
-  constexpr int AL_UNITS = 2 * 16 * 4 / 16;       // two rows of per-head rescale factors
+  constexpr int P_UNITS = (2 * 16 * 16 + 64) * 2 / 16;  // two P tiles of bf16, 64 spare slots
+  constexpr int AL_UNITS = (2 * 16 + 64) * 4 / 16;       // two rows of rescale factors, spares
   constexpr int PAGE_UNITS = PAGED ? kMaxSplitPages * 4 / 16 : 0;
   constexpr int LDS_UNITS = RING_UNITS + S::STAGING_UNITS + P_UNITS + AL_UNITS + PAGE_UNITS;
   static_assert(HG * RV + 2 * HG <= RING_UNITS * 4, "epilogue staging fits the ring");
@@ -385,19 +387,20 @@ void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
     };
     // softmax weights of tile c from its scores, into P tile c and its rescale factor
     auto tail = [&](int par, float s) {
-      float alpha = 1.f;
-      // the head's max is raised (to the tile's max) only when a score exceeds it by 2^8;
-      // every lane of the wave holds the same head, so the branch is uniform
-      if (__builtin_amdgcn_ballot_w64(s > m_run + kRescaleSlack) != 0) {
-        const float mt = max16(s);
-        alpha = fast_exp2(m_run - mt);
-        l_run *= alpha;
-        m_run = mt;
-      }
+      // The head's max is raised (to the tile's max) only when a score exceeds it by 2^8;
+      // every lane of the wave holds the same head, so the choice is uniform. It is made
+      // without a branch (the tile max is formed every time), and every lane writes (the
+      // lanes that hold no P entry or rescale factor write to a spare slot), so the tail
+      // shares one basic block with the next tile's matrix-core work.
+      const bool raise = __builtin_amdgcn_ballot_w64(s > m_run + kRescaleSlack) != 0;
+      const float m_new = raise ? max16(s) : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
       const uint16_t pb = __builtin_bit_cast(uint16_t, static_cast<__bf16>(fast_exp2(s - m_run)));
       l_run += bf16_to_f32(pb);
-      if (hi == 0) ptile[par * 256 + (lo >> 2) * 64 + hw * 4 + (lo & 3)] = pb;
-      if (lane == 0) alpha_buf[par * 16 + hw] = alpha;
+      ptile[hi == 0 ? par * 256 + (lo >> 2) * 64 + hw * 4 + (lo & 3) : 512 + lane] = pb;
+      alpha_buf[lane == 0 ? par * 16 + hw : 32 + lane] = alpha;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // visible to the next barrier's readers
     };
     // value product of tile c: rescale by the tile's alphas, then acc += P(c) C_v(c)
