@@ -57,7 +57,8 @@ def kernel_source_hash(kind: str) -> str:
     csrc = os.path.join(ROOT, "latent_decode_attention_lla_amd", "csrc")
     h = hashlib.sha256()
     files = [os.path.join(csrc, f) for f in sorted(KERNEL_SOURCES[kind])]
-    files.append(os.path.join(ROOT, "latent_decode_attention_lla_amd", "build.py"))  # flags
+    from latent_decode_attention_lla_amd import build as _build  # the compile flags
+    h.update(repr((_build.ARCH, _build.HIP_FLAGS, sorted(_build.FILE_FLAGS.items()))).encode())
     for path in files:
         f = os.path.basename(path)
         with open(path) as fh:
@@ -325,7 +326,8 @@ def main_stream_prefill(args, w):
                   else algorithmic(w, "reconstruct", L=w.T, n_new=n))
         calls[kind] = {"avg_ms": round(ms, 5), "median_ms": round(xs[len(xs) // 2], 5),
                        "algorithmic_bytes": nb, "algorithmic_flops": fl,
-                       "roofline": roofline(nb, fl, ms, measured_traffic(kind, w.name, "auto"))}
+                       "roofline": roofline(nb, fl, ms, measured_traffic(kind, w.name, "auto"),
+                                            measured_counters(kind, w.name, "auto"))}
     dominant = max(calls, key=lambda k: calls[k]["avg_ms"])
     cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_sample_tokens)
     peak_gib = (w.D * w.batch * w.Hc * n * (w.r_k + w.r_v) * es
@@ -357,14 +359,56 @@ def main_stream_prefill(args, w):
     print(json.dumps(res))
 
 
-def roofline(nbytes, flops, ms, traffic=None):
+def counters_file(kind: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kind}_{workload}_counters.json")
+
+
+def measured_counters(kind: str, workload: str, path: str):
+    """Wave-state counters of the call's dominant kernel from the committed rocprofv3 --pmc
+    summary (wait and issue-wait fractions, instructions per wave), or None when there is
+    none or the call's sources have changed since it was taken."""
+    try:
+        with open(counters_file(kind, workload)) as f:
+            ct = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if ct.get("kernel_source_hash") == kernel_source_hash(kind) and ct.get("path") == path \
+            and ct.get("workload") == workload:
+        return {k: ct[k] for k in ("kernel", "wave_wait_frac", "wave_issue_wait_frac",
+                                   "valu_insts_per_wave", "mfma_insts_per_wave",
+                                   "salu_insts_per_wave", "lds_bank_conflict_per_lds_cycle")
+                if k in ct}
+    return None
+
+
+NEAR_ROOF = 0.5  # a call reaching half of a roof's peak is taken as bound by that roof
+
+
+def roofline(nbytes, flops, ms, traffic=None, counters=None):
+    """Both fractions of peak for one call: HBM (algorithmic bytes, and the measured
+    traffic when a current summary exists) and bf16 MFMA (algorithmic flops). `bound` is
+    the roof the call is closer to, and `frac` is quoted against it. `binding` names what
+    limits the call: that roof when the call reaches NEAR_ROOF of it, else "issue" (neither
+    HBM nor the matrix cores near their peaks: instruction issue, dependency latency and
+    waits bound the call), with the committed wave-state counters as evidence."""
     gbs = nbytes / (ms * 1e-3) / 1e9
     tfs = flops / (ms * 1e-3) / 1e12
-    if flops / max(nbytes, 1) > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        return {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    hbm_frac = gbs / HBM_PEAK_GBS
+    mfma_frac = tfs / MFMA_BF16_PEAK_TFLOPS
+    meas_frac = None if traffic is None else traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    hbm_best = max(hbm_frac, meas_frac or 0.0)
+    if mfma_frac > hbm_best:
+        r = {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(mfma_frac, 4), "traffic": traffic}
+    else:
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(hbm_frac, 4), "traffic": traffic}
+    r["hbm_frac"] = round(hbm_frac, 4)
+    r["measured_hbm_frac"] = None if meas_frac is None else round(meas_frac, 4)
+    r["mfma_frac"] = round(mfma_frac, 4)
+    r["binding"] = r["bound"] if max(hbm_best, mfma_frac) >= NEAR_ROOF else "issue"
+    r["counters"] = counters
+    return r
 
 
 def main():
@@ -519,12 +563,14 @@ def main():
     dec_kind = "teacher" if teacher else ("absorbed" if absorbed else ("paged" if w.paged else "decode"))
     dec_ms, dec_med = avg(ev_dec[:n_dec * args.steps])
     dec_bytes, dec_flops = algorithmic(w, "decode")
-    dec_roof = roofline(dec_bytes, dec_flops, dec_ms, measured_traffic(dec_kind, args.workload, args.path))
+    dec_roof = roofline(dec_bytes, dec_flops, dec_ms, measured_traffic(dec_kind, args.workload, args.path),
+                        measured_counters(dec_kind, args.workload, args.path))
     if n_enc > 0:
         enc_ms, enc_med = avg(ev_enc[:n_enc * args.steps])
         enc_bytes, enc_flops = algorithmic(w, "encode", n_new=n_new)
         enc_roof = roofline(enc_bytes, enc_flops, enc_ms,
-                            measured_traffic("encode", args.workload, args.path))
+                            measured_traffic("encode", args.workload, args.path),
+                            measured_counters("encode", args.workload, args.path))
     dominant = "decode" if n_enc == 0 or dec_ms * n_dec >= enc_ms * n_enc else "encode"
 
     reference = None

@@ -15,7 +15,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblla.so")
+# LLA_LIBRARY names another build of the same library (the host-ASan build of build.py)
+LIB_PATH = os.environ.get("LLA_LIBRARY") or os.path.join(HERE, "liblla.so")
 
 LLA_OK = 0
 LLA_ERR_INVALID_ARG = -1

@@ -12,6 +12,14 @@ whose names contain one of the given fragments:
   python -m latent_decode_attention_lla_amd.rocprof_summary counters RUN_results.db \
       --kernel decode_rotary_fold
 
+``waves`` turns two SQ counter passes of one kernel (between them: SQ_WAVES, SQ_WAVE_CYCLES,
+SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_INSTS_VALU, SQ_INSTS_SALU, SQ_INSTS_MFMA, SQ_INSTS_LDS,
+SQ_LDS_BANK_CONFLICT, SQ_ACTIVE_INST_LDS) into the wave-state evidence
+bench.py reports for a call bound by neither roof:
+
+  python -m latent_decode_attention_lla_amd.rocprof_summary waves --p1 A.db --p2 B.db \
+      --kernel decode_lla2d --call decode --workload lla2d_long --out counters.json
+
 ``traffic`` scales the per-dispatch FETCH_SIZE and WRITE_SIZE (KiB) of the named kernel by
 what the same counters read for a plain device copy of N bytes read and N bytes written
 (the copy kernel whose counters are largest in the copy runs), and reports HBM bytes per
@@ -69,6 +77,13 @@ def main(argv=None):
     cn = sp.add_parser("counters")
     cn.add_argument("db")
     cn.add_argument("--kernel", required=True)
+    wv = sp.add_parser("waves")
+    wv.add_argument("--p1", required=True)
+    wv.add_argument("--p2", required=True)
+    wv.add_argument("--kernel", required=True)
+    wv.add_argument("--call", required=True)
+    wv.add_argument("--workload", required=True)
+    wv.add_argument("--out")
     t = sp.add_parser("traffic")
     for name in ("fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument(f"--{name}", required=True)
@@ -99,6 +114,39 @@ def main(argv=None):
             for k, (n, v) in sorted(counter_per_kernel(a.db, c).items()):
                 if any(x in k for x in subs):
                     print(f"| {c} | {v:.4g} | {n} | `{k[:100]}` |")
+        return
+    if a.cmd == "waves":
+        import os
+        sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+        import bench
+        c = {}
+        kname = None
+        for n in ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU",
+                  "SQ_INSTS_SALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+                  "SQ_ACTIVE_INST_LDS"):
+            for db in (a.p1, a.p2):  # each counter is taken from whichever pass holds it
+                try:
+                    kname, (_, v) = _pick(counter_per_kernel(db, n), a.kernel)
+                except SystemExit:
+                    continue
+                c[n] = v
+                break
+        waves = c.get("SQ_WAVES") or 1.0
+        res = {"kernel": kname, "counters_per_dispatch": c,
+               "wave_wait_frac": c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"],
+               "wave_issue_wait_frac": c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"],
+               "valu_insts_per_wave": (c["SQ_INSTS_VALU"] - c.get("SQ_INSTS_MFMA", 0.0)) / waves,
+               "mfma_insts_per_wave": c.get("SQ_INSTS_MFMA", 0.0) / waves,
+               "salu_insts_per_wave": c["SQ_INSTS_SALU"] / waves,
+               "call": a.call, "workload": a.workload, "path": "auto",
+               "kernel_source_hash": bench.kernel_source_hash(a.call)}
+        if c.get("SQ_ACTIVE_INST_LDS"):
+            res["lds_bank_conflict_per_lds_cycle"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]
+        txt = json.dumps(res, indent=1)
+        if a.out:
+            with open(a.out, "w") as f:
+                f.write(txt + "\n")
+        print(txt)
         return
     fk, (fn, fv) = _pick(counter_per_kernel(a.fetch, "FETCH_SIZE"), a.kernel, a.sum)
     wk, (wn, wv) = _pick(counter_per_kernel(a.write, "WRITE_SIZE"), a.kernel, a.sum)
