@@ -102,9 +102,50 @@ def parse():
     p.add_argument("--cpu-sample-seqs", type=int, default=1)
     p.add_argument("--cpu-sample-tokens", type=int, default=16384,
                    help="prompt tokens of the oracle's sample for the streamed-prefill workload")
+    p.add_argument("--ceiling-gib", type=float, default=0.0,
+                   help="time plain streaming passes over buffers of this size (read-only, "
+                        "copy, 4:1 and 1:4 read:write) and print their HBM rates instead")
     p.add_argument("--copy-calibration-gib", type=float, default=0.0,
                    help="only run a plain device copy of this size (for counter scaling)")
     return p.parse_args()
+
+
+def stream_ceilings(gib: float):
+    """HBM ceilings on this device from plain 16-byte-per-lane streaming passes
+    (include/lla_stream.h) over `gib` GiB of reads (the 1:4 mix: of writes): the rates the
+    decode (read-only), encode (4:1) and reconstruction (1:4) kernels compare against."""
+    import torch
+    from latent_decode_attention_lla_amd import lla
+    lla.load()
+    n = int(gib * 2**30) // 16
+    n -= n % 4
+    src = torch.empty(n * 16, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n * 16, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    # (mode, vectors per pass, bytes read, bytes written)
+    modes = {"read": (0, n, n * 16, 0), "copy_1to1": (1, n // 2, n // 2 * 16, n // 2 * 16),
+             "mix_4to1": (2, n // 4, n * 16, n // 4 * 16), "mix_1to4": (3, n // 4, n // 4 * 16, n * 16)}
+    res = {}
+    for wg in (1024, 2048, 4096, 8192):
+        for name, (mode, nv, rd, wr) in modes.items():
+            for _ in range(2):
+                lla.lla_stream_ceiling(mode, src, dst, nv, wg)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            reps = 10
+            ev[0].record()
+            for _ in range(reps):
+                lla.lla_stream_ceiling(mode, src, dst, nv, wg)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / reps
+            tbs = (rd + wr) / (ms * 1e-3) / 1e12
+            best = res.get(name)
+            if best is None or tbs > best["tb_per_s"]:
+                res[name] = {"tb_per_s": round(tbs, 3), "ms": round(ms, 4), "workgroups": wg,
+                             "bytes_read": rd, "bytes_written": wr,
+                             "frac_of_8tbs": round(tbs / (HBM_PEAK_GBS / 1e3), 4)}
+    print(json.dumps({"stream_ceilings": res, "buffer_gib": gib}))
 
 
 def copy_calibration(gib: float):
@@ -420,6 +461,9 @@ def main():
     import torch
     if args.copy_calibration_gib > 0:
         copy_calibration(args.copy_calibration_gib)
+        return
+    if args.ceiling_gib > 0:
+        stream_ceilings(args.ceiling_gib)
         return
 
     from latent_decode_attention_lla_amd import lla

@@ -42,7 +42,7 @@ EXPORTED = (
     "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
     "lla_decode_teacher_num_splits", "lla_decode_paged_num_splits", "lla_reconstruct",
     "lla_encode_paged", "lla_decode_paged_workspace_bytes", "lla_decode_attn_paged",
-    "lla_decode_attn_noalloc",
+    "lla_decode_attn_noalloc", "lla_stream_ceiling",
 )
 
 # bytes of the fixed split-partial array lla_decode_attn_noalloc uses (include/lla.h)
@@ -118,6 +118,8 @@ def load() -> ctypes.CDLL:
     lib.lla_decode_attn_noalloc.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, i32, vp,
                                             vp, i32, i32, vp, P(lla_decode_opts), vp]
     lib.lla_decode_attn_noalloc.restype = i32
+    lib.lla_stream_ceiling.argtypes = [i32, vp, vp, sz, i32, vp]
+    lib.lla_stream_ceiling.restype = i32
     lib.lla_decode_attn.restype = i32
     lib.lla_decode_absorbed_workspace_bytes.argtypes = [P(lla_dims), i32, i32, i32,
                                                         P(lla_decode_opts)]
@@ -257,6 +259,14 @@ def lla_decode_attn_noalloc(dims: lla_dims, codec: lla_codec, cache: lla_cache, 
         ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(cache), layer, n_ctx,
         _ptr(ctx_lens), _ptr(q), loop_begin, loop_count, _ptr(out),
         ctypes.byref(opts) if opts is not None else None, _stream(stream)))
+
+
+def lla_stream_ceiling(mode: int, src, dst, n_vectors: int, workgroups: int, stream=None) -> None:
+    """Measurement helper (include/lla_stream.h): a plain streaming pass, mode 0 read-only,
+    1 copy, 2 four reads per write, 3 four writes per read."""
+    st = load().lla_stream_ceiling(mode, _ptr(src), _ptr(dst), n_vectors, workgroups, _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"lla_stream_ceiling failed: {st}")
 
 
 def lla_decode_absorbed_workspace_bytes(dims: lla_dims, d_rope: int, n_ctx: int, loop_count: int,

@@ -2,6 +2,7 @@
 entry point include/lla.h declares, computes the closed forms of Eq. 4 and Table 5, and
 rejects bad arguments before anything is enqueued."""
 
+import glob
 import os
 import re
 
@@ -15,9 +16,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_symbols():
-    src = open(os.path.join(ROOT, "include", "lla.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(lla_[a-z0-9_]+)\s*\(", src)))
+    out = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        out |= set(re.findall(r"\b(lla_[a-z0-9_]+)\s*\(", src))
+    return sorted(out)
 
 
 def test_library_exports_every_declared_symbol():
