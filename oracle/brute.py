@@ -94,3 +94,22 @@ def brute_reconstruct_key_one(c, w_up_t, mu_t, pos, base):
 def brute_reconstruct_value_one(c, w_up_t, mu_t):
     """One rebuilt value: c [r], W_up,t [d][r], mu_t [d] -> [d]."""
     return [a + b for a, b in zip(_row_times_matT(c, w_up_t), mu_t)]
+
+
+def brute_encode_fused_one(h_loops, w_proj, mu, w_down, head, H, d, per_head):
+    """Latent of one token and latent head by scalar loops: h_loops [T][d_model], w_proj
+    [d_model][H*d], mu [T*d_in], w_down [T*d_in][r]. Loop t's projection is summed term
+    by term and placed at stacked offset t*d_in (+ h*d within LLA-2D's (t, h, d) order)."""
+    T = len(h_loops)
+    heads = [head] if per_head else list(range(H))
+    d_in = d * len(heads)
+    x = [0.0] * (T * d_in)
+    for t in range(T):
+        for k, hh in enumerate(heads):
+            for i in range(d):
+                col = hh * d + i
+                x[t * d_in + k * d + i] = math.fsum(h_loops[t][m] * w_proj[m][col]
+                                                    for m in range(len(h_loops[t])))
+    r = len(w_down[0])
+    return [math.fsum((x[a] - mu[a]) * w_down[a][j] for a in range(len(x))) for j in range(r)]
+

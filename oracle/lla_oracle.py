@@ -21,6 +21,9 @@ softmax attention follows. Readings taken where the pages are silent:
 * Score scale defaults to 1/sqrt(d_head).
 * Attention over an empty context returns zeros.
 * LLA-2D stacks its input (t, h, d) with the loop index outermost.
+* Projection-fused encode (Appendix J, "Eviction and long-context prefill"; Eq. 2): the
+  keys (values) of loop t are x_t = h_t W_proj with the layer's projection shared by
+  every loop, taken exactly (the fused path never stores x_t, so it is not rounded).
 * Decoupled (absorbed) decode, Appendix J: dimensions 0 .. d_rope-1 of a head are the
   rotary branch (one stored, already rotated key per token, shared by every loop), the
   rest the content path (the loop's reconstructed key without RoPE); scale 1/sqrt(d).
@@ -69,6 +72,7 @@ __all__ = [
     "svd_init",
     "round_bf16",
     "encode_stored",
+    "encode_fused",
 ]
 
 
@@ -478,3 +482,33 @@ def encode_stored(x: np.ndarray, mu: np.ndarray, w_down: np.ndarray, dtype: str)
     if dtype == "f32":
         return c.astype(np.float32).astype(np.float64)
     raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# Projection-fused encode: Appendix J, "Eviction and long-context prefill" (stream the
+# prefill so that no layer holds its per-loop keys and values longer than needed);
+# Section 3, Eqs. 1-2.
+# ---------------------------------------------------------------------------
+
+def encode_fused(h_loops: np.ndarray, w_proj: np.ndarray, mu: np.ndarray, w_down: np.ndarray,
+                 H: int, d: int, variant: str = "per_head") -> np.ndarray:
+    """Latents of N tokens from the hidden states that enter one layer's key (or value)
+    projection at each loop: x_t = h_t W_proj for t = 1 .. T (one projection shared by
+    every loop of the looped layer), the per-loop vectors stacked as in Eq. 1, then Eq. 2.
+
+    h_loops [T, N, d_model]; w_proj [d_model, H*d] (head h owns columns h*d .. h*d+d-1);
+    mu [Hc, T*d_in]; w_down [Hc, T*d_in, r] (Hc = H, d_in = d per head; Hc = 1, d_in = H*d
+    for LLA-2D, stacked (t, h, d)). Returns c [N, Hc, r] float64, unrounded."""
+    h_loops = np.asarray(h_loops, dtype=np.float64)
+    T, N, _ = h_loops.shape
+    x = np.stack([h_loops[t] @ np.asarray(w_proj, dtype=np.float64) for t in range(T)])  # [T, N, H*d]
+    Hc = mu.shape[0]
+    out = np.empty((N, Hc, w_down.shape[-1]))
+    for hc in range(Hc):
+        if variant == "per_head":
+            xs = stack_loops(np.transpose(x[:, :, hc * d:(hc + 1) * d], (1, 0, 2)))  # [N, T*d]
+        else:
+            xs = stack_loops(np.transpose(x, (1, 0, 2)))  # [N, T*H*d], (t, h, d)
+        out[:, hc] = encode(xs, mu[hc], w_down[hc])
+    return out
+

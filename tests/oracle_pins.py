@@ -729,6 +729,50 @@ def pin_eviction_window() -> float:
     return err
 
 
+def pin_encode_fused() -> float:
+    """Projection-fused encode: (1) a scalar brute force (oracle/brute.py) on tiny inputs,
+    per head and LLA-2D; (2) full rank: r = T*d, orthonormal W_down, W_up,t its loop slices,
+    so rebuilding loop t gives back h_t W_proj (head slice, by torch.matmul) exactly; (3)
+    the oracle's encode of captures materialised by torch.matmul, stacked by reshaping."""
+    err = 0.0
+    rng = _rng(71)
+    T, H, d, dm, N = 2, 2, 4, 6, 3
+    for variant in ("per_head", "2d"):
+        Hc = H if variant == "per_head" else 1
+        din = d if variant == "per_head" else H * d
+        r = 3
+        h = rng.standard_normal((T, N, dm))
+        wp = rng.standard_normal((dm, H * d)) / math.sqrt(dm)
+        mu = rng.standard_normal((Hc, T * din)) * 0.3
+        wd = rng.standard_normal((Hc, T * din, r)) / math.sqrt(T * din)
+        got = O.encode_fused(h, wp, mu, wd, H, d, variant)
+        for n in range(N):
+            for hc in range(Hc):
+                ref = brute.brute_encode_fused_one(h[:, n].tolist(), wp.tolist(), mu[hc].tolist(),
+                                                   wd[hc].tolist(), hc, H, d, variant == "per_head")
+                err = max(err, float(np.max(np.abs(got[n, hc] - np.array(ref)))))
+        # (3) captures by a library matmul, stacked by reshaping [N, T, H, d]
+        x = torch.matmul(torch.from_numpy(h), torch.from_numpy(wp)).numpy()  # [T, N, H*d]
+        xs = np.transpose(x.reshape(T, N, H, d), (1, 2, 0, 3))  # [N, H, T, d]
+        for hc in range(Hc):
+            stacked = xs[:, hc].reshape(N, T * d) if variant == "per_head" else \
+                np.transpose(xs, (0, 2, 1, 3)).reshape(N, T * H * d)
+            err = max(err, float(np.max(np.abs(got[:, hc] - O.encode(stacked, mu[hc], wd[hc])))))
+    # (2) full-rank round trip, per head
+    r = T * d
+    h = rng.standard_normal((T, N, dm))
+    wp = rng.standard_normal((dm, H * d))
+    mu = rng.standard_normal((H, T * d))
+    wd = np.stack([_orthonormal(r, r, 300 + hh) for hh in range(H)])
+    c = O.encode_fused(h, wp, mu, wd, H, d, "per_head")
+    x = torch.matmul(torch.from_numpy(h), torch.from_numpy(wp)).numpy()
+    for hh in range(H):
+        for t in range(T):
+            back = O.reconstruct(c[:, hh], wd[hh][t * d:(t + 1) * d], mu[hh, t * d:(t + 1) * d])
+            err = max(err, float(np.max(np.abs(back - x[t][:, hh * d:(hh + 1) * d]))))
+    return err
+
+
 ALL_PINS = {
     "closed_forms": (pin_closed_forms, 1e-9),
     "rope": (pin_rope, 1e-12),
@@ -751,4 +795,5 @@ ALL_PINS = {
     "paged_permuted": (pin_paged_permuted, 1e-12),
     "eviction_window": (pin_eviction_window, 1e-12),
     "absorbed_paged_permuted": (pin_absorbed_paged_permuted, 1e-12),
+    "encode_fused": (pin_encode_fused, 1e-12),
 }

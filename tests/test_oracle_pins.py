@@ -173,9 +173,24 @@ def _mut_window_keeps_oldest(n_pages_written, sink_pages, window_pages):
     return list(range(sink_pages + window_pages))
 
 
+def _mut_fused_loops_reversed(h_loops, w_proj, mu, w_down, H, d, variant="per_head"):
+    """Stacks the loops in reverse order."""
+    return _ORIG["encode_fused"](np.asarray(h_loops)[::-1], w_proj, mu, w_down, H, d, variant)
+
+
+def _mut_fused_next_head(h_loops, w_proj, mu, w_down, H, d, variant="per_head"):
+    """Takes each head's keys from the next head's projection columns."""
+    w = np.roll(np.asarray(w_proj), -d, axis=1)
+    return _ORIG["encode_fused"](h_loops, w, mu, w_down, H, d, variant)
+
+
+def _mut_fused_no_centering(h_loops, w_proj, mu, w_down, H, d, variant="per_head"):
+    return _ORIG["encode_fused"](h_loops, w_proj, np.zeros_like(mu), w_down, H, d, variant)
+
+
 _ORIG = {name: getattr(O, name) for name in
          ("apply_rope", "reconstruct", "attention", "_mu_slice", "rope_theta", "absorbed_keys",
-          "reconstruct_cache")}
+          "reconstruct_cache", "encode_fused")}
 
 MUTANTS = {
     "rope_sign": ("apply_rope", _mut_rope_sign),
@@ -202,6 +217,9 @@ MUTANTS = {
     "gather_pages_next_page": ("gather_pages", _mut_gather_pages_next_page),
     "window_keeps_oldest": ("window_pages", _mut_window_keeps_oldest),
     "absorbed_paged_rope_unrouted": ("decode_absorbed_paged", _mut_absorbed_paged_rope_unrouted),
+    "fused_loops_reversed": ("encode_fused", _mut_fused_loops_reversed),
+    "fused_next_head": ("encode_fused", _mut_fused_next_head),
+    "fused_no_centering": ("encode_fused", _mut_fused_no_centering),
 }
 
 
