@@ -269,6 +269,41 @@ int32_t lla_encode_paged(const lla_dims* dims, const lla_codec* codec, const lla
                          const lla_pages* pages, int32_t layer, const void* x_k, const void* x_v,
                          int32_t pos_start, int32_t n_new, void* stream);
 
+/* Projection-fused encode (Section 3, Eqs. 1-2; Appendix J, "Eviction and long-context
+ * prefill": the per-loop keys and values of a prompt need never be stored). A looped
+ * layer applies the same key and value projections at every loop, x_t = h_t W_proj, to
+ * that loop's input h_t. Eq. 2 is linear in the stacked vector, so
+ *   c = sum_t (x_t - mu_t) W_down[rows of loop t],
+ * and each loop's term can be added as soon as h_t exists. One call handles loop `loop`
+ * of `layer` for keys and values: it forms x_t for the n_new new tokens of every
+ * sequence, subtracts mu_t and adds the term to `acc`; the call for loop T - 1 rounds the
+ * sum once (to nearest even) and writes cache rows pos_start .. pos_start + n_new - 1.
+ *   proj->w_k, proj->w_v : device bfloat16 [D][d_model][H * d_head], the key and value
+ *            projections of every layer (head h owns columns h d_head .. h d_head +
+ *            d_head - 1); proj->d_model a positive multiple of 32.
+ *   h      : device bfloat16 [batch][n_new][d_model], the hidden states that enter the
+ *            projections at this loop.
+ *   acc    : device float32, acc_bytes >= lla_encode_fused_acc_bytes(dims, n_new): the
+ *            running sum, owned by the caller and kept between the calls of one layer.
+ *            Loop 0 overwrites it (no clearing needed); loops 1 .. T-1 read and update it.
+ *   codec  : w_down_k_t, mu_k, w_down_v_t, mu_v as for lla_encode.
+ * The T calls of a layer must run in loop order 0 .. T-1 with the same acc, n_new and
+ * pos_start, on one stream (or ordered by the caller); the cache rows hold the result
+ * only after loop T - 1. Built for bfloat16, d_head 128 and r_k, r_v in {16, 32, 64, 96,
+ * 128, 160}, per head and LLA-2D; other shapes give LLA_ERR_UNSUPPORTED. Otherwise
+ * arguments and errors as lla_encode, plus LLA_ERR_INVALID_ARG for 0 > loop or loop >= T
+ * and LLA_ERR_WORKSPACE for a short acc. n_new == 0 enqueues nothing. */
+typedef struct {
+  const void* w_k;
+  const void* w_v;
+  int32_t d_model;
+} lla_proj;
+size_t lla_encode_fused_acc_bytes(const lla_dims* dims, int32_t n_new);
+int32_t lla_encode_fused(const lla_dims* dims, const lla_codec* codec, const lla_proj* proj,
+                         const lla_cache* cache, int32_t layer, int32_t loop, const void* h,
+                         int32_t pos_start, int32_t n_new, float* acc, size_t acc_bytes,
+                         void* stream);
+
 /* lla_decode_attn over a paged cache (logical tokens 0 .. len_b - 1 through the block
  * table; RoPE at the logical slot). Paths as lla_decode_attn: the rotary fold kernels
  * (bfloat16 shapes they are built for, per head and LLA-2D), else the reconstruct path;

@@ -198,6 +198,75 @@ int32_t lla_encode(const lla_dims* d, const lla_codec* codec, const lla_cache* c
   return hip_status();
 }
 
+size_t lla_encode_fused_acc_bytes(const lla_dims* d, int32_t n_new) {
+  if (check_dims(d) != LLA_OK || n_new < 0) return 0;
+  const size_t bytes = static_cast<size_t>(d->batch) * n_new * latent_heads(*d) *
+                       static_cast<size_t>(d->r_k + d->r_v) * 4;
+  return (bytes + 255) / 256 * 256;
+}
+
+int32_t lla_encode_fused(const lla_dims* d, const lla_codec* codec, const lla_proj* proj,
+                         const lla_cache* cache, int32_t layer, int32_t loop, const void* h,
+                         int32_t pos_start, int32_t n_new, float* acc, size_t acc_bytes,
+                         void* stream) {
+  int32_t st = check_dims(d);
+  if (st != LLA_OK) return st;
+  if (codec == nullptr || proj == nullptr || cache == nullptr) return LLA_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= d->D || loop < 0 || loop >= d->T) return LLA_ERR_INVALID_ARG;
+  if (n_new < 0 || pos_start < 0 || static_cast<long long>(pos_start) + n_new > d->n_max)
+    return LLA_ERR_INVALID_ARG;
+  if (proj->d_model < 32 || proj->d_model % 32 != 0) return LLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {h, acc, proj->w_k, proj->w_v, codec->w_down_k_t, codec->w_down_v_t,
+                        codec->mu_k, codec->mu_v, cache->c_k, cache->c_v};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return LLA_ERR_INVALID_ARG;
+  if (!lla::encode_fused_supported(d->dtype, d->d_head, d->r_k) ||
+      !lla::encode_fused_supported(d->dtype, d->d_head, d->r_v))
+    return LLA_ERR_UNSUPPORTED;
+  // token and weight offsets inside the kernel are 32-bit per row block
+  if (static_cast<long long>(d->batch) * n_new >= (1LL << 31) - 256) return LLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(proj->d_model) * d->H * d->d_head >= (1LL << 31))
+    return LLA_ERR_UNSUPPORTED;
+  if (n_new == 0) return LLA_OK;
+  if (acc_bytes < lla_encode_fused_acc_bytes(d, n_new)) return LLA_ERR_WORKSPACE;
+  const int Hc = latent_heads(*d);
+  const int din = d_in(*d);
+  const size_t K = static_cast<size_t>(d->T) * din;
+  const size_t es = elem_bytes(*d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int rs[2] = {d->r_k, d->r_v};
+  const void* wps[2] = {proj->w_k, proj->w_v};
+  const void* wds[2] = {codec->w_down_k_t, codec->w_down_v_t};
+  const void* mus[2] = {codec->mu_k, codec->mu_v};
+  void* cs[2] = {cache->c_k, cache->c_v};
+  for (int ax = 0; ax < 2; ++ax) {
+    const int r = rs[ax];
+    lla::FusedArgs a;
+    a.h = h;
+    a.w_proj = static_cast<const char*>(wps[ax]) +
+               static_cast<size_t>(layer) * proj->d_model * d->H * d->d_head * es;
+    a.w_down_t = static_cast<const char*>(wds[ax]) + static_cast<size_t>(layer) * Hc * r * K * es;
+    a.mu = static_cast<const char*>(mus[ax]) + static_cast<size_t>(layer) * Hc * K * es;
+    a.c = static_cast<char*>(cs[ax]) +
+          static_cast<size_t>(layer) * d->batch * Hc * static_cast<size_t>(d->n_max) * r * es;
+    a.acc = acc;
+    a.Ntok = d->batch * n_new;
+    a.n_new = n_new;
+    a.pos_start = pos_start;
+    a.n_max = d->n_max;
+    a.H = d->H;
+    a.Hc = Hc;
+    a.T = d->T;
+    a.d_in = din;
+    a.d_model = proj->d_model;
+    a.loop = loop;
+    a.RT = d->r_k + d->r_v;
+    a.ao = ax == 0 ? 0 : d->r_k;
+    if (!lla::launch_encode_fused(r, a, d->variant == LLA_PER_HEAD, s)) return LLA_ERR_UNSUPPORTED;
+  }
+  return hip_status();
+}
+
 int32_t lla_decode_num_splits(const lla_dims* d, int32_t n_ctx, int32_t loop_count,
                               const lla_decode_opts* opts) {
   if (check_dims(d) != LLA_OK || n_ctx < 0 || loop_count < 1) return 0;

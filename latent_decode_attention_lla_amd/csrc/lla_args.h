@@ -34,6 +34,17 @@ struct EncodeArgs {
   int B, Hc, Kdim, n_new, pos_start, n_max;
 };
 
+// Projection-fused encode: loop `loop` of one layer and one axis (keys or values).
+struct FusedArgs {
+  const void* h;        // [Ntok][d_model], Ntok = B * n_new: the loop's projection input
+  const void* w_proj;   // layer base, [d_model][H * d]
+  const void* w_down_t; // layer base, [Hc][r][T * d_in]
+  const void* mu;       // layer base, [Hc][T * d_in]
+  void* c;              // layer base, [B][Hc][n_max][r]
+  float* acc;           // [Ntok][Hc][RT]: running sum over the loops, this axis at ao
+  int Ntok, n_new, pos_start, n_max, H, Hc, T, d_in, d_model, loop, RT, ao;
+};
+
 // Heads per workgroup of the rotary-fold kernel; H must be a multiple of it.
 #ifndef LLA_FOLD_HPW
 #define LLA_FOLD_HPW 4

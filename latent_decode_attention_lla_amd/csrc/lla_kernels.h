@@ -62,6 +62,9 @@ bool reconstruct_supported(int dtype, int d, int r);
 int reconstruct_max_loops(int dtype, int d, int r);
 
 bool launch_encode(int dtype, int r, const EncodeArgs& a, hipStream_t s);
+// Projection-fused encode of one loop and axis (bfloat16, d 128).
+bool encode_fused_supported(int dtype, int d, int r);
+bool launch_encode_fused(int r, const FusedArgs& a, bool per_head, hipStream_t s);
 bool encode_supported(int dtype, int r, int Kdim);
 
 void launch_rope_table(int d, int n_max, double base, float* t32, uint16_t* t16, hipStream_t s);

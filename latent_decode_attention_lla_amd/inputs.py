@@ -256,3 +256,33 @@ def encode_x(w: Workload, n_new: int, seed: int, device="cpu", correlated: bool 
                 x[:, :, :, t] = x[:, :, :, 0] + 0.3 * (t + 1) * eps[:, :, :, t]
         out.append(x.to(w.torch_dtype))
     return out[0], out[1]
+
+
+def fused_encode_inputs(w: Workload, n_new: int, d_model: int, seed: int, device="cpu",
+                        batch: int | None = None):
+    """Inputs of the projection-fused encode, in the workload dtype: the hidden states
+    that enter a layer's key and value projections at each loop, h [T][B][n_new][d_model]
+    ~ N(0, 1), and the projections of every layer, w_k and w_v [D][d_model][H*d]
+    ~ N(0, 1/d_model) (so the per-loop keys and values h_t W have about unit variance,
+    like the per-loop K/V drawn by encode_x)."""
+    B = batch or w.batch
+    g = _gen(seed, device)
+    dt = w.torch_dtype
+    h = _randn((w.T, B, n_new, d_model), 1.0, dt, g, device)
+    w_k = _randn((w.D, d_model, w.H * w.d), 1.0 / math.sqrt(d_model), dt, g, device)
+    w_v = _randn((w.D, d_model, w.H * w.d), 1.0 / math.sqrt(d_model), dt, g, device)
+    return h, w_k, w_v
+
+
+def gaussian_encode_codec(w: Workload, seed: int, device="cpu"):
+    """Encode-side codec with W_down ~ N(0, 1/K) (K = T*d_in), stored transposed
+    [D][Hc][r][K], and mu ~ N(0, 0.1) [D][Hc][K], in the workload dtype."""
+    g = _gen(seed, device)
+    dt = w.torch_dtype
+    K = w.T * w.d_in
+    return {
+        "w_down_k_t": _randn((w.D, w.Hc, w.r_k, K), 1.0 / math.sqrt(K), dt, g, device),
+        "w_down_v_t": _randn((w.D, w.Hc, w.r_v, K), 1.0 / math.sqrt(K), dt, g, device),
+        "mu_k": _randn((w.D, w.Hc, K), math.sqrt(0.1), dt, g, device),
+        "mu_v": _randn((w.D, w.Hc, K), math.sqrt(0.1), dt, g, device),
+    }

@@ -42,7 +42,8 @@ EXPORTED = (
     "lla_decode_teacher_workspace_bytes", "lla_decode_attn_teacher", "lla_decode_teacher_supported",
     "lla_decode_teacher_num_splits", "lla_decode_paged_num_splits", "lla_reconstruct",
     "lla_encode_paged", "lla_decode_paged_workspace_bytes", "lla_decode_attn_paged",
-    "lla_decode_attn_noalloc", "lla_stream_ceiling",
+    "lla_decode_attn_noalloc", "lla_stream_ceiling", "lla_encode_fused_acc_bytes",
+    "lla_encode_fused",
 )
 
 # bytes of the fixed split-partial array lla_decode_attn_noalloc uses (include/lla.h)
@@ -72,6 +73,10 @@ class lla_codec(ctypes.Structure):
 
 class lla_cache(ctypes.Structure):
     _fields_ = [("c_k", ctypes.c_void_p), ("c_v", ctypes.c_void_p)]
+
+
+class lla_proj(ctypes.Structure):
+    _fields_ = [("w_k", ctypes.c_void_p), ("w_v", ctypes.c_void_p), ("d_model", ctypes.c_int32)]
 
 
 class lla_pages(ctypes.Structure):
@@ -109,6 +114,11 @@ def load() -> ctypes.CDLL:
     lib.lla_rope_table_build.restype = i32
     lib.lla_encode.argtypes = [P(lla_dims), P(lla_codec), P(lla_cache), i32, vp, vp, i32, i32, vp]
     lib.lla_encode.restype = i32
+    lib.lla_encode_fused_acc_bytes.argtypes = [P(lla_dims), i32]
+    lib.lla_encode_fused_acc_bytes.restype = sz
+    lib.lla_encode_fused.argtypes = [P(lla_dims), P(lla_codec), P(lla_proj), P(lla_cache), i32, i32,
+                                     vp, i32, i32, vp, sz, vp]
+    lib.lla_encode_fused.restype = i32
     lib.lla_decode_workspace_bytes.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
     lib.lla_decode_workspace_bytes.restype = sz
     lib.lla_decode_num_splits.argtypes = [P(lla_dims), i32, i32, P(lla_decode_opts)]
@@ -230,6 +240,28 @@ def lla_encode(dims: lla_dims, codec: lla_codec, cache: lla_cache, layer: int, x
     _check("lla_encode", load().lla_encode(ctypes.byref(dims), ctypes.byref(codec),
                                            ctypes.byref(cache), layer, _ptr(x_k), _ptr(x_v),
                                            pos_start, n_new, _stream(stream)))
+
+
+def make_proj(w_k, w_v, d_model: int) -> lla_proj:
+    return lla_proj(_ptr(w_k), _ptr(w_v), d_model)
+
+
+def lla_encode_fused_acc_bytes(dims: lla_dims, n_new: int) -> int:
+    return load().lla_encode_fused_acc_bytes(ctypes.byref(dims), n_new)
+
+
+def lla_encode_fused(dims, codec, proj, cache, layer, loop, h, pos_start, n_new, acc, acc_bytes,
+                     stream=None) -> None:
+    _check("lla_encode_fused", lla_encode_fused_status(dims, codec, proj, cache, layer, loop, h,
+                                                       pos_start, n_new, acc, acc_bytes,
+                                                       _stream(stream)))
+
+
+def lla_encode_fused_status(dims, codec, proj, cache, layer, loop, h, pos_start, n_new, acc,
+                            acc_bytes, stream=0) -> int:
+    return load().lla_encode_fused(ctypes.byref(dims), ctypes.byref(codec), ctypes.byref(proj),
+                                   ctypes.byref(cache), layer, loop, _ptr(h), pos_start, n_new,
+                                   _ptr(acc), acc_bytes, stream)
 
 
 def lla_decode_workspace_bytes(dims: lla_dims, n_ctx: int, loop_count: int, opts=None) -> int:

@@ -209,6 +209,55 @@ def test_encode_rejects_bad_arguments(over, expect):
     assert st == expect
 
 
+def _fused_args(**over):
+    dims = lla.make_dims(4, 2, 16, 128, 96, 160, 2, 256)
+    a = dict(dims=dims, codec=lla.make_codec(FAKE, FAKE, None, FAKE, FAKE, None, None),
+             proj=lla.make_proj(FAKE, FAKE, 2048), cache=lla.make_cache(FAKE, FAKE), layer=1,
+             loop=3, h=FAKE, pos_start=8, n_new=100, acc=FAKE,
+             acc_bytes=2 * 100 * 16 * (96 + 160) * 4)
+    a.update(over)
+    return a
+
+
+def _fused_call(a):
+    return lla.lla_encode_fused_status(a["dims"], a["codec"], a["proj"], a["cache"], a["layer"],
+                                       a["loop"], a["h"], a["pos_start"], a["n_new"], a["acc"],
+                                       a["acc_bytes"], 0)
+
+
+def test_fused_acc_bytes():
+    dims = lla.make_dims(4, 2, 16, 128, 96, 160, 2, 256)
+    assert lla.lla_encode_fused_acc_bytes(dims, 100) == 2 * 100 * 16 * 256 * 4
+    assert lla.lla_encode_fused_acc_bytes(dims, 1) == (2 * 16 * 256 * 4 + 255) // 256 * 256
+    d2 = lla.make_dims(4, 2, 16, 128, 96, 160, 1, 256, variant=lla.LLA_2D)
+    assert lla.lla_encode_fused_acc_bytes(d2, 3) == 3072
+    assert lla.lla_encode_fused_acc_bytes(dims, -1) == 0
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("over,expect", [
+    (dict(loop=4), lla.LLA_ERR_INVALID_ARG),
+    (dict(loop=-1), lla.LLA_ERR_INVALID_ARG),
+    (dict(layer=2), lla.LLA_ERR_INVALID_ARG),
+    (dict(pos_start=200, n_new=57), lla.LLA_ERR_INVALID_ARG),
+    (dict(n_new=-1), lla.LLA_ERR_INVALID_ARG),
+    (dict(h=None), lla.LLA_ERR_INVALID_ARG),
+    (dict(acc=FAKE + 4), lla.LLA_ERR_INVALID_ARG),
+    (dict(proj=lla.make_proj(FAKE, None, 2048)), lla.LLA_ERR_INVALID_ARG),
+    (dict(proj=lla.make_proj(FAKE, FAKE, 2040)), lla.LLA_ERR_INVALID_ARG),
+    (dict(proj=lla.make_proj(FAKE, FAKE, 0)), lla.LLA_ERR_INVALID_ARG),
+    (dict(codec=lla.make_codec(FAKE, None, None, FAKE, FAKE, None, None)), lla.LLA_ERR_INVALID_ARG),
+    (dict(acc_bytes=2 * 100 * 16 * 256 * 4 - 1), lla.LLA_ERR_WORKSPACE),
+    (dict(dims=lla.make_dims(4, 2, 16, 64, 96, 160, 2, 256)), lla.LLA_ERR_UNSUPPORTED),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 48, 160, 2, 256)), lla.LLA_ERR_UNSUPPORTED),
+    (dict(dims=lla.make_dims(4, 2, 16, 128, 96, 160, 2, 256, dtype=lla.LLA_F32)),
+     lla.LLA_ERR_UNSUPPORTED),
+    (dict(n_new=0, acc_bytes=0), lla.LLA_OK),
+])
+def test_fused_encode_rejects_bad_arguments(over, expect):
+    assert _fused_call(_fused_args(**over)) == expect
+
+
 @needs_no_gpu
 def test_encode_zero_tokens_enqueues_nothing():
     st = lla.lla_encode_status(lla.make_dims(4, 2, 16, 128, 16, 32, 4, 256),
