@@ -42,6 +42,7 @@ KERNEL_SOURCES = {
                                  "decode_reconstruct.hip", "combine.hip", "rope_table.hip"),
     "absorbed": _COMMON_SOURCES + ("decode_absorbed.hip", "decode_stream.h", "combine.hip"),
     "encode": _COMMON_SOURCES + ("encode.hip",),
+    "encode_fused": _COMMON_SOURCES + ("encode_fused.hip",),
     "teacher": _COMMON_SOURCES + ("decode_teacher.hip", "decode_stream.h", "combine.hip"),
     "reconstruct": _COMMON_SOURCES + ("reconstruct.hip", "lla_recon_args.h"),
     "paged": _COMMON_SOURCES + ("decode_rotary_fold.hip", "decode_fold_wide.hip", "decode_lla2d.hip",
@@ -102,6 +103,9 @@ def parse():
     p.add_argument("--cpu-sample-seqs", type=int, default=1)
     p.add_argument("--cpu-sample-tokens", type=int, default=16384,
                    help="prompt tokens of the oracle's sample for the streamed-prefill workload")
+    p.add_argument("--prefill-encode", default="fused", choices=["fused", "captures"],
+                   help="streamed-prefill workload: pass 1 through the projection-fused encode "
+                        "(loop by loop, no per-loop K/V stored) or lla_encode of stored captures")
     p.add_argument("--ceiling-gib", type=float, default=0.0,
                    help="time plain streaming passes over buffers of this size (read-only, "
                         "copy, 4:1 and 1:4 read:write) and print their HBM rates instead")
@@ -236,6 +240,19 @@ def algorithmic(w, kind: str, L: int = 1, n_new: int = 0):
     encode: x_k and x_v read once, latents written once, W_down and mu read once;
             flops 2 T d_in (r_k + r_v) per (token, latent head)."""
     es = 2 if w.dtype == "bf16" else 4
+    if kind == "encode_fused":
+        # one (loop, layer) call, averaged over the T loops of a layer: the hidden states
+        # and both projections read once, the loop's W_down rows and mu slice, the float32
+        # accumulator written by loop 0, read and written by the middle loops and read by
+        # the last, which writes the latents; flops of both projections and the loop's
+        # share of Eq. 2, 2 d_in (r_k + r_v) per (token, latent head)
+        tok = w.batch * n_new
+        ent = tok * w.Hc * (w.r_k + w.r_v)
+        nbytes = (tok * w.d_model * es + 2 * w.d_model * w.H * w.d * es
+                  + w.Hc * (w.r_k + w.r_v) * w.d_in * es + 2 * w.Hc * w.d_in * es
+                  + (ent * 8 * (w.T - 1) + ent * es) / w.T)
+        flops = 2.0 * tok * w.d_model * w.H * w.d * 2 + 2.0 * tok * w.Hc * w.d_in * (w.r_k + w.r_v)
+        return nbytes, flops
     if kind == "reconstruct":
         # every latent of the range read once, L loops of keys and values written once,
         # W_up and mu slices; flops of rebuilding both axes on the matrix cores
@@ -300,6 +317,170 @@ def cpu_baseline_prefill(w, tokens: int):
                       f"K/V rebuilt for all {w.T} loops), fp64 NumPy, {dt:.1f} s, scaled by "
                       f"{scale:g} to the {w.n}-token prompt and {w.D} layers; host "
                       f"os.cpu_count()={os.cpu_count()}"}
+
+
+def cpu_baseline_prefill_fused(w, tokens: int):
+    """The fp64 oracle's projection-fused encode (all T loops, both axes) and materialised
+    reconstruction of `tokens` prompt tokens of one layer, scaled to the whole prompt and
+    all D layers."""
+    import numpy as np
+    from oracle import lla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    rng = np.random.default_rng(12345)
+    K = w.T * w.d_in
+    variant = "per_head" if w.variant == "per_head" else "2d"
+    h = rng.standard_normal((w.T, tokens, w.d_model))
+    wp = [rng.standard_normal((w.d_model, w.H * w.d)) / math.sqrt(w.d_model) for _ in range(2)]
+    wd = [rng.standard_normal((w.Hc, K, r)) / math.sqrt(K) for r in (w.r_k, w.r_v)]
+    mu = [rng.standard_normal((w.Hc, K)) * math.sqrt(0.1) for _ in range(2)]
+    wu = [rng.standard_normal((w.T, w.H, w.d, r)) / math.sqrt(r) for r in (w.r_k, w.r_v)]
+    t0 = time.perf_counter()
+    c = [np.transpose(O.encode_fused(h, wp[a], mu[a], wd[a], w.H, w.d, variant), (1, 0, 2))[None]
+         for a in range(2)]
+    O.reconstruct_cache(c[0], c[1], wu[0], mu[0], wu[1], mu[1], 0, w.T, 0, tokens, w.rope_base,
+                        variant)
+    dt = time.perf_counter() - t0
+    scale = (w.batch * w.n / tokens) * w.D
+    return {"value": w.batch * w.n / (dt * scale), "unit": "prompt tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{tokens} prompt tokens x {w.H} heads x 1 layer (projection-fused encode of "
+                      f"both axes over {w.T} loops from hidden size {w.d_model}, then K/V rebuilt "
+                      f"for all {w.T} loops), fp64 NumPy, {dt:.1f} s, scaled by {scale:g} to the "
+                      f"{w.n}-token prompt and {w.D} layers; host os.cpu_count()={os.cpu_count()}"}
+
+
+def prefill_working_sets(w, n: int, acc_bytes_layer: int):
+    """GiB held by the prefill's cache-side buffers at pass 1's peak (when the last loop
+    starts): the latent cache, the pass-1 state, and one layer's rebuilt K/V of pass 2.
+    Pass 1 of a looped stack runs every layer at every loop, so a layer's per-loop K/V
+    captures (or its accumulator) live until the last loop reaches that layer."""
+    es = 2 if w.dtype == "bf16" else 4
+    lat = w.D * w.batch * w.Hc * n * (w.r_k + w.r_v) * es
+    kv = 2 * w.T * w.batch * w.H * n * w.d * es
+    cap = w.D * (w.T - 1) * 2 * w.batch * n * w.H * w.d  # elements of loops 0 .. T-2
+    acc = w.D * acc_bytes_layer
+    g = 2.0 ** 30
+    return {"latents": round(lat / g, 2), "rebuilt_kv_one_layer": round(kv / g, 2),
+            "pass1_fused_accumulators": round(acc / g, 2),
+            "pass1_captures_bf16": round(cap * 2 / g, 2),
+            "pass1_captures_f32": round(cap * 4 / g, 2),
+            "fused_total": round((lat + acc + kv) / g, 2),
+            "captures_bf16_total": round((lat + cap * 2 + kv) / g, 2),
+            "one_shot_f32_total": round((lat + w.D * w.T * 2 * w.batch * n * w.H * w.d * 4
+                                         + w.D * kv) / g, 2)}
+
+
+def main_stream_prefill_fused(args, w):
+    """One step = the two-pass prefill of a prompt with the projection-fused encode.
+    Pass 1 runs the looped stack loop by loop: at loop t, every layer's key and value
+    projections of that loop's hidden states go through lla_encode_fused, which adds the
+    loop's share of Eq. 2 to the layer's float32 accumulator (no per-loop K/V is stored);
+    loop T-1 writes the latents. Pass 2, layer by layer, rebuilds the layer's K/V for all
+    loops with lla_reconstruct (its buffer is reused). One seeded hidden-state buffer
+    stands in for every (loop, layer) input."""
+    import torch
+    from latent_decode_attention_lla_amd import lla
+    from latent_decode_attention_lla_amd.harness import DeviceLatentStore
+    from latent_decode_attention_lla_amd.inputs import fused_encode_inputs, gaussian_encode_codec
+    dev = torch.device("cuda:0")
+    n = w.n
+    st = DeviceLatentStore(w, seed=3, device=dev, with_q=False)
+    ct = gaussian_encode_codec(w, seed=4, device=dev)
+    st.t.update(ct)
+    st.codec = lla.make_codec(ct["w_down_k_t"], ct["mu_k"], st.t["w_up_k"], ct["w_down_v_t"],
+                              ct["mu_v"], st.t["w_up_v"], st.rope)
+    h, w_k, w_v = fused_encode_inputs(w.replace(T=1), n, w.d_model, seed=5, device=dev)
+    h = h[0, 0]
+    proj = lla.make_proj(w_k, w_v, w.d_model)
+    acc_bytes = lla.lla_encode_fused_acc_bytes(st.dims, n)
+    ws = prefill_working_sets(w, n, acc_bytes)
+    print(f"[bench] allocating {w.name}: latents {ws['latents']} GiB, accumulators "
+          f"{ws['pass1_fused_accumulators']} GiB", file=sys.stderr, flush=True)
+    acc = torch.empty(w.D, acc_bytes // 4, dtype=torch.float32, device=dev)
+    kv = [torch.empty(w.T, w.batch, w.H, n, w.d, dtype=w.torch_dtype, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    steps = max(args.steps, 1)
+    ev = {"encode_fused": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                           for _ in range(w.T * w.D * steps)],
+          "reconstruct": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                          for _ in range(w.D * steps)]}
+
+    def step(record):
+        for t in range(w.T):
+            for layer in range(w.D):
+                e = None if record is None else ev["encode_fused"][(record * w.T + t) * w.D + layer]
+                if e is not None:
+                    e[0].record(stream)
+                lla.lla_encode_fused(st.dims, st.codec, proj, st.cache, layer, t, h, 0, n, acc[layer],
+                                     acc_bytes, sp)
+                if e is not None:
+                    e[1].record(stream)
+        for layer in range(w.D):
+            e = None if record is None else ev["reconstruct"][record * w.D + layer]
+            if e is not None:
+                e[0].record(stream)
+            lla.lla_reconstruct(st.dims, st.codec, st.cache, layer, 0, w.T, 0, n, kv[0], kv[1], sp)
+            if e is not None:
+                e[1].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s_ in range(args.steps):
+        step(s_)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    calls = {}
+    counts = {"encode_fused": w.T * w.D, "reconstruct": w.D}
+    for kind in ("encode_fused", "reconstruct"):
+        xs = sorted(a.elapsed_time(b) for a, b in ev[kind][:counts[kind] * args.steps])
+        ms = sum(xs) / len(xs)
+        nb, fl = (algorithmic(w, "encode_fused", n_new=n) if kind == "encode_fused"
+                  else algorithmic(w, "reconstruct", L=w.T, n_new=n))
+        calls[kind] = {"avg_ms": round(ms, 5), "median_ms": round(xs[len(xs) // 2], 5),
+                       "per_step": counts[kind], "algorithmic_bytes": nb, "algorithmic_flops": fl,
+                       "roofline": roofline(nb, fl, ms, measured_traffic(kind, w.name, "auto"),
+                                            measured_counters(kind, w.name, "auto"))}
+    dominant = max(calls, key=lambda k: calls[k]["avg_ms"] * calls[k]["per_step"])
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill_fused(w, args.cpu_sample_tokens)
+    res = {
+        "metric": "LLA two-pass prefill with the projection-fused encode, prompt tokens/s (pass 1: "
+                  "per loop and layer, K/V projections fused with the latent accumulation; pass 2: "
+                  "per layer, K/V rebuilt for all loops), 1 GPU",
+        "value": round(w.batch * n / (ms_step * 1e-3), 1),
+        "unit": "prompt tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian hidden states, projections and codec maps; no model "
+                "weights)",
+        "config": {"workload": w.name, "T": w.T, "D": w.D, "H": w.H, "d_head": w.d, "r_k": w.r_k,
+                   "r_v": w.r_v, "variant": w.variant, "batch": w.batch, "prompt": n,
+                   "d_model": w.d_model, "prefill_encode": "fused",
+                   "step": f"{w.T} loops x {w.D} layers of lla_encode_fused ({n} tokens), then "
+                           f"{w.D} x lla_reconstruct of {w.T} loops",
+                   "working_set_gib": ws,
+                   "device_peak_allocated_gib": round(torch.cuda.max_memory_allocated(dev) / 2**30, 2)},
+        "roofline": calls[dominant]["roofline"],
+        "roofline_kernel": "lla_" + dominant,
+        "cpu_baseline": cpu,
+        "encode_fused_call": calls["encode_fused"],
+        "reconstruct_call": calls["reconstruct"],
+        "wall_s_timed": round(wall, 3),
+        "kernel_source_hash": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
+    }
+    print(json.dumps(res))
 
 
 def main_stream_prefill(args, w):
@@ -371,10 +552,9 @@ def main_stream_prefill(args, w):
                                             measured_counters(kind, w.name, "auto"))}
     dominant = max(calls, key=lambda k: calls[k]["avg_ms"])
     cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_sample_tokens)
-    peak_gib = (w.D * w.batch * w.Hc * n * (w.r_k + w.r_v) * es
-                + 2 * w.batch * n * w.Hc * K * es + 2 * w.T * w.batch * w.H * n * w.d * es) / 2**30
-    one_shot_gib = (w.D * w.batch * w.Hc * n * (w.r_k + w.r_v) * es
-                    + w.D * (2 * w.batch * n * w.Hc * K * 4 + 2 * w.T * w.batch * w.H * n * w.d * es)) / 2**30
+    # a looped stack's pass 1 would hold every layer's captures of loops 0 .. T-2; this
+    # bench reuses one layer's capture buffer, so it times the encode, not that peak
+    ws = prefill_working_sets(w, n, lla.lla_encode_fused_acc_bytes(st.dims, n))
     res = {
         "metric": "LLA streamed two-pass prefill, prompt tokens/s (per layer in turn: encode of "
                   "the prompt's per-loop K/V, then K/V rebuilt for all loops), 1 GPU; HBM GB/s of "
@@ -386,9 +566,10 @@ def main_stream_prefill(args, w):
         "data": "synthetic (seeded Gaussian per-loop K/V and codec maps; no model weights)",
         "config": {"workload": w.name, "T": w.T, "D": w.D, "H": w.H, "d_head": w.d, "r_k": w.r_k,
                    "r_v": w.r_v, "variant": w.variant, "batch": w.batch, "prompt": n,
+                   "prefill_encode": "captures",
                    "step": f"{w.D} x (lla_encode of {n} tokens, lla_reconstruct of {w.T} loops)",
-                   "device_working_set_gib": round(peak_gib, 1),
-                   "one_shot_working_set_gib": round(one_shot_gib, 1)},
+                   "working_set_gib": ws,
+                   "device_peak_allocated_gib": round(torch.cuda.max_memory_allocated(dev) / 2**30, 2)},
         "roofline": calls[dominant]["roofline"],
         "roofline_kernel": "lla_" + dominant,
         "cpu_baseline": cpu,
@@ -478,6 +659,9 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.stream_prefill and args.prefill_encode == "fused":
+        main_stream_prefill_fused(args, w)
+        return
     if w.stream_prefill:
         main_stream_prefill(args, w)
         return

@@ -278,9 +278,10 @@ int32_t lla_encode_paged(const lla_dims* dims, const lla_codec* codec, const lla
  * of `layer` for keys and values: it forms x_t for the n_new new tokens of every
  * sequence, subtracts mu_t and adds the term to `acc`; the call for loop T - 1 rounds the
  * sum once (to nearest even) and writes cache rows pos_start .. pos_start + n_new - 1.
- *   proj->w_k, proj->w_v : device bfloat16 [D][d_model][H * d_head], the key and value
- *            projections of every layer (head h owns columns h d_head .. h d_head +
- *            d_head - 1); proj->d_model a positive multiple of 32.
+ *   proj->w_k, proj->w_v : device bfloat16 [D][H * d_head][d_model], the key and value
+ *            projections of every layer stored as a linear layer stores its weight
+ *            (output features x input features): x_t[h d_head + j] = h_t . row
+ *            (h d_head + j); proj->d_model a positive multiple of 32.
  *   h      : device bfloat16 [batch][n_new][d_model], the hidden states that enter the
  *            projections at this loop.
  *   acc    : device float32, acc_bytes >= lla_encode_fused_acc_bytes(dims, n_new): the

@@ -2,23 +2,27 @@
 // a looped layer's key (value) projection runs, one loop at a time, so a prompt's per-loop
 // keys and values are never stored ("Looped Latent Attention", Appendix J, "Eviction and
 // long-context prefill"; Section 3, Eqs. 1-2). Eq. 2 is linear in the stacked vector:
-//   c = sum_t x_t W_down[block t] - mu W_down,   x_t = h_t W_proj,
+//   c = sum_t (x_t - mu_t) W_down[block t],   x_t = h_t W_proj,
 // with block t the rows of loop t (t d_in .. t d_in + d_in - 1; within it, head h's keys at
 // h d for LLA-2D). Each call handles loop t of one layer: x_t = h_t W_proj on the matrix
-// cores (bfloat16 inputs, float32 accumulation), then, without leaving registers,
-// x_t W_down[block t] is added to a float32 accumulator the caller keeps between the
-// loops; the call of the last loop subtracts mu W_down, rounds once to the cache dtype and
-// writes the cache rows.
+// cores (bfloat16 inputs, float32 accumulation), then, without leaving registers, mu_t is
+// subtracted and (x_t - mu_t) W_down[block t] is added to a float32 accumulator the caller
+// keeps between the loops; the call of the last loop rounds the sum once to the cache
+// dtype and writes the cache rows.
 //
-// Workgroup: 4 waves and 128 tokens (32 per wave) of one latent head (per-head codec) or of
-// all heads (LLA-2D, whose latent row is shared by the heads). For each head it covers,
-// the workgroup computes X^T = W_proj[:, head]^T h^T (128 columns x 128 tokens, K = d_model)
-// with W and h staged through a 3-stage direct-to-LDS ring, 32 values of K per stage; the
-// W^T operand comes from transposing LDS reads (W rows are XOR-swizzled in 16-byte slots
-// so the reads avoid bank conflicts). A wave's result lanes hold 4 consecutive columns of
-// one token, which is the A operand of the second product with a permuted K order: x
-// (split into bfloat16 hi and lo parts, so x enters with about 16 significant bits) times
-// W_down[block t] from W_down^T's rows in the same order.
+// Workgroup: 4 waves and TPW tokens per wave (64 per head, 32 for LLA-2D, whose latent is
+// shared by all heads and is kept in registers while the workgroup runs through them). For
+// each head it covers, the workgroup computes X^T = W_proj[head]^T h^T (128 columns x
+// 4 TPW tokens, K = d_model) with W_proj^T (the weight as a linear layer stores it, rows =
+// output columns) and h staged through a 3-stage direct-to-LDS ring, 32 values of K per
+// stage. Both operands are rows of 64 bytes read as 16-byte fragments; the 16-byte slots of
+// each row are XOR-swizzled by the row index so that 16 consecutive rows fall in distinct
+// banks. The projection's output columns are loaded in a permuted order: M row
+// 16 ct + 4 j + i of the product holds column 32 (ct / 2) + 8 j + 4 (ct % 2) + i, so the 8
+// values a lane holds for one token in tiles 2 s and 2 s + 1 are the consecutive columns
+// 32 s + 8 j .. + 7. That is the A operand of the second product with K in natural order;
+// its B operand (W_down^T rows) and mu_t then come as single 16-byte loads. x - mu enters
+// that product split into bfloat16 hi and lo parts (about 16 significant bits).
 //
 // Launch order: loops 0 .. T-1 of one layer on one stream, with the same accumulator.
 // Loop 0 writes it, later loops read and update it, and loop T-1 writes the cache.
@@ -30,11 +34,9 @@ namespace lla {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kD = 128;        // head width the fused kernel is built for
-constexpr int kTokWg = 128;    // tokens per workgroup
 constexpr int kKc = 32;        // K values per ring stage
 constexpr int kStages = 3;
 constexpr int kXcds = 8;
@@ -44,20 +46,34 @@ __device__ __forceinline__ f32x4 mfma_bf16_k32(const i16x8& a, const i16x8& b, f
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// 16-byte slot of column chunk c (8 columns) in W stage row r
-__device__ __forceinline__ int w_slot(int r, int c) { return c ^ (((r & 3) << 1) ^ (((r >> 3) & 1) << 3)); }
+// Physical 16-byte slot of logical slot `sl` (0..3) in LDS row `row`: distinct banks for
+// any 16 aligned consecutive rows read at one logical slot (whether the LDS serves 8 or 16
+// lanes of a 16-byte read per cycle).
+__device__ __forceinline__ int swz(int row, int sl) {
+  return sl ^ ((((row >> 2) & 1) << 1) | (((row >> 1) ^ (row >> 3)) & 1));
+}
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) { return f32_to_bf16_rne(f); }
+// Head column held by M row q of the projection tile (see the header comment).
+__device__ __forceinline__ int perm_col(int q) {
+  const int b = q >> 5, m = q & 31;
+  return 32 * b + 8 * ((m >> 2) & 3) + 4 * (m >> 4) + (m & 3);
+}
 
 template <int R, bool PER_HEAD>
-__global__ __launch_bounds__(256) void encode_fused_kernel(FusedArgs a) {
-  constexpr int NCT = kD / 16;   // column tiles of one head
-  constexpr int NLT = R / 16;    // latent tiles
-  constexpr int TT = 2;          // token tiles per wave
-  constexpr int W_UNITS = kKc * 16;            // [32 rows][16 slots] of 16 bytes
-  constexpr int H_UNITS = kTokWg * kKc * 2 / 16;  // [128 tokens][4 slots]
-  constexpr int STAGE = W_UNITS + H_UNITS;     // 16-byte units: 16 blocks of 1 KiB
-  static_assert(STAGE == 16 * 64, "4 DMA blocks per wave and stage");
+__global__ __launch_bounds__(256, PER_HEAD ? 2 : 1) void encode_fused_kernel(FusedArgs a) {
+  constexpr int TPW = PER_HEAD ? 64 : 32;   // tokens per wave
+  constexpr int TT = TPW / 16;              // token tiles per wave
+  constexpr int TOKWG = 4 * TPW;
+  constexpr int NCT = kD / 16;              // column tiles of one head
+  constexpr int NLT = R / 16;               // latent tiles
+  constexpr int NS2 = kD / 32;              // K chunks of the second product
+  constexpr int W_UNITS = kD * 4;           // [128 rows][4 slots] of 16 bytes
+  constexpr int H_UNITS = TOKWG * 4;        // [TOKWG rows][4 slots]
+  constexpr int STAGE = W_UNITS + H_UNITS;
+  constexpr int NBLK = STAGE / 64;          // 1 KiB DMA blocks per stage
+  constexpr int BPW = NBLK / 4;             // blocks per wave
+  static_assert(NBLK % 4 == 0, "whole blocks per wave");
+  static_assert(!PER_HEAD || 4 * NLT <= 2 * NBLK, "W_down fragments fit two stages");
   __shared__ u32x4 lds[kStages * STAGE];
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -70,33 +86,36 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(FusedArgs a) {
   const int xcd = L % kXcds, slot = L / kXcds;
   const int tb = xcd + kXcds * (slot / heads_y);
   const int hc = slot % heads_y;
-  const int ntb = (a.Ntok + kTokWg - 1) / kTokWg;
+  const int ntb = (a.Ntok + TOKWG - 1) / TOKWG;
   if (tb >= ntb) return;  // padding workgroups of the last round
-  const int tok0 = tb * kTokWg;
-  const int ldw = a.H * kD;
+  const int tok0 = tb * TOKWG;
   const int nk = a.d_model / kKc;
   const int h_begin = PER_HEAD ? hc : 0;
   const int nh = PER_HEAD ? 1 : a.H;
   const int nsteps = nh * nk;
+  const int K = a.T * a.d_in;
 
   const char* hbase = static_cast<const char*>(a.h);
   const char* wbase = static_cast<const char*>(a.w_proj);
-  // DMA slots: wave w loads blocks 4 w .. 4 w + 3 of a stage; blocks 0-7 hold W rows
-  // 4 i .. 4 i + 3 (a lane: one 16-byte slot of one row), blocks 8-15 the h rows of tokens
-  // 16 (i - 8) .. + 15 (a lane: 16 bytes of one token's 32 K values)
-  uint32_t dofs[4];
-  int dkind[4];
+  // DMA slots: wave w loads blocks BPW w .. BPW w + BPW - 1 of a stage. A block's lane l
+  // writes LDS unit 64 blk + l = (row, physical slot l % 4) and fetches the logical slot
+  // that lands there. Blocks 0-7 are W_proj^T rows (M row q from head column perm_col(q));
+  // the rest are h rows of the workgroup's tokens (rows past the end repeat the last).
+  uint32_t dofs[BPW];
+  bool dw[BPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int blk = 4 * wave + j;
-    if (blk < 8) {
-      const int r = 4 * blk + lane / 16, sl = lane % 16;
-      dkind[j] = 0;
-      dofs[j] = static_cast<uint32_t>((r * ldw + 8 * w_slot(r, sl)) * 2);  // w_slot is an involution
+  for (int j = 0; j < BPW; ++j) {
+    const int blk = BPW * wave + j;
+    const int u = 64 * blk + lane;
+    if (blk < W_UNITS / 64) {
+      const int q = u >> 2, sl = swz(q, u & 3);  // swz is an involution in sl
+      dw[j] = true;
+      dofs[j] = static_cast<uint32_t>((perm_col(q) * a.d_model + 8 * sl) * 2);
     } else {
-      const int tok = min(tok0 + 16 * (blk - 8) + lane / 4, a.Ntok - 1);  // past the end: last row
-      dkind[j] = 1;
-      dofs[j] = static_cast<uint32_t>(static_cast<size_t>(tok - tok0) * a.d_model * 2 + (lane % 4) * 16);
+      const int t = (u - W_UNITS) >> 2, sl = swz(t, u & 3);
+      const int tok = min(tok0 + t, a.Ntok - 1);
+      dw[j] = false;
+      dofs[j] = static_cast<uint32_t>((static_cast<size_t>(tok - tok0) * a.d_model + 8 * sl) * 2);
     }
   }
   auto dma = [&](const char* src, u32x4* dst) {
@@ -107,28 +126,136 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(FusedArgs a) {
   auto issue = [&](int s) {
     const int hh = h_begin + s / nk, kc = s % nk;
     u32x4* stage = lds + (s % kStages) * STAGE;
-    const char* wsrc = wbase + (static_cast<size_t>(kc) * kKc * ldw + hh * kD) * 2;
+    const char* wsrc = wbase + (static_cast<size_t>(hh) * kD * a.d_model + kc * kKc) * 2;
     const char* hsrc = hbase + (static_cast<size_t>(tok0) * a.d_model + kc * kKc) * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma((dkind[j] == 0 ? wsrc : hsrc) + dofs[j], stage + (4 * wave + j) * 64);
+    for (int j = 0; j < BPW; ++j) dma((dw[j] ? wsrc : hsrc) + dofs[j], stage + (BPW * wave + j) * 64);
   };
 
-  f32x4 lat[TT][NLT];
+  // per-lane LDS units of the fragments (stage-relative)
+  int aunit[NCT], bunit[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt)
+  for (int ct = 0; ct < NCT; ++ct) aunit[ct] = (16 * ct + lo) * 4 + swz(16 * ct + lo, hi);
 #pragma unroll
-    for (int lt = 0; lt < NLT; ++lt) lat[tt][lt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t = TPW * wave + 16 * tt + lo;
+    bunit[tt] = W_UNITS + t * 4 + swz(t, hi);
+  }
+
+  f32x4 lat[PER_HEAD ? 1 : TT][PER_HEAD ? 1 : NLT];
+  if constexpr (!PER_HEAD) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int lt = 0; lt < NLT; ++lt) lat[tt][lt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   f32x4 x[NCT][TT];
+  const bool first = a.loop == 0, last = a.loop == a.T - 1;
+  uint16_t* cache = static_cast<uint16_t*>(a.c);
+
+  // Second product for head h_begin + hi_: x[2 s2 + g][tt] lane (lo, hi) element i is
+  // token 16 tt + lo of the wave and head column 32 s2 + 8 hi + 4 g + i.
+  auto second = [&](int hi_) {
+    const int hh = h_begin + hi_;
+
+    const size_t kbase = static_cast<size_t>(a.loop) * a.d_in + (PER_HEAD ? 0 : hh * kD);
+    const uint16_t* wdg = static_cast<const uint16_t*>(a.w_down_t) + static_cast<size_t>(hc) * R * K +
+                          kbase + 8 * hi;
+    const uint16_t* mut = static_cast<const uint16_t*>(a.mu) + static_cast<size_t>(hc) * K + kbase + 8 * hi;
+    if constexpr (PER_HEAD) {  // the W_down fragments have landed for every wave
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      i16x8 fh[NS2], fl[NS2];
+#pragma unroll
+      for (int s2 = 0; s2 < NS2; ++s2) {
+        const i16x8 mu8 = __builtin_bit_cast(i16x8, *reinterpret_cast<const u32x4*>(mut + 32 * s2));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = x[2 * s2 + e / 4][tt][e % 4] - bf16_to_f32(static_cast<uint16_t>(mu8[e]));
+          const uint16_t vh = f32_to_bf16_rne(v);
+          fh[s2][e] = static_cast<short>(vh);
+          fl[s2][e] = static_cast<short>(f32_to_bf16_rne(v - bf16_to_f32(vh)));
+        }
+      }
+#pragma unroll(PER_HEAD ? 2 : NLT)
+      for (int lt = 0; lt < NLT; ++lt) {
+        i16x8 bw[NS2];
+#pragma unroll
+        for (int s2 = 0; s2 < NS2; ++s2) {
+          if constexpr (PER_HEAD) {
+            const int fb = 4 * lt + s2;
+            const u32x4* src = fb < NBLK ? lds + (nsteps % kStages) * STAGE + 64 * fb
+                                         : lds + ((nsteps + 1) % kStages) * STAGE + 64 * (fb - NBLK);
+            bw[s2] = __builtin_bit_cast(i16x8, src[lane]);
+          } else {
+            bw[s2] = __builtin_bit_cast(
+                i16x8, *reinterpret_cast<const u32x4*>(wdg + static_cast<size_t>(16 * lt + lo) * K + 32 * s2));
+          }
+        }
+        f32x4 acc4;
+        if constexpr (PER_HEAD) acc4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        else acc4 = lat[tt][lt];
+#pragma unroll
+        for (int s2 = 0; s2 < NS2; ++s2) {
+          acc4 = mfma_bf16_k32(fh[s2], bw[s2], acc4);
+          acc4 = mfma_bf16_k32(fl[s2], bw[s2], acc4);
+        }
+        if constexpr (!PER_HEAD) {
+          lat[tt][lt] = acc4;
+        } else {
+          // acc4 lane (lo, hi): token 16 tt + 4 hi + i of the wave, entry 16 lt + lo
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = tok0 + TPW * wave + 16 * tt + 4 * hi + i;
+            if (tok >= a.Ntok) continue;
+            const int e = 16 * lt + lo;
+            float* arow = a.acc + (static_cast<size_t>(tok) * a.Hc + hc) * a.RT + a.ao;
+            float v = acc4[i];
+            if (!first) v += arow[e];
+            if (last) {
+              const int b = tok / a.n_new, jj = tok - b * a.n_new;
+              cache[((static_cast<size_t>(b) * a.Hc + hc) * a.n_max + a.pos_start + jj) * R + e] =
+                  f32_to_bf16_rne(v);
+            } else {
+              arow[e] = v;
+            }
+          }
+        }
+      }
+    }
+  };
 
   issue(0);
   if (nsteps > 1) issue(1);
   for (int s = 0; s < nsteps; ++s) {
-    if (s + 1 < nsteps) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (s + 1 < nsteps) {
+      if constexpr (BPW == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     asm volatile("s_barrier" ::: "memory");
     if (s + 2 < nsteps) issue(s + 2);
     const int kc = s % nk;
+    if constexpr (PER_HEAD) {
+      // Last step: the head's W_down rows of this loop go, in fragment order, into the two
+      // stages no step reads any more (fragment block fb = 4 lt + s2, lane (lo, hi) holds
+      // W_down^T[16 lt + lo][kbase + 32 s2 + 8 hi .. + 7]).
+      if (s == nsteps - 1) {
+        const uint16_t* wd = static_cast<const uint16_t*>(a.w_down_t) +
+                             (static_cast<size_t>(hc) * R + lo) * K + static_cast<size_t>(a.loop) * a.d_in + 8 * hi;
+#pragma unroll
+        for (int j = 0; j < NLT; ++j) {
+          const int fb = 4 * j + wave;  // lt = j, s2 = wave
+          u32x4* dst = fb < NBLK ? lds + (nsteps % kStages) * STAGE + 64 * fb
+                                 : lds + ((nsteps + 1) % kStages) * STAGE + 64 * (fb - NBLK);
+          dma(reinterpret_cast<const char*>(wd + static_cast<size_t>(16 * j) * K + 32 * wave), dst);
+        }
+      }
+    }
     if (kc == 0) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
@@ -136,94 +263,40 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(FusedArgs a) {
         for (int tt = 0; tt < TT; ++tt) x[ct][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const u32x4* stage = lds + (s % kStages) * STAGE;
-    const char* wst = reinterpret_cast<const char*>(stage);
-    const u32x4* hst = stage + W_UNITS;
-    // B operands: h^T of this wave's two token tiles (token 16 tt + lo, K 8 hi .. 8 hi + 7)
     i16x8 bfr[TT];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-      bfr[tt] = __builtin_bit_cast(i16x8, hst[(32 * wave + 16 * tt + lo) * 4 + hi]);
+    for (int tt = 0; tt < TT; ++tt) bfr[tt] = __builtin_bit_cast(i16x8, stage[bunit[tt]]);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      // A operand W^T of column tile ct: lane (hi, lo) holds W[8 hi + e][16 ct + lo], e = 0..7,
-      // from two transposing reads: lane (hi, 4 k + j) names W[8 hi + 4 half + k][16 ct + 4 j .. + 3]
-      i16x4 part[2];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int r = 8 * hi + 4 * half + (lo >> 2);
-        const int c = 2 * ct + ((lo & 3) >> 1);
-        const char* p = wst + r * 256 + w_slot(r, c) * 16 + (lo & 1) * 8;
-        part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-      }
-      const i16x8 afr = {part[0][0], part[0][1], part[0][2], part[0][3],
-                         part[1][0], part[1][1], part[1][2], part[1][3]};
+      const i16x8 afr = __builtin_bit_cast(i16x8, stage[aunit[ct]]);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) x[ct][tt] = mfma_bf16_k32(afr, bfr[tt], x[ct][tt]);
     }
-    if (kc == nk - 1) {
-      // x[ct][tt] lane (lo, hi): x_t[token 16 tt + lo][column 16 ct + 4 hi + i] of head hh.
-      // Second product with K = the head's 128 columns, 32 per step s2, in the order: lane
-      // group hi's element e is column 32 s2 + 4 hi + e (e < 4) or 32 s2 + 16 + 4 hi + e - 4.
-      const int hh = h_begin + s / nk;
-      const size_t kbase = static_cast<size_t>(a.loop) * a.d_in + (PER_HEAD ? 0 : hh * kD);
-      const uint16_t* wd = static_cast<const uint16_t*>(a.w_down_t) +
-                           static_cast<size_t>(hc) * R * (a.T * a.d_in) + kbase;
-      const uint16_t* mut = static_cast<const uint16_t*>(a.mu) +
-                            static_cast<size_t>(hc) * (a.T * a.d_in) + kbase + 4 * hi;
-#pragma unroll
-      for (int s2 = 0; s2 < kD / 32; ++s2) {
-        // mu_t of this lane's 8 columns (4 hi + e of tiles 2 s2 and 2 s2 + 1)
-        const u32x2 m0 = *reinterpret_cast<const u32x2*>(mut + 32 * s2);
-        const u32x2 m1 = *reinterpret_cast<const u32x2*>(mut + 32 * s2 + 16);
-        const u32x4 mm = {m0.x, m0.y, m1.x, m1.y};
-        const i16x8 mu8 = __builtin_bit_cast(i16x8, mm);
-        i16x8 ahi[TT], alo[TT];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = x[2 * s2 + e / 4][tt][e % 4] - bf16_to_f32(static_cast<uint16_t>(mu8[e]));
-            const uint16_t vh = bf16_rne(v);
-            ahi[tt][e] = static_cast<short>(vh);
-            alo[tt][e] = static_cast<short>(bf16_rne(v - bf16_to_f32(vh)));
-          }
-        }
-#pragma unroll
-        for (int lt = 0; lt < NLT; ++lt) {
-          const uint16_t* row = wd + static_cast<size_t>(16 * lt + lo) * (a.T * a.d_in) + 32 * s2 + 4 * hi;
-          const u32x2 b0 = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 b1 = *reinterpret_cast<const u32x2*>(row + 16);
-          const u32x4 bb = {b0.x, b0.y, b1.x, b1.y};
-          const i16x8 bfrag = __builtin_bit_cast(i16x8, bb);
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt) {
-            lat[tt][lt] = mfma_bf16_k32(ahi[tt], bfrag, lat[tt][lt]);
-            lat[tt][lt] = mfma_bf16_k32(alo[tt], bfrag, lat[tt][lt]);
-          }
-        }
-      }
+    if constexpr (!PER_HEAD) {
+      if (kc == nk - 1) second(s / nk);
     }
   }
+  if constexpr (PER_HEAD) second(0);
 
-  // lat[tt][lt] lane (lo, hi): the loop's term for token 32 w + 16 tt + 4 hi + i, entry 16 lt + lo
-  const bool first = a.loop == 0, last = a.loop == a.T - 1;
-  uint16_t* cache = static_cast<uint16_t*>(a.c);
+  if constexpr (!PER_HEAD) {
+    // lat[tt][lt] lane (lo, hi): token 16 tt + 4 hi + i of the wave, entry 16 lt + lo
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = tok0 + 32 * wave + 16 * tt + 4 * hi + i;
-      if (tok >= a.Ntok) continue;
-      float* arow = a.acc + (static_cast<size_t>(tok) * a.Hc + hc) * a.RT + a.ao;
-      const int b = tok / a.n_new, j = tok - b * a.n_new;
-      uint16_t* crow = cache + ((static_cast<size_t>(b) * a.Hc + hc) * a.n_max + a.pos_start + j) * R;
+      for (int i = 0; i < 4; ++i) {
+        const int tok = tok0 + TPW * wave + 16 * tt + 4 * hi + i;
+        if (tok >= a.Ntok) continue;
+        float* arow = a.acc + static_cast<size_t>(tok) * a.RT + a.ao;
+        const int b = tok / a.n_new, jj = tok - b * a.n_new;
+        uint16_t* crow = cache + (static_cast<size_t>(b) * a.n_max + a.pos_start + jj) * R;
 #pragma unroll
-      for (int lt = 0; lt < NLT; ++lt) {
-        const int e = 16 * lt + lo;
-        float v = lat[tt][lt][i];
-        if (!first) v += arow[e];
-        if (last) crow[e] = bf16_rne(v);
-        else arow[e] = v;
+        for (int lt = 0; lt < NLT; ++lt) {
+          const int e = 16 * lt + lo;
+          float v = lat[tt][lt][i];
+          if (!first) v += arow[e];
+          if (last) crow[e] = f32_to_bf16_rne(v);
+          else arow[e] = v;
+        }
       }
     }
   }
@@ -231,7 +304,8 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(FusedArgs a) {
 
 template <int R>
 void launch_axis(const FusedArgs& a, bool per_head, hipStream_t s) {
-  const int ntb = (a.Ntok + kTokWg - 1) / kTokWg;
+  const int tokwg = per_head ? 256 : 128;
+  const int ntb = (a.Ntok + tokwg - 1) / tokwg;
   const int heads_y = per_head ? a.Hc : 1;
   const long long rounds = (ntb + kXcds - 1) / kXcds;
   const unsigned blocks = static_cast<unsigned>(rounds * kXcds * heads_y);

@@ -37,7 +37,7 @@ struct EncodeArgs {
 // Projection-fused encode: loop `loop` of one layer and one axis (keys or values).
 struct FusedArgs {
   const void* h;        // [Ntok][d_model], Ntok = B * n_new: the loop's projection input
-  const void* w_proj;   // layer base, [d_model][H * d]
+  const void* w_proj;   // layer base, [H * d][d_model] (output features x input features)
   const void* w_down_t; // layer base, [Hc][r][T * d_in]
   const void* mu;       // layer base, [Hc][T * d_in]
   void* c;              // layer base, [B][Hc][n_max][r]

@@ -17,10 +17,11 @@ Table 5):
 * ``absorbed_4x``   the Ouro-1.4B 4x geometry, T=4, D=24, H=16, d=128, (96, 160), bf16,
                     decoupled decode with a 64-wide rotary branch (Appendix J, Table 14's
                     d_rope), batch 8, context 32768 (Table 13's shortest context)
-* ``prefill_64k``   the streamed two-pass prefill of one 65536-token prompt at the
-                    Ouro-1.4B 4x geometry (T=4, D=24, H=16, d=128, (96, 160), bf16): per
-                    layer, encode the prompt's per-loop K/V, then rebuild them for the
-                    second pass (Appendix J's 64k passkey cells; Table 12)
+* ``prefill_64k``   the two-pass prefill of one 65536-token prompt at the Ouro-1.4B 4x
+                    geometry (T=4, D=24, H=16, d=128, (96, 160), bf16, hidden size 2048):
+                    pass 1 encodes while the looped stack runs (the K/V projections fused
+                    with the latent accumulation, loop by loop), pass 2 rebuilds each
+                    layer's K/V for all loops (Appendix J's 64k passkey cells; Table 12)
 * ``paged_21x``     ``capacity_21x`` stored in a paged cache: 16-token pages of each
                     layer's pool in a random order, found through a block table
 * ``paged_ouro_4x`` the Ouro-1.4B 4x geometry (96, 160) for all 24 layers, 32 sequences at
@@ -76,6 +77,7 @@ class Workload:
     teacher: bool = False          # an uncompressed per-loop cache (no codec)
     stream_prefill: bool = False   # a step is the layer-by-layer two-pass prefill
     paged: bool = False            # latents in shuffled 16-token pages (a block table)
+    d_model: int = 0               # hidden size entering the K/V projections (fused encode)
 
     @property
     def Hc(self) -> int:
@@ -113,7 +115,7 @@ WORKLOADS = {
     "paged_absorbed_4x": Workload("paged_absorbed_4x", T=4, D=24, H=16, d=128, r_k=96,
                                   r_v=160, batch=8, n=32768, d_rope=64, paged=True),
     "prefill_64k": Workload("prefill_64k", T=4, D=24, H=16, d=128, r_k=96, r_v=160, batch=1,
-                            n=65536, stream_prefill=True),
+                            n=65536, stream_prefill=True, d_model=2048),
     "teacher_4k": Workload("teacher_4k", T=4, D=24, H=16, d=128, r_k=0, r_v=0, batch=32,
                            n=4096, teacher=True),
 }
@@ -262,15 +264,16 @@ def fused_encode_inputs(w: Workload, n_new: int, d_model: int, seed: int, device
                         batch: int | None = None):
     """Inputs of the projection-fused encode, in the workload dtype: the hidden states
     that enter a layer's key and value projections at each loop, h [T][B][n_new][d_model]
-    ~ N(0, 1), and the projections of every layer, w_k and w_v [D][d_model][H*d]
-    ~ N(0, 1/d_model) (so the per-loop keys and values h_t W have about unit variance,
-    like the per-loop K/V drawn by encode_x)."""
+    ~ N(0, 1), and the projections of every layer as linear-layer weights (output
+    features x input features), w_k and w_v [D][H*d][d_model] ~ N(0, 1/d_model) (so the
+    per-loop keys and values have about unit variance, like the per-loop K/V drawn by
+    encode_x)."""
     B = batch or w.batch
     g = _gen(seed, device)
     dt = w.torch_dtype
     h = _randn((w.T, B, n_new, d_model), 1.0, dt, g, device)
-    w_k = _randn((w.D, d_model, w.H * w.d), 1.0 / math.sqrt(d_model), dt, g, device)
-    w_v = _randn((w.D, d_model, w.H * w.d), 1.0 / math.sqrt(d_model), dt, g, device)
+    w_k = _randn((w.D, w.H * w.d, d_model), 1.0 / math.sqrt(d_model), dt, g, device)
+    w_v = _randn((w.D, w.H * w.d, d_model), 1.0 / math.sqrt(d_model), dt, g, device)
     return h, w_k, w_v
 
 

@@ -68,11 +68,13 @@ class Fused:
             self.call(layer, t, pos_start)
         torch.cuda.synchronize()
 
-    def oracle(self, layer: int, axis: str, b: int):
-        """(rounded latents [n_new][Hc][r], bound delta) of sequence b from the oracle."""
+    def oracle(self, layer: int, axis: str, b: int, toks=None):
+        """(rounded latents [n][Hc][r], bound delta) of sequence b's new tokens `toks` (all
+        when None) from the oracle."""
         w = self.w
-        hl = f64(self.h[:, b])  # [T][n_new][d_model]
-        wp = f64((self.w_k if axis == "k" else self.w_v)[layer])  # [d_model][H d]
+        hb = self.h[:, b] if toks is None else self.h[:, b][:, torch.as_tensor(toks, device=self.h.device)]
+        hl = f64(hb)  # [T][n][d_model]
+        wp = f64((self.w_k if axis == "k" else self.w_v)[layer]).T  # [d_model][H d]
         wd = f64(self.codec_t[f"w_down_{axis}_t"][layer]).transpose(0, 2, 1)  # [Hc][K][r]
         mu = f64(self.codec_t[f"mu_{axis}"][layer])
         variant = "per_head" if w.variant == "per_head" else "2d"
@@ -96,14 +98,16 @@ class Fused:
             delta[:, hc] = 1.01 * (term @ np.abs(wd[hc]))
         return O.round_bf16(c), delta
 
-    def check(self, layer: int, pos_start: int, seqs=None):
+    def check(self, layer: int, pos_start: int, seqs=None, toks=None):
         w = self.w
         worst = 0.0
         for axis, cache in (("k", self.c_k), ("v", self.c_v)):
             got_all = f64(cache[layer])  # [B][Hc][n_max][r]
             for b in (range(w.batch) if seqs is None else seqs):
-                ref, delta = self.oracle(layer, axis, b)
-                got = got_all[b][:, pos_start:pos_start + self.n_new].transpose(1, 0, 2)
+                ref, delta = self.oracle(layer, axis, b, toks)
+                rows = (np.arange(pos_start, pos_start + self.n_new) if toks is None
+                        else pos_start + np.asarray(toks))
+                got = got_all[b][:, rows].transpose(1, 0, 2)
                 err = np.abs(got - ref)
                 allowed = bf16_ulp(ref) + delta
                 bad = err > allowed * (1 + 1e-12)
@@ -111,6 +115,8 @@ class Fused:
                                        f"bf16 spacing + delta (max excess "
                                        f"{float(np.max(err - allowed)):.3e})")
                 worst = max(worst, float(np.max(err / bf16_ulp(ref))))
+                if toks is not None:
+                    continue
                 rest = np.concatenate([got_all[b][:, :pos_start], got_all[b][:, pos_start + self.n_new:]],
                                       axis=1)
                 assert np.all(rest == SENTINEL), f"{axis} seq {b}: rows outside the range written"
@@ -181,3 +187,20 @@ def test_fused_encode_accumulator_reuse_and_zero_tokens():
     lla.lla_encode_fused(f.dims, f.codec, f.proj, f.cache, 1, 0, f.h[0], 0, 0, f.acc, 0)
     torch.cuda.synchronize()
     assert bool((f.c_k[1] == SENTINEL).all())
+
+
+def test_fused_encode_prefill_64k_full_size_sampled():
+    """The streamed-prefill workload at full size in the launch configuration the
+    benchmark times: 65536 prompt tokens, hidden size 2048, the last of 24 layers, all
+    four loops; 96 sampled tokens (both ends, block edges, random) against the oracle."""
+    w = WORKLOADS["prefill_64k"]
+    announce(f"fused encode prefill_64k full size: {w.n} tokens, layer {w.D - 1}")
+    f = Fused(w, w.d_model, w.n, w.n, seed=23)
+    f.encode_layer(w.D - 1, 0)
+    rng = np.random.default_rng(23)
+    toks = sorted(set([0, 1, 127, 128, 129, 4095, 4096, w.n - 129, w.n - 128, w.n - 1]
+                      + rng.choice(w.n, size=86, replace=False).tolist()))
+    ulps = f.check(w.D - 1, 0, toks=toks)
+    announce(f"  max {ulps:.2f} bf16 spacings over {len(toks)} tokens x {w.H} heads")
+    for c in (f.c_k, f.c_v):  # the other layers stay untouched
+        assert bool((c[: w.D - 1] == SENTINEL).all())
