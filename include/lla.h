@@ -284,9 +284,11 @@ int32_t lla_encode_paged(const lla_dims* dims, const lla_codec* codec, const lla
  *            (h d_head + j); proj->d_model a positive multiple of 32.
  *   h      : device bfloat16 [batch][n_new][d_model], the hidden states that enter the
  *            projections at this loop.
- *   acc    : device float32, acc_bytes >= lla_encode_fused_acc_bytes(dims, n_new): the
- *            running sum, owned by the caller and kept between the calls of one layer.
- *            Loop 0 overwrites it (no clearing needed); loops 1 .. T-1 read and update it.
+ *   acc    : device float32, acc_bytes >= lla_encode_fused_acc_bytes(dims, n_new) (the
+ *            float32 running sums of every new token, latent head and entry, tokens
+ *            rounded up to whole blocks of 256; the order inside is the library's own):
+ *            owned by the caller and kept between the calls of one layer. Loop 0
+ *            overwrites it (no clearing needed); loops 1 .. T-1 read and update it.
  *   codec  : w_down_k_t, mu_k, w_down_v_t, mu_v as for lla_encode.
  * The T calls of a layer must run in loop order 0 .. T-1 with the same acc, n_new and
  * pos_start, on one stream (or ordered by the caller); the cache rows hold the result

@@ -200,9 +200,10 @@ int32_t lla_encode(const lla_dims* d, const lla_codec* codec, const lla_cache* c
 
 size_t lla_encode_fused_acc_bytes(const lla_dims* d, int32_t n_new) {
   if (check_dims(d) != LLA_OK || n_new < 0) return 0;
-  const size_t bytes = static_cast<size_t>(d->batch) * n_new * latent_heads(*d) *
-                       static_cast<size_t>(d->r_k + d->r_v) * 4;
-  return (bytes + 255) / 256 * 256;
+  // float32 running sums of every (token, latent head, entry), tokens padded to whole
+  // 256-token blocks (the kernels keep them in their own tile order)
+  const size_t tok = (static_cast<size_t>(d->batch) * n_new + 255) / 256 * 256;
+  return tok * latent_heads(*d) * static_cast<size_t>(d->r_k + d->r_v) * 4;
 }
 
 int32_t lla_encode_fused(const lla_dims* d, const lla_codec* codec, const lla_proj* proj,
@@ -239,9 +240,10 @@ int32_t lla_encode_fused(const lla_dims* d, const lla_codec* codec, const lla_pr
   const void* wds[2] = {codec->w_down_k_t, codec->w_down_v_t};
   const void* mus[2] = {codec->mu_k, codec->mu_v};
   void* cs[2] = {cache->c_k, cache->c_v};
+  lla::FusedArgs fa[2];
   for (int ax = 0; ax < 2; ++ax) {
     const int r = rs[ax];
-    lla::FusedArgs a;
+    lla::FusedArgs& a = fa[ax];
     a.h = h;
     a.w_proj = static_cast<const char*>(wps[ax]) +
                static_cast<size_t>(layer) * proj->d_model * d->H * d->d_head * es;
@@ -262,7 +264,13 @@ int32_t lla_encode_fused(const lla_dims* d, const lla_codec* codec, const lla_pr
     a.loop = loop;
     a.RT = d->r_k + d->r_v;
     a.ao = ax == 0 ? 0 : d->r_k;
-    if (!lla::launch_encode_fused(r, a, d->variant == LLA_PER_HEAD, s)) return LLA_ERR_UNSUPPORTED;
+  }
+  const bool per_head = d->variant == LLA_PER_HEAD;
+  if (per_head && lla::encode_fused_kv_supported(d->r_k, d->r_v, proj->d_model)) {
+    if (!lla::launch_encode_fused_kv(d->r_k, d->r_v, fa[0], fa[1], s)) return LLA_ERR_UNSUPPORTED;
+  } else {
+    for (int ax = 0; ax < 2; ++ax)
+      if (!lla::launch_encode_fused(rs[ax], fa[ax], per_head, s)) return LLA_ERR_UNSUPPORTED;
   }
   return hip_status();
 }

@@ -65,6 +65,9 @@ bool launch_encode(int dtype, int r, const EncodeArgs& a, hipStream_t s);
 // Projection-fused encode of one loop and axis (bfloat16, d 128).
 bool encode_fused_supported(int dtype, int d, int r);
 bool launch_encode_fused(int r, const FusedArgs& a, bool per_head, hipStream_t s);
+// Both axes in one launch (per-head codec; built (r_k, r_v) pairs, d_model a multiple of 64).
+bool encode_fused_kv_supported(int r_k, int r_v, int d_model);
+bool launch_encode_fused_kv(int r_k, int r_v, const FusedArgs& k, const FusedArgs& v, hipStream_t s);
 bool encode_supported(int dtype, int r, int Kdim);
 
 void launch_rope_table(int d, int n_max, double base, float* t32, uint16_t* t16, hipStream_t s);

@@ -214,7 +214,7 @@ def _fused_args(**over):
     a = dict(dims=dims, codec=lla.make_codec(FAKE, FAKE, None, FAKE, FAKE, None, None),
              proj=lla.make_proj(FAKE, FAKE, 2048), cache=lla.make_cache(FAKE, FAKE), layer=1,
              loop=3, h=FAKE, pos_start=8, n_new=100, acc=FAKE,
-             acc_bytes=2 * 100 * 16 * (96 + 160) * 4)
+             acc_bytes=256 * 16 * (96 + 160) * 4)
     a.update(over)
     return a
 
@@ -227,10 +227,12 @@ def _fused_call(a):
 
 def test_fused_acc_bytes():
     dims = lla.make_dims(4, 2, 16, 128, 96, 160, 2, 256)
-    assert lla.lla_encode_fused_acc_bytes(dims, 100) == 2 * 100 * 16 * 256 * 4
-    assert lla.lla_encode_fused_acc_bytes(dims, 1) == (2 * 16 * 256 * 4 + 255) // 256 * 256
+    # tokens (batch x n_new) rounded up to whole 256-token blocks
+    assert lla.lla_encode_fused_acc_bytes(dims, 100) == 256 * 16 * 256 * 4
+    assert lla.lla_encode_fused_acc_bytes(dims, 1) == 256 * 16 * 256 * 4
+    assert lla.lla_encode_fused_acc_bytes(dims, 129) == 512 * 16 * 256 * 4
     d2 = lla.make_dims(4, 2, 16, 128, 96, 160, 1, 256, variant=lla.LLA_2D)
-    assert lla.lla_encode_fused_acc_bytes(d2, 3) == 3072
+    assert lla.lla_encode_fused_acc_bytes(d2, 3) == 256 * 256 * 4
     assert lla.lla_encode_fused_acc_bytes(dims, -1) == 0
 
 
@@ -247,7 +249,7 @@ def test_fused_acc_bytes():
     (dict(proj=lla.make_proj(FAKE, FAKE, 2040)), lla.LLA_ERR_INVALID_ARG),
     (dict(proj=lla.make_proj(FAKE, FAKE, 0)), lla.LLA_ERR_INVALID_ARG),
     (dict(codec=lla.make_codec(FAKE, None, None, FAKE, FAKE, None, None)), lla.LLA_ERR_INVALID_ARG),
-    (dict(acc_bytes=2 * 100 * 16 * 256 * 4 - 1), lla.LLA_ERR_WORKSPACE),
+    (dict(acc_bytes=256 * 16 * 256 * 4 - 1), lla.LLA_ERR_WORKSPACE),
     (dict(dims=lla.make_dims(4, 2, 16, 64, 96, 160, 2, 256)), lla.LLA_ERR_UNSUPPORTED),
     (dict(dims=lla.make_dims(4, 2, 16, 128, 48, 160, 2, 256)), lla.LLA_ERR_UNSUPPORTED),
     (dict(dims=lla.make_dims(4, 2, 16, 128, 96, 160, 2, 256, dtype=lla.LLA_F32)),

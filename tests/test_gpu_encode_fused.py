@@ -150,6 +150,11 @@ def test_fused_encode_matches_oracle(w, d_model, n_new, pos_start):
     (16, 32, 32, "per_head", 2),     # one K chunk per head
     (64, 128, 64, "per_head", 2),    # two K chunks (ring shorter than its depth)
     (160, 96, 96, "per_head", 3),    # three chunks, odd head count
+    # pairs with a two-axis kernel (d_model a multiple of 64): an odd and an even number
+    # of 64-wide K steps, so the W_down rows land in either ring stage
+    (32, 64, 192, "per_head", 2),
+    (64, 64, 128, "per_head", 3),
+    (128, 128, 64, "per_head", 1),
     (32, 16, 64, "2d", 2),
     (128, 64, 160, "2d", 3),
 ])
