@@ -59,7 +59,12 @@ def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
     files = [os.path.join(csrc, f) for f in sorted(KERNEL_SOURCES[kind])]
     from latent_decode_attention_lla_amd import build as _build  # the compile flags
-    h.update(repr((_build.ARCH, _build.HIP_FLAGS, sorted(_build.FILE_FLAGS.items()))).encode())
+    # flags with include paths relative to the repository, so the hash does not depend on
+    # where the checkout lives
+    root = os.path.realpath(ROOT)
+    flags = [os.path.relpath(os.path.realpath(f), root) if os.path.isabs(f) else f
+             for f in _build.HIP_FLAGS]
+    h.update(repr((_build.ARCH, flags, sorted(_build.FILE_FLAGS.items()))).encode())
     for path in files:
         f = os.path.basename(path)
         with open(path) as fh:

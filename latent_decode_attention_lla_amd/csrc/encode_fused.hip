@@ -325,6 +325,9 @@ __device__ __forceinline__ int swz_rows(int row, int sl) {
 #ifndef LLA_FUSED_NST
 #define LLA_FUSED_NST 2
 #endif
+#ifndef LLA_FUSED_GROUP
+#define LLA_FUSED_GROUP 1
+#endif
 
 // Both axes of one loop for the per-head codec in one launch. A workgroup of 8 waves takes
 // 256 tokens and one head: its product tile is the head's 128 key columns and 128 value
@@ -351,7 +354,9 @@ __global__ __launch_bounds__(512) void encode_fused_kv_kernel(FusedArgs ka, Fuse
                 "both W_down blocks fit the stages the last step does not read");
   static_assert(BPW * 8 == NBLK && W_UNITS % 64 == 0, "whole DMA blocks per wave");
   static_assert(NST * STAGE * 16 <= 160 * 1024, "LDS");
-  static_assert(NFB <= NBLK, "one token tile of both axes' running sums fits a stage");
+  // one token tile of both axes' running sums is staged in the stages the W_down rows do
+  // not use: (nk - 1) % NST and, for two-stage tiles, (nk - 2) % NST
+  static_assert(NFB <= NBLK || NST >= 4, "running-sum tile fits the free stages");
   __shared__ u32x4 lds[NST * STAGE];
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -363,8 +368,19 @@ __global__ __launch_bounds__(512) void encode_fused_kv_kernel(FusedArgs ka, Fuse
 
   const int L = static_cast<int>(blockIdx.x);
   const int xcd = L % kXcds, slot = L / kXcds;
+#if LLA_FUSED_GROUP
+  // consecutive slots of an XCD (the workgroups it runs together) cover GT token blocks x
+  // GH heads, so both the hidden-state tiles and the projection rows are shared in L2
+  const int GH = a.Hc % 8 == 0 ? 8 : (a.Hc % 4 == 0 ? 4 : (a.Hc % 2 == 0 ? 2 : 1));
+  const int GT = 32 / GH;
+  const int grp = slot / 32, g = slot % 32;
+  const int hgroups = a.Hc / GH;
+  const int tb = xcd + kXcds * ((grp / hgroups) * GT + g / GH);
+  const int hc = (grp % hgroups) * GH + g % GH;
+#else
   const int tb = xcd + kXcds * (slot / a.Hc);
   const int hc = slot % a.Hc;
+#endif
   const int ntb = (a.Ntok + TOKWG - 1) / TOKWG;
   if (tb >= ntb) return;  // padding workgroups of the last round
   const int tok0 = tb * TOKWG;
@@ -462,19 +478,46 @@ __global__ __launch_bounds__(512) void encode_fused_kv_kernel(FusedArgs ka, Fuse
         }
       }
     }
+    // Fragment reads run one column-tile pair ahead of the MFMAs that use them (and the B
+    // fragments of the next K chunk one pair before they are needed), issued right after
+    // the current pair's first MFMA, with scheduler fences keeping that order, so LDS
+    // latency hides behind the pair's other seven MFMAs.
     const u32x4* stage = lds + (s % NST) * STAGE;
-#pragma unroll
-    for (int kh = 0; kh < NKH; ++kh) {
-      i16x8 bfr[TT];
+    auto rd_b = [&](int kh, i16x8* b) __attribute__((always_inline)) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
-        bfr[tt] = __builtin_bit_cast(i16x8, stage[W_UNITS + (brow0 + 16 * tt) * SLOTS + fu[kh]]);
+        b[tt] = __builtin_bit_cast(i16x8, stage[W_UNITS + (brow0 + 16 * tt) * SLOTS + fu[kh]]);
+    };
+    auto rd_a = [&](int kh, int ct) __attribute__((always_inline)) {
+      return __builtin_bit_cast(i16x8, stage[(arow0 + 16 * ct) * SLOTS + fu[kh]]);
+    };
+    constexpr int NPAIR = NKH * NCT / 2;
+    i16x8 bq[NKH][TT];
+    i16x8 ap[2][2];
+    rd_b(0, bq[0]);
+    ap[0][0] = rd_a(0, 0);
+    ap[0][1] = rd_a(0, 1);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const i16x8 afr = __builtin_bit_cast(i16x8, stage[(arow0 + 16 * ct) * SLOTS + fu[kh]]);
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) x[ct][tt] = mfma_bf16_k32(afr, bfr[tt], x[ct][tt]);
+    for (int q = 0; q < NPAIR; ++q) {
+      const int kh = q / (NCT / 2), ct = 2 * (q % (NCT / 2));
+      // the pair's first MFMA (waiting for its operands), then the next pair's reads, then
+      // the other seven MFMAs of this pair while those reads are in flight
+      x[ct][0] = mfma_bf16_k32(ap[q & 1][0], bq[kh][0], x[ct][0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q + 1 < NPAIR) {
+        const int kn = (q + 1) / (NCT / 2), cn = 2 * ((q + 1) % (NCT / 2));
+        ap[(q + 1) & 1][0] = rd_a(kn, cn);
+        ap[(q + 1) & 1][1] = rd_a(kn, cn + 1);
+        if (kn != kh) rd_b(kn, bq[kn]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      x[ct + 1][0] = mfma_bf16_k32(ap[q & 1][1], bq[kh][0], x[ct + 1][0]);
+#pragma unroll
+      for (int tt = 1; tt < TT; ++tt) {
+        x[ct][tt] = mfma_bf16_k32(ap[q & 1][0], bq[kh][tt], x[ct][tt]);
+        x[ct + 1][tt] = mfma_bf16_k32(ap[q & 1][1], bq[kh][tt], x[ct + 1][tt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -489,7 +532,10 @@ __global__ __launch_bounds__(512) void encode_fused_kv_kernel(FusedArgs ka, Fuse
   // are contiguous 16-byte lanes. For each token tile a wave first copies its blocks of
   // the running sum into its own slice of the stage the last step read (direct-to-LDS, so
   // the latency overlaps the hi / lo split), then reads them back per latent tile.
-  u32x4* accs = lds + ((nk - 1) % NST) * STAGE + 64 * (ax == 0 ? tg * NLTK : 4 * NLTK + tg * NLTV);
+  const int sbase = ax == 0 ? tg * NLTK : 4 * NLTK + tg * NLTV;  // the wave's staging blocks
+  auto acc_region = [&](int b) __attribute__((always_inline)) {
+    return lds + (((nk - 1 - b / NBLK) % NST + NST) % NST) * STAGE + 64 * (b % NBLK);
+  };
   auto second = [&](auto rtag, const void* mu, void* c, int ao, int fb0) __attribute__((always_inline)) {
     constexpr int R = decltype(rtag)::value;
     constexpr int NLT = R / 16;
@@ -502,7 +548,7 @@ __global__ __launch_bounds__(512) void encode_fused_kv_kernel(FusedArgs ka, Fuse
     for (int tt = 0; tt < TT; ++tt) {
       if (!first) {
 #pragma unroll
-        for (int lt = 0; lt < NLT; ++lt) dma(accw + (tt * NLT + lt) * 256, accs + 64 * lt);
+        for (int lt = 0; lt < NLT; ++lt) dma(accw + (tt * NLT + lt) * 256, acc_region(sbase + lt));
       }
       i16x8 fh[NS2], fl[NS2];
 #pragma unroll
@@ -526,7 +572,7 @@ __global__ __launch_bounds__(512) void encode_fused_kv_kernel(FusedArgs ka, Fuse
           acc4 = mfma_bf16_k32(fh[s2], bw, acc4);
           acc4 = mfma_bf16_k32(fl[s2], bw, acc4);
         }
-        if (!first) acc4 += __builtin_bit_cast(f32x4, accs[64 * lt + lane]);
+        if (!first) acc4 += __builtin_bit_cast(f32x4, acc_region(sbase + lt)[lane]);
         if (!last) {
           *reinterpret_cast<f32x4*>(accw + (tt * NLT + lt) * 256) = acc4;
         } else {
@@ -553,8 +599,15 @@ template <int RK, int RV>
 void launch_kv(const FusedArgs& k, const FusedArgs& v, hipStream_t s) {
   constexpr int KC2 = LLA_FUSED_KC, NST = LLA_FUSED_NST;
   const int ntb = (k.Ntok + 255) / 256;
+#if LLA_FUSED_GROUP
+  const int GH = k.Hc % 8 == 0 ? 8 : (k.Hc % 4 == 0 ? 4 : (k.Hc % 2 == 0 ? 2 : 1));
+  const long long per_xcd = (ntb + kXcds - 1) / kXcds;          // token blocks per XCD
+  const long long tgroups = (per_xcd + 32 / GH - 1) / (32 / GH);  // token groups per XCD
+  const unsigned blocks = static_cast<unsigned>(tgroups * (k.Hc / GH) * 32 * kXcds);
+#else
   const long long rounds = (ntb + kXcds - 1) / kXcds;
   const unsigned blocks = static_cast<unsigned>(rounds * kXcds * k.Hc);
+#endif
   hipLaunchKernelGGL((encode_fused_kv_kernel<RK, RV, KC2, NST>), dim3(blocks), dim3(512), 0, s, k, v);
 }
 

@@ -104,3 +104,16 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_source_hash_does_not_depend_on_where_the_checkout_lives(monkeypatch, tmp_path):
+    """The compile flags enter the hash with include paths relative to the repository, so
+    a copy of the tree elsewhere (or reached through a symlink) hashes the same."""
+    from latent_decode_attention_lla_amd import build as B
+    before = {k: bench.kernel_source_hash(k) for k in bench.KERNEL_SOURCES}
+    link = tmp_path / "checkout"
+    link.symlink_to(bench.ROOT)
+    monkeypatch.setattr(B, "HIP_FLAGS", [f.replace(bench.ROOT, str(link)) if f.startswith(bench.ROOT) else f
+                                         for f in B.HIP_FLAGS])
+    assert any(str(link) in f for f in B.HIP_FLAGS)
+    assert {k: bench.kernel_source_hash(k) for k in bench.KERNEL_SOURCES} == before
