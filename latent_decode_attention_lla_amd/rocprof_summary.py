@@ -92,7 +92,8 @@ def main(argv=None):
     t.add_argument("--sum", action="store_true")
     t.add_argument("--out")
     t.add_argument("--extra", default="{}", help="JSON merged into the output")
-    t.add_argument("--call", choices=["decode", "absorbed", "encode", "teacher", "reconstruct", "paged"],
+    t.add_argument("--call", choices=["decode", "absorbed", "encode", "encode_fused", "teacher",
+                                      "reconstruct", "paged"],
                    help="with --workload: record the call's source hash and algorithmic bytes")
     t.add_argument("--workload")
     a = p.parse_args(argv)
@@ -174,6 +175,8 @@ def main(argv=None):
         _, n_new, _ = bench.step_shape(w)
         if a.call == "reconstruct":
             alg, _ = bench.algorithmic(w, "reconstruct", L=w.T, n_new=n_new)
+        elif a.call == "encode_fused":
+            alg, _ = bench.algorithmic(w, "encode_fused", n_new=n_new)
         else:
             alg, _ = bench.algorithmic(w, "encode" if a.call == "encode" else "decode", n_new=n_new)
         res.update({"call": a.call, "workload": a.workload, "path": "auto",
