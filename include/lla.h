@@ -71,8 +71,14 @@ typedef enum { LLA_PER_HEAD = 0, LLA_2D = 1 } lla_variant;
  *                          P_i, Q_i linear in the latent, so the score is
  *                          c_j . (CS_j M) + CS_j m, where CS_j holds cos/sin of position j
  *                          (shared by all heads) and M (d_head x r_k) folds q into W_up.
- *                          bfloat16 only; CS and M enter the MFMA as float16.
- *   LLA_PATH_AUTO        : ROTARY_FOLD for bfloat16 per-head, RECONSTRUCT otherwise. */
+ *                          bfloat16 only; CS and M enter the MFMA as float16, so each
+ *                          folded score carries float16 rounding (relative 2^-11 of the
+ *                          score's terms): outputs stay within 2e-2 of exact attention for
+ *                          score spreads up to about 55 (scale * q.k in natural-log
+ *                          units); M overflows float16 only past 65504, far beyond that.
+ *   LLA_PATH_AUTO        : ROTARY_FOLD for the bfloat16 shapes a fold kernel is built for,
+ *                          per head and LLA-2D (the narrow, wide or LLA-2D fold kernel);
+ *                          RECONSTRUCT for everything else (float32, other shapes). */
 typedef enum { LLA_PATH_AUTO = 0, LLA_PATH_RECONSTRUCT = 1, LLA_PATH_ROTARY_FOLD = 2 } lla_path;
 
 typedef struct {
