@@ -38,10 +38,12 @@ ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-result"]
-# Per-source additions. The narrow rotary-fold kernel is bound by vector-ALU issue; having
-# its MFMA results written straight to VGPRs saves the AGPR-to-VGPR copies (five per
-# 16-token tile) without raising its register count.
-FILE_FLAGS = {"decode_rotary_fold.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source additions. The narrow rotary-fold kernel and the reconstruct kernels are bound
+# by vector-ALU issue; having their MFMA results written straight to VGPRs saves the
+# AGPR-to-VGPR copies (five per 16-token tile for the fold, eight for a rebuilt tile)
+# without raising their register counts.
+_VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {"decode_rotary_fold.hip": _VGPR_MFMA, "decode_reconstruct.hip": _VGPR_MFMA}
 
 
 def _hipcc() -> str:
