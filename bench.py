@@ -50,21 +50,44 @@ KERNEL_SOURCES = {
 }
 
 
-def kernel_source_hash(kind: str) -> str:
-    """Hash of the HIP/C++ sources behind one call kind (a key of KERNEL_SOURCES) with comments
-    and whitespace removed: it changes when that call's compiled code or launch plan can
-    change, not when a comment or the other call's sources do."""
+# The decode kernels' own sources, by a substring of their kernel names: a summary taken
+# on one of them depends on its file only, not on the other decode kernels'.
+_DECODE_KERNEL_FILES = {"decode_rotary_fold": "decode_rotary_fold.hip",
+                        "decode_fold_wide": "decode_fold_wide.hip",
+                        "decode_lla2d": "decode_lla2d.hip",
+                        "decode_reconstruct": "decode_reconstruct.hip"}
+
+
+def kernel_sources(kind: str, kernel=None) -> tuple:
+    """Sources behind a call kind; for the decode calls, when the measured kernel name(s)
+    are given, only the decode kernel file(s) those names come from."""
+    files = KERNEL_SOURCES[kind]
+    if kernel and kind in ("decode", "paged"):
+        names = kernel if isinstance(kernel, (list, tuple)) else [kernel]
+        used = {f for k, f in _DECODE_KERNEL_FILES.items() if any(k in n for n in names)}
+        if used:
+            files = tuple(f for f in files if f not in _DECODE_KERNEL_FILES.values() or f in used)
+    return files
+
+
+def kernel_source_hash(kind: str, kernel=None) -> str:
+    """Hash of the HIP/C++ sources behind one call kind (a key of KERNEL_SOURCES; with
+    `kernel`, the measured decode kernel's sources only) with comments and whitespace
+    removed, and of their compile flags: it changes when that call's compiled code or
+    launch plan can change, not when a comment or another kernel's sources do."""
     import re
     csrc = os.path.join(ROOT, "latent_decode_attention_lla_amd", "csrc")
     h = hashlib.sha256()
-    files = [os.path.join(csrc, f) for f in sorted(KERNEL_SOURCES[kind])]
+    names = sorted(kernel_sources(kind, kernel))
+    files = [os.path.join(csrc, f) for f in names]
     from latent_decode_attention_lla_amd import build as _build  # the compile flags
     # flags with include paths relative to the repository, so the hash does not depend on
     # where the checkout lives
     root = os.path.realpath(ROOT)
     flags = [os.path.relpath(os.path.realpath(f), root) if os.path.isabs(f) else f
              for f in _build.HIP_FLAGS]
-    h.update(repr((_build.ARCH, flags, sorted(_build.FILE_FLAGS.items()))).encode())
+    file_flags = sorted((f, v) for f, v in _build.FILE_FLAGS.items() if f in names)
+    h.update(repr((_build.ARCH, flags, file_flags)).encode())
     for path in files:
         f = os.path.basename(path)
         with open(path) as fh:
@@ -76,19 +99,24 @@ def kernel_source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(kind: str, workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{kind}_{workload}_traffic.json")
+def _profile_stem(kind: str, workload: str, path: str) -> str:
+    """File stem of a call's committed summaries; a forced decode path gets its own."""
+    return f"{kind}_{workload}" + ("" if path == "auto" else f"_{path}")
+
+
+def traffic_file(kind: str, workload: str, path: str = "auto") -> str:
+    return os.path.join(ROOT, "profiles", f"{_profile_stem(kind, workload, path)}_traffic.json")
 
 
 def measured_traffic(kind: str, workload: str, path: str):
     """HBM bytes per call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or
     None when there is none or the call's sources have changed since it was taken."""
     try:
-        with open(traffic_file(kind, workload)) as f:
+        with open(traffic_file(kind, workload, path)) as f:
             tr = json.load(f)
     except (OSError, ValueError):
         return None
-    if tr.get("kernel_source_hash") == kernel_source_hash(kind) and tr.get("path") == path \
+    if tr.get("kernel_source_hash") == kernel_source_hash(kind, tr.get("kernel")) and tr.get("path") == path \
             and tr.get("workload") == workload:
         return tr.get("hbm_bytes_per_launch")
     return None
@@ -586,8 +614,8 @@ def main_stream_prefill(args, w):
     print(json.dumps(res))
 
 
-def counters_file(kind: str, workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{kind}_{workload}_counters.json")
+def counters_file(kind: str, workload: str, path: str = "auto") -> str:
+    return os.path.join(ROOT, "profiles", f"{_profile_stem(kind, workload, path)}_counters.json")
 
 
 def measured_counters(kind: str, workload: str, path: str):
@@ -595,11 +623,11 @@ def measured_counters(kind: str, workload: str, path: str):
     summary (wait and issue-wait fractions, instructions per wave), or None when there is
     none or the call's sources have changed since it was taken."""
     try:
-        with open(counters_file(kind, workload)) as f:
+        with open(counters_file(kind, workload, path)) as f:
             ct = json.load(f)
     except (OSError, ValueError):
         return None
-    if ct.get("kernel_source_hash") == kernel_source_hash(kind) and ct.get("path") == path \
+    if ct.get("kernel_source_hash") == kernel_source_hash(kind, ct.get("kernel")) and ct.get("path") == path \
             and ct.get("workload") == workload:
         return {k: ct[k] for k in ("kernel", "wave_wait_frac", "wave_issue_wait_frac",
                                    "valu_insts_per_wave", "mfma_insts_per_wave",

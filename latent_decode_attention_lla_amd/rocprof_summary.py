@@ -83,6 +83,7 @@ def main(argv=None):
     wv.add_argument("--kernel", required=True)
     wv.add_argument("--call", required=True)
     wv.add_argument("--workload", required=True)
+    wv.add_argument("--path", default="auto", help="decode path the bench run forced")
     wv.add_argument("--out")
     t = sp.add_parser("traffic")
     for name in ("fetch", "write", "copy-fetch", "copy-write"):
@@ -96,6 +97,7 @@ def main(argv=None):
                                       "reconstruct", "paged"],
                    help="with --workload: record the call's source hash and algorithmic bytes")
     t.add_argument("--workload")
+    t.add_argument("--path", default="auto", help="decode path the bench run forced")
     a = p.parse_args(argv)
     if a.cmd == "kernels":
         rows = kernel_table(a.db)
@@ -139,8 +141,8 @@ def main(argv=None):
                "valu_insts_per_wave": (c["SQ_INSTS_VALU"] - c.get("SQ_INSTS_MFMA", 0.0)) / waves,
                "mfma_insts_per_wave": c.get("SQ_INSTS_MFMA", 0.0) / waves,
                "salu_insts_per_wave": c["SQ_INSTS_SALU"] / waves,
-               "call": a.call, "workload": a.workload, "path": "auto",
-               "kernel_source_hash": bench.kernel_source_hash(a.call)}
+               "call": a.call, "workload": a.workload, "path": a.path,
+               "kernel_source_hash": bench.kernel_source_hash(a.call, kname)}
         if c.get("SQ_ACTIVE_INST_LDS"):
             res["lds_bank_conflict_per_lds_cycle"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]
         txt = json.dumps(res, indent=1)
@@ -179,8 +181,8 @@ def main(argv=None):
             alg, _ = bench.algorithmic(w, "encode_fused", n_new=n_new)
         else:
             alg, _ = bench.algorithmic(w, "encode" if a.call == "encode" else "decode", n_new=n_new)
-        res.update({"call": a.call, "workload": a.workload, "path": "auto",
-                    "kernel_source_hash": bench.kernel_source_hash(a.call),
+        res.update({"call": a.call, "workload": a.workload, "path": a.path,
+                    "kernel_source_hash": bench.kernel_source_hash(a.call, fk),
                     "algorithmic_bytes_per_launch": alg,
                     "traffic_over_algorithmic": res["hbm_bytes_per_launch"] / alg})
     res.update(json.loads(a.extra))

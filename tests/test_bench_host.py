@@ -90,9 +90,9 @@ def test_committed_traffic_is_reported_only_while_current(path):
     it is re-taken); and its bytes are close to the algorithmic bytes."""
     tr = json.load(open(path))
     kind, workload = tr["call"], tr["workload"]
-    assert os.path.basename(path) == f"{kind}_{workload}_traffic.json"
+    assert path == bench.traffic_file(kind, workload, tr["path"])
     got = bench.measured_traffic(kind, workload, tr["path"])
-    if tr["kernel_source_hash"] == bench.kernel_source_hash(kind):
+    if tr["kernel_source_hash"] == bench.kernel_source_hash(kind, tr["kernel"]):
         assert got == tr["hbm_bytes_per_launch"]
     else:
         assert got is None
@@ -117,3 +117,19 @@ def test_source_hash_does_not_depend_on_where_the_checkout_lives(monkeypatch, tm
                                          for f in B.HIP_FLAGS])
     assert any(str(link) in f for f in B.HIP_FLAGS)
     assert {k: bench.kernel_source_hash(k) for k in bench.KERNEL_SOURCES} == before
+
+
+def test_decode_summary_hash_follows_the_measured_kernel_only():
+    """A decode summary taken on one decode kernel hashes that kernel's file (and the shared
+    sources), so an edit to another decode kernel leaves it current; the full call hash
+    still covers every decode kernel."""
+    fold = bench.kernel_sources("decode", "decode_rotary_fold_kernel<128, 16, 32, 4, 4, false>")
+    assert "decode_rotary_fold.hip" in fold and "decode_reconstruct.hip" not in fold
+    assert "combine.hip" in fold and "lla_plan.h" in fold
+    both = bench.kernel_sources("decode", ["decode_reconstruct_bf16_kernel<...>", "combine_kernel<...>"])
+    assert "decode_reconstruct.hip" in both and "decode_fold_wide.hip" not in both
+    assert bench.kernel_sources("decode") == bench.KERNEL_SOURCES["decode"]
+    assert bench.kernel_sources("decode", "some_other_kernel") == bench.KERNEL_SOURCES["decode"]
+    assert bench.kernel_source_hash("decode", "decode_lla2d_kernel") != bench.kernel_source_hash("decode")
+    # non-decode calls ignore the kernel name
+    assert bench.kernel_source_hash("encode", "decode_lla2d_kernel") == bench.kernel_source_hash("encode")
