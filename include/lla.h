@@ -65,7 +65,12 @@ typedef enum { LLA_PER_HEAD = 0, LLA_2D = 1 } lla_variant;
 
 /* Decode kernel family.
  *   LLA_PATH_RECONSTRUCT : rebuild each key tile with MFMA (K^T = W_up,k,t C_k^T + mu_k,t),
- *                          rotate it in registers, dot with q, online softmax.
+ *                          rotate it in registers, dot with q, online softmax. float32
+ *                          caches rotate and dot in float32; bfloat16 caches round the
+ *                          rebuilt key to float16 and contract the products of each pair
+ *                          with cos and sin (float16) against [q0, q1, q1, -q0] on the
+ *                          matrix cores, so their scores carry float16 rounding like the
+ *                          fold's, and keys beyond 65504 in magnitude overflow.
  *   LLA_PATH_ROTARY_FOLD : the same scores via an exact rewrite: for every rotary pair i
  *                          q.R(j theta_i)k = cos(j theta_i) P_i + sin(j theta_i) Q_i with
  *                          P_i, Q_i linear in the latent, so the score is
