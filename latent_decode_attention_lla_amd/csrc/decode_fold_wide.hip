@@ -120,55 +120,6 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
   const int s1 = min(len, s0 + a.split_len);
   const int ntok = max(0, s1 - s0);
 
-  // ---- this half's M^T fragments, through a per-wave LDS transpose of W_up,k,t ----
-  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w_up_k) + static_cast<size_t>(t * a.H + h) * D * RK;
-  const size_t mu_off = SHARED ? static_cast<size_t>(t * a.H + h) * D : static_cast<size_t>(h * a.T + t) * D;
-  const uint16_t* mu = reinterpret_cast<const uint16_t*>(a.mu_k) + mu_off;
-  const float* q = a.q + (static_cast<size_t>(b * a.H + h) * a.L + li) * D;
-  const float sc = a.scale_log2e;
-  uint16_t* wt = reinterpret_cast<uint16_t*>(lds) + wave * 16 * WT_STRIDE;
-  f16x8_t mf[NTMAX][NKS];
-#pragma unroll
-  for (int i = 0; i < NTMAX; ++i) {
-    const int tile = half == 0 ? i : NR0 + i;  // latent row tile; NCK is the mean row
-    const bool active = half == 0 ? (i < NT0) : (i < NT1);
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
-      const int c = lane + 64 * k;
-      if (active && tile < NCK) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(c) * RK + 16 * tile);
-        const u32x4 x0 = src[0], x1 = src[1];
-        const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          wt[(2 * j) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] & 0xffffu);
-          wt[(2 * j + 1) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] >> 16);
-        }
-      } else {
-        wt[c] = (active && tile == NCK) ? mu[c] : static_cast<uint16_t>(0);
-#pragma unroll
-        for (int j = 1; j < 16; ++j) wt[j * WT_STRIDE + c] = 0;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks2 = 0; ks2 < NKS / 2; ++ks2) {
-      const int p0 = 32 * ks2 + 8 * hi;
-      const u32x4* wrow = reinterpret_cast<const u32x4*>(wt + lo * WT_STRIDE + 2 * p0);
-      const u32x4 y0 = wrow[0], y1 = wrow[1];
-      const uint32_t wp[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x0 = __uint_as_float(wp[e] << 16);
-        const float x1 = __uint_as_float(wp[e] & 0xffff0000u);
-        const float2 qp = *reinterpret_cast<const float2*>(q + 2 * (p0 + e));
-        mf[i][ks2][e] = static_cast<_Float16>((qp.x * x0 + qp.y * x1) * sc);
-        mf[i][ks2 + NKS / 2][e] = static_cast<_Float16>((qp.y * x0 - qp.x * x1) * sc);
-      }
-    }
-    __syncthreads();
-  }
-
   // dense: this head's plane (LLA-2D: the sequence's); paged: the pool (pages are added
   // per tile)
   const size_t plane = PAGED ? 0
@@ -199,6 +150,8 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int NIW = (STAGE_BLOCKS + NW - 1) / NW;  // blocks each wave loads per stage
   constexpr int NB = LLA_WIDE_STAGES;
   static_assert(NB >= 2 && (NB - 2) * NIW <= 63, "vmcnt range");
+  // the W_up staging fits the ring's last stage, so the first tiles can be requested first
+  constexpr bool kEarly = NB >= 3 && STAGE_UNITS <= STAGE_BLOCKS * 64;
   static_assert(NB * STAGE_BLOCKS * 64 + (XCH_FLOATS + 3) / 4 <= LDS_UNITS_RING, "ring size");
   u32x4* ring = lds;
   float* xch = reinterpret_cast<float*>(lds + NB * STAGE_BLOCKS * 64);  // [wave][16]
@@ -309,16 +262,92 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
     }
   };
 
+  // ---- this half's M^T fragments, through a per-wave LDS transpose of W_up,k,t ----
+  // Every W_up,k,t row this wave needs is requested at once (one memory round trip), and
+  // with kEarly the ring's first tiles are already in flight: the staging then sits in the
+  // ring's last stage, which the prologue does not fill.
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w_up_k) + static_cast<size_t>(t * a.H + h) * D * RK;
+  const size_t mu_off = SHARED ? static_cast<size_t>(t * a.H + h) * D : static_cast<size_t>(h * a.T + t) * D;
+  const uint16_t* mu = reinterpret_cast<const uint16_t*>(a.mu_k) + mu_off;
+  const float* q = a.q + (static_cast<size_t>(b * a.H + h) * a.L + li) * D;
+  const float sc = a.scale_log2e;
+  uint16_t* wt = reinterpret_cast<uint16_t*>(lds + (kEarly ? (NB - 1) * STAGE_BLOCKS * 64 : 0)) +
+                 wave * 16 * WT_STRIDE;
+  u32x4 wpre[NTMAX][D / 64][2];
+  uint16_t mpre[D / 64];
+#pragma unroll
+  for (int i = 0; i < NTMAX; ++i) {
+    const int tile = half == 0 ? i : NR0 + i;
+    const bool active = half == 0 ? (i < NT0) : (i < NT1);
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      if (active && tile < NCK) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(lane + 64 * k) * RK + 16 * tile);
+        wpre[i][k][0] = src[0];
+        wpre[i][k][1] = src[1];
+      } else {
+        wpre[i][k][0] = u32x4{0u, 0u, 0u, 0u};
+        wpre[i][k][1] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) mpre[k] = mu[lane + 64 * k];
+  if (kEarly && ntile > 0) {
+#pragma unroll
+    for (int tl = 0; tl < NB - 1; ++tl) issue(tl);
+  }
+  f16x8_t mf[NTMAX][NKS];
+#pragma unroll
+  for (int i = 0; i < NTMAX; ++i) {
+    const int tile = half == 0 ? i : NR0 + i;  // latent row tile; NCK is the mean row
+    const bool active = half == 0 ? (i < NT0) : (i < NT1);
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int c = lane + 64 * k;
+      if (active && tile < NCK) {
+        const u32x4 x0 = wpre[i][k][0], x1 = wpre[i][k][1];
+        const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          wt[(2 * j) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] & 0xffffu);
+          wt[(2 * j + 1) * WT_STRIDE + c] = static_cast<uint16_t>(w8[j] >> 16);
+        }
+      } else {
+        wt[c] = (active && tile == NCK) ? mpre[k] : static_cast<uint16_t>(0);
+#pragma unroll
+        for (int j = 1; j < 16; ++j) wt[j * WT_STRIDE + c] = 0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks2 = 0; ks2 < NKS / 2; ++ks2) {
+      const int p0 = 32 * ks2 + 8 * hi;
+      const u32x4* wrow = reinterpret_cast<const u32x4*>(wt + lo * WT_STRIDE + 2 * p0);
+      const u32x4 y0 = wrow[0], y1 = wrow[1];
+      const uint32_t wp[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x0 = __uint_as_float(wp[e] << 16);
+        const float x1 = __uint_as_float(wp[e] & 0xffff0000u);
+        const float2 qp = *reinterpret_cast<const float2*>(q + 2 * (p0 + e));
+        mf[i][ks2][e] = static_cast<_Float16>((qp.x * x0 + qp.y * x1) * sc);
+        mf[i][ks2 + NKS / 2][e] = static_cast<_Float16>((qp.y * x0 - qp.x * x1) * sc);
+      }
+    }
+    __syncthreads();
+  }
+  if (!kEarly && ntile > 0) {
+#pragma unroll
+    for (int tl = 0; tl < NB - 1; ++tl) issue(tl);
+  }
+
   float m_run = kMaxInit, l_run = 0.f;
   float acc[VSH];
 #pragma unroll
   for (int e = 0; e < VSH; ++e) acc[e] = 0.f;
 
   const int mypl = SHARED ? 0 : hw;
-  if (ntile > 0) {
-#pragma unroll
-    for (int tl = 0; tl < NB - 1; ++tl) issue(tl);
-  }
 
   // The tile loop, compiled once per half so that which row tiles, latent rows and value
   // entries a wave owns are compile-time constants (no branches inside the loop).
