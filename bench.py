@@ -631,7 +631,8 @@ def measured_counters(kind: str, workload: str, path: str):
             and ct.get("workload") == workload:
         return {k: ct[k] for k in ("kernel", "wave_wait_frac", "wave_issue_wait_frac",
                                    "valu_insts_per_wave", "mfma_insts_per_wave",
-                                   "salu_insts_per_wave", "lds_bank_conflict_per_lds_cycle")
+                                   "salu_insts_per_wave", "lds_bank_conflict_pct",
+                                   "lds_conflicts_per_access", "mfma_busy_frac")
                 if k in ct}
     return None
 

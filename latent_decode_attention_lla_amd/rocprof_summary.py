@@ -12,10 +12,16 @@ whose names contain one of the given fragments:
   python -m latent_decode_attention_lla_amd.rocprof_summary counters RUN_results.db \
       --kernel decode_rotary_fold
 
-``waves`` turns two SQ counter passes of one kernel (between them: SQ_WAVES, SQ_WAVE_CYCLES,
+``waves`` turns two counter passes of one kernel (between them: SQ_WAVES, SQ_WAVE_CYCLES,
 SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_INSTS_VALU, SQ_INSTS_SALU, SQ_INSTS_MFMA, SQ_INSTS_LDS,
-SQ_LDS_BANK_CONFLICT, SQ_ACTIVE_INST_LDS) into the wave-state evidence
-bench.py reports for a call bound by neither roof:
+SQ_LDS_BANK_CONFLICT, SQ_ACTIVE_INST_LDS, SQ_LDS_IDX_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES,
+GRBM_GUI_ACTIVE) into the wave-state evidence bench.py reports for a call bound by neither
+roof. SQ_WAVE_CYCLES and the SQ_WAIT_* / SQ_ACTIVE_INST_* counters are in quad-cycles
+summed over waves; SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE are cycles summed over CUs,
+SQ_VALU_MFMA_BUSY_CYCLES cycles summed over SIMDs, GRBM_GUI_ACTIVE the dispatch's GPU
+cycles. The bank-conflict figures follow rocprofv3's own derived metrics (LDSBankConflict:
+percent of the dispatch's cycles a CU's LDS is stalled by conflicts; LdsBankConflict:
+conflict cycles per conflict-free LDS cycle):
 
   python -m latent_decode_attention_lla_amd.rocprof_summary waves --p1 A.db --p2 B.db \
       --kernel decode_lla2d --call decode --workload lla2d_long --out counters.json
@@ -68,6 +74,26 @@ def _pick(agg: dict, sub: str, add: bool = False):
             (min(v[0] for _, v in hits), sum(v[1] for _, v in hits)))
 
 
+def derive(c: dict, cus: int, xccs: int) -> dict:
+    """Per-wave and per-cycle figures from one dispatch's summed counters. The dispatch's
+    GPU cycles are GRBM_GUI_ACTIVE over the XCDs (the database holds its sum over them,
+    rocprofv3's derived metrics take the largest)."""
+    waves = c.get("SQ_WAVES") or 1.0
+    res = {"wave_wait_frac": c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"],
+           "wave_issue_wait_frac": c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"],
+           "valu_insts_per_wave": (c["SQ_INSTS_VALU"] - c.get("SQ_INSTS_MFMA", 0.0)) / waves,
+           "mfma_insts_per_wave": c.get("SQ_INSTS_MFMA", 0.0) / waves,
+           "salu_insts_per_wave": c["SQ_INSTS_SALU"] / waves}
+    gpu = c.get("GRBM_GUI_ACTIVE", 0.0) / xccs
+    if gpu > 0 and "SQ_LDS_BANK_CONFLICT" in c:
+        res["lds_bank_conflict_pct"] = 100.0 * c["SQ_LDS_BANK_CONFLICT"] / gpu / cus
+    if "SQ_LDS_IDX_ACTIVE" in c and c["SQ_LDS_IDX_ACTIVE"] > c.get("SQ_LDS_BANK_CONFLICT", 0.0):
+        res["lds_conflicts_per_access"] = c["SQ_LDS_BANK_CONFLICT"] / (c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"])
+    if gpu > 0 and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        res["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gpu * 4 * cus)
+    return res
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sp = p.add_subparsers(dest="cmd", required=True)
@@ -84,6 +110,8 @@ def main(argv=None):
     wv.add_argument("--call", required=True)
     wv.add_argument("--workload", required=True)
     wv.add_argument("--path", default="auto", help="decode path the bench run forced")
+    wv.add_argument("--cus", type=int, default=256, help="compute units of the device")
+    wv.add_argument("--xccs", type=int, default=8, help="XCDs of the device")
     wv.add_argument("--out")
     t = sp.add_parser("traffic")
     for name in ("fetch", "write", "copy-fetch", "copy-write"):
@@ -126,7 +154,8 @@ def main(argv=None):
         kname = None
         for n in ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU",
                   "SQ_INSTS_SALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
-                  "SQ_ACTIVE_INST_LDS"):
+                  "SQ_ACTIVE_INST_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES",
+                  "GRBM_GUI_ACTIVE"):
             for db in (a.p1, a.p2):  # each counter is taken from whichever pass holds it
                 try:
                     kname, (_, v) = _pick(counter_per_kernel(db, n), a.kernel)
@@ -134,17 +163,10 @@ def main(argv=None):
                     continue
                 c[n] = v
                 break
-        waves = c.get("SQ_WAVES") or 1.0
         res = {"kernel": kname, "counters_per_dispatch": c,
-               "wave_wait_frac": c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"],
-               "wave_issue_wait_frac": c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"],
-               "valu_insts_per_wave": (c["SQ_INSTS_VALU"] - c.get("SQ_INSTS_MFMA", 0.0)) / waves,
-               "mfma_insts_per_wave": c.get("SQ_INSTS_MFMA", 0.0) / waves,
-               "salu_insts_per_wave": c["SQ_INSTS_SALU"] / waves,
                "call": a.call, "workload": a.workload, "path": a.path,
                "kernel_source_hash": bench.kernel_source_hash(a.call, kname)}
-        if c.get("SQ_ACTIVE_INST_LDS"):
-            res["lds_bank_conflict_per_lds_cycle"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]
+        res.update(derive(c, a.cus, a.xccs))
         txt = json.dumps(res, indent=1)
         if a.out:
             with open(a.out, "w") as f:
