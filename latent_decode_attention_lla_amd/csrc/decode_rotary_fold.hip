@@ -61,6 +61,9 @@ constexpr float kRescaleSlack = 8.0f;
 #ifndef LLA_FOLD_WAVES_PER_EU
 #define LLA_FOLD_WAVES_PER_EU 0  // 0: let the compiler choose
 #endif
+#ifndef LLA_FOLD_TAB_DMA
+#define LLA_FOLD_TAB_DMA 1      // 1: cos/sin tiles go straight to LDS (direct-to-LDS loads)
+#endif
 
 template <typename V>
 __device__ __forceinline__ V stream_load(const V* p) {
@@ -292,7 +295,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   };
 
   // Two row buffers used in turn: chunk c computes from one while chunk c + 1 loads into
-  // the other; the table of chunk c + 1 goes through registers into the other LDS half.
+  // the other; the table of chunk c + 1 goes straight into the other LDS half.
   // Paged rows: the pages of a chunk's tiles (uniform across the workgroup; rows clamped to
   // the context's last token lie in the last tile's page) are read with scalar loads one
   // chunk ahead of the rows that need them, so the lookup is off the loads' issue path.
@@ -325,37 +328,71 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   };
 
   Rows<RK, RV, TPC> ra, rb;
-  u32x4 tb[TPT];
   u32x4* tab0 = lds;
   u32x4* tab1 = lds + TAB_CHUNK;
+#if LLA_FOLD_TAB_DMA
+  // The chunk's table is TPC * NKS blocks of 1 KiB (one MFMA fragment each), contiguous in
+  // the table for chunks inside the context; each wave moves its share of the blocks with
+  // direct-to-LDS loads (lane l: bytes 16 l .. 16 l + 15 of a block). The loads are
+  // complete once the barrier that follows them has been passed (__syncthreads waits for
+  // this wave's loads, and every wave reaches it).
+  constexpr int TAB_BLOCKS = TPC * NKS;
+  constexpr int NBW = (TAB_BLOCKS + HPW - 1) / HPW;  // blocks per wave (surplus ones repeat)
+  auto issue_tab = [&](int c, u32x4* dst) {
+    const int tile0 = (s0 >> 4) + c * TPC;
+#pragma unroll
+    for (int k = 0; k < NBW; ++k) {
+      const int blk = min(wave + HPW * k, TAB_BLOCKS - 1);
+      const int tile = min(tile0 + blk / NKS, tile_max);
+      const char* src = reinterpret_cast<const char*>(tab_g) +
+                        (static_cast<size_t>(tile) * NKS + blk % NKS) * 1024 + lane * 16;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)(dst + blk * 64), 16, 0, 0);
+    }
+  };
+#else
+  u32x4 tb[TPT];
+#endif
+  u32x4* tab_next = tab1;  // where load_chunk puts the table of the chunk it loads
   auto load_chunk = [&](Rows<RK, RV, TPC>& R, int c, const Pages& P) {
     const int tile0 = (s0 >> 4) + c * TPC;
     const int tok0 = s0 + c * TPC * 16;
+#if LLA_FOLD_TAB_DMA
+    issue_tab(c, tab_next);
+#endif
     if (c < nfull) {
+#if !LLA_FOLD_TAB_DMA
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
         const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
         tb[k] = tab_g[static_cast<size_t>(tile0) * NKS * 64 + u];
       }
+#endif
       if constexpr (PAGED) load_paged(R, P, tile0, tok0, std::false_type{});
       else load_rows<false, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
     } else {
+#if !LLA_FOLD_TAB_DMA
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
         const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
         const int tile = min(tile0 + u / (NKS * 64), tile_max);
         tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];
       }
+#endif
       if constexpr (PAGED) load_paged(R, P, tile0, tok0, std::true_type{});
       else load_rows<true, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
     }
   };
   auto store_tab = [&](u32x4* dst) {
+#if LLA_FOLD_TAB_DMA
+    (void)dst;  // the direct-to-LDS loads wrote it
+#else
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       const int u = k * NTHR + static_cast<int>(threadIdx.x);
       if (kTabEven || u < TAB_CHUNK) dst[u] = tb[k];
     }
+#endif
   };
   auto compute = [&](int c, const Rows<RK, RV, TPC>& R, const u32x4* tcur) {
     if (c < nfull) compute_chunk(c, R, tcur, std::true_type{});
@@ -368,6 +405,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
     pb = fetch_pages(1);
   }
   if (nchunk > 0) {
+    tab_next = tab0;
     load_chunk(ra, 0, pa);
     store_tab(tab0);
   }
@@ -375,6 +413,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   for (int c = 0; c < nchunk; c += 2) {
     // even chunk: compute from (ra, tab0), prefetch into (rb, tab1)
     const bool more1 = c + 1 < nchunk;
+    tab_next = tab1;
     if (more1) load_chunk(rb, c + 1, pb);
     if constexpr (PAGED) pa = fetch_pages(c + 2);
     compute(c, ra, tab0);
@@ -383,6 +422,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
     if (!more1) break;
     // odd chunk: compute from (rb, tab1), prefetch into (ra, tab0)
     const bool more2 = c + 2 < nchunk;
+    tab_next = tab0;
     if (more2) load_chunk(ra, c + 2, pa);
     if constexpr (PAGED) pb = fetch_pages(c + 3);
     compute(c + 1, rb, tab1);
