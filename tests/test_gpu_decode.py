@@ -295,3 +295,25 @@ def test_fold_and_reconstruct_agree_at_scale():
     err = max_abs(a, b)
     announce(f"fold vs reconstruct over 96 x 16 outputs: max-abs {err:.3e}")
     assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("variant", ["per_head", "lla2d"])
+@pytest.mark.parametrize("H", [4, 6])
+@pytest.mark.parametrize("d,r_k,r_v", [(64, 16, 24), (64, 16, 32), (64, 32, 32), (64, 256, 256),
+                                       (128, 16, 32), (128, 32, 64), (128, 96, 160), (128, 128, 128)])
+def test_bf16_reconstruct_every_shape(d, r_k, r_v, H, variant):
+    """The literal rebuild-then-rotate kernel for bfloat16 caches at every shape it is built
+    for, per head and LLA-2D, with 4 heads per workgroup (H = 4) and one (H = 6), a
+    ragged tail tile, one and three splits, all 4 loops, every output against the oracle.
+    (64, 16, 24) is the one shape whose value-latent slice per lane (6 entries) is read as
+    single dwords."""
+    base = WORKLOADS["lla2d_long" if variant == "lla2d" else "ouro_layer_4x"]
+    w = base.replace(D=1, batch=2, n=77, d=d, r_k=r_k, r_v=r_v, H=H)
+    st = DeviceLatentStore(w, seed=41)
+    for splits in (1, 3):
+        out = st.decode(0, 0, 4, opts=lla.make_opts(splits, RECON))
+        ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n)
+        err = max_abs(f64(out), ref)
+        announce(f"reconstruct {variant} d={d} ranks=({r_k}, {r_v}) H={H} splits={splits}: "
+                 f"{rel_note(err, BF16_TOL)}")
+        assert err <= BF16_TOL
