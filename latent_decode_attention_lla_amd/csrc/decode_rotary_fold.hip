@@ -62,7 +62,7 @@ constexpr float kRescaleSlack = 8.0f;
 #define LLA_FOLD_WAVES_PER_EU 0  // 0: let the compiler choose
 #endif
 #ifndef LLA_FOLD_TAB_DMA
-#define LLA_FOLD_TAB_DMA 1      // 1: cos/sin tiles go straight to LDS (direct-to-LDS loads)
+#define LLA_FOLD_TAB_DMA 1      // 1: dense caches' cos/sin tiles go straight to LDS
 #endif
 
 template <typename V>
@@ -295,7 +295,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   };
 
   // Two row buffers used in turn: chunk c computes from one while chunk c + 1 loads into
-  // the other; the table of chunk c + 1 goes straight into the other LDS half.
+  // the other; the table of chunk c + 1 goes into the other LDS half.
   // Paged rows: the pages of a chunk's tiles (uniform across the workgroup; rows clamped to
   // the context's last token lie in the last tile's page) are read with scalar loads one
   // chunk ahead of the rows that need them, so the lookup is off the loads' issue path.
@@ -330,12 +330,14 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   Rows<RK, RV, TPC> ra, rb;
   u32x4* tab0 = lds;
   u32x4* tab1 = lds + TAB_CHUNK;
-#if LLA_FOLD_TAB_DMA
-  // The chunk's table is TPC * NKS blocks of 1 KiB (one MFMA fragment each), contiguous in
-  // the table for chunks inside the context; each wave moves its share of the blocks with
-  // direct-to-LDS loads (lane l: bytes 16 l .. 16 l + 15 of a block). The loads are
-  // complete once the barrier that follows them has been passed (__syncthreads waits for
-  // this wave's loads, and every wave reaches it).
+  // Dense caches: the chunk's table is TPC * NKS blocks of 1 KiB (one MFMA fragment each),
+  // contiguous in the table for chunks inside the context; each wave moves its share of the
+  // blocks with direct-to-LDS loads (lane l: bytes 16 l .. 16 l + 15 of a block). The loads
+  // are complete once the barrier that follows them has been passed (__syncthreads waits
+  // for this wave's loads, and every wave reaches it). Paged caches stage the table through
+  // registers (measured faster there: the transfers then do not queue behind the
+  // page-dependent row loads).
+  constexpr bool kTabDma = LLA_FOLD_TAB_DMA && !PAGED;
   constexpr int TAB_BLOCKS = TPC * NKS;
   constexpr int NBW = (TAB_BLOCKS + HPW - 1) / HPW;  // blocks per wave (surplus ones repeat)
   auto issue_tab = [&](int c, u32x4* dst) {
@@ -350,49 +352,43 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
                                        (void __attribute__((address_space(3)))*)(dst + blk * 64), 16, 0, 0);
     }
   };
-#else
-  u32x4 tb[TPT];
-#endif
+  u32x4 tb[kTabDma ? 1 : TPT];
   u32x4* tab_next = tab1;  // where load_chunk puts the table of the chunk it loads
   auto load_chunk = [&](Rows<RK, RV, TPC>& R, int c, const Pages& P) {
     const int tile0 = (s0 >> 4) + c * TPC;
     const int tok0 = s0 + c * TPC * 16;
-#if LLA_FOLD_TAB_DMA
-    issue_tab(c, tab_next);
-#endif
+    if constexpr (kTabDma) issue_tab(c, tab_next);
     if (c < nfull) {
-#if !LLA_FOLD_TAB_DMA
+      if constexpr (!kTabDma) {
 #pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
-        tb[k] = tab_g[static_cast<size_t>(tile0) * NKS * 64 + u];
+        for (int k = 0; k < TPT; ++k) {
+          const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
+          tb[k] = tab_g[static_cast<size_t>(tile0) * NKS * 64 + u];
+        }
       }
-#endif
       if constexpr (PAGED) load_paged(R, P, tile0, tok0, std::false_type{});
       else load_rows<false, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
     } else {
-#if !LLA_FOLD_TAB_DMA
+      if constexpr (!kTabDma) {
 #pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
-        const int tile = min(tile0 + u / (NKS * 64), tile_max);
-        tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];
+        for (int k = 0; k < TPT; ++k) {
+          const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
+          const int tile = min(tile0 + u / (NKS * 64), tile_max);
+          tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];
+        }
       }
-#endif
       if constexpr (PAGED) load_paged(R, P, tile0, tok0, std::true_type{});
       else load_rows<true, RK, RV, TPC>(R, ck, cv, tok0, s1, lo, hi);
     }
   };
   auto store_tab = [&](u32x4* dst) {
-#if LLA_FOLD_TAB_DMA
-    (void)dst;  // the direct-to-LDS loads wrote it
-#else
+    if constexpr (!kTabDma) {
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int u = k * NTHR + static_cast<int>(threadIdx.x);
-      if (kTabEven || u < TAB_CHUNK) dst[u] = tb[k];
+      for (int k = 0; k < TPT; ++k) {
+        const int u = k * NTHR + static_cast<int>(threadIdx.x);
+        if (kTabEven || u < TAB_CHUNK) dst[u] = tb[k];
+      }
     }
-#endif
   };
   auto compute = [&](int c, const Rows<RK, RV, TPC>& R, const u32x4* tcur) {
     if (c < nfull) compute_chunk(c, R, tcur, std::true_type{});
