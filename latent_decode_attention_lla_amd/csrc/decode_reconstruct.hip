@@ -193,6 +193,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #ifndef LLA_RECON_TPC16
 #define LLA_RECON_TPC16 4  // 16-token tiles per chunk for (d, r_k, r_v) = (128, 16, 32)
 #endif
+#ifndef LLA_RECON_WAVES_PER_EU
+#define LLA_RECON_WAVES_PER_EU 0  // 0: let the compiler choose
+#endif
+#ifndef LLA_RECON_TAB_DMA
+#define LLA_RECON_TAB_DMA 1  // 1: dense caches' cos/sin tiles go straight to LDS
+#endif
 #ifndef LLA_RECON_NT
 #define LLA_RECON_NT 1  // 1: stream cache rows with non-temporal loads
 #endif
@@ -255,7 +261,11 @@ __device__ __forceinline__ void load_recon_rows(ReconRows<NK, E, VS, TPC>& R, in
 }
 
 template <int D, int RK, int RV, int HPW, int TPC, bool PAGED>
-__global__ __launch_bounds__(64 * HPW) void decode_reconstruct_bf16_kernel(DecodeArgs a, PageArgs pg) {
+__global__ __launch_bounds__(64 * HPW)
+#if LLA_RECON_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(LLA_RECON_WAVES_PER_EU)))
+#endif
+void decode_reconstruct_bf16_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int KS = KStep<bf16_t, RK>::value;
   using M = Mfma<bf16_t, KS>;
   constexpr int E = M::E;
@@ -435,34 +445,62 @@ __global__ __launch_bounds__(64 * HPW) void decode_reconstruct_bf16_kernel(Decod
   };
 
   Rows ra, rb;
-  u32x4 tb[TPT];
   u32x4* tab0 = lds;
   u32x4* tab1 = lds + TAB_CHUNK;
+  // Dense caches: the chunk's table (TPC * NKS fragment blocks of 1 KiB, contiguous for
+  // chunks inside the context) goes to LDS by direct-to-LDS loads dealt to the waves (lane
+  // l: bytes 16 l .. 16 l + 15 of a block), complete once the barrier that follows them has
+  // been passed. Paged caches stage it through registers (the transfers would queue behind
+  // the page-dependent row loads).
+  constexpr bool kTabDma = LLA_RECON_TAB_DMA && !PAGED;
+  constexpr int TAB_BLOCKS = TPC * NKS;
+  constexpr int NBW = (TAB_BLOCKS + HPW - 1) / HPW;  // blocks per wave (surplus ones repeat)
+  auto issue_tab = [&](int c, u32x4* dst) {
+    const int tile0 = (s0 >> 4) + c * TPC;
+#pragma unroll
+    for (int k = 0; k < NBW; ++k) {
+      const int blk = min(wave + HPW * k, TAB_BLOCKS - 1);
+      const int tile = min(tile0 + blk / NKS, tile_max);
+      const char* src = reinterpret_cast<const char*>(tab_g) +
+                        (static_cast<size_t>(tile) * NKS + blk % NKS) * 1024 + lane * 16;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)(dst + blk * 64), 16, 0, 0);
+    }
+  };
+  u32x4 tb[kTabDma ? 1 : TPT];
+  u32x4* tab_next = tab1;  // where load_chunk puts the table of the chunk it loads
   auto load_chunk = [&](Rows& R, int c, const Pages& P) {
     const int tile0 = (s0 >> 4) + c * TPC;
     const int tok0 = s0 + c * TPC * 16;
+    if constexpr (kTabDma) issue_tab(c, tab_next);
     if (c < nfull) {
+      if constexpr (!kTabDma) {
 #pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
-        tb[k] = tab_g[static_cast<size_t>(tile0) * NKS * 64 + u];
+        for (int k = 0; k < TPT; ++k) {
+          const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
+          tb[k] = tab_g[static_cast<size_t>(tile0) * NKS * 64 + u];
+        }
       }
       load_rows(R, P, tile0, tok0, std::false_type{});
     } else {
+      if constexpr (!kTabDma) {
 #pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
-        const int tile = min(tile0 + u / (NKS * 64), tile_max);
-        tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];
+        for (int k = 0; k < TPT; ++k) {
+          const int u = min(k * NTHR + static_cast<int>(threadIdx.x), TAB_CHUNK - 1);
+          const int tile = min(tile0 + u / (NKS * 64), tile_max);
+          tb[k] = tab_g[static_cast<size_t>(tile) * NKS * 64 + (u % (NKS * 64))];
+        }
       }
       load_rows(R, P, tile0, tok0, std::true_type{});
     }
   };
   auto store_tab = [&](u32x4* dst) {
+    if constexpr (!kTabDma) {
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int u = k * NTHR + static_cast<int>(threadIdx.x);
-      if (kTabEven || u < TAB_CHUNK) dst[u] = tb[k];
+      for (int k = 0; k < TPT; ++k) {
+        const int u = k * NTHR + static_cast<int>(threadIdx.x);
+        if (kTabEven || u < TAB_CHUNK) dst[u] = tb[k];
+      }
     }
   };
   auto compute = [&](int c, const Rows& R, const u32x4* tcur) {
@@ -476,6 +514,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_reconstruct_bf16_kernel(Decod
     pb = fetch_pages(1);
   }
   if (nchunk > 0) {
+    tab_next = tab0;
     load_chunk(ra, 0, pa);
     store_tab(tab0);
   }
@@ -483,6 +522,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_reconstruct_bf16_kernel(Decod
   for (int c = 0; c < nchunk; c += 2) {
     // even chunk: compute from (ra, tab0), prefetch into (rb, tab1)
     const bool more1 = c + 1 < nchunk;
+    tab_next = tab1;
     if (more1) load_chunk(rb, c + 1, pb);
     if constexpr (PAGED) pa = fetch_pages(c + 2);
     compute(c, ra, tab0);
@@ -491,6 +531,7 @@ __global__ __launch_bounds__(64 * HPW) void decode_reconstruct_bf16_kernel(Decod
     if (!more1) break;
     // odd chunk: compute from (rb, tab1), prefetch into (ra, tab0)
     const bool more2 = c + 2 < nchunk;
+    tab_next = tab0;
     if (more2) load_chunk(ra, c + 2, pa);
     if constexpr (PAGED) pb = fetch_pages(c + 3);
     compute(c + 1, rb, tab1);
