@@ -18,7 +18,8 @@
 // with weights rounded to bfloat16.
 //
 // Workgroup: HG heads (one wave each) of one (sequence, loop, split). Cache rows and cos/sin
-// tiles stream through a direct-to-LDS ring of kStages stages, kAhead tiles ahead. Each wave
+// tiles stream through a direct-to-LDS ring of kStages stages, kAhead tiles ahead (5 with 8
+// heads, one workgroup per CU; 3 with 4 heads, so that two workgroups share a CU). Each wave
 // runs its tiles as a three-deep software pipeline, one workgroup barrier per tile:
 //   iteration c:  score MFMAs and latent dot of tile c (operands read in iteration c - 1)
 //                 softmax of tile c - 1 (its score carried in a register), P tile c - 1 out
@@ -48,12 +49,18 @@ constexpr float kMaxInit = -1.0e30f;   // finite stand-in for -inf: the first va
 constexpr float kRescaleSlack = 8.0f;  // raise the running max only when exceeded by 2^8
 constexpr int kXcds = 8;
 #ifndef LLA_2D_AHEAD
-#define LLA_2D_AHEAD 5
+#define LLA_2D_AHEAD 5      // ring lookahead with 8 heads per workgroup (one per CU)
 #endif
-constexpr int kAhead = LLA_2D_AHEAD;     // tile c + kAhead is requested in iteration c
-// tiles c - 2 .. c + kAhead live in iteration c; an even count keeps the P buffer parity
-// a function of the stage index
-constexpr int kStages = (kAhead + 4) / 2 * 2;
+#ifndef LLA_2D_AHEAD_SMALL
+#define LLA_2D_AHEAD_SMALL 3  // with fewer heads per workgroup (two workgroups per CU)
+#endif
+// tile c + ahead is requested in iteration c; tiles c - 2 .. c + ahead live in iteration c,
+// and an even stage count keeps the P buffer parity a function of the stage index
+template <int HG>
+struct Ring {
+  static constexpr int kAhead = HG >= 8 ? LLA_2D_AHEAD : LLA_2D_AHEAD_SMALL;
+  static constexpr int kStages = (kAhead + 4) / 2 * 2;
+};
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -137,19 +144,26 @@ __global__ __launch_bounds__(64 * HG) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_lla2d_kernel(DecodeArgs a, PageArgs pg) {
   using S = Shape<D, RK, RV, HG>;
   constexpr int NW = S::NW, NKS = S::NKS, NCK = S::NCK, NT = S::NT, NRT = S::NRT, VT = S::VT;
+  constexpr int kAhead = Ring<HG>::kAhead;
+  constexpr int kStages = Ring<HG>::kStages;
   constexpr int RING_UNITS = kStages * S::STAGE_UNITS;
+  // The W_up transpose staging of the prologue sits in ring stages kAhead.. when it fits
+  // there (the prologue fills stages 0 .. kAhead - 1 only, and the first barrier of the
+  // tile loop comes before any load into stage kAhead); else after the ring.
+  constexpr bool kStagingInRing = (kStages - kAhead) * S::STAGE_UNITS >= S::STAGING_UNITS;
+  constexpr int STAGING_EXTRA = kStagingInRing ? 0 : S::STAGING_UNITS;
   constexpr int P_UNITS = (2 * 16 * 16 + 64) * 2 / 16;  // two P tiles of bf16, 64 spare slots
   constexpr int AL_UNITS = (2 * 16 + 64) * 4 / 16;       // two rows of rescale factors, spares
   constexpr int PAGE_UNITS = PAGED ? kMaxSplitPages * 4 / 16 : 0;
-  constexpr int LDS_UNITS = RING_UNITS + S::STAGING_UNITS + P_UNITS + AL_UNITS + PAGE_UNITS;
+  constexpr int LDS_UNITS = RING_UNITS + STAGING_EXTRA + P_UNITS + AL_UNITS + PAGE_UNITS;
   static_assert(HG * RV + 2 * HG <= RING_UNITS * 4, "epilogue staging fits the ring");
 
   __shared__ u32x4 lds[LDS_UNITS];
-  uint16_t* staging = reinterpret_cast<uint16_t*>(lds + RING_UNITS);
+  uint16_t* staging = reinterpret_cast<uint16_t*>(lds + (kStagingInRing ? kAhead * S::STAGE_UNITS : RING_UNITS));
   // P tiles [2][token / 4][16 heads][token % 4]: a lane's 4 weights of one head are 8 bytes
-  uint16_t* ptile = reinterpret_cast<uint16_t*>(lds + RING_UNITS + S::STAGING_UNITS);
-  float* alpha_buf = reinterpret_cast<float*>(lds + RING_UNITS + S::STAGING_UNITS + P_UNITS);  // [2][16]
-  int* split_pages = reinterpret_cast<int*>(lds + RING_UNITS + S::STAGING_UNITS + P_UNITS + AL_UNITS);
+  uint16_t* ptile = reinterpret_cast<uint16_t*>(lds + RING_UNITS + STAGING_EXTRA);
+  float* alpha_buf = reinterpret_cast<float*>(lds + RING_UNITS + STAGING_EXTRA + P_UNITS);  // [2][16]
+  int* split_pages = reinterpret_cast<int*>(lds + RING_UNITS + STAGING_EXTRA + P_UNITS + AL_UNITS);
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
