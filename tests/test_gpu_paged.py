@@ -40,6 +40,8 @@ def _oracle_paged(st, layer, loop_begin, loop_count, seqs, n_ctx, ctx_lens=None)
     ("capacity_21x", {}, lla.LLA_PATH_AUTO, 3),
     ("capacity_21x", {"r_k": 32, "r_v": 64}, lla.LLA_PATH_AUTO, 0),
     ("capacity_21x", {}, lla.LLA_PATH_RECONSTRUCT, 0),
+    ("capacity_21x", {"H": 6}, lla.LLA_PATH_RECONSTRUCT, 2),  # one head per workgroup
+    ("capacity_21x", {"H": 6, "d": 64, "r_v": 24}, lla.LLA_PATH_RECONSTRUCT, 0),
     ("ouro_layer_4x", {}, lla.LLA_PATH_AUTO, 2),            # wide fold, a pair of waves per head
     ("ouro_layer_4x", {}, lla.LLA_PATH_AUTO, 0),
     ("ouro_layer_4x", {}, lla.LLA_PATH_RECONSTRUCT, 2),
