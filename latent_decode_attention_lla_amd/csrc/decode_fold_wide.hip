@@ -14,8 +14,8 @@
 // Per tile of 16 tokens both halves compute their partial scores, swap them through LDS,
 // and then run the same online softmax on the full scores (so both hold identical maxima
 // and sums) while accumulating their own half of the value latent. Cache rows and cos/sin
-// tiles reach LDS through direct-to-LDS loads issued LLA_WIDE_STAGES - 1 tiles ahead, so
-// the prefetch depth costs no registers.
+// tiles reach LDS through direct-to-LDS loads issued two or three tiles ahead (as deep as
+// two workgroups per CU allow), so the prefetch depth costs no registers.
 //
 // LLA-2D (Section 3, "The LLA-2D variant"): every head reads the same latent plane of its
 // sequence, and mu_t of head h is the (t, h) slice of the stacked mean. Workgroups that
@@ -37,8 +37,8 @@ constexpr float kMaxInit = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kXcds = 8;
 
-#ifndef LLA_WIDE_STAGES
-#define LLA_WIDE_STAGES 3  // depth of the direct-to-LDS ring (tiles in flight + 1)
+#ifndef LLA_WIDE_MAX_STAGES
+#define LLA_WIDE_MAX_STAGES 4  // deepest direct-to-LDS ring (tiles in flight + 1)
 #endif
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -74,14 +74,21 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int VSH = RVH / 4;            // value entries per lane
   constexpr int WT_STRIDE = D + 8;
   constexpr int STAGE_UNITS = NH * HPW * 16 * WT_STRIDE * 2 / 16;
-  constexpr int XCH_FLOATS = NH * HPW * 16;  // partial scores of one tile
-  constexpr int RING_UNITS =
-      LLA_WIDE_STAGES * ((SHARED ? 1 : HPW) * (((16 * (RK / 8 + 1) + 63) / 64) + ((16 * (RV / 8 + 1) + 63) / 64)) + D / 32) * 64;
-  constexpr int LDS_UNITS_RING = RING_UNITS + (XCH_FLOATS + 3) / 4;
+  constexpr int NIK = RK / 32, NIV = RV / 32;         // 1 KiB blocks of a plane's 16 rows
+  constexpr int NPL = SHARED ? 1 : HPW;               // latent planes per stage
+  constexpr int STAGE_BLOCKS = NPL * (NIK + NIV) + NKS;  // 1 KiB blocks
+  // Per head, a pair's partial scores are swapped through its own key rows of the stage
+  // being read; LLA-2D heads share the plane, so there they get a region of their own.
+  constexpr bool kXchInStage = !SHARED && NH == 2;
+  constexpr int XCH_UNITS = NH == 2 && !kXchInStage ? (NH * HPW * 16 + 3) / 4 : 0;
   constexpr int PAGE_UNITS = PAGED ? kMaxSplitPages * 4 / 16 : 0;  // the split's page indices
+  // Ring depth: as many stages as keep the workgroup within 80 KiB (two per CU), at least 3.
+  constexpr int NB_FIT = (80 * 1024 / 16 - XCH_UNITS - PAGE_UNITS) / (STAGE_BLOCKS * 64);
+  constexpr int NB = NB_FIT < 3 ? 3 : (NB_FIT > LLA_WIDE_MAX_STAGES ? LLA_WIDE_MAX_STAGES : NB_FIT);
+  constexpr int LDS_UNITS_RING = NB * STAGE_BLOCKS * 64 + XCH_UNITS;
   constexpr int LDS_UNITS = LDS_UNITS_RING + PAGE_UNITS > STAGE_UNITS ? LDS_UNITS_RING + PAGE_UNITS
                                                                       : STAGE_UNITS;
-  static_assert(RK % 16 == 0 && RV % 16 == 0 && VSH % 4 == 0 && D % 32 == 0, "shape");
+  static_assert(RK % 32 == 0 && RV % 32 == 0 && VSH % 4 == 0 && D % 32 == 0, "shape");
 
   __shared__ u32x4 lds[LDS_UNITS];
 
@@ -134,27 +141,25 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
   const int nfull = ntok >> 4;  // tiles whose 16 tokens all lie in the context
 
   // ---- the ring: per stage one tile of 16 tokens --------------------------------------
-  // For every latent plane of the stage a key region (16 rows of KSP 16-byte slots: the
-  // row's KSL slots plus one padding slot, so that the 16 rows start in different LDS
-  // banks) and a value region (VSP slots per row), then the NKS 1 KiB blocks of the
-  // cos/sin tile. Every region is filled by 1 KiB direct-to-LDS loads
-  // (global_load_lds_dwordx4: lane l writes bytes 16 l .. 16 l + 15 of the block).
-  constexpr int KSL = RK / 8, KSP = KSL + 1;
-  constexpr int VSL = RV / 8, VSP = VSL + 1;
-  constexpr int NIK = (16 * KSP + 63) / 64;
-  constexpr int NIV = (16 * VSP + 63) / 64;
-  constexpr int NPL = SHARED ? 1 : HPW;
+  // For every latent plane of the stage a key region (16 rows of KSL 16-byte slots) and a
+  // value region (VSL slots per row), then the NKS 1 KiB blocks of the cos/sin tile. Every
+  // region is filled by 1 KiB direct-to-LDS loads (global_load_lds_dwordx4: lane l writes
+  // bytes 16 l .. 16 l + 15 of the block). Row r keeps its slots XOR-permuted within each
+  // aligned group of four by (r >> 2) & 3: the rows are 64-byte multiples long, so without
+  // it rows r and r + 4 would start in the same bank, and with it the 16 rows of a read
+  // cover all 64 banks once.
+  constexpr int KSL = RK / 8;
+  constexpr int VSL = RV / 8;
   constexpr int PLB = NIK + NIV;                    // 1 KiB blocks per plane
-  constexpr int STAGE_BLOCKS = NPL * PLB + NKS;
+  static_assert(16 * KSL == 64 * NIK && 16 * VSL == 64 * NIV, "ring shape");
   constexpr int NW = NH * HPW;
   constexpr int NIW = (STAGE_BLOCKS + NW - 1) / NW;  // blocks each wave loads per stage
-  constexpr int NB = LLA_WIDE_STAGES;
   static_assert(NB >= 2 && (NB - 2) * NIW <= 63, "vmcnt range");
   // the W_up staging fits the ring's last stage, so the first tiles can be requested first
   constexpr bool kEarly = NB >= 3 && STAGE_UNITS <= STAGE_BLOCKS * 64;
-  static_assert(NB * STAGE_BLOCKS * 64 + (XCH_FLOATS + 3) / 4 <= LDS_UNITS_RING, "ring size");
+  static_assert(LDS_UNITS_RING + PAGE_UNITS <= 80 * 1024 / 16 || NB == 3, "ring size");
   u32x4* ring = lds;
-  float* xch = reinterpret_cast<float*>(lds + NB * STAGE_BLOCKS * 64);  // [wave][16]
+  float* xch = reinterpret_cast<float*>(lds + NB * STAGE_BLOCKS * 64);  // [wave][16] (LLA-2D)
 
   // Per block slot of this wave: the block index in the stage, this lane's source address
   // for the next tile to be issued, and the byte step from one tile to the next. Tiles
@@ -181,10 +186,10 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
     } else {
       const int pl = bi / PLB, r = bi - pl * PLB;
       const bool isk = r < NIK;
-      const int sp = isk ? KSP : VSP, sl = isk ? KSL : VSL;
-      const int slot = (isk ? r : r - NIK) * 64 + lane;
-      const int row = min(slot / sp, 15);
-      const int col = min(slot % sp, sl - 1) * 16;
+      const int sl = isk ? KSL : VSL;
+      const int slot = (isk ? r : r - NIK) * 64 + lane;  // physical slot in the region
+      const int row = slot / sl;
+      const int col = ((slot % sl) ^ ((row >> 2) & 3)) * 16;  // its row's logical slot
       // dense: plane pl's rows start poff rows after this head's; paged: head pl's rows
       // of a page start hrow rows into it
       const size_t poff = PAGED ? static_cast<size_t>(SHARED ? 0 : hg * HPW + pl) * kPage
@@ -348,6 +353,8 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
   for (int e = 0; e < VSH; ++e) acc[e] = 0.f;
 
   const int mypl = SHARED ? 0 : hw;
+  const int swz = ((lo >> 2) & 3) << 4;  // byte XOR of this lane's token row (row lo)
+  static_assert(!kXchInStage || 2 * NR0 < KSL, "half 1 owns key slots for the exchange");
 
   // The tile loop, compiled once per half so that which row tiles, latent rows and value
   // entries a wave owns are compile-time constants (no branches inside the loop).
@@ -363,11 +370,27 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
       // that every wave is done with tile c - 1, whose stage the next issue overwrites
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * NIW) : "memory");
       ring_barrier();
-      issue(c + NB - 1);
       const u32x4* st = ring + (c % NB) * STAGE_BLOCKS * 64;
       const char* kreg = reinterpret_cast<const char*>(st + (mypl * PLB) * 64);
       const char* vreg = reinterpret_cast<const char*>(st + (mypl * PLB + NIK) * 64);
       const u32x4* treg = st + (NPL * PLB) * 64;
+      const char* krow = kreg + lo * (KSL * 16);
+      const char* vrow = vreg + lo * (VSL * 16);
+
+      // Every LDS operand of the tile is requested at once, before the next tile's loads
+      // are issued, so that their latencies overlap instead of adding up.
+      f16x8_t bfr[NKS];
+      u32x2 kw[NCKh > 0 ? NCKh : 1];
+      u32x2 vw[VSH / 4];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) bfr[ks] = __builtin_bit_cast(f16x8_t, treg[ks * 64 + lane]);
+#pragma unroll
+      for (int m = 0; m < NCKh; ++m)
+        kw[m] = *reinterpret_cast<const u32x2*>(krow + ((32 * (KT0 + m) + 8 * hi) ^ swz));
+#pragma unroll
+      for (int m = 0; m < VSH / 4; ++m)
+        vw[m] = *reinterpret_cast<const u32x2*>(vrow + ((2 * (HALF * RVH + hi * VSH) + 8 * m) ^ swz));
+      issue(c + NB - 1);
 
       // (1) this half's partial score for the 16 tokens, published to LDS
       f32x4 g[NT];
@@ -375,25 +398,33 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
       for (int i = 0; i < NT; ++i) g[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const f16x8_t bf = __builtin_bit_cast(f16x8_t, treg[ks * 64 + lane]);
 #pragma unroll
-        for (int i = 0; i < NT; ++i) g[i] = mfma_f16(mf[i][ks], bf, g[i]);
+        for (int i = 0; i < NT; ++i) g[i] = mfma_f16(mf[i][ks], bfr[ks], g[i]);
       }
       // element 0 of the mean tile: the mean row for hi = 0, an all-zero padding row of
       // M^T (so exactly 0) for the other lane groups
       float pp = MEAN ? g[NT - 1][0] : 0.f;
 #pragma unroll
       for (int m = 0; m < NCKh; ++m) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(kreg + lo * (KSP * 16) + 32 * (KT0 + m) + 8 * hi);
+        const u32x2 w = kw[m];
         pp += __uint_as_float(w.x << 16) * g[m][0] + __uint_as_float(w.x & 0xffff0000u) * g[m][1] +
               __uint_as_float(w.y << 16) * g[m][2] + __uint_as_float(w.y & 0xffff0000u) * g[m][3];
       }
       const float part = sum_xor32(sum_xor16(pp));
       float full = part;
       if constexpr (NH == 2) {
-        if (hi == 0) xch[wave * 16 + lo] = part;
+        // Per head the partial goes to logical slot 16 HALF of key rows 0..3 (lane lo:
+        // float lo & 3 of row lo >> 2), cells only this half reads, which it has read for
+        // this tile; the stage is not refilled before the next tile's barrier.
+        float* mine = kXchInStage ? reinterpret_cast<float*>(const_cast<char*>(kreg) + (lo >> 2) * (KSL * 16) +
+                                                             16 * HALF * NR0 * 2 + 4 * (lo & 3))
+                                  : xch + wave * 16 + lo;
+        const float* theirs = kXchInStage ? reinterpret_cast<const float*>(kreg + (lo >> 2) * (KSL * 16) +
+                                                                           16 * (1 - HALF) * NR0 * 2 + 4 * (lo & 3))
+                                          : xch + (wave ^ 1) * 16 + lo;
+        if (hi == 0) *mine = part;
         ring_barrier();
-        const float other = xch[(wave ^ 1) * 16 + lo];
+        const float other = *theirs;
         full = HALF == 0 ? part + other : other + part;  // same order in both halves
       }
 
@@ -410,10 +441,9 @@ void decode_fold_wide_kernel(DecodeArgs a, PageArgs pg) {
       }
       const float p = fast_exp2(s - m_run);
       l_run += p;
-      const char* vp = vreg + lo * (VSP * 16) + 2 * (HALF * RVH + hi * VSH);
 #pragma unroll
       for (int m = 0; m < VSH / 4; ++m) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vp + 8 * m);
+        const u32x2 w = vw[m];
         acc[4 * m + 0] += p * __uint_as_float(w.x << 16);
         acc[4 * m + 1] += p * __uint_as_float(w.x & 0xffff0000u);
         acc[4 * m + 2] += p * __uint_as_float(w.y << 16);
@@ -513,7 +543,8 @@ void launch(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
 }  // namespace
 
 // Per shape: (d, r_k, r_v, heads per workgroup per head, heads per workgroup LLA-2D).
-// Ring depth is LLA_WIDE_STAGES; the LDS of a workgroup must stay within 160 KiB.
+// The ring takes as many stages (3 .. LLA_WIDE_MAX_STAGES) as keep a workgroup within
+// 80 KiB of LDS.
 #ifndef LLA_WIDE_HPW_PH
 #define LLA_WIDE_HPW_PH 2
 #endif
