@@ -187,7 +187,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void reconstruct_kernel(ReconArgs a
             pk[e] = static_cast<uint32_t>(f32_to_bf16_rne(v[2 * e])) |
                     (static_cast<uint32_t>(f32_to_bf16_rne(v[2 * e + 1])) << 16);
         }
-        *reinterpret_cast<u32x4*>(out + static_cast<size_t>(tk) * D + d0) = pk;
+        // written once and read by a later kernel: stream it past the caches
+        __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(out + static_cast<size_t>(tk) * D + d0));
       }
     }
     lds_wait();  // the next tile's writes into the staging tile come after these reads
