@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
 # on one of them depends on its file only, not on the other decode kernels'.
 _DECODE_KERNEL_FILES = {"decode_rotary_fold": "decode_rotary_fold.hip",
                         "decode_fold_wide": "decode_fold_wide.hip",
+                        "decode_fold_head": "decode_fold_wide.hip",
                         "decode_lla2d": "decode_lla2d.hip",
                         "decode_reconstruct": "decode_reconstruct.hip"}
 

@@ -222,6 +222,22 @@ def test_lla2d_ragged_poisoned(path, H):
         assert max_abs(got[:3], ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("H", [2, 6])
+@pytest.mark.parametrize("d,r_k,r_v", [(128, 96, 160), (128, 64, 64), (128, 128, 128), (64, 256, 256)])
+def test_bf16_wide_fold_two_heads_per_workgroup(d, r_k, r_v, H):
+    """The per-head wide fold with a head count that is not a multiple of 4, so that its
+    workgroups take 2 heads instead of 4: every shape, a ragged tail tile, one and three
+    splits, all 4 loops, every output against the oracle."""
+    w = WORKLOADS["ouro_layer_4x"].replace(D=1, batch=2, n=93, d=d, r_k=r_k, r_v=r_v, H=H)
+    st = DeviceLatentStore(w, seed=23)
+    for splits in (1, 3):
+        out = st.decode(0, 0, 4, opts=lla.make_opts(splits, FOLD))
+        ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n)
+        err = max_abs(f64(out), ref)
+        announce(f"wide fold H={H} d={d} ranks=({r_k}, {r_v}) splits={splits}: {rel_note(err, BF16_TOL)}")
+        assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("variant", ["per_head", "lla2d"])
 @pytest.mark.parametrize("d,r_k,r_v", [(128, 64, 64), (128, 128, 128), (64, 256, 256)])
 def test_bf16_table8_ranks_every_output(d, r_k, r_v, variant):

@@ -55,6 +55,8 @@ def _oracle_paged(st, layer, loop_begin, loop_count, seqs, n_ctx, ctx_lens=None)
     ("lla2d_long", {"r_k": 64, "r_v": 64}, lla.LLA_PATH_AUTO, 2),     # LLA-2D kernel, other ranks
     ("lla2d_long", {"r_k": 128, "r_v": 128}, lla.LLA_PATH_AUTO, 0),   # wide fold, shared plane
     ("ouro_layer_4x", {"r_k": 64, "r_v": 64}, lla.LLA_PATH_AUTO, 3),  # wide fold, per head
+    ("ouro_layer_4x", {"H": 6}, lla.LLA_PATH_AUTO, 2),      # wide fold, 2 heads per workgroup
+    ("ouro_layer_4x", {"H": 8}, lla.LLA_PATH_AUTO, 0),      # wide fold, 4 heads per workgroup, 2 groups
 ])
 def test_shuffled_pool_matches_dense_and_oracle(name, over, path, splits):
     """The dense and paged decodes run the same kernel (narrow fold, wide fold or
