@@ -142,7 +142,8 @@ def parse():
                         "(loop by loop, no per-loop K/V stored) or lla_encode of stored captures")
     p.add_argument("--ceiling-gib", type=float, default=0.0,
                    help="time plain streaming passes over buffers of this size (read-only, "
-                        "copy, 4:1 and 1:4 read:write) and print their HBM rates instead")
+                        "copy, 4:1 and 1:4 read:write; per-wave chunks through LDS, registers "
+                        "or both) and print their HBM rates instead")
     p.add_argument("--copy-calibration-gib", type=float, default=0.0,
                    help="only run a plain device copy of this size (for counter scaling)")
     return p.parse_args()
@@ -156,33 +157,38 @@ def stream_ceilings(gib: float):
     from latent_decode_attention_lla_amd import lla
     lla.load()
     n = int(gib * 2**30) // 16
-    n -= n % 4
+    n -= n % (64 * 4 * 512 * 16)  # whole 16-block runs of 1 KiB per wave at 512 workgroups
     src = torch.empty(n * 16, dtype=torch.uint8, device="cuda")
     dst = torch.empty(n * 16, dtype=torch.uint8, device="cuda")
     src.random_(0, 255)
     # (mode, vectors per pass, bytes read, bytes written)
     modes = {"read": (0, n, n * 16, 0), "copy_1to1": (1, n // 2, n // 2 * 16, n // 2 * 16),
              "mix_4to1": (2, n // 4, n * 16, n // 4 * 16), "mix_1to4": (3, n // 4, n // 4 * 16, n * 16)}
+    # per-wave contiguous chunks at 2 workgroups of 4 waves per CU: the same reads through
+    # direct-to-LDS loads, through registers, and half through each
+    wave_modes = {"read_wave_lds": (4, n, n * 16, 0), "read_wave_regs": (5, n, n * 16, 0),
+                  "read_wave_mixed": (6, n, n * 16, 0)}
     res = {}
-    for wg in (1024, 2048, 4096, 8192):
-        for name, (mode, nv, rd, wr) in modes.items():
-            for _ in range(2):
-                lla.lla_stream_ceiling(mode, src, dst, nv, wg)
-            torch.cuda.synchronize()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            reps = 10
-            ev[0].record()
-            for _ in range(reps):
-                lla.lla_stream_ceiling(mode, src, dst, nv, wg)
-            ev[1].record()
-            torch.cuda.synchronize()
-            ms = ev[0].elapsed_time(ev[1]) / reps
-            tbs = (rd + wr) / (ms * 1e-3) / 1e12
-            best = res.get(name)
-            if best is None or tbs > best["tb_per_s"]:
-                res[name] = {"tb_per_s": round(tbs, 3), "ms": round(ms, 4), "workgroups": wg,
-                             "bytes_read": rd, "bytes_written": wr,
-                             "frac_of_8tbs": round(tbs / (HBM_PEAK_GBS / 1e3), 4)}
+    runs = [(wg, m) for wg in (1024, 2048, 4096, 8192) for m in modes.items()]
+    runs += [(512, m) for m in wave_modes.items()]
+    for wg, (name, (mode, nv, rd, wr)) in runs:
+        for _ in range(2):
+            lla.lla_stream_ceiling(mode, src, dst, nv, wg)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        reps = 10
+        ev[0].record()
+        for _ in range(reps):
+            lla.lla_stream_ceiling(mode, src, dst, nv, wg)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        tbs = (rd + wr) / (ms * 1e-3) / 1e12
+        best = res.get(name)
+        if best is None or tbs > best["tb_per_s"]:
+            res[name] = {"tb_per_s": round(tbs, 3), "ms": round(ms, 4), "workgroups": wg,
+                         "bytes_read": rd, "bytes_written": wr,
+                         "frac_of_8tbs": round(tbs / (HBM_PEAK_GBS / 1e3), 4)}
     print(json.dumps({"stream_ceilings": res, "buffer_gib": gib}))
 
 

@@ -1,7 +1,8 @@
 /*
  * lla_stream.h - measurement helper of liblla.so, not part of the method: plain streaming
  * kernels that give the HBM ceilings (a read-only pass, a copy, 4:1 and 1:4 read:write
- * mixes) the latent-store kernels are compared against on the same device.
+ * mixes, and read-only passes through LDS or registers) the latent-store kernels are
+ * compared against on the same device.
  */
 #ifndef LLA_STREAM_H_
 #define LLA_STREAM_H_
@@ -18,9 +19,15 @@ extern "C" {
  *   mode 1: dst[i] = src[i]                                            (1 read : 1 write)
  *   mode 2: dst[i] = src[i] ^ src[i + n] ^ src[i + 2n] ^ src[i + 3n]   (4 reads : 1 write)
  *   mode 3: dst[i + k n] = src[i], k = 0 .. 3                          (1 read : 4 writes)
+ *   modes 4-6: read src[0 .. n) with every wave (4 per workgroup) streaming its own
+ *           contiguous chunk of 1 KiB blocks: mode 4 through a ring of buffer loads to
+ *           LDS, mode 5 through registers, mode 6 half through each; n must split into the
+ *           same whole number of blocks per wave, a multiple of 16 and at least 32, each
+ *           chunk under 2 GiB (else -1); nothing is written unless a checksum of the data
+ *           hits one fixed value (then 16 bytes to dst[0]).
  * src and dst are device pointers, 16-byte aligned, owned by the caller, large enough for
  * the mode (mode 2 reads 4n vectors, mode 3 writes 4n, mode 0 writes `workgroups`).
- * workgroups: 256-thread workgroups of the grid-stride loop.
+ * workgroups: 256-thread workgroups of the grid (a grid-stride loop in modes 0-3).
  * Returns 0, -1 for invalid arguments (nothing enqueued), -4 when the launch failed. */
 int32_t lla_stream_ceiling(int32_t mode, const void* src, void* dst, size_t n_vectors,
                            int32_t workgroups, void* stream);

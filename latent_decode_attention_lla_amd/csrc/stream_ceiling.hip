@@ -1,7 +1,10 @@
 // Plain streaming kernels that measure the HBM ceilings the decode and encode kernels are
 // compared against (gfx950): a read-only pass, a copy (1:1), and 4:1 and 1:4 read:write
-// mixes. Every lane moves 16-byte vectors with a grid-stride loop; nothing here belongs to
-// the method.
+// mixes, each a grid-stride loop moving 16-byte vectors per lane; and read-only passes in
+// which every wave streams its own contiguous chunk in 1 KiB blocks, through a ring of
+// direct-to-LDS loads, through registers, or alternating the two (the access pattern of
+// the decode kernels' rings, to compare the two load paths). Nothing here belongs to the
+// method.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,13 +50,100 @@ __global__ __launch_bounds__(256) void stream_kernel(int mode, const u32x4* __re
   }
 }
 
+// Per-wave chunk streaming (modes 4..6): wave w of the grid reads its own contiguous chunk
+// of bpw 1 KiB blocks in order.
+//   mode 4: buffer loads to LDS into a 16-slot ring per wave, 15 blocks in flight (one
+//           dword of each block is read back from LDS once it has landed)
+//   mode 5: plain loads into a 16-block register ring
+//   mode 6: the first half of the chunk through the LDS ring, the second half through an
+//           8-block register ring, one block of each per step
+template <int MODE>
+__global__ __launch_bounds__(256) void stream_wave_kernel(const u32x4* __restrict__ src, u32x4* dst,
+                                                          size_t bpw) {
+  constexpr int R = 16;
+  __shared__ u32x4 ring[4][R][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t w = static_cast<size_t>(blockIdx.x) * 4 + wave;
+  const u32x4* base = src + w * bpw * 64;
+  uint32_t acc = 0;
+  u32x4 racc = {0u, 0u, 0u, 0u};
+  if constexpr (MODE == 5) {
+    u32x4 buf[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) buf[k] = __builtin_nontemporal_load(base + static_cast<size_t>(k) * 64 + lane);
+    for (size_t i = 0; i < bpw; i += R) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        racc ^= buf[k];
+        const size_t nx = i + R + k;
+        buf[k] = __builtin_nontemporal_load(base + (nx < bpw ? nx : 0) * 64 + lane);
+      }
+    }
+  } else {
+    constexpr int RR = MODE == 6 ? 8 : 0;       // register ring (mode 6)
+    const size_t nl = MODE == 6 ? bpw / 2 : bpw;  // blocks through the LDS ring
+    const u32x4* rbase = base + nl * 64;         // mode 6: the register half
+    const size_t nr = bpw - nl;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4*>(base), 0, static_cast<int>(nl * 1024), 0x00020000);
+    auto issue = [&](size_t j) {
+      const size_t blk = j < nl ? j : 0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&ring[wave][j % R][0],
+                                               16, lane * 16, static_cast<uint32_t>(blk * 1024), 0, 0);
+    };
+    u32x4 buf[RR > 0 ? RR : 1];
+    if constexpr (RR > 0) {
+#pragma unroll
+      for (int k = 0; k < RR; ++k) buf[k] = __builtin_nontemporal_load(rbase + static_cast<size_t>(k) * 64 + lane);
+    }
+    for (int j = 0; j < R - 1; ++j) issue(j);
+    for (size_t j0 = 0; j0 < nl; j0 += 8) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const size_t j = j0 + k;
+        issue(j + R - 1);
+        // at most the later R - 1 ring blocks (and the register ring) outstanding: block j
+        // has landed (the read-back dword only consumes the data)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(R - 1 + RR) : "memory");
+        uint32_t v;
+        const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[wave][j % R][lane]));
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+        acc ^= v;
+        if constexpr (RR > 0) {
+          racc ^= buf[k];
+          const size_t nx = j + RR;
+          buf[k] = __builtin_nontemporal_load(rbase + (nx < nr ? nx : 0) * 64 + lane);
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if ((acc ^ racc.x ^ racc.y ^ racc.z ^ racc.w) == 0x9e3779b9u) dst[0] = racc;  // keeps the loads
+}
+
 }  // namespace
 
 extern "C" int32_t lla_stream_ceiling(int32_t mode, const void* src, void* dst, size_t n_vectors,
                                       int32_t workgroups, void* stream) {
-  if (mode < 0 || mode > 3 || src == nullptr || dst == nullptr || n_vectors == 0 || workgroups < 1)
+  if (mode < 0 || mode > 6 || src == nullptr || dst == nullptr || n_vectors == 0 || workgroups < 1)
     return -1;
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return -1;
+  if (mode >= 4) {
+    // whole 1 KiB blocks, the same number per wave, a multiple of 16 and at least 32 per
+    // wave, chunk below 2 GiB
+    const size_t waves = static_cast<size_t>(workgroups) * 4;
+    if (n_vectors % (64 * waves) != 0) return -1;
+    const size_t bpw = n_vectors / 64 / waves;
+    if (bpw < 32 || bpw % 16 != 0 || bpw * 1024 >= (size_t{1} << 31)) return -1;
+    const dim3 g(static_cast<unsigned>(workgroups)), b(256);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4* sp = static_cast<const u32x4*>(src);
+    u32x4* dp = static_cast<u32x4*>(dst);
+    if (mode == 4) hipLaunchKernelGGL(stream_wave_kernel<4>, g, b, 0, s, sp, dp, bpw);
+    else if (mode == 5) hipLaunchKernelGGL(stream_wave_kernel<5>, g, b, 0, s, sp, dp, bpw);
+    else hipLaunchKernelGGL(stream_wave_kernel<6>, g, b, 0, s, sp, dp, bpw);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+  }
   hipLaunchKernelGGL(stream_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), mode, static_cast<const u32x4*>(src),
                      static_cast<u32x4*>(dst), n_vectors);
