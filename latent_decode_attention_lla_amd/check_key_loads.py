@@ -1,10 +1,11 @@
-"""Check, on the gfx950 assembly of decode_fold_wide.hip, that the key loads the per-head
-fold kernel issues as inline assembly are safe: on every control-flow path from such a
-load, its destination registers are neither read nor written by any instruction before
-the `; keys` marker that ties them to the kernel's explicit vmcnt wait.
+"""Check, on the gfx950 assembly of the fold kernels, that the cache-row loads they issue as
+inline assembly (the per-head wide fold's keys; the dense narrow fold's key and value
+rows) are safe: on every control-flow path from such a load, its destination registers
+are neither read nor written by any instruction before the `; keys` marker that ties them
+to the kernel's explicit vmcnt wait.
 
-usage: python -m latent_decode_attention_lla_amd.check_key_loads [asm.s]
-(without an argument the file is compiled to assembly with the library's flags)"""
+usage: python -m latent_decode_attention_lla_amd.check_key_loads [asm.s ...]
+(without an argument both sources are compiled to assembly with the library's flags)"""
 import os
 import re
 import subprocess
@@ -24,8 +25,15 @@ def regs(text):
     return out
 
 
+# the kernels whose nontemporal loads are all inline assembly: the per-head wide fold
+# (dense and paged) and the narrow fold's ring instances (dense caches, chunks in flight
+# > 0; its paged instances load with ordinary, compiler-tracked loads)
+KERNELS = re.compile(r"^(_Z\S*decode_fold_head_kernel\S*|_Z\S*decode_rotary_fold_kernel\S*ELi[1-9]\d*ELb0E\S*):", re.M)
+SOURCES = ("decode_fold_wide.hip", "decode_rotary_fold.hip")
+
+
 def functions(asm):
-    for m in re.finditer(r"^(_Z\S*decode_fold_head_kernel\S*):", asm, re.M):
+    for m in KERNELS.finditer(asm):
         end = asm.index(".Lfunc_end", m.end())
         yield m.group(1), asm[m.end():end].splitlines()
 
@@ -66,6 +74,8 @@ def check_function(lines):
              if k == "inst" and re.match(r"global_load_dwordx[24] .* nt$", t) and "off" not in t.split(",")[1]]
     problems = []
     for i in loads:
+        if not insts[i][1].split(",")[2].strip().startswith("s["):
+            problems.append((insts[i][1], "(its base is not in scalar registers)"))
         dst = regs(insts[i][1].split(",")[0])
         seen, stack = set(), [i + 1]
         while stack:
@@ -86,18 +96,20 @@ def check_function(lines):
 
 def main(argv):
     if argv:
-        asm = open(argv[0]).read()
+        asm = "\n".join(open(p).read() for p in argv)
     else:
         here = os.path.dirname(os.path.abspath(__file__))
         sys.path.insert(0, os.path.dirname(here))
         from latent_decode_attention_lla_amd import build as B
-        src = os.path.join(B.CSRC, "decode_fold_wide.hip")
+        parts = []
         with tempfile.TemporaryDirectory() as d:
-            out = os.path.join(d, "k.s")
-            cmd = [B._hipcc(), *B.HIP_FLAGS, *B.FILE_FLAGS.get("decode_fold_wide.hip", []), "-I", B.CSRC,
-                   "-x", "hip", "--cuda-device-only", "-S", src, "-o", out]
-            subprocess.run(cmd, check=True, capture_output=True)
-            asm = open(out).read()
+            for fname in SOURCES:
+                out = os.path.join(d, fname + ".s")
+                cmd = [B._hipcc(), *B.HIP_FLAGS, *B.FILE_FLAGS.get(fname, []), "-I", B.CSRC,
+                       "-x", "hip", "--cuda-device-only", "-S", os.path.join(B.CSRC, fname), "-o", out]
+                subprocess.run(cmd, check=True, capture_output=True)
+                parts.append(open(out).read())
+        asm = "\n".join(parts)
     bad = 0
     for name, lines in functions(asm):
         n, problems = check_function(lines)

@@ -52,6 +52,12 @@ constexpr float kRescaleSlack = 8.0f;
 #ifndef LLA_FOLD_TPC16
 #define LLA_FOLD_TPC16 4        // 16-token tiles per chunk for r_k = 16
 #endif
+#ifndef LLA_FOLD_RING_TPC16
+#define LLA_FOLD_RING_TPC16 2   // the same, dense caches (ring)
+#endif
+#ifndef LLA_FOLD_RING_DA16
+#define LLA_FOLD_RING_DA16 3    // chunks in flight per wave, r_k = 16, dense caches
+#endif
 #ifndef LLA_FOLD_NT
 #define LLA_FOLD_NT 1           // 1: stream cache rows with non-temporal loads
 #endif
@@ -61,9 +67,17 @@ constexpr float kRescaleSlack = 8.0f;
 #ifndef LLA_FOLD_WAVES_PER_EU
 #define LLA_FOLD_WAVES_PER_EU 0  // 0: let the compiler choose
 #endif
+#ifndef LLA_FOLD_RING
+#define LLA_FOLD_RING 1         // 1: dense caches keep several chunks in flight (a ring)
+#endif
 #ifndef LLA_FOLD_TAB_DMA
 #define LLA_FOLD_TAB_DMA 1      // 1: dense caches' cos/sin tiles go straight to LDS
 #endif
+
+// Finishes this wave's LDS reads, then waits for the workgroup.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <typename V>
 __device__ __forceinline__ V stream_load(const V* p) {
@@ -133,7 +147,7 @@ __device__ __forceinline__ void load_rows_paged(Rows<RK, RV, TPC>& R, const uint
   }
 }
 
-template <int D, int RK, int RV, int HPW, int TPC, bool PAGED>
+template <int D, int RK, int RV, int HPW, int TPC, int DA, bool PAGED>
 __global__ __launch_bounds__(64 * HPW)
 #if LLA_FOLD_WAVES_PER_EU
 __attribute__((amdgpu_waves_per_eu(LLA_FOLD_WAVES_PER_EU)))
@@ -145,12 +159,18 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int VS = RV / 4;         // value-latent entries per lane
   constexpr int NTHR = 64 * HPW;
   constexpr int TAB_CHUNK = TPC * NKS * 64;  // 16-byte units of table per chunk
+  constexpr int TAB_BLOCKS = TPC * NKS;      // 1 KiB table blocks (MFMA fragments) per chunk
+  constexpr bool kRing = DA > 0 && !PAGED;  // dense caches: DA chunks in flight
+  constexpr int NBWR = (TAB_BLOCKS + HPW - 1) / HPW;  // table blocks per wave per chunk
   static_assert(RK % 16 == 0 && RV % 32 == 0 && D % 32 == 0, "shape");
   constexpr int TPT = (TAB_CHUNK + NTHR - 1) / NTHR;  // table units per thread per chunk
   constexpr bool kTabEven = TAB_CHUNK % NTHR == 0;
   constexpr int WT_STRIDE = D + 8;   // float16 row stride of the transposed W staging
   constexpr int STAGE_UNITS = HPW * 16 * WT_STRIDE * 2 / 16;
-  constexpr int LDS_UNITS = (2 * TAB_CHUNK > STAGE_UNITS) ? 2 * TAB_CHUNK : STAGE_UNITS;
+  constexpr int TAB_UNITS = (kRing ? DA + 1 : 2) * TAB_CHUNK;
+  constexpr int LDS_UNITS = (TAB_UNITS > STAGE_UNITS) ? TAB_UNITS : STAGE_UNITS;
+  static_assert(!kRing || DA >= 2, "ring depth");
+  constexpr int DAR = kRing ? DA : 2;
 
   __shared__ u32x4 lds[LDS_UNITS];
 
@@ -236,7 +256,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
 
   // One chunk: TPC tiles of 16 tokens, from the rows in R and the table in LDS buffer tcur.
   // FULL: every token of the chunk is in the context (no masking).
-  auto compute_chunk = [&](int c, const Rows<RK, RV, TPC>& R, const u32x4* tcur, auto full) {
+  auto compute_chunk = [&](int c, const auto& R, const u32x4* tcur, auto full) {
     constexpr bool FULL = decltype(full)::value;
 #pragma unroll
     for (int tt = 0; tt < TPC; ++tt) {
@@ -255,7 +275,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
       float part = g[NMT - 1][0];
 #pragma unroll
       for (int m = 0; m < NCK; ++m) {
-        const uint2 w = R.k[tt][m];
+        const auto w = R.k[tt][m];
         part += __uint_as_float(w.x << 16) * g[m][0] + __uint_as_float(w.x & 0xffff0000u) * g[m][1] +
                 __uint_as_float(w.y << 16) * g[m][2] + __uint_as_float(w.y & 0xffff0000u) * g[m][3];
       }
@@ -294,6 +314,118 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
     }
   };
 
+  auto compute = [&](int c, const auto& R, const u32x4* tcur) {
+    if (c < nfull) compute_chunk(c, R, tcur, std::true_type{});
+    else compute_chunk(c, R, tcur, std::false_type{});
+  };
+
+  if constexpr (kRing) {
+    // ---- dense caches: DAR chunks in flight per wave ----------------------------------
+    // Rows go to registers, the chunk's cos/sin blocks to a ring of DAR + 1 LDS stages.
+    // Chunk c's loads are issued DAR chunks ahead, at the end of chunk c - DAR's step (rows)
+    // and right after its barrier (table); every wave issues the same count per chunk, the
+    // chunks past the end included (their addresses clamp to the last row and tile), so a
+    // single wait for "at most (DAR - 1) chunks outstanding" means chunk c has landed.
+    // The table moves with buffer loads to LDS (MUBUF): a pending FLAT global_load_lds
+    // would make the compiler wait for every load in flight before reading any register a
+    // plain load wrote. The rows are inline-assembly loads the compiler neither counts
+    // nor waits for; the explicit wait orders their use, and hold_rows ties the registers
+    // to it (no instruction may touch them between the load and the marker: the built
+    // assembly is checked for that).
+    constexpr int NVL = RV / 32;
+    constexpr int KRB = RK * 2, VRB = RV * 2;  // bytes per latent row
+    constexpr int NLC = NBWR + TPC * (NCK + NVL);  // loads per chunk per wave
+    static_assert((DAR - 1) * NLC <= 63, "vmcnt range");
+    constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+    struct RowsR {
+      u32x2 k[TPC][NCK];
+      u32x4 v[TPC][NVL];
+    };
+    // the loads take a scalar base: the head's plane and each tile's first row are formed
+    // from wave-uniform values held in scalar registers
+    const size_t plane_u = static_cast<size_t>(b * a.H + __builtin_amdgcn_readfirstlane(h)) * a.n_max;
+    const char* ckb = reinterpret_cast<const char*>(a.c_k) + plane_u * KRB;
+    const char* cvb = reinterpret_cast<const char*>(a.c_v) + plane_u * VRB;
+    const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4*>(tab_g), 0, (tile_max + 1) * NKS * 1024, kRsrcWord3);
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto issue_tab = [&](int c) {
+      u32x4* st = lds + (c % (DAR + 1)) * TAB_CHUNK;
+      const int tile0 = (s0 >> 4) + c * TPC;
+#pragma unroll
+      for (int k = 0; k < NBWR; ++k) {
+        const int bi = min(wv + HPW * k, TAB_BLOCKS - 1);  // surplus blocks repeat
+        const int tile = min(tile0 + bi / NKS, tile_max);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (__attribute__((address_space(3))) void*)(st + bi * 64), 16,
+                                                 (bi % NKS) * 1024 + lane * 16, tile * NKS * 1024, 0, 0);
+      }
+    };
+    auto load_rows_r = [&](RowsR& R, int c) {
+#pragma unroll
+      for (int tt = 0; tt < TPC; ++tt) {
+        // the tile's first row (wave-uniform) and this lane's row from it; rows past the
+        // context repeat its last one
+        const int r0 = __builtin_amdgcn_readfirstlane(min(s0 + 16 * (c * TPC + tt), s1 - 1));
+        const int rl = min(lo, s1 - 1 - r0);
+        const char* kb = ckb + static_cast<size_t>(r0) * KRB;
+        const char* vb = cvb + static_cast<size_t>(r0) * VRB;
+        const uint32_t ko = static_cast<uint32_t>(rl * KRB + 8 * hi);
+        const uint32_t vo = static_cast<uint32_t>(rl * VRB + hi * (RV / 2));
+#pragma unroll
+        for (int m = 0; m < NCK; ++m)
+          asm volatile("global_load_dwordx2 %0, %1, %2 offset:%3 nt"
+                       : "=v"(R.k[tt][m]) : "v"(ko), "s"(kb), "n"(32 * m) : "memory");
+#pragma unroll
+        for (int m = 0; m < NVL; ++m)
+          asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3 nt"
+                       : "=v"(R.v[tt][m]) : "v"(vo), "s"(vb), "n"(16 * m) : "memory");
+      }
+    };
+    auto hold_rows = [&](RowsR& R) {
+#pragma unroll
+      for (int tt = 0; tt < TPC; ++tt) {
+#pragma unroll
+        for (int m = 0; m < NCK; ++m) asm volatile("; keys %0" : "+v"(R.k[tt][m]));
+#pragma unroll
+        for (int m = 0; m < NVL; ++m) asm volatile("; keys %0" : "+v"(R.v[tt][m]));
+      }
+    };
+    auto chunk_step = [&](int c, RowsR& R) {
+      // chunk c's rows and table blocks (this wave's) have landed once at most the later
+      // DAR - 1 chunks' loads are outstanding; the barrier then makes every wave's blocks
+      // visible, and tells that every wave is done with chunk c - 1's stage, which takes
+      // chunk c + DAR's table
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DAR - 1) * NLC) : "memory");
+      hold_rows(R);
+      ring_barrier();
+      issue_tab(c + DAR);
+      compute(c, R, lds + (c % (DAR + 1)) * TAB_CHUNK);
+      load_rows_r(R, c + DAR);  // the buffer's next chunk, once its rows are used
+    };
+    if (nchunk > 0) {
+      RowsR rr[DAR];
+#pragma unroll
+      for (int u = 0; u < DAR; ++u) {
+        issue_tab(u);
+        load_rows_r(rr[u], u);
+      }
+      // whole rounds of DAR chunks (each buffer in a fixed place in the round), then the rest
+      int c0 = 0;
+      for (; c0 + DAR <= nchunk; c0 += DAR) {
+#pragma unroll
+        for (int u = 0; u < DAR; ++u) chunk_step(c0 + u, rr[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < DAR - 1; ++u) {
+        if (c0 + u < nchunk) chunk_step(c0 + u, rr[u]);
+      }
+      // the requests past the end land before the LDS and the registers are reused
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < DAR; ++u) hold_rows(rr[u]);
+    }
+    __syncthreads();
+  } else {
   // Two row buffers used in turn: chunk c computes from one while chunk c + 1 loads into
   // the other; the table of chunk c + 1 goes into the other LDS half.
   // Paged rows: the pages of a chunk's tiles (uniform across the workgroup; rows clamped to
@@ -338,8 +470,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   // registers (measured faster there: the transfers then do not queue behind the
   // page-dependent row loads).
   constexpr bool kTabDma = LLA_FOLD_TAB_DMA && !PAGED;
-  constexpr int TAB_BLOCKS = TPC * NKS;
-  constexpr int NBW = (TAB_BLOCKS + HPW - 1) / HPW;  // blocks per wave (surplus ones repeat)
+  constexpr int NBW = NBWR;  // blocks per wave (surplus ones repeat)
   auto issue_tab = [&](int c, u32x4* dst) {
     const int tile0 = (s0 >> 4) + c * TPC;
 #pragma unroll
@@ -390,10 +521,6 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
       }
     }
   };
-  auto compute = [&](int c, const Rows<RK, RV, TPC>& R, const u32x4* tcur) {
-    if (c < nfull) compute_chunk(c, R, tcur, std::true_type{});
-    else compute_chunk(c, R, tcur, std::false_type{});
-  };
 
   Pages pa{}, pb{};
   if constexpr (PAGED) {
@@ -424,6 +551,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
     compute(c + 1, rb, tab1);
     if (more2) store_tab(tab0);
     __syncthreads();
+  }
   }
 
 
@@ -490,27 +618,41 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   }
 }
 
-template <int D, int RK, int RV, int HPW, int TPC, bool PAGED = false>
+template <int D, int RK, int RV, int HPW, int TPC, int DA, bool PAGED = false>
 void launch(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
   dim3 grid(a.S, (a.H / HPW) * a.L, a.B);
-  hipLaunchKernelGGL((decode_rotary_fold_kernel<D, RK, RV, HPW, TPC, PAGED>), grid, dim3(64 * HPW), 0,
+  hipLaunchKernelGGL((decode_rotary_fold_kernel<D, RK, RV, HPW, TPC, DA, PAGED>), grid, dim3(64 * HPW), 0,
                      s, a, pg);
+}
+
+// Dense caches: the ring pipeline, with RHPW heads per workgroup when H allows it (DA = 0:
+// the two-buffer loop of paged caches).
+template <int D, int RK, int RV, int TPC, int RTPC, int DA, int RHPW>
+void launch_dense(const DecodeArgs& a, hipStream_t s) {
+  if constexpr (!LLA_FOLD_RING || DA == 0) {
+    launch<D, RK, RV, LLA_FOLD_HPW, TPC, 0>(a, PageArgs{}, s);
+  } else {
+    if (a.H % RHPW == 0) launch<D, RK, RV, RHPW, RTPC, DA>(a, PageArgs{}, s);
+    else launch<D, RK, RV, LLA_FOLD_HPW, RTPC, DA>(a, PageArgs{}, s);
+  }
 }
 
 }  // namespace
 
-// (d, r_k, r_v, tiles per chunk); heads per workgroup is LLA_FOLD_HPW (H must be a
-// multiple of it).
+// (d, r_k, r_v, tiles per chunk with a paged cache, then with a dense one: tiles per
+// chunk, chunks in flight (0: no ring, measured no faster for that shape) and heads per
+// workgroup when H is a multiple of it); heads per workgroup is otherwise LLA_FOLD_HPW
+// (H must be a multiple of it).
 // Wider latents go to decode_fold_wide.hip (a pair of waves per head).
-#define LLA_FOLD_SHAPES(X)        \
-  X(128, 16, 32, LLA_FOLD_TPC16)  \
-  X(128, 32, 64, 2)               \
-  X(64, 16, 32, 4)                \
-  X(64, 32, 32, 2)
+#define LLA_FOLD_SHAPES(X)                                                     \
+  X(128, 16, 32, LLA_FOLD_TPC16, LLA_FOLD_RING_TPC16, LLA_FOLD_RING_DA16, 8)   \
+  X(128, 32, 64, 2, 2, 0, 4)                                                   \
+  X(64, 16, 32, 4, 2, 4, 8)                                                    \
+  X(64, 32, 32, 2, 1, 4, 8)
 
 bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v) {
   if (dtype != 1) return false;
-#define X(D_, RK_, RV_, TPC_) \
+#define X(D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_) \
   if (d == D_ && r_k == RK_ && r_v == RV_) return true;
   LLA_FOLD_SHAPES(X)
 #undef X
@@ -520,10 +662,10 @@ bool decode_rotary_fold_supported(int dtype, int d, int r_k, int r_v) {
 bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                hipStream_t s) {
   if (dtype != 1 || a.H % LLA_FOLD_HPW != 0) return false;
-#define X(D_, RK_, RV_, TPC_)                                  \
-  if (d == D_ && r_k == RK_ && r_v == RV_) {                   \
-    launch<D_, RK_, RV_, LLA_FOLD_HPW, TPC_>(a, PageArgs{}, s); \
-    return true;                                               \
+#define X(D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_)                     \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                          \
+    launch_dense<D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_>(a, s);        \
+    return true;                                                      \
   }
   LLA_FOLD_SHAPES(X)
 #undef X
@@ -533,10 +675,10 @@ bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeA
 bool launch_decode_rotary_fold_paged(int dtype, int d, int r_k, int r_v, const DecodeArgs& a,
                                      const PageArgs& pg, hipStream_t s) {
   if (dtype != 1 || a.H % LLA_FOLD_HPW != 0 || pg.table == nullptr) return false;
-#define X(D_, RK_, RV_, TPC_)                                  \
-  if (d == D_ && r_k == RK_ && r_v == RV_) {                   \
-    launch<D_, RK_, RV_, LLA_FOLD_HPW, TPC_, true>(a, pg, s);  \
-    return true;                                               \
+#define X(D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_)                   \
+  if (d == D_ && r_k == RK_ && r_v == RV_) {                       \
+    launch<D_, RK_, RV_, LLA_FOLD_HPW, TPC_, 0, true>(a, pg, s);   \
+    return true;                                                   \
   }
   LLA_FOLD_SHAPES(X)
 #undef X

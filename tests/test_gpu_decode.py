@@ -238,6 +238,26 @@ def test_bf16_wide_fold_two_heads_per_workgroup(d, r_k, r_v, H):
         assert err <= BF16_TOL
 
 
+@pytest.mark.parametrize("H", [4, 12, 16])
+@pytest.mark.parametrize("d,r_k,r_v", [(128, 16, 32), (128, 32, 64), (64, 16, 32), (64, 32, 32)])
+def test_bf16_narrow_fold_every_shape_and_head_group(d, r_k, r_v, H):
+    """The narrow fold over a dense cache keeps several chunks of rows in flight per wave,
+    with 8 heads per workgroup where the shape and H allow it and 4 otherwise: every shape
+    it is built for, head counts that take each grouping, contexts that end inside the
+    first chunk, on a round boundary and past several rounds with a ragged tail, one and
+    three splits, all 4 loops, every output against the oracle."""
+    for n in (16, 93, 517):
+        w = WORKLOADS["capacity_21x"].replace(D=1, batch=2, n=n, d=d, r_k=r_k, r_v=r_v, H=H)
+        st = DeviceLatentStore(w, seed=29)
+        for splits in (1, 3):
+            out = st.decode(0, 0, 4, opts=lla.make_opts(splits, FOLD))
+            ref = oracle_decode(st, 0, 0, 4, range(w.batch), w.n)
+            err = max_abs(f64(out), ref)
+            announce(f"narrow fold H={H} d={d} ranks=({r_k}, {r_v}) n={n} splits={splits}: "
+                     f"{rel_note(err, BF16_TOL)}")
+            assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("variant", ["per_head", "lla2d"])
 @pytest.mark.parametrize("d,r_k,r_v", [(128, 64, 64), (128, 128, 128), (64, 256, 256)])
 def test_bf16_table8_ranks_every_output(d, r_k, r_v, variant):

@@ -1,7 +1,9 @@
-"""The per-head wide fold kernel issues its key loads as inline assembly, which the compiler
-neither counts nor waits for; the kernel's own vmcnt wait orders their use. This checks,
-on the gfx950 assembly of every instance as built, that no instruction reads or writes a
-key load's destination registers before the marker that ties them to that wait."""
+"""The per-head wide fold kernel issues its key loads, and the narrow fold over a dense cache
+its key and value row loads, as inline assembly, which the compiler neither counts nor
+waits for; each kernel's own vmcnt wait orders their use. This checks, on the gfx950
+assembly of every instance as built, that no instruction reads or writes such a load's
+destination registers before the marker that ties them to that wait, and that every such
+load takes a scalar base."""
 import pytest
 
 from latent_decode_attention_lla_amd import check_key_loads
@@ -11,7 +13,10 @@ def test_key_load_registers_untouched_until_their_wait(capsys):
     rc = check_key_loads.main([])
     out = capsys.readouterr().out
     lines = [ln for ln in out.splitlines() if "key loads" in ln]
-    assert len(lines) == 16, out          # 4 shapes x 2 heads-per-workgroup x dense/paged
+    wide = [ln for ln in lines if "decode_fold_head_kernel" in ln]
+    narrow = [ln for ln in lines if "decode_rotary_fold_kernel" in ln]
+    assert len(wide) == 16, out    # 4 shapes x 2 heads-per-workgroup x dense/paged
+    assert len(narrow) == 6, out   # 3 shapes with the ring, 4 and 8 heads per workgroup
     assert all(" 0 unsafe uses" in ln and not ln.split(":")[1].strip().startswith("0 key") for ln in lines), out
     assert rc == 0, out
 
