@@ -35,6 +35,7 @@ def _w(name, **kw):
 # kernel id -> (workload, decode kind, path, paged instance to compare)
 KERNELS = {
     "narrow_fold": (_w("capacity_21x", H=8), "latent", FOLD, True),
+    "narrow_fold_h4": (_w("capacity_21x", H=4), "latent", FOLD, False),
     "wide_fold": (_w("ouro_layer_4x", H=4), "latent", FOLD, True),
     "wide_fold_2d": (_w("lla2d_long", H=16, r_k=128, r_v=128), "latent", FOLD, False),
     "lla2d_h16": (_w("lla2d_long", H=16), "latent", FOLD, True),
