@@ -321,9 +321,9 @@ int32_t lla_encode_fused(const lla_dims* dims, const lla_codec* codec, const lla
 /* lla_decode_attn over a paged cache (logical tokens 0 .. len_b - 1 through the block
  * table; RoPE at the logical slot). Paths as lla_decode_attn: the rotary fold kernels
  * (bfloat16 shapes they are built for, per head and LLA-2D), else the reconstruct path;
- * asking for the rotary fold elsewhere gives LLA_ERR_UNSUPPORTED. On the wide fold kernel
- * (r_k >= 64, and LLA-2D) a context split spans at most 4096 tokens, so num_splits of
- * opts may be raised to that. workspace >=
+ * asking for the rotary fold elsewhere gives LLA_ERR_UNSUPPORTED. On the fold kernels a
+ * context split spans at most 4096 tokens (256 pages, whose indices a workgroup keeps
+ * in LDS), so num_splits of opts may be raised to that. workspace >=
  * lla_decode_paged_workspace_bytes(dims, n_ctx, loop_count, opts). Other arguments and
  * errors as lla_decode_attn; block table entries as for lla_encode_paged. */
 size_t lla_decode_paged_workspace_bytes(const lla_dims* dims, int32_t n_ctx, int32_t loop_count,

@@ -25,10 +25,10 @@ def regs(text):
     return out
 
 
-# the kernels whose nontemporal loads are all inline assembly: the per-head wide fold
-# (dense and paged) and the narrow fold's ring instances (dense caches, chunks in flight
-# > 0; its paged instances load with ordinary, compiler-tracked loads)
-KERNELS = re.compile(r"^(_Z\S*decode_fold_head_kernel\S*|_Z\S*decode_rotary_fold_kernel\S*ELi[1-9]\d*ELb0E\S*):", re.M)
+# the kernels whose nontemporal loads are all inline assembly: the per-head wide fold and
+# the narrow fold's ring instances (chunks in flight > 0), dense and paged; the narrow
+# fold's two-buffer instances load with ordinary, compiler-tracked loads
+KERNELS = re.compile(r"^(_Z\S*decode_fold_head_kernel\S*|_Z\S*decode_rotary_fold_kernel\S*ELi[1-9]\d*ELb[01]E\S*):", re.M)
 SOURCES = ("decode_fold_wide.hip", "decode_rotary_fold.hip")
 
 

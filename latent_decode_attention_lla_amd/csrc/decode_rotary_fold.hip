@@ -160,7 +160,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   constexpr int NTHR = 64 * HPW;
   constexpr int TAB_CHUNK = TPC * NKS * 64;  // 16-byte units of table per chunk
   constexpr int TAB_BLOCKS = TPC * NKS;      // 1 KiB table blocks (MFMA fragments) per chunk
-  constexpr bool kRing = DA > 0 && !PAGED;  // dense caches: DA chunks in flight
+  constexpr bool kRing = DA > 0;  // DA chunks in flight (else the two-buffer loop)
   constexpr int NBWR = (TAB_BLOCKS + HPW - 1) / HPW;  // table blocks per wave per chunk
   static_assert(RK % 16 == 0 && RV % 32 == 0 && D % 32 == 0, "shape");
   constexpr int TPT = (TAB_CHUNK + NTHR - 1) / NTHR;  // table units per thread per chunk
@@ -172,7 +172,9 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   static_assert(!kRing || DA >= 2, "ring depth");
   constexpr int DAR = kRing ? DA : 2;
 
-  __shared__ u32x4 lds[LDS_UNITS];
+  // the ring's paged instances keep the split's pages after the table stages
+  constexpr int PAGE_UNITS = (kRing && PAGED) ? kMaxSplitPages / 4 : 0;
+  __shared__ u32x4 lds[LDS_UNITS + PAGE_UNITS];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -341,11 +343,42 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
       u32x2 k[TPC][NCK];
       u32x4 v[TPC][NVL];
     };
-    // the loads take a scalar base: the head's plane and each tile's first row are formed
-    // from wave-uniform values held in scalar registers
-    const size_t plane_u = static_cast<size_t>(b * a.H + __builtin_amdgcn_readfirstlane(h)) * a.n_max;
+    // the loads take a scalar base: the head's plane (paged: its rows in page 0 of the
+    // pool), each tile's page and first row are formed from wave-uniform values held in
+    // scalar registers
+    const int hu = __builtin_amdgcn_readfirstlane(h);
+    const size_t plane_u = PAGED ? static_cast<size_t>(hu) * kPage : static_cast<size_t>(b * a.H + hu) * a.n_max;
     const char* ckb = reinterpret_cast<const char*>(a.c_k) + plane_u * KRB;
     const char* cvb = reinterpret_cast<const char*>(a.c_v) + plane_u * VRB;
+    const size_t kpage = static_cast<size_t>(a.H) * kPage * KRB;  // bytes per page (paged)
+    const size_t vpage = static_cast<size_t>(a.H) * kPage * VRB;
+    // paged: the pages of a chunk's tiles (rows past the context lie in the last tile's
+    // page), looked up with scalar loads before the chunk's compute step and used after it
+    struct PagesR {
+      int p[TPC];
+    };
+    // The split's pages are read from the block table into LDS once (at most
+    // kMaxSplitPages: the host caps a split's length to that many pages): a lookup is
+    // then an LDS read, where a global load here would be a vector load (the inline
+    // assembly below clobbers memory, so the compiler cannot use a scalar load) that the
+    // compiler would wait for with a vmcnt counting only its own loads, draining the ring.
+    int* split_pages = reinterpret_cast<int*>(lds + LDS_UNITS);
+    if constexpr (PAGED) {
+      const int ntiles = min(tile_max - (s0 >> 4) + 1, kMaxSplitPages);
+      for (int i = threadIdx.x; i < ntiles; i += NTHR) split_pages[i] = page_of(pg, b, (s0 >> 4) + i);
+      __syncthreads();
+    }
+    auto pages_of = [&](int c) {
+      PagesR P{};
+      if constexpr (PAGED) {
+#pragma unroll
+        for (int tt = 0; tt < TPC; ++tt) {
+          const int i = min(min((s0 >> 4) + c * TPC + tt, tile_max) - (s0 >> 4), kMaxSplitPages - 1);
+          P.p[tt] = __builtin_amdgcn_readfirstlane(split_pages[__builtin_amdgcn_readfirstlane(i)]);
+        }
+      }
+      return P;
+    };
     const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<u32x4*>(tab_g), 0, (tile_max + 1) * NKS * 1024, kRsrcWord3);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -360,7 +393,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
                                                  (bi % NKS) * 1024 + lane * 16, tile * NKS * 1024, 0, 0);
       }
     };
-    auto load_rows_r = [&](RowsR& R, int c) {
+    auto load_rows_r = [&](RowsR& R, int c, const PagesR& P) {
 #pragma unroll
       for (int tt = 0; tt < TPC; ++tt) {
         // the tile's first row (wave-uniform) and this lane's row from it; rows past the
@@ -369,6 +402,11 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
         const int rl = min(lo, s1 - 1 - r0);
         const char* kb = ckb + static_cast<size_t>(r0) * KRB;
         const char* vb = cvb + static_cast<size_t>(r0) * VRB;
+        if constexpr (PAGED) {  // a tile is one page; r0 - 16 * tile is its row in the page
+          const int pr = r0 - 16 * min((s0 >> 4) + c * TPC + tt, tile_max);
+          kb = ckb + static_cast<size_t>(P.p[tt]) * kpage + pr * KRB;
+          vb = cvb + static_cast<size_t>(P.p[tt]) * vpage + pr * VRB;
+        }
         const uint32_t ko = static_cast<uint32_t>(rl * KRB + 8 * hi);
         const uint32_t vo = static_cast<uint32_t>(rl * VRB + hi * (RV / 2));
 #pragma unroll
@@ -399,15 +437,16 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
       hold_rows(R);
       ring_barrier();
       issue_tab(c + DAR);
+      const PagesR P = pages_of(c + DAR);
       compute(c, R, lds + (c % (DAR + 1)) * TAB_CHUNK);
-      load_rows_r(R, c + DAR);  // the buffer's next chunk, once its rows are used
+      load_rows_r(R, c + DAR, P);  // the buffer's next chunk, once its rows are used
     };
     if (nchunk > 0) {
       RowsR rr[DAR];
 #pragma unroll
       for (int u = 0; u < DAR; ++u) {
         issue_tab(u);
-        load_rows_r(rr[u], u);
+        load_rows_r(rr[u], u, pages_of(u));
       }
       // whole rounds of DAR chunks (each buffer in a fixed place in the round), then the rest
       int c0 = 0;
@@ -625,21 +664,21 @@ void launch(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
                      s, a, pg);
 }
 
-// Dense caches: the ring pipeline, with RHPW heads per workgroup when H allows it (DA = 0:
-// the two-buffer loop of paged caches).
-template <int D, int RK, int RV, int TPC, int RTPC, int DA, int RHPW>
-void launch_dense(const DecodeArgs& a, hipStream_t s) {
+// The ring pipeline, with RHPW heads per workgroup when H allows it (DA = 0: the
+// two-buffer loop).
+template <int D, int RK, int RV, int TPC, int RTPC, int DA, int RHPW, bool PAGED>
+void launch_shape(const DecodeArgs& a, const PageArgs& pg, hipStream_t s) {
   if constexpr (!LLA_FOLD_RING || DA == 0) {
-    launch<D, RK, RV, LLA_FOLD_HPW, TPC, 0>(a, PageArgs{}, s);
+    launch<D, RK, RV, LLA_FOLD_HPW, TPC, 0, PAGED>(a, pg, s);
   } else {
-    if (a.H % RHPW == 0) launch<D, RK, RV, RHPW, RTPC, DA>(a, PageArgs{}, s);
-    else launch<D, RK, RV, LLA_FOLD_HPW, RTPC, DA>(a, PageArgs{}, s);
+    if (a.H % RHPW == 0) launch<D, RK, RV, RHPW, RTPC, DA, PAGED>(a, pg, s);
+    else launch<D, RK, RV, LLA_FOLD_HPW, RTPC, DA, PAGED>(a, pg, s);
   }
 }
 
 }  // namespace
 
-// (d, r_k, r_v, tiles per chunk with a paged cache, then with a dense one: tiles per
+// (d, r_k, r_v, tiles per chunk of the two-buffer loop, then of the ring: tiles per
 // chunk, chunks in flight (0: no ring, measured no faster for that shape) and heads per
 // workgroup when H is a multiple of it); heads per workgroup is otherwise LLA_FOLD_HPW
 // (H must be a multiple of it).
@@ -664,7 +703,7 @@ bool launch_decode_rotary_fold(int dtype, int d, int r_k, int r_v, const DecodeA
   if (dtype != 1 || a.H % LLA_FOLD_HPW != 0) return false;
 #define X(D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_)                     \
   if (d == D_ && r_k == RK_ && r_v == RV_) {                          \
-    launch_dense<D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_>(a, s);        \
+    launch_shape<D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_, false>(a, PageArgs{}, s); \
     return true;                                                      \
   }
   LLA_FOLD_SHAPES(X)
@@ -677,7 +716,7 @@ bool launch_decode_rotary_fold_paged(int dtype, int d, int r_k, int r_v, const D
   if (dtype != 1 || a.H % LLA_FOLD_HPW != 0 || pg.table == nullptr) return false;
 #define X(D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_)                   \
   if (d == D_ && r_k == RK_ && r_v == RV_) {                       \
-    launch<D_, RK_, RV_, LLA_FOLD_HPW, TPC_, 0, true>(a, pg, s);   \
+    launch_shape<D_, RK_, RV_, TPC_, RTPC_, DA_, RHPW_, true>(a, pg, s); \
     return true;                                                   \
   }
   LLA_FOLD_SHAPES(X)

@@ -84,9 +84,9 @@ Plan plan_paged(const lla_dims& d, int n_ctx, int loop_count, const lla_decode_o
   lla_decode_opts o{0, fold ? LLA_PATH_ROTARY_FOLD : LLA_PATH_RECONSTRUCT};
   if (opts != nullptr) o.num_splits = opts->num_splits;
   Plan p = plan_splits(d, n_ctx, loop_count, &o);
-  // the wide fold kernel keeps a split's page indices in LDS: at most kMaxSplitPages pages
+  // the fold kernels keep a split's page indices in LDS: at most kMaxSplitPages pages
   constexpr int kMaxLen = lla::kMaxSplitPages * lla::kPage;
-  if (fold && fold_kind(d) == kFoldWide && p.split_len > kMaxLen) {
+  if (fold && fold_kind(d) != kFoldNone && p.split_len > kMaxLen) {
     p.split_len = kMaxLen;
     p.S = (n_ctx + kMaxLen - 1) / kMaxLen;
   }

@@ -101,16 +101,21 @@ def test_splits_count_the_kernels_waves_per_head():
         assert lla.lla_decode_num_splits(dims, n, 1, recon) == rec
 
 
-def test_paged_splits_of_the_wide_fold_span_at_most_4096_tokens():
-    """The wide fold kernel keeps a split's page indices in LDS (256 pages of 16 tokens);
-    the narrow fold and reconstruct paths plan like the dense cache."""
+def test_paged_splits_of_the_fold_kernels_span_at_most_4096_tokens():
+    """The fold kernels keep a split's page indices in LDS (256 pages of 16 tokens), so
+    their paged splits span at most 4096 tokens; the reconstruct path plans like the
+    dense cache."""
     wide = lla.make_dims(4, 1, 16, 128, 96, 160, 32, 32768)
     assert lla.lla_decode_num_splits(wide, 32768, 1) == 2
     assert lla.lla_decode_paged_num_splits(wide, 32768, 1) == 8
     assert lla.lla_decode_paged_num_splits(wide, 4096, 1) == lla.lla_decode_num_splits(wide, 4096, 1)
     assert lla.lla_decode_paged_num_splits(wide, 32769, 1) == 0  # n_ctx > n_max
-    narrow = lla.make_dims(4, 1, 16, 128, 32, 32, 32, 32768)
-    assert lla.lla_decode_paged_num_splits(narrow, 32768, 1) == lla.lla_decode_num_splits(narrow, 32768, 1)
+    narrow = lla.make_dims(4, 1, 16, 128, 16, 32, 32, 32768)
+    assert lla.lla_decode_num_splits(narrow, 32768, 1) < 8
+    assert lla.lla_decode_paged_num_splits(narrow, 32768, 1) == 8
+    assert lla.lla_decode_paged_num_splits(narrow, 4096, 1) == lla.lla_decode_num_splits(narrow, 4096, 1)
+    recon = lla.make_opts(0, lla.LLA_PATH_RECONSTRUCT)
+    assert lla.lla_decode_paged_num_splits(narrow, 32768, 1, recon) == lla.lla_decode_num_splits(narrow, 32768, 1, recon)
     nb = lla.lla_decode_paged_workspace_bytes(wide, 32768, 1)
     assert nb == 32 * 16 * 8 * (2 + 160) * 4
     # LLA-2D: one wave per head (its own kernel), splits of the paged cache capped alike

@@ -16,7 +16,7 @@ def test_key_load_registers_untouched_until_their_wait(capsys):
     wide = [ln for ln in lines if "decode_fold_head_kernel" in ln]
     narrow = [ln for ln in lines if "decode_rotary_fold_kernel" in ln]
     assert len(wide) == 16, out    # 4 shapes x 2 heads-per-workgroup x dense/paged
-    assert len(narrow) == 6, out   # 3 shapes with the ring, 4 and 8 heads per workgroup
+    assert len(narrow) == 12, out  # 3 shapes with the ring, 4 and 8 heads, dense and paged
     assert all(" 0 unsafe uses" in ln and not ln.split(":")[1].strip().startswith("0 key") for ln in lines), out
     assert rc == 0, out
 
