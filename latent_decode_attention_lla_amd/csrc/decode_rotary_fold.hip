@@ -22,13 +22,15 @@
 // (Appendix J, "Absorbed attention") and applies W_up,v,t and mu_v,t once at the end.
 //
 // Workgroup: HPW waves = HPW heads of one (sequence, loop, context split); they walk the
-// same token range, TPC tiles of 16 tokens per chunk, with the next chunk's cache rows
-// and table tile loaded while the current one is computed. With a paged cache a 16-token
-// tile is one page: its rows come from the page the block table names for it, and
-// everything else (positions, the table of angles) follows the logical token index. Each lane keeps an online
-// softmax for its token column; the running max is raised only when a score exceeds it
-// by more than 2^8 (scores live in the exp2 domain), which is exact because the same max
-// is used by the running sum and the accumulator.
+// same token range in chunks of TPC tiles of 16 tokens. The ring instances (DA > 0) keep
+// DA chunks of cache rows (registers) and table tiles (LDS) in flight per wave; the
+// two-buffer instances (DA = 0) load the next chunk while the current one is computed.
+// With a paged cache a 16-token tile is one page: its rows come from the page the block
+// table names for it, and everything else (positions, the table of angles) follows the
+// logical token index. Each lane keeps an online softmax for its token column; the
+// running max is raised only when a score exceeds it by more than 2^8 (scores live in the
+// exp2 domain), which is exact because the same max is used by the running sum and the
+// accumulator.
 #include <type_traits>
 
 #include "lla_device.h"
