@@ -81,6 +81,30 @@ def test_shuffled_pool_matches_dense_and_oracle(name, over, path, splits):
     assert same
 
 
+@pytest.mark.parametrize("H", [16, 4])
+def test_paged_narrow_fold_split_spans_at_most_256_pages(H):
+    """A fold kernel keeps a split's page indices in LDS, 256 at most, so the host splits a
+    paged context into spans of at most 4096 tokens: at 4500 tokens the auto plan takes two
+    splits, the first filling every slot. Both the paged decode and the dense one match the
+    oracle (their split boundaries differ, so they need not agree bit for bit)."""
+    w = WORKLOADS["capacity_21x"].replace(batch=2, n=4500, D=1, H=H)
+    st = DeviceLatentStore(w, seed=73)
+    lens = [4500, 4100]
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    opts = lla.make_opts(0, lla.LLA_PATH_ROTARY_FOLD)
+    n_split = lla.lla_decode_paged_num_splits(st.dims, w.n, w.T, opts)
+    assert n_split >= 2
+    dense = st.decode(0, 0, w.T, ctx_lens=ctx, opts=opts).clone()
+    st.paginate(seed=74, spare_pages=3)
+    paged = st.decode_paged(0, 0, w.T, ctx_lens=ctx, opts=opts)
+    torch.cuda.synchronize()
+    ref = _oracle_paged(st, 0, 0, w.T, range(2), w.n, lens)
+    for label, got in (("paged", paged), ("dense", dense)):
+        err = max_abs(f64(got), ref)
+        announce(f"narrow fold H={H} n=4500 {label} ({n_split} paged splits): {rel_note(err, BF16_TOL)}")
+        assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("name", ["capacity_21x", "ouro_layer_4x", "lla2d_long"])
 def test_pages_past_the_context_are_not_read(name):
     """Pages of the pool the table does not name for a token below len_b hold NaN (spares
