@@ -324,7 +324,7 @@ void decode_rotary_fold_kernel(DecodeArgs a, PageArgs pg) {
   };
 
   if constexpr (kRing) {
-    // ---- dense caches: DAR chunks in flight per wave ----------------------------------
+    // ---- DAR chunks in flight per wave (dense and paged caches) -----------------------
     // Rows go to registers, the chunk's cos/sin blocks to a ring of DAR + 1 LDS stages.
     // Chunk c's loads are issued DAR chunks ahead, at the end of chunk c - DAR's step (rows)
     // and right after its barrier (table); every wave issues the same count per chunk, the
