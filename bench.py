@@ -168,9 +168,14 @@ def stream_ceilings(gib: float):
     # direct-to-LDS loads, through registers, and half through each
     wave_modes = {"read_wave_lds": (4, n, n * 16, 0), "read_wave_regs": (5, n, n * 16, 0),
                   "read_wave_mixed": (6, n, n * 16, 0)}
+    # the narrow fold's latent-row pattern (mode 7: per wave one key and one value row plane
+    # in 16-row tiles, 8 in flight) at 16 and 32 waves per CU
+    n7 = {wg: n - n % (96 * 4 * wg * 8) for wg in (1024, 2048)}
+    row_modes = {f"read_rows_fold_{wg // 64}w": (wg, (7, n7[wg], n7[wg] * 16, 0)) for wg in n7}
     res = {}
     runs = [(wg, m) for wg in (1024, 2048, 4096, 8192) for m in modes.items()]
     runs += [(512, m) for m in wave_modes.items()]
+    runs += [(wg, (name, m)) for name, (wg, m) in row_modes.items()]
     for wg, (name, (mode, nv, rd, wr)) in runs:
         for _ in range(2):
             lla.lla_stream_ceiling(mode, src, dst, nv, wg)

@@ -1,8 +1,8 @@
 /*
  * lla_stream.h - measurement helper of liblla.so, not part of the method: plain streaming
  * kernels that give the HBM ceilings (a read-only pass, a copy, 4:1 and 1:4 read:write
- * mixes, and read-only passes through LDS or registers) the latent-store kernels are
- * compared against on the same device.
+ * mixes, read-only passes through LDS or registers, and the narrow fold's row pattern)
+ * the latent-store kernels are compared against on the same device.
  */
 #ifndef LLA_STREAM_H_
 #define LLA_STREAM_H_
@@ -25,6 +25,12 @@ extern "C" {
  *           same whole number of blocks per wave, a multiple of 16 and at least 32, each
  *           chunk under 2 GiB (else -1); nothing is written unless a checksum of the data
  *           hits one fixed value (then 16 bytes to dst[0]).
+ *   mode 7: the latent-row pattern of the narrow fold kernel: read src[0 .. n) as 4 ·
+ *           workgroups key planes of 32-byte rows (the first third) and as many value
+ *           planes of 64-byte rows (the rest), every wave streaming one plane of each in
+ *           16-row tiles (a 512-byte and a 1 KiB wave load per tile, 8 tiles in flight);
+ *           n must be 96 vectors times the wave count times a multiple of 8 (else -1);
+ *           writes as modes 4-6.
  * src and dst are device pointers, 16-byte aligned, owned by the caller, large enough for
  * the mode (mode 2 reads 4n vectors, mode 3 writes 4n, mode 0 writes `workgroups`).
  * workgroups: 256-thread workgroups of the grid (a grid-stride loop in modes 0-3).

@@ -13,6 +13,7 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // mode 0: read n vectors of src, one xor-fold per workgroup into dst[block]
 // mode 1: dst[i] = src[i]
@@ -121,13 +122,57 @@ __global__ __launch_bounds__(256) void stream_wave_kernel(const u32x4* __restric
   if ((acc ^ racc.x ^ racc.y ^ racc.z ^ racc.w) == 0x9e3779b9u) dst[0] = racc;  // keeps the loads
 }
 
+// Mode 7, the latent-row pattern of the narrow fold: wave w streams row plane w of a key
+// region (32-byte rows; src[0 .. n/3)) and of a value region (64-byte rows; the rest) in
+// 16-row tiles, one 8-byte load per lane of key rows (512 bytes a wave) and one 16-byte
+// load of value rows (1 KiB) per tile, 8 tiles in flight in a register ring.
+__global__ __launch_bounds__(256) void stream_rows_kernel(const char* __restrict__ src, u32x4* dst,
+                                                          size_t waves, size_t tiles) {
+  constexpr int R = 8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lo = lane & 15, hi = lane >> 4;
+  const size_t w = static_cast<size_t>(blockIdx.x) * 4 + wave;
+  const char* kp = src + w * tiles * 512 + lo * 32 + 8 * hi;
+  const char* vp = src + waves * tiles * 512 + w * tiles * 1024 + lo * 64 + 16 * hi;
+  u32x2 kb[R];
+  u32x4 vb[R];
+  u32x4 racc = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    kb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kp + static_cast<size_t>(t) * 512));
+    vb[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + static_cast<size_t>(t) * 1024));
+  }
+  for (size_t t0 = 0; t0 < tiles; t0 += R) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      racc.x ^= kb[k].x;
+      racc.y ^= kb[k].y;
+      racc ^= vb[k];
+      const size_t nx = t0 + R + k < tiles ? t0 + R + k : 0;
+      kb[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kp + nx * 512));
+      vb[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + nx * 1024));
+    }
+  }
+  if ((racc.x ^ racc.y ^ racc.z ^ racc.w) == 0x9e3779b9u) dst[0] = racc;  // keeps the loads
+}
+
 }  // namespace
 
 extern "C" int32_t lla_stream_ceiling(int32_t mode, const void* src, void* dst, size_t n_vectors,
                                       int32_t workgroups, void* stream) {
-  if (mode < 0 || mode > 6 || src == nullptr || dst == nullptr || n_vectors == 0 || workgroups < 1)
+  if (mode < 0 || mode > 7 || src == nullptr || dst == nullptr || n_vectors == 0 || workgroups < 1)
     return -1;
   if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return -1;
+  if (mode == 7) {
+    // whole 16-row tiles (1536 bytes) per wave, a multiple of 8 of them, at least 8
+    const size_t waves = static_cast<size_t>(workgroups) * 4;
+    if (n_vectors % (96 * waves) != 0) return -1;
+    const size_t tiles = n_vectors / 96 / waves;
+    if (tiles < 8 || tiles % 8 != 0) return -1;
+    hipLaunchKernelGGL(stream_rows_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const char*>(src),
+                       static_cast<u32x4*>(dst), waves, tiles);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+  }
   if (mode >= 4) {
     // whole 1 KiB blocks, the same number per wave, a multiple of 16 and at least 32 per
     // wave, chunk below 2 GiB

@@ -296,7 +296,8 @@ def lla_decode_attn_noalloc(dims: lla_dims, codec: lla_codec, cache: lla_cache, 
 def lla_stream_ceiling(mode: int, src, dst, n_vectors: int, workgroups: int, stream=None) -> None:
     """Measurement helper (include/lla_stream.h): a plain streaming pass, mode 0 read-only,
     1 copy, 2 four reads per write, 3 four writes per read; 4-6 read-only with every wave
-    streaming its own chunk through direct-to-LDS loads (4), registers (5) or both (6)."""
+    streaming its own chunk through direct-to-LDS loads (4), registers (5) or both (6);
+    7 the narrow fold's latent-row pattern (per wave a key and a value row plane)."""
     st = load().lla_stream_ceiling(mode, _ptr(src), _ptr(dst), n_vectors, workgroups, _stream(stream))
     if st != 0:
         raise RuntimeError(f"lla_stream_ceiling failed: {st}")
